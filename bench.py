@@ -1,0 +1,387 @@
+"""Benchmark of the block-quantized decode hot path on one MI355X.
+
+Headline workload: Q4_K matvec, W[14336, 4096] (uniform[-1,1) quantized to
+Q4_K, 33,030,144 packed bytes), x[4096] ~ N(0,1). One step runs every row
+of the path that this workload has, on HBM-resident inputs:
+  qmv_q4k          f32 activation
+  quantize_act_q8  the activation to (xq, xs, xsum)
+  qmv_q4k_q8       int8 dot4 against the same weights
+value = packed weight bytes read by the two matvecs / step time (GB/s).
+Weights rotate over 32 device copies (1.06 GB) so every launch reads them
+from HBM, not from the 256 MB last-level cache (warm numbers, one copy, are
+reported beside).
+
+The other workloads are measured after the headline and reported under
+"others": Q8_0 4096x4096, Q6_K 128256x4096, the MoE layer (router + fused
+gate/up/SiLU + down + combine, 128 experts, top-8, T = 1/4/16 tokens, in
+tokens/s) and the m=512 Q4_K prefill GEMM on int8 MFMA (TOPS).
+
+Prints ONE JSON line. `--gpus N` with N > 1 is refused: this path runs on a
+single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_I8_PEAK_TOPS = 5000.0
+N2, K2 = 14336, 4096
+Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
+METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
+KERNEL_SOURCES = ["include/qmv.h", "moe_ggml_block_amd/csrc/common.hpp",
+                  "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/qmv_dense.hip"]
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def rotated(host_bytes, copies: int):
+    """`copies` device copies of one host buffer, each 256-byte aligned."""
+    import torch
+    one = torch.from_numpy(host_bytes.reshape(-1)).cuda()
+    nb = one.numel()
+    stride = (nb + 255) // 256 * 256
+    big = torch.empty(stride * copies, dtype=torch.uint8, device="cuda")
+    views = []
+    for i in range(copies):
+        v = big[i * stride:i * stride + nb]
+        v.copy_(one)
+        views.append(v)
+    del one
+    return big, views
+
+
+def capture(fn, calls: int):
+    """A HIP graph of fn(0) .. fn(calls-1) launched back to back on one stream.
+    Replaying it removes the host's per-launch cost from the timing."""
+    import torch
+    for i in range(min(calls, 3)):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(fn, calls: int, replays: int = 20) -> float:
+    """Average ms per fn call, over `replays` replays of a `calls`-call graph."""
+    import torch
+    g = capture(fn, calls)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) / (replays * calls)
+
+
+def traffic_from_profile(kernel_hash: str):
+    """HBM bytes per launch of qmv_q4k from the committed PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "qmv_q4k_14336x4096_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("kernel_source_hash") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds: float = 10.0):
+    """The oracle, as it stands, on the headline step: f64 Q4_K matvec plus the
+    f32 q8 quantizer and the f64 q8-activation matvec, full 14336x4096 shape,
+    repeated until `seconds` of CPU time have run. Single-threaded C."""
+    import oracle
+    import synth
+    w = synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2)
+    x = synth.normal(synth.SEED_X, K2)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.matvec("q4k", w, x, N2, K2)
+        xq, xs, _ = oracle.quantize_act_q8(x, 1, K2)
+        oracle.matvec_q8act("q4k", w, xq, xs, N2, K2)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(2 * Q4K_BYTES * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full oracle steps (Q4_K 14336x4096 f64 matvec + q8 quantize + f64 q8-activation "
+                      f"matvec) in {el:.1f} s on one host thread"}
+
+
+def headline(steps: int, warmup: int, copies: int):
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+
+    log(f"headline: generating Q4_K {N2}x{K2} and {copies} device copies")
+    w_host = synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2)
+    big, W = rotated(w_host, copies)
+    x = torch.from_numpy(synth.normal(synth.SEED_X, K2)).cuda()
+    y = torch.empty(N2, device="cuda")
+    y8 = torch.empty(N2, device="cuda")
+    xq = torch.empty(K2, dtype=torch.int8, device="cuda")
+    xs = torch.empty(K2 // 32, device="cuda")
+    xsum = torch.empty(K2 // 32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
+        qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum))
+        qmv.qmv_q4k_q8(W[(i + copies // 2) % copies], xq, xs, xsum, N2, K2, y=y8)
+
+    # one graph holds `copies` steps (every weight copy once per matvec);
+    # the timed region replays it until exactly `steps` steps have run.
+    full = capture(step, copies)
+    rem = steps % copies
+    tail = capture(step, rem) if rem else None
+    for _ in range(max(1, warmup // copies)):
+        full.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps // copies):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del full, tail
+
+    # the dominant kernel alone: 4 passes over the copies per graph, on the
+    # same stream, timed with events around the replays
+    q4k_ms = time_graph(lambda i: qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y), 4 * copies, 10)
+    k_f32 = q4k_ms
+    k_qa = time_graph(lambda i: qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum)), 128, 10)
+    k_q8 = time_graph(lambda i: qmv.qmv_q4k_q8(W[i % copies], xq, xs, xsum, N2, K2, y=y8), 4 * copies, 10)
+    k_f32_warm = time_graph(lambda i: qmv.qmv_q4k(W[0], x, N2, K2, y=y), 128, 10)
+    k_q8_warm = time_graph(lambda i: qmv.qmv_q4k_q8(W[0], xq, xs, xsum, N2, K2, y=y8), 128, 10)
+    del big, W
+    torch.cuda.empty_cache()
+    return {
+        "ms_per_step": ms,
+        "q4k_launch_ms": q4k_ms,
+        "kernels": {
+            "qmv_q4k_cold_us": round(k_f32 * 1e3, 3),
+            "qmv_q4k_cold_gbs": round(Q4K_BYTES / k_f32 / 1e6, 1),
+            "qmv_q4k_warm_gbs": round(Q4K_BYTES / k_f32_warm / 1e6, 1),
+            "quantize_act_q8_us": round(k_qa * 1e3, 3),
+            "qmv_q4k_q8_cold_us": round(k_q8 * 1e3, 3),
+            "qmv_q4k_q8_cold_gbs": round(Q4K_BYTES / k_q8 / 1e6, 1),
+            "qmv_q4k_q8_warm_gbs": round(Q4K_BYTES / k_q8_warm / 1e6, 1),
+        },
+    }
+
+
+def dense_other(fmt: str, n: int, k: int, copies: int):
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    f = {"q8_0": synth.FMT_Q8_0, "q6k": synth.FMT_Q6K}[fmt]
+    fn = {"q8_0": qmv.qmv_q8_0, "q6k": qmv.qmv_q6k}[fmt]
+    w_host = synth.weights(f, synth.SEED_W, n, k)
+    nbytes = w_host.nbytes
+    big, W = rotated(w_host, copies)
+    del w_host
+    x = torch.from_numpy(synth.normal(synth.SEED_X, k)).cuda()
+    y = torch.empty(n, device="cuda")
+    cold = time_graph(lambda i: fn(W[i % copies], x, n, k, y=y), max(4 * copies, 24), 10)
+    warm = time_graph(lambda i: fn(W[0], x, n, k, y=y), 64, 10)
+    del big, W
+    torch.cuda.empty_cache()
+    return {"shape": f"{n}x{k}", "packed_bytes": nbytes, "cold_us": round(cold * 1e3, 3),
+            "cold_gbs": round(nbytes / cold / 1e6, 1), "cold_hbm_pct": round(nbytes / cold / 1e6 / HBM_PEAK_GBS * 100, 1),
+            "warm_gbs": round(nbytes / warm / 1e6, 1), "weight_copies": copies}
+
+
+def moe_other(bank_copies: int = 3, logit_sets: int = 64):
+    import numpy as np
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    E, topk, hidden, inter = 128, 8, 2048, 768
+    log("moe: generating banks")
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, hidden, inter)
+    per_expert = (gate.nbytes + up.nbytes + down.nbytes) // E
+    bg, G = rotated(gate, bank_copies)
+    bu, U = rotated(up, bank_copies)
+    bd, D = rotated(down, bank_copies)
+    del gate, up, down
+    out = {}
+    for T in (1, 4, 16):
+        lg = [torch.from_numpy(synth.moe_logits(T, E, r)).cuda() for r in range(logit_sets)]
+        x = torch.from_numpy(synth.normal(synth.SEED_X, T * hidden)).cuda()
+        ids = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+        wts = torch.empty((T, topk), device="cuda")
+        y = torch.empty((T, hidden), device="cuda")
+        ws = torch.empty(qmv.moe_ffn_workspace_bytes(T, topk, hidden, inter), dtype=torch.uint8, device="cuda")
+
+        def layer(i):
+            b = i % bank_copies
+            qmv.moe_route(lg[i % logit_sets], T, E, topk, out=(ids, wts))
+            qmv.moe_ffn_q4k_q6k(G[b], U[b], D[b], x, ids, wts, T, topk, hidden, inter, E, y=y, ws=ws)
+
+        ms = time_graph(layer, 2 * logit_sets, 5)
+        # unique experts actually routed, averaged over the logit sets
+        uniq = []
+        for r in range(logit_sets):
+            i_, _ = qmv.moe_route(lg[r], T, E, topk)
+            uniq.append(len(np.unique(i_.cpu().numpy())))
+        u = float(np.mean(uniq))
+        out[f"T{T}"] = {"tokens_per_s": round(T / (ms * 1e-3), 1), "layer_us": round(ms * 1e3, 3),
+                        "unique_experts": u, "gbs_unique_experts": round(u * per_expert / (ms * 1e-3) / 1e9, 1)}
+    del bg, bu, bd, G, U, D
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_other(copies: int = 16):
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    m, n, k = 512, 4096, 4096
+    w_host = synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k)
+    big, W = rotated(w_host, copies)
+    x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, m * k)).cuda()
+    xq, xs, xsum = qmv.quantize_act_q8(x, m, k)
+    res = {}
+    for bm in (128, 256):
+        y = torch.empty((m, n), device="cuda")
+        ms = time_graph(lambda i: qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y), 2 * copies, 5)
+        tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        res[f"bm{bm}"] = {"us": round(ms * 1e3, 2), "tops": round(tops, 2),
+                          "mfma_i8_pct": round(tops / MFMA_I8_PEAK_TOPS * 100, 2)}
+    qa = time_graph(lambda i: qmv.quantize_act_q8(x, m, k, out=(xq, xs, xsum)), 32, 5)
+    res["quantize_act_q8_us"] = round(qa * 1e3, 2)
+    del big, W
+    torch.cuda.empty_cache()
+    return res
+
+
+def profile_run(copies: int):
+    """Short eager run for rocprofv3: 64 launches each of qmv_q4k and
+    qmv_q4k_q8 over the rotating weight copies, 64 quantize_act_q8 calls, and
+    8 plain device-to-device copies of 64 MiB (a copy kernel of known traffic
+    that calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    w_host = synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2)
+    big, W = rotated(w_host, copies)
+    x = torch.from_numpy(synth.normal(synth.SEED_X, K2)).cuda()
+    y = torch.empty(N2, device="cuda")
+    xq, xs, xsum = qmv.quantize_act_q8(x, 1, K2)
+    for i in range(64):
+        qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
+    for i in range(64):
+        qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum))
+    for i in range(64):
+        qmv.qmv_q4k_q8(W[i % copies], xq, xs, xsum, N2, K2, y=y)
+    a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(8):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, copy 64MiB x8",
+                      "q4k_bytes": Q4K_BYTES, "copy_bytes": 64 << 20}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--profile", action="store_true", help="short eager run for rocprofv3")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--copies", type=int, default=32)
+    ap.add_argument("--no-others", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this decode path runs on one GPU; --gpus must be 1 "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import moe_ggml_block_amd as qmv  # noqa: F401  (fails loudly without libqmv.so)
+
+    if a.profile:
+        profile_run(a.copies)
+        return
+    khash = source_hash(KERNEL_SOURCES)
+    h = headline(a.steps, a.warmup, a.copies)
+    log(f"headline done: {h['ms_per_step'] * 1e3:.2f} us/step")
+    value = 2 * Q4K_BYTES / (h["ms_per_step"] * 1e-3) / 1e9
+    q4k_us = h["q4k_launch_ms"] * 1e3
+    achieved = Q4K_BYTES / (h["q4k_launch_ms"] * 1e-3) / 1e9
+    traffic = traffic_from_profile(khash)
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(h["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Q4_K matvec 14336x4096, batch 1: f32-activation matvec + q8 activation "
+                               "quantize + int8-dot4 matvec per step",
+                   "n": N2, "k": K2, "weight_copies": a.copies, "cache": "cold (rotating copies)"},
+        "hbm_pct": round(value / HBM_PEAK_GBS * 100, 2),
+        "roofline": {"kernel": "qmv_q4k", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": Q4K_BYTES, "avg_launch_us": round(q4k_us, 3),
+                     "kernel_source_hash": khash},
+        "kernels": h["kernels"],
+    }
+    if not a.no_others:
+        others = {}
+        log("others: q8_0")
+        others["q8_0_4096x4096"] = dense_other("q8_0", 4096, 4096, 64)
+        log("others: q6k")
+        others["q6k_128256x4096"] = dense_other("q6k", 128256, 4096, 3)
+        log("others: moe")
+        others["moe_layer"] = moe_other()
+        log("others: prefill")
+        others["prefill_q4k_512x4096x4096"] = prefill_other()
+        res["others"] = others
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * qmv -- GGML block-quantized matrix-vector products and the indexed-MoE
+ * decode path, as hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * C ABI. Every entry point:
+ *  - takes device pointers owned by the caller (the library never allocates
+ *    or frees device memory) and a HIP stream (NULL = the null stream);
+ *  - validates shapes and pointer alignment on the host and returns a
+ *    negative qmv_status before launching anything if they are wrong;
+ *  - otherwise enqueues its kernels asynchronously on `stream` and returns
+ *    QMV_OK, or QMV_ELAUNCH if the HIP runtime rejected a launch;
+ *  - fully overwrites its outputs (nothing is accumulated into them);
+ *  - is stateless and may be called from several host threads.
+ *
+ * Weight blocks are the raw GGML/GGUF bytes, verbatim, row-major: row r of a
+ * [n, k] matrix occupies bytes [r*(k/B)*S, (r+1)*(k/B)*S) where B is the
+ * block's weight count and S its byte size. An expert bank [E, n, k] is the
+ * E matrices back to back (expert e starts at byte e*n*(k/B)*S).
+ *
+ *   Q8_0  B = 32,  S = 34:  f16 d, int8 q[32];        w = d*q
+ *   Q4_K  B = 256, S = 144: f16 d, f16 dmin, 12 bytes of 6-bit scales and
+ *                           mins for 8 sub-blocks of 32, 128 bytes of 4-bit
+ *                           codes;                    w = d*sc_j*q - dmin*m_j
+ *   Q6_K  B = 256, S = 210: ql[128] low nibbles, qh[64] 2-bit highs,
+ *                           int8 sc[16], f16 d;       w = d*sc_t*(q - 32)
+ *
+ * Field order and sizes: hanzo-ml `src/vulkan_backend.rs`, functions
+ * `quantize_q8_blocks` (Q8_0), `quantize_q4k` / `quantize_q4k_split` (Q4_K),
+ * `quantize_q6k` / `quantize_q6k_split` (Q6_K). Bit packing inside the
+ * fields: the public GGML k-quant packing.
+ *
+ * Alignment: weight pointers 16-byte aligned; f32 activation pointers
+ * 16-byte aligned; int8 activation pointers 16-byte aligned; other outputs
+ * 4-byte aligned (QMV_EALIGN otherwise). Buffers allocated by hipMalloc or
+ * PyTorch meet this.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; declared here so that callers need no HIP headers. */
+typedef struct ihipStream_t *qmv_stream_t;
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_EINVAL = -1,      /* bad shape: k not a block multiple, n/m <= 0, topk out of [1,E], null pointer, workspace too small */
+    QMV_EALIGN = -2,      /* a pointer does not meet the alignment above */
+    QMV_ELAUNCH = -3,     /* hipGetLastError reported a failure after a launch */
+    QMV_EUNSUPPORTED = -4 /* valid but outside what this build implements (e.g. E > 4096) */
+} qmv_status;
+
+/* Library version string, and a static message for a status code. */
+const char *qmv_version(void);
+const char *qmv_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * Dense decode matvecs, f32 activation: y[r] = sum_c W_deq[r, c] * x[c].
+ * w: n*(k/B)*S bytes; x: f32[k]; y: f32[n]. Accumulation in f32.
+ * Defined by `matvec_q8_0_gpu`, `matvec_q4k_gpu_off`, `matvec_q6k_gpu_off`
+ * (y[nout] = Wq * x[k] over blocks read verbatim, no requantization).
+ * k % 32 == 0 (Q8_0) or k % 256 == 0 (Q4_K, Q6_K); n >= 1.
+ * ---------------------------------------------------------------------- */
+int qmv_q8_0(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+int qmv_q4k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+int qmv_q6k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * q8 activation quantizer (`quantize_act_q8`: xq int8, xs f32 scale, xsum
+ * f32 dequantized block sum, per 32 consecutive values of each row).
+ * x: f32[m, k]; xq: int8[m, k]; xs, xsum: f32[m, k/32]. Per block:
+ *   amax = max|x|; inv = 127/amax, xs = amax/127 (inv = 0, xs = 1 if amax = 0);
+ *   xq = clamp(round_half_away(x*inv), -127, 127); xsum = xs * sum(xq).
+ * Every f32 step is a single correctly rounded IEEE operation, so the result
+ * is bit-identical to any IEEE f32 implementation of the same steps.
+ * k % 32 == 0; m >= 1.
+ * ---------------------------------------------------------------------- */
+int quantize_act_q8(const float *x, int8_t *xq, float *xs, float *xsum, int64_t m, int64_t k,
+                    qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Q4_K matvec against a q8 activation (the int8-dot decode path of
+ * `matvec_q4k_gpu_off` / `matvec_q4k_dp4a_blk`):
+ *   y[r] = sum_b ( d*sc_j*xs[b]*S[r,b] - dmin*m_j*xsum[b] ),
+ *   S[r,b] = sum_{i<32} q[r, 32b+i] * xq[32b+i]  (exact int32 dot4 sums),
+ * which equals W_deq . (xs*xq) up to f32 rounding.
+ * w: n*(k/256)*144 bytes; xq: int8[k]; xs, xsum: f32[k/32]; y: f32[n].
+ * ---------------------------------------------------------------------- */
+int qmv_q4k_q8(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
+               int64_t n, int64_t k, qmv_stream_t stream);
+
+/* Debug export of the integer part of qmv_q4k_q8: sums[r, b] = S[r, b]
+ * (int32[n, k/32]) computed by the same dot4 sequence as qmv_q4k_q8. */
+int qmv_debug_blocksums_q4k_q8(const void *w, const int8_t *xq, int32_t *sums, int64_t n,
+                               int64_t k, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MoE router (`moe_route_vk`: softmax + top-k + renormalize in one kernel).
+ * logits: f32[T, E]; ids: int32[T, topk]; wts: f32[T, topk].
+ * Per token the topk largest logits are selected (equal values: lower
+ * expert index first; NaN ranks below every number), ids are written in
+ * descending-logit order and wts[j] = exp(l_j - l_max) / sum over the
+ * selected of exp(l - l_max) (the softmax denominator cancels). If every
+ * selected logit is -inf/NaN the weights are 1/topk.
+ * 1 <= topk <= min(E, 64); 1 <= E <= 4096; T >= 1.
+ * ---------------------------------------------------------------------- */
+int moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t E, int64_t topk,
+              qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-gather matvec over a resident bank (`moe_matvec_gpu`):
+ *   y[s, r] = sum_c W[ids[s], r, c] * x[s / x_div, c],  s < nslots, r < n.
+ * bank: E*n*(k/B)*S bytes; x: f32[nslots/x_div rounded up, k];
+ * ids: int32[nslots]; y: f32[nslots, n] in slot order.
+ * Slots routed to the same expert share one read of that expert's rows.
+ * A slot whose id is outside [0, E) gets a zero output row.
+ * x_div >= 1 (gate/up of a routed token: x_div = topk; down: x_div = 1).
+ * ---------------------------------------------------------------------- */
+int moe_qmv_q4k(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
+                int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+int moe_qmv_q6k(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
+                int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MoE FFN layer over routed slots s = topk*t + j, e = ids[s]
+ * (the engine composition of `moe_matvec_*` gate/up, `silu_mul`, down and
+ * the `broadcast_mul(scores).sum` combine):
+ *   h_s = silu(W_gate[e] x_t) * (W_up[e] x_t)   gate/up: Q4_K [E, inter, hidden]
+ *   d_s = W_down[e] h_s                          down:    Q6_K [E, hidden, inter]
+ *   y_t = sum_j wts[t, j] * d_{topk*t + j}       (fixed j order)
+ * x: f32[T, hidden]; ids: int32[T, topk]; wts: f32[T, topk]; y: f32[T, hidden].
+ * ws: caller-owned device workspace of at least moe_ffn_workspace_bytes()
+ * bytes (16-byte aligned); its contents on return are unspecified.
+ * hidden % 256 == 0, inter % 256 == 0.
+ * ---------------------------------------------------------------------- */
+int64_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter);
+int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
+                    const int32_t *ids, const float *wts, float *y, void *ws, int64_t ws_bytes,
+                    int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
+                    qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Q4_K prefill GEMM on int8 MFMA (`mmq_q4k_rt_gpu`: affine Q4_K x q8
+ * activation, epilogue xs*(D*dot - M*xsum)):
+ *   Y[i, r] = sum_b ( xs[i,b]*d_r*sc_rj*S[i,r,b] - xsum[i,b]*dmin_r*m_rj ),
+ *   S[i,r,b] = sum_{l<32} xq[i, 32b+l] * q[r, 32b+l]  (int32, exact),
+ * w: n*(k/256)*144 bytes; xq: int8[m, k]; xs, xsum: f32[m, k/32];
+ * Y: f32[m, n]. bm = rows of Y per workgroup tile, 128 or 256.
+ * k % 256 == 0; m, n >= 1 (ragged tiles are masked).
+ * ---------------------------------------------------------------------- */
+int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
+            int64_t m, int64_t n, int64_t k, int bm, qmv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

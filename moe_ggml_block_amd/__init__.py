@@ -1,0 +1,200 @@
+"""Python binding of libqmv.so (include/qmv.h): argument marshalling only.
+
+Every function takes torch tensors that already live on a ROCm device,
+passes their raw pointers and sizes to the C ABI on the current HIP stream
+(or the one given) and raises QmvError on a non-zero status. All arithmetic
+runs in the gfx950 kernels of libqmv.so; there is no fallback of any kind:
+if the library cannot be loaded, importing this package raises.
+
+torch is imported first so that the HIP runtime it ships (soname
+libamdhip64.so.7) is the one libqmv.so binds to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime libqmv.so links against)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m moe_ggml_block_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_SIGS = {
+    "qmv_q8_0": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q4k": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q6k": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "quantize_act_q8": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q4k_q8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_debug_blocksums_q4k_q8": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "moe_route": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "moe_qmv_q4k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_qmv_q6k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
+    "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _i32
+_lib.moe_ffn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.moe_ffn_workspace_bytes.restype = _i64
+_lib.qmv_version.restype = ctypes.c_char_p
+_lib.qmv_strerror.argtypes = [_i32]
+_lib.qmv_strerror.restype = ctypes.c_char_p
+
+EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "qmv_version", "qmv_strerror")
+
+BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210)}
+
+
+class QmvError(RuntimeError):
+    pass
+
+
+def version() -> str:
+    return _lib.qmv_version().decode()
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise QmvError(f"{name}: status {rc} ({_lib.qmv_strerror(rc).decode()})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def row_bytes(fmt: str, k: int) -> int:
+    bw, bb = BLOCK[fmt]
+    return k // bw * bb
+
+
+def _need(t, numel_bytes, name):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < numel_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {numel_bytes}")
+
+
+# ----------------------------------------------------------------- matvecs
+def _dense(name, fmt, w, x, n, k, y=None, stream=None):
+    _need(w, n * row_bytes(fmt, k), "w")
+    _need(x, 4 * k, "x")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _need(y, 4 * n, "y")
+    _check(getattr(_lib, name)(_p(w), _p(x), _p(y), n, k, _stream(stream)), name)
+    return y
+
+
+def qmv_q8_0(w, x, n, k, y=None, stream=None):
+    return _dense("qmv_q8_0", "q8_0", w, x, n, k, y, stream)
+
+
+def qmv_q4k(w, x, n, k, y=None, stream=None):
+    return _dense("qmv_q4k", "q4k", w, x, n, k, y, stream)
+
+
+def qmv_q6k(w, x, n, k, y=None, stream=None):
+    return _dense("qmv_q6k", "q6k", w, x, n, k, y, stream)
+
+
+def quantize_act_q8(x, m, k, out=None, stream=None):
+    _need(x, 4 * m * k, "x")
+    if out is None:
+        out = (torch.empty((m, k), dtype=torch.int8, device=x.device),
+               torch.empty((m, k // 32), dtype=torch.float32, device=x.device),
+               torch.empty((m, k // 32), dtype=torch.float32, device=x.device))
+    xq, xs, xsum = out
+    _check(_lib.quantize_act_q8(_p(x), _p(xq), _p(xs), _p(xsum), m, k, _stream(stream)), "quantize_act_q8")
+    return xq, xs, xsum
+
+
+def qmv_q4k_q8(w, xq, xs, xsum, n, k, y=None, stream=None):
+    _need(w, n * row_bytes("q4k", k), "w")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=xq.device)
+    _check(_lib.qmv_q4k_q8(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), n, k, _stream(stream)), "qmv_q4k_q8")
+    return y
+
+
+def qmv_debug_blocksums_q4k_q8(w, xq, n, k, stream=None):
+    sums = torch.empty((n, k // 32), dtype=torch.int32, device=xq.device)
+    _check(_lib.qmv_debug_blocksums_q4k_q8(_p(w), _p(xq), _p(sums), n, k, _stream(stream)),
+           "qmv_debug_blocksums_q4k_q8")
+    return sums
+
+
+# --------------------------------------------------------------------- MoE
+def moe_route(logits, T, E, topk, out=None, stream=None):
+    _need(logits, 4 * T * E, "logits")
+    if out is None:
+        out = (torch.empty((T, topk), dtype=torch.int32, device=logits.device),
+               torch.empty((T, topk), dtype=torch.float32, device=logits.device))
+    ids, wts = out
+    _check(_lib.moe_route(_p(logits), _p(ids), _p(wts), T, E, topk, _stream(stream)), "moe_route")
+    return ids, wts
+
+
+def _moe(name, fmt, bank, x, x_div, ids, nslots, n, k, E, y, stream):
+    _need(bank, E * n * row_bytes(fmt, k), "bank")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=x.device)
+    _check(getattr(_lib, name)(_p(bank), _p(x), x_div, _p(ids), _p(y), nslots, n, k, E, _stream(stream)), name)
+    return y
+
+
+def moe_qmv_q4k(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    return _moe("moe_qmv_q4k", "q4k", bank, x, x_div, ids, nslots, n, k, E, y, stream)
+
+
+def moe_qmv_q6k(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    return _moe("moe_qmv_q6k", "q6k", bank, x, x_div, ids, nslots, n, k, E, y, stream)
+
+
+def moe_ffn_workspace_bytes(T, topk, hidden, inter) -> int:
+    return int(_lib.moe_ffn_workspace_bytes(T, topk, hidden, inter))
+
+
+def moe_ffn_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=None, ws=None, stream=None):
+    nb = moe_ffn_workspace_bytes(T, topk, hidden, inter)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _check(_lib.moe_ffn_q4k_q6k(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), _p(ws),
+                                ws.numel() * ws.element_size(), T, topk, hidden, inter, E, _stream(stream)),
+           "moe_ffn_q4k_q6k")
+    return y
+
+
+# ----------------------------------------------------------------- prefill
+def qmm_q4k(w, xq, xs, xsum, m, n, k, bm=128, y=None, stream=None):
+    _need(w, n * row_bytes("q4k", k), "w")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(_lib.qmm_q4k(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), m, n, k, bm, _stream(stream)), "qmm_q4k")
+    return y
+
+
+def raw(name):
+    """The raw ctypes function of an export (for tests of the C ABI itself)."""
+    return getattr(_lib, name)

@@ -1,0 +1,79 @@
+"""The C ABI on the CPU: libqmv.so loads, exports every function include/qmv.h
+declares, and rejects bad arguments on the host before any launch. No call
+here reaches a kernel (each one fails validation first), so no GPU is used.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+LIB = os.path.join(ROOT, "moe_ggml_block_amd", "libqmv.so")
+
+QMV_EINVAL, QMV_EALIGN = -1, -2
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import moe_ggml_block_amd.build as b
+        b.build()
+    import torch  # noqa: F401  (same HIP runtime the binding uses)
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for n in ("qmv_q8_0", "qmv_q4k", "qmv_q6k", "quantize_act_q8", "qmv_q4k_q8", "moe_route",
+              "moe_qmv_q4k", "moe_qmv_q6k", "moe_ffn_q4k_q6k", "qmm_q4k"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_binding_exports_match_header():
+    import moe_ggml_block_amd as qmv
+    assert sorted(qmv.EXPORTS) == _declared()
+
+
+def test_host_validation_returns_before_launch(lib):
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.qmv_q4k.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.qmv_q4k.restype = i32
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10001)
+    assert lib.qmv_q4k(None, fake, fake, 4, 256, None) == QMV_EINVAL
+    assert lib.qmv_q4k(fake, fake, fake, 4, 300, None) == QMV_EINVAL
+    assert lib.qmv_q4k(fake, fake, fake, 0, 256, None) == QMV_EINVAL
+    assert lib.qmv_q4k(odd, fake, fake, 4, 256, None) == QMV_EALIGN
+    lib.qmv_q8_0.argtypes = lib.qmv_q4k.argtypes
+    lib.qmv_q8_0.restype = i32
+    assert lib.qmv_q8_0(fake, fake, fake, 4, 48, None) == QMV_EINVAL
+    lib.moe_route.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.moe_route.restype = i32
+    assert lib.moe_route(fake, fake, fake, 2, 8, 9, None) == QMV_EINVAL   # topk > E
+    assert lib.moe_route(fake, fake, fake, 2, 128, 0, None) == QMV_EINVAL
+    lib.qmm_q4k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.qmm_q4k.restype = i32
+    assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 64, None) == QMV_EINVAL  # bm
+    lib.moe_ffn_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.moe_ffn_workspace_bytes.restype = i64
+    assert lib.moe_ffn_workspace_bytes(16, 8, 2048, 768) == 16 * 8 * (2048 + 768) * 4
+    lib.moe_ffn_q4k_q6k.argtypes = [vp] * 8 + [i64] * 6 + [vp]
+    lib.moe_ffn_q4k_q6k.restype = i32
+    assert lib.moe_ffn_q4k_q6k(fake, fake, fake, fake, fake, fake, fake, fake, 100, 16, 8, 2048, 768, 128,
+                               None) == QMV_EINVAL  # workspace too small
+    lib.qmv_strerror.restype = ctypes.c_char_p
+    assert b"alignment" in lib.qmv_strerror(QMV_EALIGN)

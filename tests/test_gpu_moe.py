@@ -1,0 +1,198 @@
+"""GPU parity: router, expert-gather matvecs, the fused MoE FFN layer, and the
+int8-MFMA prefill GEMM, against the CPU oracle on the same seeded inputs.
+
+Router ids: bit-exact. Everything f32: scale-relative error <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_ggml_block_amd as qmv
+import oracle
+import synth
+from gpu_util import TOL, announce, dev, host, scalerel
+
+pytestmark = pytest.mark.gpu
+
+E, TOPK, HIDDEN, INTER = 128, 8, 2048, 768
+
+
+# ------------------------------------------------------------------ router
+@pytest.mark.parametrize("T,E_,topk", [(1, 128, 8), (4, 128, 8), (16, 128, 8), (33, 128, 8),
+                                       (5, 8, 2), (3, 64, 64), (7, 200, 5), (2, 4096, 16), (9, 1, 1)])
+def test_route_matches_oracle(T, E_, topk):
+    announce(f"route T={T} E={E_} topk={topk}")
+    lg = synth.normal(synth.SEED_LOGITS, T * E_).reshape(T, E_)
+    ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+    ids, w = qmv.moe_route(dev(lg), T, E_, topk)
+    assert np.array_equal(host(ids), ids_ref)
+    assert scalerel(w_ref, host(w)) <= TOL
+
+
+def test_route_ties_nan_and_inf():
+    T, E_, topk = 6, 128, 8
+    lg = np.round(synth.normal(7, T * E_).reshape(T, E_) * 2).astype(np.float32)  # many ties
+    lg[1, :] = 0.0
+    lg[2, ::3] = np.nan
+    lg[3, :] = -np.inf
+    lg[4, :] = np.nan
+    lg[4, 100] = 1.0
+    lg[5, 7] = np.inf
+    announce("route ties/nan/inf")
+    ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+    ids, w = qmv.moe_route(dev(lg), T, E_, topk)
+    assert np.array_equal(host(ids), ids_ref)
+    gw = host(w)
+    assert np.array_equal(np.isnan(gw), np.isnan(w_ref))
+    ok = ~np.isnan(w_ref)
+    assert np.abs(gw[ok] - w_ref[ok]).max() <= TOL
+
+
+# --------------------------------------------------------- gather matvecs
+def _ids(T, topk, E_, seed=0):
+    # the pages' synthetic routing: slot i -> (i*7 + 3) mod E
+    return np.array([(i * 7 + 3 + seed) % E_ for i in range(T * topk)], dtype=np.int32)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("E_,n,k,nslots,x_div", [(8, 256, 256, 4, 2), (16, 512, 256, 12, 4),
+                                                 (4, 768, 512, 2, 1), (128, 768, 2048, 8, 8),
+                                                 (128, 2048, 768, 16, 1), (5, 100, 1024, 9, 3)])
+def test_moe_qmv_matches_oracle(fmt, E_, n, k, nslots, x_div):
+    announce(f"moe_qmv {fmt} E={E_} n={n} k={k} nslots={nslots}")
+    f = synth.FMT_Q4K if fmt == "q4k" else synth.FMT_Q6K
+    bank = synth.moe_bank(f, 30, E_, n, k)
+    rows = (nslots + x_div - 1) // x_div
+    x = synth.normal(31, rows * k).reshape(rows, k)
+    ids = _ids(nslots, 1, E_)
+    ids[nslots // 2] = ids[0]  # repeated expert
+    ref = oracle.moe_qmv(fmt, bank, x, x_div, ids, nslots, n, k, E_)
+    fn = qmv.moe_qmv_q4k if fmt == "q4k" else qmv.moe_qmv_q6k
+    got = host(fn(dev(bank), dev(x), x_div, dev(ids), nslots, n, k, E_))
+    assert scalerel(ref, got) <= TOL
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_moe_qmv_invalid_ids_zero_rows(fmt):
+    E_, n, k, nslots = 6, 64, 512, 7
+    f = synth.FMT_Q4K if fmt == "q4k" else synth.FMT_Q6K
+    bank = synth.moe_bank(f, 32, E_, n, k)
+    x = synth.normal(33, nslots * k).reshape(nslots, k)
+    ids = np.array([2, -1, 5, 6, 2, 100, 0], dtype=np.int32)
+    announce(f"moe_qmv invalid ids {fmt}")
+    ref = oracle.moe_qmv(fmt, bank, x, 1, ids, nslots, n, k, E_)
+    fn = qmv.moe_qmv_q4k if fmt == "q4k" else qmv.moe_qmv_q6k
+    y = torch.full((nslots, n), float("nan"), device="cuda")
+    fn(dev(bank), dev(x), 1, dev(ids), nslots, n, k, E_, y=y)
+    got = host(y)
+    assert not np.isnan(got).any()
+    assert np.all(got[[1, 3, 5]] == 0.0)
+    assert scalerel(ref, got) <= TOL
+
+
+def test_moe_qmv_all_slots_one_expert():
+    E_, n, k, nslots = 4, 300, 2048, 16
+    bank = synth.moe_bank(synth.FMT_Q4K, 34, E_, n, k)
+    x = synth.normal(35, nslots * k).reshape(nslots, k)
+    ids = np.full(nslots, 3, dtype=np.int32)
+    announce("moe_qmv one expert")
+    ref = oracle.moe_qmv("q4k", bank, x, 1, ids, nslots, n, k, E_)
+    got = host(qmv.moe_qmv_q4k(dev(bank), dev(x), 1, dev(ids), nslots, n, k, E_))
+    assert scalerel(ref, got) <= TOL
+
+
+# ---------------------------------------------------------------- FFN layer
+_BANKS = {}
+
+
+def _banks():
+    if not _BANKS:
+        _BANKS["gate"] = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, INTER, HIDDEN)
+        _BANKS["up"] = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, INTER, HIDDEN)
+        _BANKS["down"] = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, HIDDEN, INTER)
+        _BANKS["dev"] = {k: dev(v) for k, v in list(_BANKS.items())}
+    return _BANKS
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_moe_layer_full_config(T):
+    """Router + fused FFN at the full MoE shape (128 experts, top-8, gate/up
+    Q4_K [768, 2048], down Q6_K [2048, 768])."""
+    announce(f"moe layer T={T}")
+    b = _banks()
+    lg = synth.moe_logits(T, E)
+    x = synth.normal(synth.SEED_X, T * HIDDEN).reshape(T, HIDDEN)
+    ids_ref, w_ref = oracle.moe_route(lg, T, E, TOPK)
+    y_ref, h_ref, _ = oracle.moe_ffn(b["gate"], b["up"], b["down"], x, ids_ref, w_ref.astype(np.float32),
+                                     T, TOPK, HIDDEN, INTER, E)
+    d = b["dev"]
+    ids, w = qmv.moe_route(dev(lg), T, E, TOPK)
+    assert np.array_equal(host(ids), ids_ref)
+    y = qmv.moe_ffn_q4k_q6k(d["gate"], d["up"], d["down"], dev(x), ids, w, T, TOPK, HIDDEN, INTER, E)
+    assert scalerel(y_ref, host(y)) <= TOL, scalerel(y_ref, host(y))
+    # the fused gate/up + SiLU stage on its own
+    h = qmv.moe_qmv_q4k(d["gate"], dev(x), TOPK, ids, T * TOPK, INTER, HIDDEN, E)
+    g_ref = oracle.moe_qmv("q4k", b["gate"], x, TOPK, ids_ref.reshape(-1), T * TOPK, INTER, HIDDEN, E)
+    assert scalerel(g_ref, host(h)) <= TOL
+
+
+def test_moe_layer_repeated_and_invalid_ids():
+    T = 4
+    b = _banks()
+    x = synth.normal(40, T * HIDDEN).reshape(T, HIDDEN)
+    ids = np.array([[5, 9, 5, 1, 2, 3, 4, 6], [5, 5, 5, 5, 5, 5, 5, 5],
+                    [127, 0, -3, 64, 65, 66, 67, 68], [1, 2, 3, 4, 5, 6, 7, 8]], dtype=np.int32)
+    wts = synth.uniform(41, T * TOPK).reshape(T, TOPK) * 0.5 + 0.5
+    announce("moe layer repeated/invalid ids")
+    y_ref, _, _ = oracle.moe_ffn(b["gate"], b["up"], b["down"], x, ids, wts, T, TOPK, HIDDEN, INTER, E)
+    d = b["dev"]
+    y = qmv.moe_ffn_q4k_q6k(d["gate"], d["up"], d["down"], dev(x), dev(ids), dev(wts), T, TOPK, HIDDEN, INTER, E)
+    assert scalerel(y_ref, host(y)) <= TOL
+
+
+def test_moe_layer_small_shapes():
+    for E_, T, topk, hidden, inter in [(1, 1, 1, 256, 256), (6, 3, 2, 512, 256), (33, 5, 4, 1024, 512)]:
+        announce(f"moe layer small E={E_} T={T} topk={topk} hidden={hidden} inter={inter}")
+        gate = synth.moe_bank(synth.FMT_Q4K, 50, E_, inter, hidden)
+        up = synth.moe_bank(synth.FMT_Q4K, 51, E_, inter, hidden)
+        down = synth.moe_bank(synth.FMT_Q6K, 52, E_, hidden, inter)
+        x = synth.normal(53, T * hidden).reshape(T, hidden)
+        lg = synth.normal(54, T * E_).reshape(T, E_)
+        ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+        y_ref, _, _ = oracle.moe_ffn(gate, up, down, x, ids_ref, w_ref.astype(np.float32), T, topk, hidden, inter, E_)
+        ids, w = qmv.moe_route(dev(lg), T, E_, topk)
+        y = qmv.moe_ffn_q4k_q6k(dev(gate), dev(up), dev(down), dev(x), ids, w, T, topk, hidden, inter, E_)
+        assert scalerel(y_ref, host(y)) <= TOL
+
+
+# ------------------------------------------------------------------ prefill
+@pytest.mark.parametrize("m,n,k,bm", [(1, 32, 256, 128), (40, 70, 512, 128), (130, 96, 1024, 256),
+                                      (257, 33, 2048, 256), (128, 64, 4096, 128)])
+def test_qmm_small_shapes(m, n, k, bm):
+    announce(f"qmm m={m} n={n} k={k} bm={bm}")
+    w = synth.weights(synth.FMT_Q4K, 60, n, k)
+    x = synth.normal(61, m * k).reshape(m, k)
+    xq, xs, xsum = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q4k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q4k(dev(w), dev(xq), dev(xs), dev(xsum), m, n, k, bm=bm))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+@pytest.mark.parametrize("bm", [128, 256])
+def test_qmm_full_config_sampled_rows(bm):
+    """m=512 tokens x W[4096, 4096]: every output column of 24 sampled rows
+    (first/last tiles and interior) against the oracle."""
+    m = n = k = 4096
+    m = 512
+    announce(f"qmm full bm={bm}")
+    w = synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k)
+    x = synth.normal(synth.SEED_PREFILL_X, m * k).reshape(m, k)
+    xq, xs, xsum = qmv.quantize_act_q8(dev(x), m, k)
+    rq, rs, _ = oracle.quantize_act_q8(x, m, k)
+    assert np.array_equal(host(xq), rq)
+    Y = host(qmv.qmm_q4k(dev(w), xq, xs, xsum, m, n, k, bm=bm))
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 128, 129, 200, 255, 256, 300, 383, 384, 400, 450,
+                     479, 480, 495, 500, 509, 510, 511])
+    ref = oracle.qmm("q4k", w, rq, rs, m, n, k, mrows=rows)
+    assert scalerel(ref, Y[rows]) <= TOL, scalerel(ref, Y[rows])
+    assert np.isfinite(Y).all()
