@@ -290,7 +290,7 @@ def prefill_other(copies: int = 16):
     return res
 
 
-def profile_run(copies: int):
+def profile_run(copies: int, other_shapes: bool = False):
     """Short eager run for rocprofv3: 64 launches each of qmv_q4k and
     qmv_q4k_q8 over the rotating weight copies, 64 quantize_act_q8 calls, and
     8 plain device-to-device copies of 64 MiB (a copy kernel of known traffic
@@ -314,14 +314,25 @@ def profile_run(copies: int):
     a.fill_(1)
     for _ in range(8):
         b.copy_(a)
+    del big, W
+    if other_shapes:
+        for fmt, fn, n, k, reps in (("q8_0", qmv.qmv_q8_0, 4096, 4096, 32), ("q6k", qmv.qmv_q6k, 128256, 4096, 8)):
+            f = {"q8_0": synth.FMT_Q8_0, "q6k": synth.FMT_Q6K}[fmt]
+            bigo, Wo = rotated(synth.weights(f, synth.SEED_W, n, k), 3)
+            yo = torch.empty(n, device="cuda")
+            for i in range(reps):
+                fn(Wo[i % 3], x, n, k, y=yo)
+            del bigo, Wo
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, copy 64MiB x8",
+    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, copy 64MiB x8"
+                      + (", qmv_q8_0 4096x4096 x32, qmv_q6k 128256x4096 x8" if other_shapes else ""),
                       "q4k_bytes": Q4K_BYTES, "copy_bytes": 64 << 20}))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--profile", action="store_true", help="short eager run for rocprofv3")
+    ap.add_argument("--profile-all", action="store_true", help="--profile plus the Q8_0 and Q6_K shapes")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
@@ -341,8 +352,8 @@ def main():
         sys.exit(1)
     import moe_ggml_block_amd as qmv  # noqa: F401  (fails loudly without libqmv.so)
 
-    if a.profile:
-        profile_run(a.copies)
+    if a.profile or a.profile_all:
+        profile_run(a.copies, a.profile_all)
         return
     khash = source_hash(KERNEL_SOURCES)
     h = headline(a.steps, a.warmup, a.copies)

@@ -1,18 +1,21 @@
 // Per-lane block decoders for the raw GGML layouts (gfx950).
 //
-// A row of a weight matrix is cut into "units" that one lane decodes and
-// dots against activation values it keeps in registers:
-//   Q8_0: a unit is a pair of consecutive 34-byte blocks (68 bytes, dword
-//         aligned when k % 64 == 0), 64 weights.
-//   Q4_K: a unit is one 16-byte run of the 128 code bytes of a superblock
-//         (chunk c = 0..7), i.e. 16 weights of sub-block 2*(c/2) (low
-//         nibbles) and 16 of sub-block 2*(c/2)+1 (high nibbles), plus the
-//         superblock's 16-byte header (d, dmin, packed scales).
-//   Q6_K: a unit is (half h, quarter lq) of a superblock: for each of the
-//         four 32-weight groups g of half h the 8 weights l = 8*lq..8*lq+7,
-//         32 weights in all, read from 8 bytes of ql (twice), 8 of qh,
-//         the 8 sub-scales of the half and d.
-// Weight value conventions (block layouts: hanzo-ml `src/vulkan_backend.rs`,
+// A weight row is cut into "units" of 64 weights that one lane decodes and
+// dots against 64 activation values it holds in registers (four runs of 16
+// consecutive values, X[16*g + t]):
+//   Q8_0: unit u = blocks 2u, 2u+1 (68 bytes, dword aligned when k % 64 == 0);
+//         runs at 64u + 16g.
+//   Q4_K: unit u = (superblock s = u/4, pair p = u%4): the 32 code bytes
+//         qs[32p .. 32p+32) (low nibbles = sub-block 2p, high = 2p+1) and the
+//         16-byte header (d, dmin, packed 6-bit scales/mins); runs at
+//         256s + 64p + 16g (runs 0,1 under the low nibbles, 2,3 under the high).
+//   Q6_K: unit u = (superblock s = u/4, half h = (u%4)/2, lh = u%2): for the
+//         four 32-weight groups g of half h the 16 weights l = 16lh..16lh+15,
+//         from 16 bytes of ql (twice), 16 of qh, the sub-scales and d; runs at
+//         256s + 128h + 32g + 16lh. Q6_K superblocks are 210 bytes, so these
+//         fields sit at any even address: they are read with dword loads at
+//         2-byte alignment (gfx950 global loads handle unaligned addresses).
+// Weight values (block layouts: hanzo-ml `src/vulkan_backend.rs`,
 // `quantize_q8_blocks`, `quantize_q4k_split`, `quantize_q6k_split`; bit
 // packing inside fields: public GGML k-quants):
 //   Q8_0 w = d*q;  Q4_K w = d*sc_j*q - dmin*m_j;  Q6_K w = d*sc_t*(q-32).
@@ -24,69 +27,126 @@
 // 68-byte steps); gfx950 global loads need dword alignment only.
 typedef uint32_t v4u_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// ---------------------------------------------------------------- Q8_0 ---
-struct Q8Pair {
-    uint32_t d[17];
+// Two nibble codes (bytes 0..15) of one 16-bit half of a dword -> f32 pair.
+// gfx950 v_cvt_pk_f32_fp8 reads the bytes as OCP E4M3; a byte q in 0..15 is
+// the E4M3 value q * 2^-9 exactly (subnormal for q < 8), so the pair comes
+// back as (q0, q1) * 2^-9 and the 2^9 is folded into the block scale.
+QMV_DEV float2 nib2f_lo(uint32_t v) {
+    auto r = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+    return make_float2(r[0], r[1]);
+}
+QMV_DEV float2 nib2f_hi(uint32_t v) {
+    auto r = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+    return make_float2(r[0], r[1]);
+}
+
+// Activation registers of one unit: 64 values and the sums of the 4 runs.
+struct UnitX {
+    float v[64];
+    float s[4];
 };
 
-QMV_DEV void q8_load(Q8Pair &P, const uint8_t *p) {
-    const v4u_a4 *v = reinterpret_cast<const v4u_a4 *>(p);
-    v4u_a4 a = v[0], b = v[1], c = v[2], e = v[3];
-    P.d[0] = a.x; P.d[1] = a.y; P.d[2] = a.z; P.d[3] = a.w;
-    P.d[4] = b.x; P.d[5] = b.y; P.d[6] = b.z; P.d[7] = b.w;
-    P.d[8] = c.x; P.d[9] = c.y; P.d[10] = c.z; P.d[11] = c.w;
-    P.d[12] = e.x; P.d[13] = e.y; P.d[14] = e.z; P.d[15] = e.w;
-    P.d[16] = reinterpret_cast<const uint32_t *>(p)[16];
+QMV_DEV void load_x_runs(UnitX &X, const float *x, int r0, int r1, int r2, int r3) {
+    const int base[4] = {r0, r1, r2, r3};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float4 *a = reinterpret_cast<const float4 *>(x + base[g]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 q = a[t];
+            X.v[16 * g + 4 * t + 0] = q.x;
+            X.v[16 * g + 4 * t + 1] = q.y;
+            X.v[16 * g + 4 * t + 2] = q.z;
+            X.v[16 * g + 4 * t + 3] = q.w;
+            acc += (q.x + q.y) + (q.z + q.w);
+        }
+        X.s[g] = acc;
+    }
 }
 
-// x holds the 64 activation values of the pair.
-QMV_DEV float q8_pair_dot(const Q8Pair &P, const float *x) {
-    float a = 0.0f, b = 0.0f;
+// Activation staging in LDS: unit u's 64 values (in X.v order) sit at float
+// offset XSTRIDE*u; the 4-float pad makes the 16-byte reads of 8 consecutive
+// lanes (consecutive units) fall in disjoint LDS banks.
+constexpr int XSTRIDE = 68;
+
+QMV_DEV void load_x_lds(UnitX &X, const float *xl, int u) {
+    const float4 *a = reinterpret_cast<const float4 *>(xl + XSTRIDE * u);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        uint32_t qa = funnel(P.d[t + 1], P.d[t], 2);  // codes of block A start at byte 2
-        uint32_t qb = P.d[9 + t];                     // codes of block B start at byte 36
-        a = fmaf(sbyte_f<0>(qa), x[4 * t + 0], a);
-        a = fmaf(sbyte_f<1>(qa), x[4 * t + 1], a);
-        a = fmaf(sbyte_f<2>(qa), x[4 * t + 2], a);
-        a = fmaf(sbyte_f<3>(qa), x[4 * t + 3], a);
-        b = fmaf(sbyte_f<0>(qb), x[32 + 4 * t + 0], b);
-        b = fmaf(sbyte_f<1>(qb), x[32 + 4 * t + 1], b);
-        b = fmaf(sbyte_f<2>(qb), x[32 + 4 * t + 2], b);
-        b = fmaf(sbyte_f<3>(qb), x[32 + 4 * t + 3], b);
+    for (int g = 0; g < 4; ++g) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 q = a[4 * g + t];
+            X.v[16 * g + 4 * t + 0] = q.x;
+            X.v[16 * g + 4 * t + 1] = q.y;
+            X.v[16 * g + 4 * t + 2] = q.z;
+            X.v[16 * g + 4 * t + 3] = q.w;
+            acc += (q.x + q.y) + (q.z + q.w);
+        }
+        X.s[g] = acc;
     }
-    float da = h2f(P.d[0]);
-    float db = h2f(P.d[8] >> 16);
-    return da * a + db * b;
 }
+
+// Cooperative fill of the staged layout from x[0..k) (float4 granules; a
+// granule never straddles two runs). Every thread of the block calls it.
+template <class F>
+QMV_DEV void stage_x(float *xl, const float *x, int k) {
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    for (int i4 = threadIdx.x; i4 < k / 4; i4 += blockDim.x) {
+        const int i = 4 * i4;
+        int j;
+        const int u = F::xslot(i, &j);
+        *reinterpret_cast<float4 *>(xl + XSTRIDE * u + j) = x4[i4];
+    }
+}
+
+// ---------------------------------------------------------------- Q8_0 ---
+struct Q8Unit {
+    static constexpr int BW = 32, BB = 34;
+    static constexpr int UNITS_PER_BLOCKS = 2;  // informational
+    struct Raw {
+        uint32_t d[17];
+    };
+    static __device__ __forceinline__ int units_per_row(int k) { return k / 64; }
+    static __device__ __forceinline__ void load_x(UnitX &X, const float *x, int u) {
+        load_x_runs(X, x, 64 * u, 64 * u + 16, 64 * u + 32, 64 * u + 48);
+    }
+    // activation index i -> (unit, position within the unit's 64 values)
+    static __device__ __forceinline__ int xslot(int i, int *j) {
+        *j = i & 63;
+        return i >> 6;
+    }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) {
+        const uint8_t *p = row + 68 * u;
+        const v4u_a4 *v = reinterpret_cast<const v4u_a4 *>(p);
+        const v4u_a4 a = v[0], b = v[1], c = v[2], e = v[3];
+        R.d[0] = a.x; R.d[1] = a.y; R.d[2] = a.z; R.d[3] = a.w;
+        R.d[4] = b.x; R.d[5] = b.y; R.d[6] = b.z; R.d[7] = b.w;
+        R.d[8] = c.x; R.d[9] = c.y; R.d[10] = c.z; R.d[11] = c.w;
+        R.d[12] = e.x; R.d[13] = e.y; R.d[14] = e.z; R.d[15] = e.w;
+        R.d[16] = reinterpret_cast<const uint32_t *>(p)[16];
+    }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitX &X, int) {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t qa = funnel(R.d[t + 1], R.d[t], 2);  // block A codes start at byte 2
+            const uint32_t qb = R.d[9 + t];                     // block B codes start at byte 36
+            a = fmaf(sbyte_f<0>(qa), X.v[4 * t + 0], a);
+            a = fmaf(sbyte_f<1>(qa), X.v[4 * t + 1], a);
+            a = fmaf(sbyte_f<2>(qa), X.v[4 * t + 2], a);
+            a = fmaf(sbyte_f<3>(qa), X.v[4 * t + 3], a);
+            b = fmaf(sbyte_f<0>(qb), X.v[32 + 4 * t + 0], b);
+            b = fmaf(sbyte_f<1>(qb), X.v[32 + 4 * t + 1], b);
+            b = fmaf(sbyte_f<2>(qb), X.v[32 + 4 * t + 2], b);
+            b = fmaf(sbyte_f<3>(qb), X.v[32 + 4 * t + 3], b);
+        }
+        return h2f(R.d[0]) * a + h2f(R.d[8] >> 16) * b;
+    }
+};
 
 // ---------------------------------------------------------------- Q4_K ---
-// Activation registers of one Q4_K unit: the 16 values under the low
-// nibbles (sub-block 2p, l = 16hh..16hh+15), the 16 under the high nibbles
-// (sub-block 2p+1) and their sums.
-struct Q4KX {
-    float lo[16], hi[16];
-    float slo, shi;
-};
-
-// s: superblock index within the row, c: chunk 0..7.
-QMV_DEV void q4k_load_x(Q4KX &X, const float *x, int s, int c) {
-    const int p = c >> 1, hh = c & 1;
-    const float4 *a = reinterpret_cast<const float4 *>(x + 256 * s + 64 * p + 16 * hh);
-    const float4 *b = reinterpret_cast<const float4 *>(x + 256 * s + 64 * p + 32 + 16 * hh);
-    float sl = 0.0f, sh = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float4 u = a[t], v = b[t];
-        X.lo[4 * t] = u.x; X.lo[4 * t + 1] = u.y; X.lo[4 * t + 2] = u.z; X.lo[4 * t + 3] = u.w;
-        X.hi[4 * t] = v.x; X.hi[4 * t + 1] = v.y; X.hi[4 * t + 2] = v.z; X.hi[4 * t + 3] = v.w;
-        sl += (u.x + u.y) + (u.z + u.w);
-        sh += (v.x + v.y) + (v.z + v.w);
-    }
-    X.slo = sl;
-    X.shi = sh;
-}
-
 // 6-bit scales and mins of sub-blocks 2p and 2p+1 from the header dwords
 // m1 = scales[0..3], m2 = scales[4..7], m3 = scales[8..11]:
 //   j < 4 : sc = s[j] & 63,                   m = s[j+4] & 63
@@ -106,119 +166,125 @@ QMV_DEV void q4k_scales(uint32_t m1, uint32_t m2, uint32_t m3, int p, uint32_t *
     }
 }
 
-// Partial dot of one Q4_K unit: q = the 16 code bytes, m = the 16 header bytes.
-QMV_DEV float q4k_unit_dot(uint4 q, uint4 m, const Q4KX &X, int p) {
-    float alo = 0.0f, ahi = 0.0f;
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t lo = qw[t] & 0x0F0F0F0Fu;
-        const uint32_t hi = qw[t] & 0xF0F0F0F0u;  // 16*q per byte, 1/16 folded below
-        alo = fmaf(ubyte_f<0>(lo), X.lo[4 * t + 0], alo);
-        alo = fmaf(ubyte_f<1>(lo), X.lo[4 * t + 1], alo);
-        alo = fmaf(ubyte_f<2>(lo), X.lo[4 * t + 2], alo);
-        alo = fmaf(ubyte_f<3>(lo), X.lo[4 * t + 3], alo);
-        ahi = fmaf(ubyte_f<0>(hi), X.hi[4 * t + 0], ahi);
-        ahi = fmaf(ubyte_f<1>(hi), X.hi[4 * t + 1], ahi);
-        ahi = fmaf(ubyte_f<2>(hi), X.hi[4 * t + 2], ahi);
-        ahi = fmaf(ubyte_f<3>(hi), X.hi[4 * t + 3], ahi);
+struct Q4KUnit {
+    static constexpr int BW = 256, BB = 144;
+    struct Raw {
+        uint4 q0, q1, m;
+    };
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load_x(UnitX &X, const float *x, int u) {
+        const int b = 256 * (u >> 2) + 64 * (u & 3);
+        load_x_runs(X, x, b, b + 16, b + 32, b + 48);
     }
-    uint32_t sc2, mn2;
-    q4k_scales(m.y, m.z, m.w, p, &sc2, &mn2);
-    const float d = h2f(m.x), dmin = h2f(m.x >> 16);
-    const float dlo = d * ubyte_f<0>(sc2);
-    const float dhi = d * ubyte_f<1>(sc2);
-    const float mlo = dmin * ubyte_f<0>(mn2);
-    const float mhi = dmin * ubyte_f<1>(mn2);
-    float r = dlo * alo;
-    r = fmaf(dhi, ahi * 0.0625f, r);
-    r = fmaf(-mlo, X.slo, r);
-    r = fmaf(-mhi, X.shi, r);
-    return r;
-}
+    // unit (s, p) covers x[256s + 64p, +64) in order
+    static __device__ __forceinline__ int xslot(int i, int *j) {
+        *j = i & 63;
+        return i >> 6;
+    }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) {
+        const uint8_t *blk = row + (size_t)(u >> 2) * 144;
+        const int p = u & 3;
+        R.q0 = ld16(blk + 16 + 32 * p);
+        R.q1 = ld16(blk + 32 + 32 * p);
+        R.m = ld16(blk);
+    }
+    // Integer-free dot: nibbles -> f32 pairs (x 2^-9) -> fma against x.
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitX &X, int u) {
+        const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+        float alo = 0.0f, ahi = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t lo = qw[t] & 0x0F0F0F0Fu;
+            const uint32_t hi = (qw[t] >> 4) & 0x0F0F0F0Fu;
+            const float2 l0 = nib2f_lo(lo), l1 = nib2f_hi(lo);
+            const float2 h0 = nib2f_lo(hi), h1 = nib2f_hi(hi);
+            alo = fmaf(l0.x, X.v[4 * t + 0], alo);
+            alo = fmaf(l0.y, X.v[4 * t + 1], alo);
+            alo = fmaf(l1.x, X.v[4 * t + 2], alo);
+            alo = fmaf(l1.y, X.v[4 * t + 3], alo);
+            ahi = fmaf(h0.x, X.v[32 + 4 * t + 0], ahi);
+            ahi = fmaf(h0.y, X.v[32 + 4 * t + 1], ahi);
+            ahi = fmaf(h1.x, X.v[32 + 4 * t + 2], ahi);
+            ahi = fmaf(h1.y, X.v[32 + 4 * t + 3], ahi);
+        }
+        uint32_t sc2, mn2;
+        q4k_scales(R.m.y, R.m.z, R.m.w, u & 3, &sc2, &mn2);
+        const float d = h2f(R.m.x), dmin = h2f(R.m.x >> 16);
+        const float d9 = d * 512.0f;  // undo the 2^-9 of the fp8 read
+        float r = (d9 * ubyte_f<0>(sc2)) * alo;
+        r = fmaf(d9 * ubyte_f<1>(sc2), ahi, r);
+        r = fmaf(-(dmin * ubyte_f<0>(mn2)), X.s[0] + X.s[1], r);
+        r = fmaf(-(dmin * ubyte_f<1>(mn2)), X.s[2] + X.s[3], r);
+        return r;
+    }
+};
 
 // ---------------------------------------------------------------- Q6_K ---
-// Activation registers of one Q6_K unit: for group g = 0..3 the 8 values at
-// 128h + 32g + 8lq + t, and their sums.
-struct Q6KX {
-    float v[4][8];
-    float s[4];
-};
+// 16 / 8 bytes at an even address, one global load each (see file comment).
+QMV_DEV uint4 ld16u(const uint8_t *p) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    return *q;
+}
+QMV_DEV uint2 ld8u(const uint8_t *p) {
+    const uint2 *q = reinterpret_cast<const uint2 *>(p);
+    return *q;
+}
 
-QMV_DEV void q6k_load_x(Q6KX &X, const float *x, int sb, int u) {
-    const int h = u >> 2, lq = u & 3;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float4 *a = reinterpret_cast<const float4 *>(x + 256 * sb + 128 * h + 32 * g + 8 * lq);
-        float4 p0 = a[0], p1 = a[1];
-        X.v[g][0] = p0.x; X.v[g][1] = p0.y; X.v[g][2] = p0.z; X.v[g][3] = p0.w;
-        X.v[g][4] = p1.x; X.v[g][5] = p1.y; X.v[g][6] = p1.z; X.v[g][7] = p1.w;
-        X.s[g] = ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
+struct Q6KUnit {
+    static constexpr int BW = 256, BB = 210;
+    struct Raw {
+        uint4 a, b, h;
+        uint2 sc;
+        uint32_t d;
+    };
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load_x(UnitX &X, const float *x, int u) {
+        const int b = 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1);
+        load_x_runs(X, x, b, b + 32, b + 64, b + 96);
     }
-}
-
-// Raw dwords of one Q6_K unit, fetched with dword-aligned loads; the
-// superblock itself may start at any even byte (210-byte blocks).
-struct Q6KRaw {
-    uint32_t a[3], b[3], hq[3], sc[3];
-    uint32_t d;
-    uint32_t sa;  // byte misalignment of the superblock start (0 or 2)
-};
-
-// Load 8 bytes starting at the even address p as 3 aligned dwords; the third
-// is read only when p is not dword aligned (otherwise it would step past a
-// field that ends at the last byte of the buffer).
-QMV_DEV void ld8u(uint32_t out[3], const uint8_t *p) {
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t *b = reinterpret_cast<const uint32_t *>(a & ~(uintptr_t)3);
-    const uint32_t off3 = (a & 3) ? 2u : 1u;
-    out[0] = b[0];
-    out[1] = b[1];
-    out[2] = b[off3];
-}
-
-QMV_DEV void q6k_load(Q6KRaw &R, const uint8_t *blk, int u) {
-    const int h = u >> 2, lq = u & 3;
-    ld8u(R.a, blk + 64 * h + 8 * lq);
-    ld8u(R.b, blk + 64 * h + 32 + 8 * lq);
-    ld8u(R.hq, blk + 128 + 32 * h + 8 * lq);
-    ld8u(R.sc, blk + 192 + 8 * h);
-    R.d = ld2(blk + 208);
-    R.sa = (uint32_t)((uintptr_t)blk & 3);
-}
-
-QMV_DEV float q6k_unit_dot(const Q6KRaw &R, const Q6KX &X, int u) {
-    const uint32_t s = R.sa;
-    const uint32_t A[2] = {funnel(R.a[1], R.a[0], s), funnel(R.a[2], R.a[1], s)};
-    const uint32_t Bq[2] = {funnel(R.b[1], R.b[0], s), funnel(R.b[2], R.b[1], s)};
-    const uint32_t H[2] = {funnel(R.hq[1], R.hq[0], s), funnel(R.hq[2], R.hq[1], s)};
-    const uint32_t S0 = funnel(R.sc[1], R.sc[0], s), S1 = funnel(R.sc[2], R.sc[1], s);
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // x index i = 256s + 128h + 32g + 16lh + t -> unit 4s + 2h + lh, slot 16g + t
+    static __device__ __forceinline__ int xslot(int i, int *j) {
+        const int s = i >> 8, h = (i >> 7) & 1, g = (i >> 5) & 3, lh = (i >> 4) & 1, t = i & 15;
+        *j = 16 * g + t;
+        return 4 * s + 2 * h + lh;
+    }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) {
+        const uint8_t *blk = row + (size_t)(u >> 2) * 210;
+        const int h = (u >> 1) & 1, lh = u & 1;
+        R.a = ld16u(blk + 64 * h + 16 * lh);
+        R.b = ld16u(blk + 64 * h + 32 + 16 * lh);
+        R.h = ld16u(blk + 128 + 32 * h + 16 * lh);
+        R.sc = ld8u(blk + 192 + 8 * h);
+        R.d = ld2(blk + 208);
+    }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitX &X, int u) {
+        const uint32_t A[4] = {R.a.x, R.a.y, R.a.z, R.a.w};
+        const uint32_t B[4] = {R.b.x, R.b.y, R.b.z, R.b.w};
+        const uint32_t H[4] = {R.h.x, R.h.y, R.h.z, R.h.w};
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t q0 = (A[w] & 0x0F0F0F0Fu) | ((H[w] << 4) & 0x30303030u);
-        const uint32_t q1 = (Bq[w] & 0x0F0F0F0Fu) | ((H[w] << 2) & 0x30303030u);
-        const uint32_t q2 = ((A[w] >> 4) & 0x0F0F0F0Fu) | (H[w] & 0x30303030u);
-        const uint32_t q3 = ((Bq[w] >> 4) & 0x0F0F0F0Fu) | ((H[w] >> 2) & 0x30303030u);
-        const uint32_t qq[4] = {q0, q1, q2, q3};
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t q0 = (A[t] & 0x0F0F0F0Fu) | ((H[t] << 4) & 0x30303030u);
+            const uint32_t q1 = (B[t] & 0x0F0F0F0Fu) | ((H[t] << 2) & 0x30303030u);
+            const uint32_t q2 = ((A[t] >> 4) & 0x0F0F0F0Fu) | (H[t] & 0x30303030u);
+            const uint32_t q3 = ((B[t] >> 4) & 0x0F0F0F0Fu) | ((H[t] >> 2) & 0x30303030u);
+            const uint32_t qq[4] = {q0, q1, q2, q3};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            acc[g] = fmaf(ubyte_f<0>(qq[g]), X.v[g][4 * w + 0], acc[g]);
-            acc[g] = fmaf(ubyte_f<1>(qq[g]), X.v[g][4 * w + 1], acc[g]);
-            acc[g] = fmaf(ubyte_f<2>(qq[g]), X.v[g][4 * w + 2], acc[g]);
-            acc[g] = fmaf(ubyte_f<3>(qq[g]), X.v[g][4 * w + 3], acc[g]);
+            for (int g = 0; g < 4; ++g) {
+                acc[g] = fmaf(ubyte_f<0>(qq[g]), X.v[16 * g + 4 * t + 0], acc[g]);
+                acc[g] = fmaf(ubyte_f<1>(qq[g]), X.v[16 * g + 4 * t + 1], acc[g]);
+                acc[g] = fmaf(ubyte_f<2>(qq[g]), X.v[16 * g + 4 * t + 2], acc[g]);
+                acc[g] = fmaf(ubyte_f<3>(qq[g]), X.v[16 * g + 4 * t + 3], acc[g]);
+            }
         }
+        // sub-scale of group g: sc[8h + 2g + lh] = byte 2g + lh of the 8 bytes
+        const int lh = u & 1;
+        const uint32_t s0 = R.sc.x >> (8 * lh), s1 = R.sc.y >> (8 * lh);
+        const float c0 = sbyte_f<0>(s0), c1 = sbyte_f<2>(s0), c2 = sbyte_f<0>(s1), c3 = sbyte_f<2>(s1);
+        float r = c0 * fmaf(-32.0f, X.s[0], acc[0]);
+        r = fmaf(c1, fmaf(-32.0f, X.s[1], acc[1]), r);
+        r = fmaf(c2, fmaf(-32.0f, X.s[2], acc[2]), r);
+        r = fmaf(c3, fmaf(-32.0f, X.s[3], acc[3]), r);
+        return h2f(R.d) * r;
     }
-    // sub-scale of group g: sc[8h + 2g + lq/2] = byte 2g + lq/2 of {S1:S0}
-    const uint32_t bsel = (uint32_t)((u & 3) >> 1) * 8u;
-    const float d = h2f(R.d);
-    const float sc0 = (float)(int8_t)((S0 >> bsel) & 0xFFu);
-    const float sc1 = (float)(int8_t)((S0 >> (bsel + 16u)) & 0xFFu);
-    const float sc2 = (float)(int8_t)((S1 >> bsel) & 0xFFu);
-    const float sc3 = (float)(int8_t)((S1 >> (bsel + 16u)) & 0xFFu);
-    float r = sc0 * fmaf(-32.0f, X.s[0], acc[0]);
-    r = fmaf(sc1, fmaf(-32.0f, X.s[1], acc[1]), r);
-    r = fmaf(sc2, fmaf(-32.0f, X.s[2], acc[2]), r);
-    r = fmaf(sc3, fmaf(-32.0f, X.s[3], acc[3]), r);
-    return d * r;
-}
+};

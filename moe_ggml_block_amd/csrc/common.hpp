@@ -56,6 +56,28 @@ QMV_DEV int group_isum(int v) {
     return v;
 }
 
+// Sum over aligned groups of G lanes with DPP row operations (no LDS):
+// xor-1 and xor-2 quad permutes, half-row and row mirrors, then the row
+// broadcasts of lanes 15 and 31. The total lands in the LAST lane of each
+// group (for G <= 16 in every lane of the group). Call in wave-uniform
+// control flow: every lane must execute it.
+template <int CTRL, int ROW_MASK>
+QMV_DEV float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(t);
+}
+
+template <int G>
+QMV_DEV float group_sum_last(float v) {
+    if (G >= 2) v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    if (G >= 4) v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    if (G >= 8) v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    if (G >= 16) v = dpp_add<0x140, 0xF>(v); // row_mirror
+    if (G >= 32) v = dpp_add<0x142, 0xA>(v); // row_bcast15 into rows 1, 3
+    if (G >= 64) v = dpp_add<0x143, 0xC>(v); // row_bcast31 into rows 2, 3
+    return v;
+}
+
 QMV_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Non-temporal-free plain 16-byte load.

@@ -177,65 +177,59 @@ __device__ void zero_invalid(const int32_t *__restrict__ ids, int nslots, int E,
     }
 }
 
-// ------------------------------------------------- Q4_K gather matvec ---
-// Rows of the expert are split over row blocks of RBLK rows; inside a block
-// each wave takes 64/G rows per pass. For each chunk of SB slots the lanes
-// load those slots' activation values into registers, then stream the rows.
-// DUAL: two banks (gate, up) against the same activation, output
+// ------------------------------------------------------ gather matvec ---
+// Rows of the expert are split over row blocks of `rblk` rows; inside a block
+// the four waves take passes of 64/G rows in turn. For each chunk of SB slots
+// the lanes load those slots' activation values into registers, then stream
+// the rows. DUAL: two banks (gate, up) against the same activation, output
 // silu(gate.x) * (up.x); otherwise one bank, plain output.
-template <int G, int UPL, int SB, bool DUAL>
-__global__ __launch_bounds__(256) void k_moe_q4k(const uint8_t *__restrict__ bank,
-                                                 const uint8_t *__restrict__ bank2,
-                                                 const float *__restrict__ x, int x_div,
-                                                 const int32_t *__restrict__ ids,
-                                                 float *__restrict__ y, int nslots, int n, int k,
-                                                 int E, int rblk) {
+template <class F, int G, int UPL, int SB, bool DUAL>
+__global__ __launch_bounds__(256) void k_moe(const uint8_t *__restrict__ bank,
+                                             const uint8_t *__restrict__ bank2,
+                                             const float *__restrict__ x, int x_div,
+                                             const int32_t *__restrict__ ids,
+                                             float *__restrict__ y, int nslots, int n, int k,
+                                             int E, int rblk) {
     __shared__ uint32_t bitmap[MAX_E / 32];
     __shared__ int slot_list[MAX_SLOTS];
     __shared__ int shared[2];
     constexpr int RPP = 64 / G;
+    using Raw = typename F::Raw;
     const int r0 = blockIdx.x * rblk;
     const int r1 = min(n, r0 + rblk);
     if (blockIdx.y == 0) zero_invalid(ids, nslots, E, y, n, r0, r1);
     const Group grp = find_group(ids, nslots, E, blockIdx.y, bitmap, slot_list, shared);
     if (grp.expert < 0) return;
-    const int U = (k / 256) * 8;
-    const int row_bytes = (k / 256) * 144;
+    const int U = F::units_per_row(k);
+    const size_t row_bytes = (size_t)(k / F::BW) * F::BB;
     const uint8_t *wb = bank + (size_t)grp.expert * n * row_bytes;
     const uint8_t *wb2 = DUAL ? bank2 + (size_t)grp.expert * n * row_bytes : nullptr;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gl = lane & (G - 1), grow = lane / G;
-    const int c = gl & 7, pr = c >> 1;
+    bool uv[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) uv[i] = gl + G * i < U;
 
     for (int sc0 = 0; sc0 < grp.count; sc0 += SB) {
         const int ns = min(SB, grp.count - sc0);
-        Q4KX X[SB][UPL];
-        bool uv[UPL];
+        UnitX X[SB][UPL];
         int sl[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) sl[j] = j < ns ? slot_list[sc0 + j] : -1;
 #pragma unroll
-        for (int i = 0; i < UPL; ++i) {
-            const int u = gl + G * i;
-            uv[i] = u < U;
+        for (int i = 0; i < UPL; ++i)
 #pragma unroll
             for (int j = 0; j < SB; ++j)
-                if (uv[i] && j < ns) q4k_load_x(X[j][i], x + (size_t)(sl[j] / x_div) * k, u >> 3, c);
-        }
+                if (uv[i] && j < ns) F::load_x(X[j][i], x + (size_t)(sl[j] / x_div) * k, gl + G * i);
         for (int rb = r0 + wave * RPP; rb < r1; rb += WAVES * RPP) {
             const int r = rb + grow;
             const bool rv = r < r1;
-            uint4 qd[UPL], md[UPL], qd2[UPL], md2[UPL];
+            Raw R[UPL], R2[UPL];
 #pragma unroll
             for (int i = 0; i < UPL; ++i)
                 if (rv && uv[i]) {
-                    const size_t off = (size_t)r * row_bytes + (size_t)((gl + G * i) >> 3) * 144;
-                    qd[i] = ld16(wb + off + 16 + 16 * c);
-                    md[i] = ld16(wb + off);
-                    if (DUAL) {
-                        qd2[i] = ld16(wb2 + off + 16 + 16 * c);
-                        md2[i] = ld16(wb2 + off);
-                    }
+                    F::load(R[i], wb + (size_t)r * row_bytes, gl + G * i);
+                    if (DUAL) F::load(R2[i], wb2 + (size_t)r * row_bytes, gl + G * i);
                 }
 #pragma unroll
             for (int j = 0; j < SB; ++j) {
@@ -244,71 +238,12 @@ __global__ __launch_bounds__(256) void k_moe_q4k(const uint8_t *__restrict__ ban
 #pragma unroll
                 for (int i = 0; i < UPL; ++i)
                     if (rv && uv[i]) {
-                        a += q4k_unit_dot(qd[i], md[i], X[j][i], pr);
-                        if (DUAL) b += q4k_unit_dot(qd2[i], md2[i], X[j][i], pr);
+                        a += F::dot(R[i], X[j][i], gl + G * i);
+                        if (DUAL) b += F::dot(R2[i], X[j][i], gl + G * i);
                     }
-                a = group_sum<G>(a);
-                if (DUAL) b = group_sum<G>(b);
-                if (gl == 0 && rv) y[(size_t)sl[j] * n + r] = DUAL ? silu(a) * b : a;
-            }
-        }
-    }
-}
-
-// ------------------------------------------------- Q6_K gather matvec ---
-template <int G, int UPL, int SB>
-__global__ __launch_bounds__(256) void k_moe_q6k(const uint8_t *__restrict__ bank,
-                                                 const float *__restrict__ x, int x_div,
-                                                 const int32_t *__restrict__ ids,
-                                                 float *__restrict__ y, int nslots, int n, int k,
-                                                 int E, int rblk) {
-    __shared__ uint32_t bitmap[MAX_E / 32];
-    __shared__ int slot_list[MAX_SLOTS];
-    __shared__ int shared[2];
-    constexpr int RPP = 64 / G;
-    const int r0 = blockIdx.x * rblk;
-    const int r1 = min(n, r0 + rblk);
-    if (blockIdx.y == 0) zero_invalid(ids, nslots, E, y, n, r0, r1);
-    const Group grp = find_group(ids, nslots, E, blockIdx.y, bitmap, slot_list, shared);
-    if (grp.expert < 0) return;
-    const int U = (k / 256) * 8;
-    const size_t row_bytes = (size_t)(k / 256) * 210;
-    const uint8_t *wb = bank + (size_t)grp.expert * n * row_bytes;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int gl = lane & (G - 1), grow = lane / G;
-    const int u8 = gl & 7;
-
-    for (int sc0 = 0; sc0 < grp.count; sc0 += SB) {
-        const int ns = min(SB, grp.count - sc0);
-        Q6KX X[SB][UPL];
-        bool uv[UPL];
-        int sl[SB];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) sl[j] = j < ns ? slot_list[sc0 + j] : -1;
-#pragma unroll
-        for (int i = 0; i < UPL; ++i) {
-            const int u = gl + G * i;
-            uv[i] = u < U;
-#pragma unroll
-            for (int j = 0; j < SB; ++j)
-                if (uv[i] && j < ns) q6k_load_x(X[j][i], x + (size_t)(sl[j] / x_div) * k, u >> 3, u8);
-        }
-        for (int rb = r0 + wave * RPP; rb < r1; rb += WAVES * RPP) {
-            const int r = rb + grow;
-            const bool rv = r < r1;
-            Q6KRaw R[UPL];
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv && uv[i]) q6k_load(R[i], wb + (size_t)r * row_bytes + (size_t)((gl + G * i) >> 3) * 210, u8);
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                if (j >= ns) break;
-                float a = 0.0f;
-#pragma unroll
-                for (int i = 0; i < UPL; ++i)
-                    if (rv && uv[i]) a += q6k_unit_dot(R[i], X[j][i], u8);
-                a = group_sum<G>(a);
-                if (gl == 0 && rv) y[(size_t)sl[j] * n + r] = a;
+                a = group_sum_last<G>(a);
+                if (DUAL) b = group_sum_last<G>(b);
+                if (gl == G - 1 && rv) y[(size_t)sl[j] * n + r] = DUAL ? silu(a) * b : a;
             }
         }
     }
@@ -339,33 +274,27 @@ int pick_rblk(int64_t n, int G, int64_t groups) {
     return rblk;
 }
 
-int launch_moe_q4k(const uint8_t *bank, const uint8_t *bank2, const float *x, int64_t x_div,
-                   const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
-                   hipStream_t s) {
-    const int U = (int)(k / 256) * 8;
+template <class F, bool DUAL>
+int launch_moe(const uint8_t *bank, const uint8_t *bank2, const float *x, int64_t x_div,
+               const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, hipStream_t s) {
+    const int64_t U = k / 64;
     const int G = next_pow2_le64(U);
-    const int upl = (U + G - 1) / G;
     const int64_t groups = E < nslots ? E : nslots;
     const int rblk = pick_rblk(n, G, groups);
     const dim3 grid((unsigned)div_up(n, rblk), (unsigned)groups);
-    const bool dual = bank2 != nullptr;
-#define MQ(GG, UU, SB)                                                                          \
-    do {                                                                                      \
-        if (dual)                                                                             \
-            hipLaunchKernelGGL((k_moe_q4k<GG, UU, SB, true>), grid, dim3(256), 0, s, bank, bank2, x, \
-                               (int)x_div, ids, y, (int)nslots, (int)n, (int)k, (int)E, rblk);  \
-        else                                                                                  \
-            hipLaunchKernelGGL((k_moe_q4k<GG, UU, SB, false>), grid, dim3(256), 0, s, bank, bank2, x, \
-                               (int)x_div, ids, y, (int)nslots, (int)n, (int)k, (int)E, rblk);  \
-    } while (0)
+#define MQ(GG, UU, SB)                                                                                 \
+    hipLaunchKernelGGL((k_moe<F, GG, UU, SB, DUAL>), grid, dim3(256), 0, s, bank, bank2, x, (int)x_div, ids, y, \
+                       (int)nslots, (int)n, (int)k, (int)E, rblk)
     switch (G) {
+        case 1: MQ(1, 1, 2); break;
+        case 2: MQ(2, 1, 2); break;
+        case 4: MQ(4, 1, 2); break;
         case 8: MQ(8, 1, 2); break;
         case 16: MQ(16, 1, 2); break;
         case 32: MQ(32, 1, 2); break;
         default:
-            if (upl == 1) MQ(64, 1, 2);
-            else if (upl == 2) MQ(64, 2, 1);
-            else if (upl <= 4) MQ(64, 4, 1);
+            if (U <= 64) MQ(64, 1, 2);
+            else if (U <= 128) MQ(64, 2, 1);
             else return QMV_EUNSUPPORTED;
     }
 #undef MQ
@@ -373,37 +302,23 @@ int launch_moe_q4k(const uint8_t *bank, const uint8_t *bank2, const float *x, in
     return QMV_OK;
 }
 
+int launch_moe_q4k(const uint8_t *bank, const uint8_t *bank2, const float *x, int64_t x_div,
+                   const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                   hipStream_t s) {
+    if (bank2) return launch_moe<Q4KUnit, true>(bank, bank2, x, x_div, ids, y, nslots, n, k, E, s);
+    return launch_moe<Q4KUnit, false>(bank, nullptr, x, x_div, ids, y, nslots, n, k, E, s);
+}
+
 int launch_moe_q6k(const uint8_t *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
                    int64_t nslots, int64_t n, int64_t k, int64_t E, hipStream_t s) {
-    const int U = (int)(k / 256) * 8;
-    const int G = next_pow2_le64(U);
-    const int upl = (U + G - 1) / G;
-    const int64_t groups = E < nslots ? E : nslots;
-    const int rblk = pick_rblk(n, G, groups);
-    const dim3 grid((unsigned)div_up(n, rblk), (unsigned)groups);
-#define MQ(GG, UU, SB)                                                                              \
-    hipLaunchKernelGGL((k_moe_q6k<GG, UU, SB>), grid, dim3(256), 0, s, bank, x, (int)x_div, ids, y, \
-                       (int)nslots, (int)n, (int)k, (int)E, rblk)
-    switch (G) {
-        case 8: MQ(8, 1, 2); break;
-        case 16: MQ(16, 1, 2); break;
-        case 32: MQ(32, 1, 2); break;
-        default:
-            if (upl == 1) MQ(64, 1, 2);
-            else if (upl == 2) MQ(64, 2, 1);
-            else if (upl <= 4) MQ(64, 4, 1);
-            else return QMV_EUNSUPPORTED;
-    }
-#undef MQ
-    QMV_LAUNCH_CHECK();
-    return QMV_OK;
+    return launch_moe<Q6KUnit, false>(bank, nullptr, x, x_div, ids, y, nslots, n, k, E, s);
 }
 
 int check_moe_args(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
                    int64_t nslots, int64_t n, int64_t k, int64_t E) {
     if (!bank || !x || !ids || !y || x_div < 1 || nslots < 1 || n < 1 || E < 1 || k < 256 || k % 256)
         return QMV_EINVAL;
-    if (E > MAX_E || nslots > MAX_SLOTS || k > 4 * 64 * 32 || n > (1 << 24) ||
+    if (E > MAX_E || nslots > MAX_SLOTS || k > 8192 || n > (1 << 24) ||
         (int64_t)E * n * (k / 256) * 210 > ((int64_t)1 << 40))
         return QMV_EUNSUPPORTED;
     if (!aligned(bank, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(y, 4)) return QMV_EALIGN;

@@ -4,180 +4,102 @@
 // `matvec_q4k_gpu_off` and `matvec_q6k_gpu_off` (y[nout] = Wq * x[k], blocks
 // read verbatim from a resident buffer, no requantization).
 //
-// Work mapping: a row is cut into U units (see blocks.hpp). An aligned group
-// of G lanes (G = next power of two >= U, at most 64) owns one row; lane i of
-// the group decodes units i, i+G, i+2G, ... (UPL of them). The activation
-// values under a lane's units never change from row to row, so each lane
-// loads them into registers once and the wave then streams rows: 64/G rows
-// per pass, RB passes' loads issued before any of their math. Partial sums
-// are reduced across the G lanes with cross-lane shuffles.
+// Work mapping. A row is cut into U units of 64 weights (blocks.hpp). An
+// aligned group of G lanes (G = next power of two >= U, at most 64) owns one
+// row; lane i of the group decodes units i and i+G (UPL <= 2). The
+// activation values under a lane's units are the same for every row, so each
+// lane loads its 64*UPL values into registers once (from L1/L2: x is small
+// and shared by every wave) and the wave then streams rows, 64/G per pass.
+// Each wave owns a contiguous range of passes and keeps a ring of NB passes
+// in flight: the weight loads of pass i+NB are issued as soon as pass i has
+// been decoded, so HBM latency is covered by NB passes of decode work (and
+// by the other waves of the SIMD). All loads are unconditional -- row and
+// unit indices past the end are clamped to valid ones and their results
+// discarded -- so the compiler can wait for exactly the oldest pass
+// (s_waitcnt vmcnt(N)) instead of draining the ring. Partial sums are
+// reduced across the G lanes with DPP.
+//
+// Launch shape: the grid is sized from the occupancy of the kernel so that
+// every wave is resident at once (one round, no tail), each wave taking an
+// equal share of the passes.
 #include "blocks.hpp"
 
 namespace {
 
+#ifndef QMV_NB
+#define QMV_NB 4
+#endif
+#ifndef QMV_ROUNDS_X4
+#define QMV_ROUNDS_X4 4
+#endif
 constexpr int WAVES_PER_BLOCK = 4;
+constexpr int NB = QMV_NB;  // passes in flight per wave
+// waves launched = resident waves * ROUNDS_X4 / 4
+constexpr int ROUNDS_X4 = QMV_ROUNDS_X4;
 
-struct RowSched {
-    int n;             // rows
-    int passes;        // ceil(n / rows_per_pass)
-    int per_wave;      // passes per wave
-};
-
-// --------------------------------------------------------------------- Q4_K
-template <int G, int UPL, int RB>
-__global__ __launch_bounds__(256) void k_qmv_q4k(const uint8_t *__restrict__ w,
-                                                 const float *__restrict__ x,
-                                                 float *__restrict__ y, RowSched rs, int U,
-                                                 int row_bytes) {
+template <class F, int G, int UPL>
+__global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
+                                               const float *__restrict__ x,
+                                               float *__restrict__ y, int n, int k,
+                                               int row_bytes, int per_wave) {
+    extern __shared__ float xlds[];
     constexpr int RPP = 64 / G;
-    const int lane = threadIdx.x & 63;
-    const int gl = lane & (G - 1);
-    const int grow = lane / G;
-    const int wave = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
-    const int p0 = wave * rs.per_wave;
-    if (p0 >= rs.passes) return;
-    const int p1 = min(rs.passes, p0 + rs.per_wave);
-    const int c = gl & 7, pr = c >> 1;
-
-    Q4KX X[UPL];
+    using Raw = typename F::Raw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int gl = lane & (G - 1), grow = lane / G;
+    const int U = F::units_per_row(k);
+    const int passes = (n + RPP - 1) / RPP;
+    const int wave = blockIdx.x * WAVES_PER_BLOCK + (tid >> 6);
+    const int p0 = wave * per_wave;
+    const int p1 = min(passes, p0 + per_wave);
+    const bool idle = p0 >= p1;  // still takes part in the x staging barrier
     bool uv[UPL];
+    int uu[UPL];  // unit actually read (clamped into the row)
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
-        const int u = gl + G * i;
-        uv[i] = u < U;
-        if (uv[i]) q4k_load_x(X[i], x, u >> 3, c);
+        uv[i] = gl + G * i < U;
+        uu[i] = uv[i] ? gl + G * i : U - 1;
     }
-
-    for (int pass = p0; pass < p1; pass += RB) {
-        uint4 qd[RB][UPL], md[RB][UPL];
-        bool rv[RB];
-        int rr[RB];
+    Raw R[NB][UPL];
+    auto load_pass = [&](Raw (&B)[UPL], int pass) {
+        const int r = max(min(pass * RPP + grow, n - 1), 0);
+        const uint8_t *row = w + (size_t)r * row_bytes;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            rr[b] = (pass + b) * RPP + grow;
-            rv[b] = (pass + b) < p1 && rr[b] < rs.n;
+        for (int i = 0; i < UPL; ++i) F::load(B[i], row, uu[i]);
+    };
+    // The ring only works if the passes' loads are issued oldest-first: a
+    // scheduling barrier after each pass keeps the compiler from reordering
+    // them (the first buffer consumed must be the first one requested).
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        load_pass(R[j], min(p0 + j, p1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // activations: coalesced loads into the padded LDS layout, then each
+    // lane reads its units' values (conflict-free) into registers
+    stage_x<F>(xlds, x, k);
+    __syncthreads();
+    UnitX X[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) load_x_lds(X[i], xlds, uu[i]);
+    if (idle) return;
+
+    for (int pass = p0; pass < p1; pass += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int ps = pass + j;
+            const int r = ps * RPP + grow;
+            float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < UPL; ++i) {
-                if (rv[b] && uv[i]) {
-                    const uint8_t *blk = w + (size_t)rr[b] * row_bytes + (size_t)((gl + G * i) >> 3) * 144;
-                    qd[b][i] = ld16(blk + 16 + 16 * c);
-                    md[b][i] = ld16(blk);
-                }
+                const float d = F::dot(R[j][i], X[i], uu[i]);
+                acc += uv[i] ? d : 0.0f;
             }
-        }
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv[b] && uv[i]) acc += q4k_unit_dot(qd[b][i], md[b][i], X[i], pr);
-            acc = group_sum<G>(acc);
-            if (gl == 0 && rv[b]) y[rr[b]] = acc;
-        }
-    }
-}
-
-// --------------------------------------------------------------------- Q6_K
-template <int G, int UPL, int RB>
-__global__ __launch_bounds__(256) void k_qmv_q6k(const uint8_t *__restrict__ w,
-                                                 const float *__restrict__ x,
-                                                 float *__restrict__ y, RowSched rs, int U,
-                                                 int row_bytes) {
-    constexpr int RPP = 64 / G;
-    const int lane = threadIdx.x & 63;
-    const int gl = lane & (G - 1);
-    const int grow = lane / G;
-    const int wave = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
-    const int p0 = wave * rs.per_wave;
-    if (p0 >= rs.passes) return;
-    const int p1 = min(rs.passes, p0 + rs.per_wave);
-    const int u8 = gl & 7;
-
-    Q6KX X[UPL];
-    bool uv[UPL];
-#pragma unroll
-    for (int i = 0; i < UPL; ++i) {
-        const int u = gl + G * i;
-        uv[i] = u < U;
-        if (uv[i]) q6k_load_x(X[i], x, u >> 3, u8);
-    }
-
-    for (int pass = p0; pass < p1; pass += RB) {
-        Q6KRaw R[RB][UPL];
-        bool rv[RB];
-        int rr[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            rr[b] = (pass + b) * RPP + grow;
-            rv[b] = (pass + b) < p1 && rr[b] < rs.n;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv[b] && uv[i])
-                    q6k_load(R[b][i], w + (size_t)rr[b] * row_bytes + (size_t)((gl + G * i) >> 3) * 210, u8);
-        }
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv[b] && uv[i]) acc += q6k_unit_dot(R[b][i], X[i], u8);
-            acc = group_sum<G>(acc);
-            if (gl == 0 && rv[b]) y[rr[b]] = acc;
-        }
-    }
-}
-
-// --------------------------------------------------------------------- Q8_0
-template <int G, int UPL, int RB>
-__global__ __launch_bounds__(256) void k_qmv_q8_0(const uint8_t *__restrict__ w,
-                                                  const float *__restrict__ x,
-                                                  float *__restrict__ y, RowSched rs, int U,
-                                                  int row_bytes) {
-    constexpr int RPP = 64 / G;
-    const int lane = threadIdx.x & 63;
-    const int gl = lane & (G - 1);
-    const int grow = lane / G;
-    const int wave = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
-    const int p0 = wave * rs.per_wave;
-    if (p0 >= rs.passes) return;
-    const int p1 = min(rs.passes, p0 + rs.per_wave);
-
-    float X[UPL][64];
-    bool uv[UPL];
-#pragma unroll
-    for (int i = 0; i < UPL; ++i) {
-        const int u = gl + G * i;
-        uv[i] = u < U;
-        if (uv[i]) {
-            const float4 *a = reinterpret_cast<const float4 *>(x + 64 * u);
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float4 v = a[t];
-                X[i][4 * t] = v.x; X[i][4 * t + 1] = v.y; X[i][4 * t + 2] = v.z; X[i][4 * t + 3] = v.w;
-            }
-        }
-    }
-
-    for (int pass = p0; pass < p1; pass += RB) {
-        Q8Pair P[RB][UPL];
-        bool rv[RB];
-        int rr[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            rr[b] = (pass + b) * RPP + grow;
-            rv[b] = (pass + b) < p1 && rr[b] < rs.n;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv[b] && uv[i]) q8_load(P[b][i], w + (size_t)rr[b] * row_bytes + (size_t)(gl + G * i) * 68);
-        }
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv[b] && uv[i]) acc += q8_pair_dot(P[b][i], X[i]);
-            acc = group_sum<G>(acc);
-            if (gl == 0 && rv[b]) y[rr[b]] = acc;
+            __builtin_amdgcn_sched_barrier(0);
+            load_pass(R[j], min(ps + NB, p1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            acc = group_sum_last<G>(acc);
+            if (gl == G - 1 && ps < p1 && r < n) y[r] = acc;
         }
     }
 }
@@ -185,7 +107,7 @@ __global__ __launch_bounds__(256) void k_qmv_q8_0(const uint8_t *__restrict__ w,
 // ------------------------------------------------------- generic fallback
 // One wave per row, lanes over blocks, byte loads: any k that is a block
 // multiple and any alignment of rows (used when the unit tiling above does
-// not apply, e.g. Q8_0 with k % 64 == 32 or very long rows).
+// not apply: Q8_0 with k % 64 == 32, or rows longer than 2*64 units).
 __device__ float block_dot_generic(int fmt, const uint8_t *b, const float *x) {
     float acc = 0.0f;
     if (fmt == 0) {
@@ -250,81 +172,91 @@ __global__ __launch_bounds__(256) void k_qmv_generic(int fmt, const uint8_t *__r
 }
 
 // ------------------------------------------------------------- dispatch
-RowSched make_sched(int64_t n, int G, int64_t target_waves) {
-    RowSched rs;
-    rs.n = (int)n;
-    const int rpp = 64 / G;
-    rs.passes = (int)((n + rpp - 1) / rpp);
-    int per = (int)((rs.passes + target_waves - 1) / target_waves);
-    rs.per_wave = per < 1 ? 1 : per;
-    return rs;
+struct DevInfo {
+    int device = -1;
+    int cus = 256;
+};
+
+int compute_units() {
+    static thread_local DevInfo info;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (info.device != dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        info.device = dev;
+        info.cus = cus;
+    }
+    return info.cus;
 }
 
-// Waves to aim for: enough rows in flight to cover HBM latency on 256 CUs,
-// few enough that each wave amortizes its activation loads over many rows.
-constexpr int64_t TARGET_WAVES = 4096;
+// Resident waves of a kernel on the whole device (one full round).
+template <class K>
+int64_t resident_waves(K kernel, size_t lds) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
+        per_cu = 2;
+    return (int64_t)per_cu * compute_units() * WAVES_PER_BLOCK * ROUNDS_X4 / 4;
+}
 
-#define QMV_DISPATCH(KERNEL, G, UPL, ...)                                                     \
-    do {                                                                                    \
-        RowSched rs = make_sched(n, G, TARGET_WAVES);                                       \
-        const int64_t waves = (rs.passes + rs.per_wave - 1) / rs.per_wave;                  \
-        const dim3 grid((unsigned)((waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));      \
-        hipLaunchKernelGGL((KERNEL<G, UPL, 2>), grid, dim3(256), 0, stream, __VA_ARGS__, rs, \
-                           (int)U, (int)row_bytes);                                         \
-    } while (0)
-
-template <int F>
-int launch_dense(const uint8_t *w, const float *x, float *y, int64_t n, int64_t k, hipStream_t stream) {
-    // units per row and their tiling
-    const int64_t bw = F == 0 ? 32 : 256, bb = F == 0 ? 34 : (F == 1 ? 144 : 210);
-    const int64_t row_bytes = k / bw * bb;
-    int64_t U;
-    bool tiled;
-    if (F == 0) {
-        U = k / 64;
-        tiled = (k % 64 == 0) && U >= 1;
-    } else {
-        U = (k / 256) * 8;
-        tiled = true;
+template <class F, int G, int UPL>
+void launch(const uint8_t *w, const float *x, float *y, int64_t n, int64_t k, int64_t row_bytes,
+            hipStream_t s) {
+    const int64_t rpp = 64 / G;
+    const int64_t passes = (n + rpp - 1) / rpp;
+    const size_t lds = (size_t)(k / 64) * XSTRIDE * 4;
+    // occupancy depends on (device, LDS bytes) only: remember the last answer
+    static thread_local int c_dev = -1;
+    static thread_local size_t c_lds = 0;
+    static thread_local int64_t c_target = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != c_dev || lds != c_lds) {
+        c_target = resident_waves(k_dense<F, G, UPL>, lds);
+        c_dev = dev;
+        c_lds = lds;
     }
-    const int G = next_pow2_le64(U);
-    const int64_t upl = (U + G - 1) / G;
-    if (!tiled || upl > (F == 0 ? 2 : 4)) {
+    const int64_t target = c_target;
+    int64_t per = (passes + target - 1) / target;
+    if (per < 1) per = 1;
+    const int64_t waves = (passes + per - 1) / per;
+    const dim3 grid((unsigned)((waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
+    hipLaunchKernelGGL((k_dense<F, G, UPL>), grid, dim3(256), lds, s, w, x, y, (int)n, (int)k, (int)row_bytes,
+                       (int)per);
+}
+
+template <class F>
+int launch_dense(const uint8_t *w, const float *x, float *y, int64_t n, int64_t k, hipStream_t s) {
+    const int64_t row_bytes = k / F::BW * F::BB;
+    const bool tiled = (k % 64 == 0) && k <= 8192;  // units of 64 weights, x fits LDS
+    const int64_t U = k / 64;
+    const int fmt = F::BB == 34 ? 0 : (F::BB == 144 ? 1 : 2);
+    if (!tiled) {
         const dim3 grid((unsigned)((n + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
-        hipLaunchKernelGGL(k_qmv_generic, grid, dim3(256), 0, stream, F, w, x, y, n, k, row_bytes);
+        hipLaunchKernelGGL(k_qmv_generic, grid, dim3(256), 0, s, fmt, w, x, y, n, k, row_bytes);
         QMV_LAUNCH_CHECK();
         return QMV_OK;
     }
-#define QMV_CASES(KERNEL)                                                     \
-    switch (G) {                                                              \
-        case 1: QMV_DISPATCH(KERNEL, 1, 1, w, x, y); break;                   \
-        case 2: QMV_DISPATCH(KERNEL, 2, 1, w, x, y); break;                   \
-        case 4: QMV_DISPATCH(KERNEL, 4, 1, w, x, y); break;                   \
-        case 8: QMV_DISPATCH(KERNEL, 8, 1, w, x, y); break;                   \
-        case 16: QMV_DISPATCH(KERNEL, 16, 1, w, x, y); break;                 \
-        case 32: QMV_DISPATCH(KERNEL, 32, 1, w, x, y); break;                 \
-        default:                                                              \
-            if (upl == 1) QMV_DISPATCH(KERNEL, 64, 1, w, x, y);               \
-            else if (upl == 2) QMV_DISPATCH(KERNEL, 64, 2, w, x, y);          \
-            else if (F != 0 && upl == 3) QMV_DISPATCH(KERNEL, 64, 3, w, x, y);\
-            else if (F != 0) QMV_DISPATCH(KERNEL, 64, 4, w, x, y);            \
+    const int G = next_pow2_le64(U);
+    switch (G) {
+        case 1: launch<F, 1, 1>(w, x, y, n, k, row_bytes, s); break;
+        case 2: launch<F, 2, 1>(w, x, y, n, k, row_bytes, s); break;
+        case 4: launch<F, 4, 1>(w, x, y, n, k, row_bytes, s); break;
+        case 8: launch<F, 8, 1>(w, x, y, n, k, row_bytes, s); break;
+        case 16: launch<F, 16, 1>(w, x, y, n, k, row_bytes, s); break;
+        case 32: launch<F, 32, 1>(w, x, y, n, k, row_bytes, s); break;
+        default:
+            if (U <= 64) launch<F, 64, 1>(w, x, y, n, k, row_bytes, s);
+            else launch<F, 64, 2>(w, x, y, n, k, row_bytes, s);
     }
-    if (F == 0) {
-        QMV_CASES(k_qmv_q8_0)
-    } else if (F == 1) {
-        QMV_CASES(k_qmv_q4k)
-    } else {
-        QMV_CASES(k_qmv_q6k)
-    }
-#undef QMV_CASES
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
 
-template <int F>
+template <class F>
 int dense_entry(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream) {
-    const int64_t bw = F == 0 ? 32 : 256;
-    if (!w || !x || !y || n < 1 || k < bw || k % bw) return QMV_EINVAL;
+    if (!w || !x || !y || n < 1 || k < F::BW || k % F::BW) return QMV_EINVAL;
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 24) return QMV_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMV_EALIGN;
     return launch_dense<F>(static_cast<const uint8_t *>(w), x, y, n, k, (hipStream_t)stream);
@@ -333,11 +265,11 @@ int dense_entry(const void *w, const float *x, float *y, int64_t n, int64_t k, q
 }  // namespace
 
 extern "C" int qmv_q8_0(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
-    return dense_entry<0>(w, x, y, n, k, s);
+    return dense_entry<Q8Unit>(w, x, y, n, k, s);
 }
 extern "C" int qmv_q4k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
-    return dense_entry<1>(w, x, y, n, k, s);
+    return dense_entry<Q4KUnit>(w, x, y, n, k, s);
 }
 extern "C" int qmv_q6k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
-    return dense_entry<2>(w, x, y, n, k, s);
+    return dense_entry<Q6KUnit>(w, x, y, n, k, s);
 }
