@@ -37,7 +37,8 @@ N2, K2 = 14336, 4096
 Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
 METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
 KERNEL_SOURCES = ["include/qmv.h", "moe_ggml_block_amd/csrc/common.hpp",
-                  "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/qmv_dense.hip"]
+                  "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/dense.hpp",
+                  "moe_ggml_block_amd/csrc/qmv_dense.hip"]
 
 
 def log(msg: str) -> None:

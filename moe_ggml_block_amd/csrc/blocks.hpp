@@ -88,22 +88,60 @@ QMV_DEV void load_x_lds(UnitX &X, const float *xl, int u) {
     }
 }
 
-// Cooperative fill of the staged layout from x[0..k) (float4 granules; a
-// granule never straddles two runs). Every thread of the block calls it.
+// Cooperative fill of the staged layout from x[0..k), in two phases so the
+// global loads can be issued before the weight loads (a wait for them then
+// does not wait for the weights): fetch() loads this thread's float4 granules
+// (at most STAGE_MAX of them, k <= 4*256*STAGE_MAX), store() writes them to
+// their slots. A granule never straddles two runs.
+constexpr int STAGE_MAX = 8;
+
+// Native vector types: HIP's float4/uint4 wrapper structs are copied with
+// memcpy, which keeps a private-memory (scratch) copy alive here.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef f32x4 StageRegs[STAGE_MAX];
+
+// Indices past the end are clamped to the last granule (loaded and stored
+// again, harmlessly), which keeps both phases branch-free and in registers.
+QMV_DEV void fetch_x(StageRegs &S, const float *x, int k) {
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    const int last = k / 4 - 1;
+#pragma unroll
+    for (int m = 0; m < STAGE_MAX; ++m) S[m] = x4[min((int)threadIdx.x + 256 * m, last)];
+}
+
 template <class F>
-QMV_DEV void stage_x(float *xl, const float *x, int k) {
-    const float4 *x4 = reinterpret_cast<const float4 *>(x);
-    for (int i4 = threadIdx.x; i4 < k / 4; i4 += blockDim.x) {
-        const int i = 4 * i4;
+QMV_DEV void store_x(float *xl, const StageRegs &S, int k) {
+    const int last = k / 4 - 1;
+#pragma unroll
+    for (int m = 0; m < STAGE_MAX; ++m) {
+        const int i4 = min((int)threadIdx.x + 256 * m, last);
         int j;
-        const int u = F::xslot(i, &j);
-        *reinterpret_cast<float4 *>(xl + XSTRIDE * u + j) = x4[i4];
+        const int u = F::xslot(4 * i4, &j);
+        *reinterpret_cast<f32x4 *>(xl + XSTRIDE * u + j) = S[m];
     }
 }
 
+// f32 activation pack and its per-unit staging (shared by the f32 units).
+struct ActF32 {
+    const float *x;
+};
+
+template <class F>
+struct F32Act {
+    using Act = ActF32;
+    using X = UnitX;
+    using Stage = StageRegs;
+    static constexpr int ACT_STRIDE = XSTRIDE;
+    static __device__ __forceinline__ void fetch(Stage &S, ActF32 a, int k) { fetch_x(S, a.x, k); }
+    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) { store_x<F>(xl, S, k); }
+    static __device__ __forceinline__ void load_lds(UnitX &X, const float *xl, int u) { load_x_lds(X, xl, u); }
+};
+
 // ---------------------------------------------------------------- Q8_0 ---
-struct Q8Unit {
+struct Q8Unit : F32Act<Q8Unit> {
     static constexpr int BW = 32, BB = 34;
+    static constexpr int RING = 1;  // row passes in flight per wave (measured best)
     static constexpr int UNITS_PER_BLOCKS = 2;  // informational
     struct Raw {
         uint32_t d[17];
@@ -166,8 +204,9 @@ QMV_DEV void q4k_scales(uint32_t m1, uint32_t m2, uint32_t m3, int p, uint32_t *
     }
 }
 
-struct Q4KUnit {
+struct Q4KUnit : F32Act<Q4KUnit> {
     static constexpr int BW = 256, BB = 144;
+    static constexpr int RING = 2;
     struct Raw {
         uint4 q0, q1, m;
     };
@@ -230,8 +269,9 @@ QMV_DEV uint2 ld8u(const uint8_t *p) {
     return *q;
 }
 
-struct Q6KUnit {
+struct Q6KUnit : F32Act<Q6KUnit> {
     static constexpr int BW = 256, BB = 210;
+    static constexpr int RING = 2;
     struct Raw {
         uint4 a, b, h;
         uint2 sc;
@@ -286,5 +326,96 @@ struct Q6KUnit {
         r = fmaf(c2, fmaf(-32.0f, X.s[2], acc[2]), r);
         r = fmaf(c3, fmaf(-32.0f, X.s[3], acc[3]), r);
         return h2f(R.d) * r;
+    }
+};
+
+// ------------------------------------------------------ Q4_K x q8 (dot4) ---
+// Same 64-weight unit as Q4KUnit: unit u = (s, p) covers sub-blocks 2p and
+// 2p+1 of superblock s, which are exactly q8 activation blocks 2u and 2u+1.
+// Its activation form is the 64 int8 codes xq[64u .. 64u+64) as 16 dwords
+// plus xs and xsum of blocks 2u, 2u+1; staged in LDS at 20 dwords per unit
+// (8 consecutive units' 16-byte reads land in disjoint banks).
+struct ActQ8 {
+    const int8_t *xq;
+    const float *xs;
+    const float *xsum;
+};
+
+struct UnitQ8 {
+    int32_t q[16];
+    float xs[2], xsum[2];
+};
+
+// Exact integer sums of one unit: S_lo over sub-block 2p (low nibbles),
+// S_hi over sub-block 2p+1 (high nibbles), 4 code x 4 activation bytes per
+// v_dot4 (codes 0..15 are non-negative int8).
+QMV_DEV void q4k_q8_sums(const Q4KUnit::Raw &R, const int32_t *xq16, int32_t *slo, int32_t *shi) {
+    const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+    int32_t a = 0, b = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        a = __builtin_amdgcn_sdot4((int)(qw[t] & 0x0F0F0F0Fu), xq16[t], a, false);
+        b = __builtin_amdgcn_sdot4((int)((qw[t] >> 4) & 0x0F0F0F0Fu), xq16[8 + t], b, false);
+    }
+    *slo = a;
+    *shi = b;
+}
+
+struct Q4KQ8Unit {
+    static constexpr int BW = 256, BB = 144;
+    static constexpr int RING = 2;
+    static constexpr int ACT_STRIDE = 20;
+    using Act = ActQ8;
+    using X = UnitQ8;
+    using Raw = Q4KUnit::Raw;
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) { Q4KUnit::load(R, row, u); }
+    // per thread: up to 4 dwords of xq (k <= 4096 per pass of 256 threads,
+    // 2 passes for k <= 8192) and up to 1 block's xs/xsum
+    typedef u32x4 Stage[3];  // 2 x 16 bytes of xq, then {xs, xsum, -, -}
+    // (branch-free: indices past the end are clamped and re-stored)
+    static __device__ __forceinline__ void fetch(Stage &S, ActQ8 a, int k) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(a.xq);
+        const int lastq = k / 16 - 1, lastb = k / 32 - 1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) S[m] = q[min((int)threadIdx.x + 256 * m, lastq)];
+        const int b = min((int)threadIdx.x, lastb);
+        S[2].x = __float_as_uint(a.xs[b]);
+        S[2].y = __float_as_uint(a.xsum[b]);
+    }
+    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) {
+        uint32_t *l = reinterpret_cast<uint32_t *>(xl);
+        const int lastq = k / 16 - 1, lastb = k / 32 - 1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = min((int)threadIdx.x + 256 * m, lastq);  // dwords 4i..4i+3 of unit i/4
+            *reinterpret_cast<u32x4 *>(l + ACT_STRIDE * (i >> 2) + 4 * (i & 3)) = S[m];
+        }
+        const int b = min((int)threadIdx.x, lastb);
+        xl[ACT_STRIDE * (b >> 1) + 16 + (b & 1)] = __uint_as_float(S[2].x);
+        xl[ACT_STRIDE * (b >> 1) + 18 + (b & 1)] = __uint_as_float(S[2].y);
+    }
+    static __device__ __forceinline__ void load_lds(UnitQ8 &X, const float *xl, int u) {
+        const int4 *p = reinterpret_cast<const int4 *>(xl + ACT_STRIDE * u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int4 v = p[t];
+            X.q[4 * t] = v.x; X.q[4 * t + 1] = v.y; X.q[4 * t + 2] = v.z; X.q[4 * t + 3] = v.w;
+        }
+        const float4 f = reinterpret_cast<const float4 *>(xl + ACT_STRIDE * u)[4];
+        X.xs[0] = f.x; X.xs[1] = f.y; X.xsum[0] = f.z; X.xsum[1] = f.w;
+    }
+    // y contribution: d*sc_j*xs_b*S_b - dmin*m_j*xsum_b for the unit's two blocks
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8 &X, int u) {
+        int32_t slo, shi;
+        q4k_q8_sums(R, X.q, &slo, &shi);
+        uint32_t sc2, mn2;
+        q4k_scales(R.m.y, R.m.z, R.m.w, u & 3, &sc2, &mn2);
+        const float d = h2f(R.m.x), dmin = h2f(R.m.x >> 16);
+        float r = (d * ubyte_f<0>(sc2)) * (X.xs[0] * (float)slo);
+        r = fmaf(d * ubyte_f<1>(sc2), X.xs[1] * (float)shi, r);
+        r = fmaf(-(dmin * ubyte_f<0>(mn2)), X.xsum[0], r);
+        r = fmaf(-(dmin * ubyte_f<1>(mn2)), X.xsum[1], r);
+        return r;
     }
 };
