@@ -35,6 +35,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_I8_PEAK_TOPS = 5000.0
 N2, K2 = 14336, 4096
 Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
+# one qmv_q4k launch: every packed row (2,304 B) plus its f32 output, and x once
+Q4K_LAUNCH_BYTES = Q4K_BYTES + 4 * N2 + 4 * K2  # 33,103,872
+CALIB_BYTES = 64 << 20                         # the counter-calibration copy
+TRAFFIC_JSON = os.path.join("profiles", "qmv_q4k_14336x4096_traffic.json")
 METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
 KERNEL_SOURCES = ["include/qmv.h", "moe_ggml_block_amd/csrc/common.hpp",
                   "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/dense.hpp",
@@ -104,7 +108,7 @@ def time_graph(fn, calls: int, replays: int = 20) -> float:
 def traffic_from_profile(kernel_hash: str):
     """HBM bytes per launch of qmv_q4k from the committed PMC summary, if it was
     taken on the current kernel source (else None)."""
-    p = os.path.join(ROOT, "profiles", "qmv_q4k_14336x4096_traffic.json")
+    p = os.path.join(ROOT, TRAFFIC_JSON)
     if not os.path.exists(p):
         return None
     try:
@@ -294,8 +298,9 @@ def prefill_other(copies: int = 16):
 def profile_run(copies: int, other_shapes: bool = False):
     """Short eager run for rocprofv3: 64 launches each of qmv_q4k and
     qmv_q4k_q8 over the rotating weight copies, 64 quantize_act_q8 calls, and
-    8 plain device-to-device copies of 64 MiB (a copy kernel of known traffic
-    that calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
+    8 launches of torch's elementwise neg over 16 Mi floats (a copy kernel
+    that reads and writes exactly 64 MiB: it calibrates the FETCH_SIZE and
+    WRITE_SIZE counters)."""
     import torch
     import moe_ggml_block_amd as qmv
     import synth
@@ -310,11 +315,10 @@ def profile_run(copies: int, other_shapes: bool = False):
         qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum))
     for i in range(64):
         qmv.qmv_q4k_q8(W[i % copies], xq, xs, xsum, N2, K2, y=y)
-    a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    a = torch.ones(CALIB_BYTES // 4, device="cuda")
     b = torch.empty_like(a)
-    a.fill_(1)
     for _ in range(8):
-        b.copy_(a)
+        torch.neg(a, out=b)
     del big, W
     if other_shapes:
         for fmt, fn, n, k, reps in (("q8_0", qmv.qmv_q8_0, 4096, 4096, 32), ("q6k", qmv.qmv_q6k, 128256, 4096, 8)):
@@ -325,15 +329,61 @@ def profile_run(copies: int, other_shapes: bool = False):
                 fn(Wo[i % 3], x, n, k, y=yo)
             del bigo, Wo
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, copy 64MiB x8"
+    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, neg 64MiB x8"
                       + (", qmv_q8_0 4096x4096 x32, qmv_q6k 128256x4096 x8" if other_shapes else ""),
-                      "q4k_bytes": Q4K_BYTES, "copy_bytes": 64 << 20}))
+                      "q4k_bytes": Q4K_BYTES, "copy_bytes": CALIB_BYTES}))
+
+
+def counter_rows(csv_path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3
+    counter_collection.csv."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """HBM-side bytes per qmv_q4k launch from two rocprofv3 --pmc runs of
+    `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by what the counter reads for the 64 MiB neg copy. Writes the
+    summary next to the other profiles and returns it."""
+    import statistics
+
+    def pick(rows, key):
+        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named like {key!r}")
+        return statistics.median(vals), len(vals)
+
+    fetch, write = counter_rows(fetch_csv, "FETCH_SIZE"), counter_rows(write_csv, "WRITE_SIZE")
+    f_q, nf = pick(fetch, "k_dense<Q4KUnit, 64, 1>")
+    w_q, nw = pick(write, "k_dense<Q4KUnit, 64, 1>")
+    f_c, _ = pick(fetch, "neg_kernel")
+    w_c, _ = pick(write, "neg_kernel")
+    fs, ws = CALIB_BYTES / (f_c * 1024), CALIB_BYTES / (w_c * 1024)
+    hbm = f_q * 1024 * fs + w_q * 1024 * ws
+    d = {"kernel": "qmv_q4k (k_dense<Q4KUnit, 64, 1>)", "workload": "Q4_K 14336x4096, 32 rotating weight copies",
+         "kernel_source_hash": source_hash(KERNEL_SOURCES),
+         "fetch_kib_median": f_q, "write_kib_median": w_q, "dispatches": [nf, nw],
+         "calib_fetch_kib": f_c, "calib_write_kib": w_c, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+         "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": Q4K_LAUNCH_BYTES,
+         "ratio_to_algorithmic": round(hbm / Q4K_LAUNCH_BYTES, 4)}
+    with open(os.path.join(ROOT, TRAFFIC_JSON), "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    return d
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--profile", action="store_true", help="short eager run for rocprofv3")
     ap.add_argument("--profile-all", action="store_true", help="--profile plus the Q8_0 and Q6_K shapes")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize two rocprofv3 --pmc runs of --profile into the traffic file, then exit")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
@@ -342,6 +392,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     a = ap.parse_args()
+    if a.write_traffic:
+        print(json.dumps(write_traffic(*a.write_traffic)))
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this decode path runs on one GPU; --gpus must be 1 "
               "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
@@ -361,7 +414,7 @@ def main():
     log(f"headline done: {h['ms_per_step'] * 1e3:.2f} us/step")
     value = 2 * Q4K_BYTES / (h["ms_per_step"] * 1e-3) / 1e9
     q4k_us = h["q4k_launch_ms"] * 1e3
-    achieved = Q4K_BYTES / (h["q4k_launch_ms"] * 1e-3) / 1e9
+    achieved = Q4K_LAUNCH_BYTES / (h["q4k_launch_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile(khash)
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -374,7 +427,7 @@ def main():
         "hbm_pct": round(value / HBM_PEAK_GBS * 100, 2),
         "roofline": {"kernel": "qmv_q4k", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": Q4K_BYTES, "avg_launch_us": round(q4k_us, 3),
+                     "algorithmic_bytes_per_launch": Q4K_LAUNCH_BYTES, "avg_launch_us": round(q4k_us, 3),
                      "kernel_source_hash": khash},
         "kernels": h["kernels"],
     }
