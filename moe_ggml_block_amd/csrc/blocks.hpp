@@ -93,6 +93,20 @@ QMV_DEV void load_x_lds(UnitX &X, const float *xl, int u) {
 // does not wait for the weights): fetch() loads this thread's float4 granules
 // (at most STAGE_MAX of them, k <= 4*256*STAGE_MAX), store() writes them to
 // their slots. A granule never straddles two runs.
+// Row passes each wave keeps in flight, per format (measured).
+#ifndef QMV_RING_Q8
+#define QMV_RING_Q8 1
+#endif
+#ifndef QMV_RING_Q4K
+#define QMV_RING_Q4K 2
+#endif
+#ifndef QMV_RING_Q6K
+#define QMV_RING_Q6K 2
+#endif
+#ifndef QMV_RING_Q4KQ8
+#define QMV_RING_Q4KQ8 2
+#endif
+
 constexpr int STAGE_MAX = 8;
 
 // Native vector types: HIP's float4/uint4 wrapper structs are copied with
@@ -141,7 +155,7 @@ struct F32Act {
 // ---------------------------------------------------------------- Q8_0 ---
 struct Q8Unit : F32Act<Q8Unit> {
     static constexpr int BW = 32, BB = 34;
-    static constexpr int RING = 1;  // row passes in flight per wave (measured best)
+    static constexpr int RING = QMV_RING_Q8;  // row passes in flight per wave (measured best)
     static constexpr int UNITS_PER_BLOCKS = 2;  // informational
     struct Raw {
         uint32_t d[17];
@@ -206,7 +220,7 @@ QMV_DEV void q4k_scales(uint32_t m1, uint32_t m2, uint32_t m3, int p, uint32_t *
 
 struct Q4KUnit : F32Act<Q4KUnit> {
     static constexpr int BW = 256, BB = 144;
-    static constexpr int RING = 2;
+    static constexpr int RING = QMV_RING_Q4K;
     struct Raw {
         uint4 q0, q1, m;
     };
@@ -271,7 +285,7 @@ QMV_DEV uint2 ld8u(const uint8_t *p) {
 
 struct Q6KUnit : F32Act<Q6KUnit> {
     static constexpr int BW = 256, BB = 210;
-    static constexpr int RING = 2;
+    static constexpr int RING = QMV_RING_Q6K;
     struct Raw {
         uint4 a, b, h;
         uint2 sc;
@@ -363,7 +377,7 @@ QMV_DEV void q4k_q8_sums(const Q4KUnit::Raw &R, const int32_t *xq16, int32_t *sl
 
 struct Q4KQ8Unit {
     static constexpr int BW = 256, BB = 144;
-    static constexpr int RING = 2;
+    static constexpr int RING = QMV_RING_Q4KQ8;
     static constexpr int ACT_STRIDE = 20;
     using Act = ActQ8;
     using X = UnitQ8;

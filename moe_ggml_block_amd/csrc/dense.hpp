@@ -54,9 +54,13 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     // not one far-apart stream each.
     const int wave = blockIdx.x * WAVES_PER_BLOCK + (tid >> 6);
     const int nwaves = gridDim.x * WAVES_PER_BLOCK;
+    // passes of this wave (0 for the spare waves of the last workgroup); the
+    // loop below runs at least once so that no branch separates the ring
+    // loads from the barrier (the compiler would sink them past it), and the
+    // spare waves discard their clamped pass.
     const int p0 = 0;
-    const int p1 = wave < passes ? (passes - wave + nwaves - 1) / nwaves : 0;
-    const bool idle = p0 >= p1;  // still takes part in the x staging barrier
+    const int pr = (passes - wave + nwaves - 1) / nwaves;  // wave < nwaves
+    const int p1 = max(pr, 1);
     bool uv[UPL];
     int uu[UPL];  // unit actually read (clamped into the row)
 #pragma unroll
@@ -89,9 +93,9 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     typename F::X X[UPL];
 #pragma unroll
     for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
-    if (idle) return;
 
-    for (int pass = p0; pass < p1; pass += NB) {
+    int pass = p0;
+    do {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int ps = pass + j;
@@ -106,9 +110,10 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
             load_pass(R[j], min(ps + NB, p1 - 1));
             __builtin_amdgcn_sched_barrier(0);
             acc = group_sum_last<G>(acc);
-            if (gl == G - 1 && ps < p1 && r < n) y[r] = acc;
+            if (gl == G - 1 && ps < pr && r < n) y[r] = acc;
         }
-    }
+        pass += NB;
+    } while (pass < p1);
 }
 
 struct DevInfo {
