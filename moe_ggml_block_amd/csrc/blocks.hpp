@@ -117,18 +117,24 @@ typedef f32x4 StageRegs[STAGE_MAX];
 
 // Indices past the end are clamped to the last granule (loaded and stored
 // again, harmlessly), which keeps both phases branch-free and in registers.
+// Granules (16 bytes of x per thread of a 256-thread block) that a row of
+// k <= 64*G*UPL activations needs: k/4 float4 over 256 threads.
+constexpr int stage_granules(int G, int UPL) {
+    return G * UPL / 16 < 1 ? 1 : (G * UPL / 16 > STAGE_MAX ? STAGE_MAX : G * UPL / 16);
+}
+template <int NS>
 QMV_DEV void fetch_x(StageRegs &S, const float *x, int k) {
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
     const int last = k / 4 - 1;
 #pragma unroll
-    for (int m = 0; m < STAGE_MAX; ++m) S[m] = x4[min((int)threadIdx.x + 256 * m, last)];
+    for (int m = 0; m < NS; ++m) S[m] = x4[min((int)threadIdx.x + 256 * m, last)];
 }
 
-template <class F>
+template <class F, int NS>
 QMV_DEV void store_x(float *xl, const StageRegs &S, int k) {
     const int last = k / 4 - 1;
 #pragma unroll
-    for (int m = 0; m < STAGE_MAX; ++m) {
+    for (int m = 0; m < NS; ++m) {
         const int i4 = min((int)threadIdx.x + 256 * m, last);
         int j;
         const int u = F::xslot(4 * i4, &j);
@@ -147,8 +153,10 @@ struct F32Act {
     using X = UnitX;
     using Stage = StageRegs;
     static constexpr int ACT_STRIDE = XSTRIDE;
-    static __device__ __forceinline__ void fetch(Stage &S, ActF32 a, int k) { fetch_x(S, a.x, k); }
-    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) { store_x<F>(xl, S, k); }
+    template <int NS>
+    static __device__ __forceinline__ void fetch(Stage &S, ActF32 a, int k) { fetch_x<NS>(S, a.x, k); }
+    template <int NS>
+    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) { store_x<F, NS>(xl, S, k); }
     static __device__ __forceinline__ void load_lds(UnitX &X, const float *xl, int u) { load_x_lds(X, xl, u); }
 };
 
@@ -388,6 +396,7 @@ struct Q4KQ8Unit {
     // 2 passes for k <= 8192) and up to 1 block's xs/xsum
     typedef u32x4 Stage[3];  // 2 x 16 bytes of xq, then {xs, xsum, -, -}
     // (branch-free: indices past the end are clamped and re-stored)
+    template <int NS>  // (the q8 stage is always 2 granules of xq + scales)
     static __device__ __forceinline__ void fetch(Stage &S, ActQ8 a, int k) {
         const u32x4 *q = reinterpret_cast<const u32x4 *>(a.xq);
         const int lastq = k / 16 - 1, lastb = k / 32 - 1;
@@ -397,6 +406,7 @@ struct Q4KQ8Unit {
         S[2].x = __float_as_uint(a.xs[b]);
         S[2].y = __float_as_uint(a.xsum[b]);
     }
+    template <int NS>
     static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) {
         uint32_t *l = reinterpret_cast<uint32_t *>(xl);
         const int lastq = k / 16 - 1, lastb = k / 32 - 1;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     }
     // activations first (their wait must not drain the weight ring)
     typename F::Stage S;
-    F::fetch(S, act, k);
+    F::template fetch<stage_granules(G, UPL)>(S, act, k);
     Raw R[NB][UPL];
     auto load_pass = [&](Raw (&B)[UPL], int pass) {
         const int r = max(min((pass * nwaves + wave) * RPP + grow, n - 1), 0);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     }
     // activations: coalesced loads into the padded LDS layout, then each
     // lane reads its units' values (conflict-free) into registers
-    F::store(xlds, S, k);
+    F::template store<stage_granules(G, UPL)>(xlds, S, k);
     __syncthreads();
     typename F::X X[UPL];
 #pragma unroll

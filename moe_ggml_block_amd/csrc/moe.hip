@@ -9,81 +9,149 @@
 //    resident [E, n, k] bank, output in slot order, ids never read back;
 //  - `silu_mul` and the engine's `broadcast_mul(scores).sum` combine.
 //
-// Expert grouping: workgroup (row block rb, group g) serves the g-th distinct
-// expert present in ids (ascending expert id) and every slot routed to it, in
-// slot order, so an expert's rows are streamed from HBM once per call however
-// many slots chose it. The grouping is recomputed by each workgroup from ids
-// (a bitmap of present experts in LDS and a ballot compaction of the slots);
-// the grid has min(E, nslots) groups and workgroups past the number of
-// distinct experts exit at once.
+// Expert grouping: a work item (expert g, row block rb) covers the rows of
+// the block of the g-th distinct expert present in ids (ascending expert id)
+// for every slot routed to it, in slot order, so an expert's rows come from
+// HBM once per call however many slots chose it (a second slot re-reads the
+// block's rows from L2). Each workgroup copies ids into LDS once and derives
+// the grouping there (a bitmap of present experts, their ordered list, and a
+// ballot compaction of the slots of an item's expert); the workgroups then
+// loop over the items, whose number is known only on the device.
+//
+// The activation row of a slot is staged through registers into a padded
+// LDS layout (the dense kernels' layout), the weight loads of the block's
+// first passes are issued before that staging, and each lane then keeps its
+// unit's 64 activation values in registers while it streams rows.
+//
+// In the layer, gate and up are one gather over interleaved rows (gate row
+// i, then up row i) so that one wave holds both dots of a row and writes
+// h = silu(g) * u directly; the down pass is organised by token: workgroup
+// (row block, token) streams the rows of the block for each routed expert
+// and sums them with the routing weights itself, so no workgroup waits for
+// another and no separate combine kernel runs.
+#include <cmath>
+
 #include "blocks.hpp"
 
 namespace {
 
 constexpr int MAX_E = 4096;
-constexpr int MAX_SLOTS = 4096;
+constexpr int MAX_SLOTS = 2048;
 constexpr int WAVES = 4;
+constexpr int SMALL_E = 256;  // router: one workgroup per token up to this E
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- router ---
-// One wave per token, VPL logits per lane (lane l holds experts l + 64 v).
-// topk rounds of a wave-wide argmax on (value desc, index asc); NaN and
-// padding rank as -inf, padding and taken entries carry index INT_MAX so a
-// real -inf entry always beats them.
+// Sort key of (logit, expert): larger key = earlier in the top-k order.
+// NaN ranks as -inf, -0 as +0, and equal logits put the lower expert first.
+QMV_DEV uint64_t route_key(float v, int e) {
+    v = (v != v) ? -INFINITY : v + 0.0f;
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// E <= 256, one workgroup per token. An expert's rank is the number of keys
+// above its own. With EP = next power of two >= E, the key list is cut into
+// P = min(256/EP, EP) partitions of L = EP/P keys; thread (part, e) counts
+// partition `part` for expert e, so each thread does at most EP*EP/256
+// compares (64 at E = 128).
+__global__ __launch_bounds__(256) void k_route_small(const float *__restrict__ logits,
+                                                     int32_t *__restrict__ ids,
+                                                     float *__restrict__ wts, int E, int EP,
+                                                     int topk) {
+    __shared__ uint64_t keys[SMALL_E];
+    __shared__ int part_cnt[256];
+    __shared__ float sel_v[64];
+    __shared__ int sel_e[64];
+    __shared__ float sel_p[64];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float *lg = logits + (size_t)t * E;
+    float v = -INFINITY;
+    if (tid < EP) {
+        uint64_t key = 0;  // padding ranks below every real key
+        if (tid < E) {
+            v = lg[tid];
+            key = route_key(v, tid);
+        }
+        keys[tid] = key;
+    }
+    __syncthreads();
+    const int P = (256 / EP < EP) ? 256 / EP : EP, L = EP / P;
+    const int e = tid % EP, part = tid / EP;
+    int c = 0;
+    if (part < P) {
+        const uint64_t mine = keys[e];
+        // 8 independent LDS reads in flight per step (L is a power of two)
+        if (L >= 8) {
+            for (int i = part * L; i < (part + 1) * L; i += 8) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) c += keys[i + q] > mine ? 1 : 0;
+            }
+        } else {
+            for (int i = part * L; i < (part + 1) * L; ++i) c += keys[i] > mine ? 1 : 0;
+        }
+    }
+    part_cnt[tid] = c;
+    __syncthreads();
+    if (tid < E) {
+        int rank = 0;
+        for (int p = 0; p < P; ++p) rank += part_cnt[p * EP + tid];
+        if (rank < topk) {
+            sel_v[rank] = (v != v) ? -INFINITY : v;
+            sel_e[rank] = tid;
+        }
+    }
+    __syncthreads();
+    if (tid < topk) {
+        const float lmax = sel_v[0];
+        sel_p[tid] = (lmax == -INFINITY) ? 1.0f : expf(sel_v[tid] - lmax);
+    }
+    __syncthreads();
+    if (tid < topk) {
+        float den = 0.0f;
+        for (int j = 0; j < topk; ++j) den += sel_p[j];
+        ids[(size_t)t * topk + tid] = sel_e[tid];
+        wts[(size_t)t * topk + tid] = sel_p[tid] / den;
+    }
+}
+
+// Any E <= 4096: one wave per token, VPL keys per lane (lane l holds
+// experts l + 64 v); topk rounds of a wave-wide maximum of the keys.
 template <int VPL>
-__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits,
-                                                   int32_t *__restrict__ ids,
-                                                   float *__restrict__ wts, int T, int E, int topk) {
+__global__ __launch_bounds__(256) void k_route_wave(const float *__restrict__ logits,
+                                                    int32_t *__restrict__ ids,
+                                                    float *__restrict__ wts, int T, int E, int topk) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (t >= T) return;
-    float v[VPL];
-    int ix[VPL];
+    uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + 64 * i;
-        if (e < E) {
-            float l = logits[(size_t)t * E + e];
-            v[i] = (l != l) ? -INFINITY : l;
-            ix[i] = e;
-        } else {
-            v[i] = -INFINITY;
-            ix[i] = 0x7FFFFFFF;
-        }
+        key[i] = e < E ? route_key(logits[(size_t)t * E + e], e) : 0;
     }
-    float my_v = -INFINITY;
-    int my_i = 0x7FFFFFFF;
+    uint64_t my = 0;
     for (int j = 0; j < topk; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+        uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (v[i] > bv || (v[i] == bv && ix[i] < bi)) {
-                bv = v[i];
-                bi = ix[i];
-            }
+        for (int i = 0; i < VPL; ++i) best = key[i] > best ? key[i] : best;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
+            const uint64_t o = __shfl_xor(best, off);
+            best = o > best ? o : best;
         }
-        // remove the winner from its owner's registers
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
-            if (ix[i] == bi) {
-                v[i] = -INFINITY;
-                ix[i] = 0x7FFFFFFF;
-            }
-        if (lane == j) {
-            my_v = bv;
-            my_i = bi;
-        }
+            if (key[i] == best) key[i] = 0;  // keys are unique: only the winner
+        if (lane == j) my = best;
     }
+    // back from the key to (expert, logit)
+    const int my_e = (int)~(uint32_t)my;
+    const uint32_t ord = (uint32_t)(my >> 32);
+    const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+    const float my_v = __uint_as_float(bits);
     const float lmax = __shfl(my_v, 0);
     float p = 0.0f;
     if (lane < topk) p = (lmax == -INFINITY) ? 1.0f : expf(my_v - lmax);
@@ -91,227 +159,493 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
     if (lane < topk) {
-        ids[(size_t)t * topk + lane] = my_i;
+        ids[(size_t)t * topk + lane] = my_e;
         wts[(size_t)t * topk + lane] = p / den;
     }
 }
 
-// --------------------------------------------------------- grouping ---
-struct Group {
-    int expert;  // -1: no such group
-    int count;   // slots routed to it
+// ------------------------------------------------------ gather matvec ---
+struct MoeArgs {
+    const uint8_t *bank;   // [E, n, k]; PAIR: the gate bank [E, n/2, k]
+    const uint8_t *bank2;  // PAIR: the up bank [E, n/2, k]
+    const float *x;
+    int x_div;
+    const int32_t *ids;
+    float *y;  // [nslots, n]; PAIR: [nslots, n/2]
+    int nslots, n, k, E;
 };
 
-// Whole workgroup: find the g-th distinct valid expert of ids[0..nslots) and
-// write its slots (ascending) to slot_list. Every thread gets the result.
-__device__ Group find_group(const int32_t *__restrict__ ids, int nslots, int E, int g,
-                            uint32_t *bitmap, int *slot_list, int *shared) {
-    const int tid = threadIdx.x;
-    const int words = (E + 31) >> 5;
-    for (int i = tid; i < words; i += blockDim.x) bitmap[i] = 0u;
+// Dynamic LDS of k_moe: activation staging, ids (int16, -1 = out of
+// range), slot list, present experts (uint16), per-expert slot counts and
+// item offsets (int32).
+size_t moe_lds_bytes(int k, int act_stride, int nslots, int E) {
+    const int64_t p = E < nslots ? E : nslots;  // present experts at most
+    return (size_t)(k / 64) * act_stride * 4 + (size_t)div_up(nslots, 2) * 4 * 2 + (size_t)div_up(p, 2) * 4 +
+           (size_t)(2 * p + 1) * 4;
+}
+
+// Persistent over work items: an item is a block of rows of one present
+// expert, for every slot routed to that expert (in slot order):
+// y[s, r] = W[e, r, :] . x[s / x_div]. An expert chosen by c slots gets
+// row blocks about 1/c as tall as a single-slot expert's, so every item
+// costs about the same; the rows of a block are read from HBM once and from
+// L2 for the further slots. The items (known only on the device) are dealt
+// to the workgroups in turn.
+// PAIR: virtual row 2i is gate row i and 2i+1 is up row i; a pass holds
+// whole pairs (64/G even), and the lane group of the up row writes
+// y[s, i] = silu(gate . x) * (up . x).
+template <class F, int G, int UPL, bool PAIR>
+__global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
+    extern __shared__ float4 dyn4[];
+    float *xlds = reinterpret_cast<float *>(dyn4);
+    const int ns2 = (a.nslots + 1) / 2 * 2;
+    const int pmax = a.E < a.nslots ? a.E : a.nslots;
+    int16_t *s_ids = reinterpret_cast<int16_t *>(xlds + (a.k / 64) * F::ACT_STRIDE);
+    uint16_t *slot_list = reinterpret_cast<uint16_t *>(s_ids + ns2);
+    uint16_t *experts = slot_list + ns2;
+    int *cnt = reinterpret_cast<int *>(experts + (pmax + 1) / 2 * 2);
+    int *item0 = cnt + pmax;  // pmax + 1 entries
+    __shared__ uint32_t bitmap[MAX_E / 32];
+    __shared__ int wprefix[MAX_E / 32];  // present experts in lower words
+    __shared__ int sh[4];                // present, invalid, slot count, items
+    constexpr int NB = F::RING;
+    constexpr int RPP = 64 / G;
+    constexpr int STEP = WAVES * RPP;  // one pass per wave
+    static_assert(!PAIR || RPP % 2 == 0, "pairs need an even number of rows per pass");
+    using Raw = typename F::Raw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // ids -> LDS, bitmap of the present experts, count of invalid slots
+    const int words = (a.E + 31) >> 5;
+    for (int i = tid; i < words; i += 256) bitmap[i] = 0u;
+    for (int i = tid; i < pmax; i += 256) cnt[i] = 0;
+    if (tid == 0) sh[1] = 0;
     __syncthreads();
-    for (int s = tid; s < nslots; s += blockDim.x) {
-        const int e = ids[s];
-        if (e >= 0 && e < E) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    for (int s = tid; s < a.nslots; s += 256) {
+        const int e = a.ids[s];
+        const bool ok = e >= 0 && e < a.E;
+        s_ids[s] = (int16_t)(ok ? e : -1);
+        if (ok) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+        else atomicAdd(&sh[1], 1);
     }
     __syncthreads();
-    if (tid < 64) {
-        // wave 0: locate the word holding the g-th set bit by a running popcount
-        int base = 0, found = -1;
-        for (int w0 = 0; w0 < words && found < 0; w0 += 64) {
-            const int wi = w0 + tid;
-            const uint32_t bits = wi < words ? bitmap[wi] : 0u;
-            int c = __popc(bits);
-            // inclusive scan of c across the wave
+    if (wave == 0) {
+        // present experts in ascending order (running popcount over words)
+        int base = 0;
+        for (int w0 = 0; w0 < words; w0 += 64) {
+            const int wi = w0 + lane;
+            uint32_t bits = wi < words ? bitmap[wi] : 0u;
+            const int c = __popc(bits);
             int incl = c;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int o = __shfl_up(incl, off);
-                if (tid >= off) incl += o;
+                if (lane >= off) incl += o;
             }
-            const int excl = incl - c;
-            const bool hit = (g >= base + excl) && (g < base + incl);
-            const unsigned long long m = __ballot(hit);
-            if (m) {
-                const int src = __ffsll((long long)m) - 1;
-                if (tid == src) {
-                    uint32_t b = bits;
-                    int need = g - base - excl;
-                    while (need-- > 0) b &= b - 1;
-                    shared[0] = wi * 32 + (__ffs((int)b) - 1);
-                }
-                found = 1;
+            int pos = base + incl - c;
+            if (wi < words) wprefix[wi] = pos;
+            while (bits) {
+                experts[pos++] = (uint16_t)(wi * 32 + __ffs((int)bits) - 1);
+                bits &= bits - 1;
             }
             base += __shfl(incl, 63);
         }
-        if (found < 0 && tid == 0) shared[0] = -1;
+        if (lane == 0) sh[0] = base;
     }
     __syncthreads();
-    Group G;
-    G.expert = shared[0];
-    G.count = 0;
-    if (G.expert < 0) return G;
-    if (tid < 64) {
-        int cnt = 0;
-        for (int s0 = 0; s0 < nslots; s0 += 64) {
-            const int s = s0 + tid;
-            const bool f = s < nslots && ids[s] == G.expert;
-            const unsigned long long m = __ballot(f);
-            if (f) slot_list[cnt + __popcll(m & ((1ull << tid) - 1ull))] = s;
-            cnt += __popcll(m);
+    const int present = sh[0], ninvalid = sh[1];
+    // slots per present expert (its rank: present experts below it)
+    for (int s = tid; s < a.nslots; s += 256) {
+        const int e = s_ids[s];
+        if (e >= 0) atomicAdd(&cnt[wprefix[e >> 5] + __popc(bitmap[e >> 5] & ((1u << (e & 31)) - 1u))], 1);
+    }
+    __syncthreads();
+    // rows per item of a single-slot expert, so that the items about match
+    // the workgroups: n * valid slots / grid, in whole passes
+    const int nvalid = a.nslots - ninvalid;
+    int base_rows = (int)(((int64_t)a.n * (nvalid > 0 ? nvalid : 1) + gridDim.x - 1) / gridDim.x);
+    base_rows = (base_rows + STEP - 1) / STEP * STEP;
+    auto rows_of = [&](int c) {  // rows per item of an expert with c slots
+        int r = (base_rows + c - 1) / c;
+        r = (r + STEP - 1) / STEP * STEP;
+        return r < a.n ? r : (a.n + STEP - 1) / STEP * STEP;
+    };
+    if (wave == 0) {
+        // item offsets: item0[g] = items of the experts below g
+        int base = 0;
+        for (int g0 = 0; g0 < present; g0 += 64) {
+            const int g = g0 + lane;
+            const int c = g < present ? (a.n + rows_of(cnt[g]) - 1) / rows_of(cnt[g]) : 0;
+            int incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            if (g < present) item0[g] = base + incl - c;
+            base += __shfl(incl, 63);
         }
-        if (tid == 0) shared[1] = cnt;
+        if (lane == 0) {
+            item0[present] = base;
+            sh[3] = base;
+        }
     }
     __syncthreads();
-    G.count = shared[1];
-    return G;
-}
-
-// Zero the output rows [r0, r1) of slots whose id is out of range.
-__device__ void zero_invalid(const int32_t *__restrict__ ids, int nslots, int E, float *y, int n,
-                             int r0, int r1) {
-    for (int s = 0; s < nslots; ++s) {
-        const int e = ids[s];
-        if (e < 0 || e >= E)
-            for (int r = r0 + (int)threadIdx.x; r < r1; r += blockDim.x) y[(size_t)s * n + r] = 0.0f;
+    const int nitems = sh[3];
+    if (!PAIR && ninvalid > 0) {
+        // slots with an out-of-range id get zero rows (row ranges dealt out)
+        const int chunk = (a.n + gridDim.x - 1) / gridDim.x;
+        const int r0 = blockIdx.x * chunk, len = min(a.n, r0 + chunk) - r0;
+        for (int i = tid; i < a.nslots * len; i += 256) {
+            const int s = i / len, r = r0 + i % len;
+            if (s_ids[s] < 0) a.y[(size_t)s * a.n + r] = 0.0f;
+        }
     }
-}
 
-// ------------------------------------------------------ gather matvec ---
-// Rows of the expert are split over row blocks of `rblk` rows; inside a block
-// the four waves take passes of 64/G rows in turn. For each chunk of SB slots
-// the lanes load those slots' activation values into registers, then stream
-// the rows. DUAL: two banks (gate, up) against the same activation, output
-// silu(gate.x) * (up.x); otherwise one bank, plain output.
-template <class F, int G, int UPL, int SB, bool DUAL>
-__global__ __launch_bounds__(256) void k_moe(const uint8_t *__restrict__ bank,
-                                             const uint8_t *__restrict__ bank2,
-                                             const float *__restrict__ x, int x_div,
-                                             const int32_t *__restrict__ ids,
-                                             float *__restrict__ y, int nslots, int n, int k,
-                                             int E, int rblk) {
-    __shared__ uint32_t bitmap[MAX_E / 32];
-    __shared__ int slot_list[MAX_SLOTS];
-    __shared__ int shared[2];
-    constexpr int RPP = 64 / G;
-    using Raw = typename F::Raw;
-    const int r0 = blockIdx.x * rblk;
-    const int r1 = min(n, r0 + rblk);
-    if (blockIdx.y == 0) zero_invalid(ids, nslots, E, y, n, r0, r1);
-    const Group grp = find_group(ids, nslots, E, blockIdx.y, bitmap, slot_list, shared);
-    if (grp.expert < 0) return;
-    const int U = F::units_per_row(k);
-    const size_t row_bytes = (size_t)(k / F::BW) * F::BB;
-    const uint8_t *wb = bank + (size_t)grp.expert * n * row_bytes;
-    const uint8_t *wb2 = DUAL ? bank2 + (size_t)grp.expert * n * row_bytes : nullptr;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int U = F::units_per_row(a.k);
+    const size_t row_bytes = (size_t)(a.k / F::BW) * F::BB;
+    const int nrows_bank = PAIR ? a.n / 2 : a.n;  // rows per expert in a bank
+    const int ny = PAIR ? a.n / 2 : a.n;          // output row length
     const int gl = lane & (G - 1), grow = lane / G;
     bool uv[UPL];
+    int uu[UPL];
 #pragma unroll
-    for (int i = 0; i < UPL; ++i) uv[i] = gl + G * i < U;
+    for (int i = 0; i < UPL; ++i) {
+        uv[i] = gl + G * i < U;
+        uu[i] = uv[i] ? gl + G * i : U - 1;
+    }
 
-    for (int sc0 = 0; sc0 < grp.count; sc0 += SB) {
-        const int ns = min(SB, grp.count - sc0);
-        UnitX X[SB][UPL];
-        int sl[SB];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) sl[j] = j < ns ? slot_list[sc0 + j] : -1;
-#pragma unroll
-        for (int i = 0; i < UPL; ++i)
-#pragma unroll
-            for (int j = 0; j < SB; ++j)
-                if (uv[i] && j < ns) F::load_x(X[j][i], x + (size_t)(sl[j] / x_div) * k, gl + G * i);
-        for (int rb = r0 + wave * RPP; rb < r1; rb += WAVES * RPP) {
-            const int r = rb + grow;
-            const bool rv = r < r1;
-            Raw R[UPL], R2[UPL];
-#pragma unroll
-            for (int i = 0; i < UPL; ++i)
-                if (rv && uv[i]) {
-                    F::load(R[i], wb + (size_t)r * row_bytes, gl + G * i);
-                    if (DUAL) F::load(R2[i], wb2 + (size_t)r * row_bytes, gl + G * i);
-                }
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                if (j >= ns) break;
-                float a = 0.0f, b = 0.0f;
-#pragma unroll
-                for (int i = 0; i < UPL; ++i)
-                    if (rv && uv[i]) {
-                        a += F::dot(R[i], X[j][i], gl + G * i);
-                        if (DUAL) b += F::dot(R2[i], X[j][i], gl + G * i);
-                    }
-                a = group_sum_last<G>(a);
-                if (DUAL) b = group_sum_last<G>(b);
-                if (gl == G - 1 && rv) y[(size_t)sl[j] * n + r] = DUAL ? silu(a) * b : a;
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        // the expert of the item: last g with item0[g] <= it
+        int lo = 0, hi = present - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (item0[mid] <= it) lo = mid;
+            else hi = mid - 1;
+        }
+        const int g = lo;
+        const int expert = experts[g];
+        const int rblk = rows_of(cnt[g]);
+        const int r0 = (it - item0[g]) * rblk, len = min(a.n, r0 + rblk) - r0;
+        __syncthreads();  // the previous item's slot list is no longer read
+        if (wave == 0) {
+            int c = 0;
+            for (int s0 = 0; s0 < a.nslots; s0 += 64) {
+                const int s = s0 + lane;
+                const bool f = s < a.nslots && s_ids[s] == expert;
+                const unsigned long long m = __ballot(f);
+                if (f) slot_list[c + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)s;
+                c += __popcll(m);
             }
+            if (lane == 0) sh[2] = c;
+        }
+        __syncthreads();
+        const int count = sh[2];
+        const uint8_t *wb = a.bank + (size_t)expert * nrows_bank * row_bytes;
+        const uint8_t *wb2 = PAIR ? a.bank2 + (size_t)expert * nrows_bank * row_bytes : wb;
+        // passes of RPP rows inside the block; pass q of this wave is block
+        // pass q*WAVES + wave. Spare waves run one clamped pass, store nothing.
+        const int bpasses = (len + RPP - 1) / RPP;
+        const int pr = (bpasses - wave + WAVES - 1) / WAVES;
+        const int p1 = pr > 1 ? pr : 1;
+        auto load_pass = [&](Raw (&B)[UPL], int pass) {
+            const int v = r0 + min((pass * WAVES + wave) * RPP + grow, len - 1);
+            const uint8_t *row = PAIR ? ((v & 1) ? wb2 : wb) + (size_t)(v >> 1) * row_bytes
+                                      : wb + (size_t)v * row_bytes;
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) F::load(B[i], row, uu[i]);
+        };
+
+        for (int c = 0; c < count; ++c) {
+            const int slot = slot_list[c];
+            typename F::Stage S;
+            F::template fetch<stage_granules(G, UPL)>(S, ActF32{a.x + (size_t)(slot / a.x_div) * a.k}, a.k);
+            Raw R[NB][UPL];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                load_pass(R[j], min(j, p1 - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();  // the previous slot's LDS reads are done
+            F::template store<stage_granules(G, UPL)>(xlds, S, a.k);
+            __syncthreads();
+            typename F::X X[UPL];
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
+            float *yrow = a.y + (size_t)slot * ny;
+            int pass = 0;
+            do {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int ps = pass + j;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < UPL; ++i) {
+                        const float d = F::dot(R[j][i], X[i], uu[i]);
+                        acc += uv[i] ? d : 0.0f;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_pass(R[j], min(ps + NB, p1 - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc = group_sum_last<G>(acc);
+                    const int rr = (ps * WAVES + wave) * RPP + grow;
+                    if (PAIR) {
+                        const float gate = __shfl(acc, lane - G);  // the pair's gate row
+                        if ((grow & 1) && gl == G - 1 && ps < pr && rr < len)
+                            yrow[(r0 + rr) >> 1] = silu(gate) * acc;
+                    } else if (gl == G - 1 && ps < pr && rr < len) {
+                        yrow[r0 + rr] = acc;
+                    }
+                }
+                pass += NB;
+            } while (pass < p1);
         }
     }
 }
 
-// ------------------------------------------------------------ combine ---
-// y[t, r] = sum_j wts[t, j] * d[topk*t + j, r], j ascending.
-__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ d,
-                                                     const float *__restrict__ wts,
-                                                     float *__restrict__ y, int T, int topk,
-                                                     int hidden) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)T * hidden) return;
-    const int t = (int)(i / hidden), r = (int)(i % hidden);
-    float acc = 0.0f;
-    for (int j = 0; j < topk; ++j)
-        acc = fmaf(wts[(size_t)t * topk + j], d[((size_t)t * topk + j) * hidden + r], acc);
-    y[i] = acc;
+// ------------------------------------------- down pass + weighted combine ---
+// Workgroup (row block rb, token t):
+//   y[t, r] = sum_j wts[t, j] * W_down[ids[t, j], r, :] . h[topk*t + j, :]
+// for r in the block. The h rows of a chunk of the token's slots are staged
+// into LDS; the (slot, pass) items of the chunk are dealt to the four waves
+// in turn, each wave adds wts*dot into its own LDS row accumulator, and the
+// four accumulators are summed in wave order at the end (the result does
+// not depend on timing). Slots whose id is out of range contribute nothing.
+struct DownArgs {
+    const uint8_t *bank;  // Q6_K [E, n, k]
+    const float *h;       // [T*topk, k]
+    const int32_t *ids;
+    const float *wts;
+    float *y;  // [T, n]
+    int n, k, E, topk, rblk, chunk;
+};
+
+template <class F, int G>
+__global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
+    extern __shared__ float4 dyn4[];
+    float *hlds = reinterpret_cast<float *>(dyn4);  // chunk x (k/64) units
+    float *acc_lds = hlds + (size_t)a.chunk * (a.k / 64) * F::ACT_STRIDE;  // [WAVES][rblk]
+    constexpr int NB = F::RING;
+    constexpr int RPP = 64 / G;
+    using Raw = typename F::Raw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.y;
+    const int r0 = blockIdx.x * a.rblk, r1 = min(a.n, r0 + a.rblk), len = r1 - r0;
+    const int U = F::units_per_row(a.k);
+    const int ust = (a.k / 64) * F::ACT_STRIDE;  // LDS floats per staged slot
+    const size_t row_bytes = (size_t)(a.k / F::BW) * F::BB;
+    const int gl = lane & (G - 1), grow = lane / G;
+    const bool uv = gl < U;
+    const int uu = uv ? gl : U - 1;
+    const int bpasses = (len + RPP - 1) / RPP;
+    // the token's experts (out of range -> -1) and weights
+    __shared__ int s_e[64];
+    __shared__ float s_w[64];
+    for (int i = tid; i < WAVES * a.rblk; i += 256) acc_lds[i] = 0.0f;
+    if (tid < a.topk) {
+        const int e = a.ids[(size_t)t * a.topk + tid];
+        s_e[tid] = (e >= 0 && e < a.E) ? e : -1;
+        s_w[tid] = a.wts[(size_t)t * a.topk + tid];
+    }
+    __syncthreads();
+
+    for (int j0 = 0; j0 < a.topk; j0 += a.chunk) {
+        const int nch = min(a.chunk, a.topk - j0);
+        const int nitems = nch * bpasses;
+        // this wave's items q = wave, wave + 4, ...: slot j0 + q / bpasses,
+        // pass q % bpasses
+        const int pr = (nitems - wave + WAVES - 1) / WAVES;
+        const int p1 = pr > 1 ? pr : 1;
+        auto load_item = [&](Raw &B, int qi) {
+            const int q = min(qi * WAVES + wave, nitems - 1);
+            const int j = q / bpasses;
+            const int rr = (q - j * bpasses) * RPP + grow;
+            const int e = max(s_e[j0 + j], 0);
+            const int r = r0 + min(rr, len - 1);
+            F::load(B, a.bank + ((size_t)e * a.n + r) * row_bytes, uu);
+        };
+        Raw R[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            load_item(R[j], min(j, p1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();  // the previous chunk's LDS reads are done
+        const int k4 = a.k / 4;
+        for (int i = tid; i < nch * k4; i += 256) {
+            const int j = i / k4, c4 = i - j * k4;
+            const f32x4 hv = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j0 + j) * a.k + 4 * c4);
+            int jj;
+            const int u = F::xslot(4 * c4, &jj);
+            *reinterpret_cast<f32x4 *>(hlds + j * ust + F::ACT_STRIDE * u + jj) = hv;
+        }
+        __syncthreads();
+        int cur = -1;
+        typename F::X X;
+        int qi = 0;
+        do {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int qs = qi + b;
+                const int q = min(qs * WAVES + wave, nitems - 1);
+                const int j = q / bpasses;
+                const int rr = (q - j * bpasses) * RPP + grow;
+                if (j != cur) {  // wave-uniform
+                    F::load_lds(X, hlds + j * ust, uu);
+                    cur = j;
+                }
+                float d = F::dot(R[b], X, uu);
+                d = uv ? d : 0.0f;
+                __builtin_amdgcn_sched_barrier(0);
+                load_item(R[b], min(qs + NB, p1 - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                d = group_sum_last<G>(d);
+                if (gl == G - 1 && qs < pr && rr < len && s_e[j0 + j] >= 0)
+                    acc_lds[wave * a.rblk + rr] += s_w[j0 + j] * d;
+            }
+            qi += NB;
+        } while (qi < p1);
+    }
+    __syncthreads();
+    for (int r = tid; r < len; r += 256) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) v += acc_lds[w * a.rblk + r];
+        a.y[(size_t)t * a.n + r0 + r] = v;
+    }
 }
 
 // --------------------------------------------------------------- launch ---
-// Rows per workgroup: keep >= ~2048 workgroups-worth of waves when few
-// experts are active, while each wave still streams several rows.
-int pick_rblk(int64_t n, int G, int64_t groups) {
-    const int rpp = 64 / G;
-    int rblk = WAVES * rpp * 4;  // 4 passes per wave
-    while (rblk > WAVES * rpp && div_up(n, rblk) * groups < 1024) rblk /= 2;
-    return rblk;
+// Resident workgroups of a kernel on the device (one round).
+template <class K>
+int64_t resident_wgs(K kernel, size_t lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
+        per_cu = 2;
+    return (int64_t)per_cu * cus;
 }
 
-template <class F, bool DUAL>
-int launch_moe(const uint8_t *bank, const uint8_t *bank2, const float *x, int64_t x_div,
-               const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, hipStream_t s) {
-    const int64_t U = k / 64;
-    const int G = next_pow2_le64(U);
-    const int64_t groups = E < nslots ? E : nslots;
-    const int rblk = pick_rblk(n, G, groups);
-    const dim3 grid((unsigned)div_up(n, rblk), (unsigned)groups);
-#define MQ(GG, UU, SB)                                                                                 \
-    hipLaunchKernelGGL((k_moe<F, GG, UU, SB, DUAL>), grid, dim3(256), 0, s, bank, bank2, x, (int)x_div, ids, y, \
-                       (int)nslots, (int)n, (int)k, (int)E, rblk)
-    switch (G) {
-        case 1: MQ(1, 1, 2); break;
-        case 2: MQ(2, 1, 2); break;
-        case 4: MQ(4, 1, 2); break;
-        case 8: MQ(8, 1, 2); break;
-        case 16: MQ(16, 1, 2); break;
-        case 32: MQ(32, 1, 2); break;
-        default:
-            if (U <= 64) MQ(64, 1, 2);
-            else if (U <= 128) MQ(64, 2, 1);
-            else return QMV_EUNSUPPORTED;
+// Expected number of distinct experts among nslots ids spread over E.
+double expected_present(int64_t nslots, int64_t E) {
+    const double p = (double)E * (1.0 - std::pow(1.0 - 1.0 / (double)E, (double)nslots));
+    return p < 1.0 ? 1.0 : p;
+}
+
+template <class F, int G, int UPL, bool PAIR>
+int launch_moe_t(MoeArgs a, hipStream_t s) {
+    const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E);
+    static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
+    if (cache[0] != (int64_t)lds) {
+        cache[1] = resident_wgs(k_moe<F, G, UPL, PAIR>, lds);
+        cache[0] = (int64_t)lds;
     }
-#undef MQ
+    // one round of resident workgroups, but no more than the items of the
+    // expected number of present experts at one pass per wave could fill
+    const int64_t step = WAVES * (64 / G);
+    const double pe = expected_present(a.nslots, a.E);
+    int64_t grid = cache[1];
+    const int64_t most = (int64_t)(pe * (double)div_up(a.n, step)) + 1;
+    if (grid > most) grid = most;
+    hipLaunchKernelGGL((k_moe<F, G, UPL, PAIR>), dim3((unsigned)grid), dim3(256), lds, s, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
 
-int launch_moe_q4k(const uint8_t *bank, const uint8_t *bank2, const float *x, int64_t x_div,
-                   const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
-                   hipStream_t s) {
-    if (bank2) return launch_moe<Q4KUnit, true>(bank, bank2, x, x_div, ids, y, nslots, n, k, E, s);
-    return launch_moe<Q4KUnit, false>(bank, nullptr, x, x_div, ids, y, nslots, n, k, E, s);
+template <class F>
+int launch_moe(MoeArgs a, hipStream_t s) {
+    const int64_t U = a.k / 64;
+    switch (next_pow2_le64(U)) {
+        case 1: return launch_moe_t<F, 1, 1, false>(a, s);
+        case 2: return launch_moe_t<F, 2, 1, false>(a, s);
+        case 4: return launch_moe_t<F, 4, 1, false>(a, s);
+        case 8: return launch_moe_t<F, 8, 1, false>(a, s);
+        case 16: return launch_moe_t<F, 16, 1, false>(a, s);
+        case 32: return launch_moe_t<F, 32, 1, false>(a, s);
+        default:
+            if (U <= 64) return launch_moe_t<F, 64, 1, false>(a, s);
+            if (U <= 128) return launch_moe_t<F, 64, 2, false>(a, s);
+            return QMV_EUNSUPPORTED;
+    }
 }
 
-int launch_moe_q6k(const uint8_t *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
-                   int64_t nslots, int64_t n, int64_t k, int64_t E, hipStream_t s) {
-    return launch_moe<Q6KUnit, false>(bank, nullptr, x, x_div, ids, y, nslots, n, k, E, s);
+// gate/up of the layer: pairs need 64/G even, so G <= 32 (two units per
+// lane above k = 2048)
+int launch_gate_up(MoeArgs a, hipStream_t s) {
+    const int64_t U = a.k / 64;
+    switch (next_pow2_le64(U)) {
+        case 1: return launch_moe_t<Q4KUnit, 1, 1, true>(a, s);
+        case 2: return launch_moe_t<Q4KUnit, 2, 1, true>(a, s);
+        case 4: return launch_moe_t<Q4KUnit, 4, 1, true>(a, s);
+        case 8: return launch_moe_t<Q4KUnit, 8, 1, true>(a, s);
+        case 16: return launch_moe_t<Q4KUnit, 16, 1, true>(a, s);
+        case 32: return launch_moe_t<Q4KUnit, 32, 1, true>(a, s);
+        default:
+            if (U <= 64) return launch_moe_t<Q4KUnit, 32, 2, true>(a, s);
+            return QMV_EUNSUPPORTED;
+    }
+}
+
+// Slots staged at once by the down pass: as many as fit 48 KB of LDS, <= 8.
+int down_chunk(int64_t k, int64_t topk) {
+    const int64_t per = (k / 64) * XSTRIDE * 4;
+    int64_t c = 49152 / per;
+    if (c > 8) c = 8;
+    if (c < 1) c = 1;
+    return (int)(c < topk ? c : topk);
+}
+
+template <int G>
+int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
+    constexpr int RPP = 64 / G;
+    const size_t lds0 = (size_t)a.chunk * (a.k / 64) * XSTRIDE * 4;
+    static thread_local int64_t cache[2] = {-1, -1};
+    if (cache[0] != (int64_t)lds0) {
+        cache[1] = resident_wgs(k_moe_down<Q6KUnit, G>, lds0 + WAVES * 64 * 4);
+        cache[0] = (int64_t)lds0;
+    }
+    // rows per workgroup: within one round of resident workgroups, and
+    // enough (slot, pass) items to keep the four waves busy
+    // (at most 1024 rows: the row accumulators take WAVES*rblk floats of LDS)
+    int rblk = RPP;
+    while (rblk < a.n && rblk < 1024 &&
+           (div_up(a.n, rblk) * T > cache[1] || (int64_t)a.topk * (rblk / RPP) < WAVES))
+        rblk *= 2;
+    a.rblk = rblk;
+    const size_t lds = lds0 + (size_t)WAVES * a.rblk * 4;
+    const dim3 grid((unsigned)div_up(a.n, a.rblk), (unsigned)T);
+    hipLaunchKernelGGL((k_moe_down<Q6KUnit, G>), grid, dim3(256), lds, s, a);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+int launch_down(DownArgs a, int64_t T, hipStream_t s) {
+    switch (next_pow2_le64(a.k / 64)) {
+        case 4: return launch_down_g<4>(a, T, s);
+        case 8: return launch_down_g<8>(a, T, s);
+        case 16: return launch_down_g<16>(a, T, s);
+        case 32: return launch_down_g<32>(a, T, s);
+        case 64: return launch_down_g<64>(a, T, s);
+        default: return QMV_EUNSUPPORTED;  // k / 64 <= 64 (inter <= 4096) on this path
+    }
+}
+
+MoeArgs gather_args(const void *bank, const void *bank2, const float *x, int64_t x_div, const int32_t *ids,
+                    float *y, int64_t nslots, int64_t n, int64_t k, int64_t E) {
+    MoeArgs a{};
+    a.bank = static_cast<const uint8_t *>(bank);
+    a.bank2 = static_cast<const uint8_t *>(bank2);
+    a.x = x;
+    a.x_div = (int)x_div;
+    a.ids = ids;
+    a.y = y;
+    a.nslots = (int)nslots;
+    a.n = (int)n;
+    a.k = (int)k;
+    a.E = (int)E;
+    return a;
 }
 
 int check_moe_args(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
@@ -332,14 +666,19 @@ extern "C" int moe_route(const float *logits, int32_t *ids, float *wts, int64_t 
     if (!logits || !ids || !wts || T < 1 || E < 1 || topk < 1 || topk > E || topk > 64) return QMV_EINVAL;
     if (E > MAX_E || T > (1 << 28)) return QMV_EUNSUPPORTED;
     if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(wts, 4)) return QMV_EALIGN;
-    const dim3 grid((unsigned)div_up(T, WAVES));
     hipStream_t s = (hipStream_t)stream;
+    if (E <= SMALL_E) {
+        int ep = 1;
+        while (ep < E) ep <<= 1;
+        hipLaunchKernelGGL(k_route_small, dim3((unsigned)T), dim3(256), 0, s, logits, ids, wts, (int)E, ep,
+                           (int)topk);
+        QMV_LAUNCH_CHECK();
+        return QMV_OK;
+    }
+    const dim3 grid((unsigned)div_up(T, WAVES));
     const int vpl = (int)div_up(E, 64);
-#define RT(V) hipLaunchKernelGGL((k_moe_route<V>), grid, dim3(256), 0, s, logits, ids, wts, (int)T, (int)E, (int)topk)
-    if (vpl <= 1) RT(1);
-    else if (vpl <= 2) RT(2);
-    else if (vpl <= 4) RT(4);
-    else if (vpl <= 8) RT(8);
+#define RT(V) hipLaunchKernelGGL((k_route_wave<V>), grid, dim3(256), 0, s, logits, ids, wts, (int)T, (int)E, (int)topk)
+    if (vpl <= 8) RT(8);
     else if (vpl <= 16) RT(16);
     else if (vpl <= 32) RT(32);
     else RT(64);
@@ -352,24 +691,20 @@ extern "C" int moe_qmv_q4k(const void *bank, const float *x, int64_t x_div, cons
                            int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
     const int rc = check_moe_args(bank, x, x_div, ids, y, nslots, n, k, E);
     if (rc) return rc;
-    return launch_moe_q4k(static_cast<const uint8_t *>(bank), nullptr, x, x_div, ids, y, nslots, n, k, E,
-                          (hipStream_t)stream);
+    return launch_moe<Q4KUnit>(gather_args(bank, nullptr, x, x_div, ids, y, nslots, n, k, E), (hipStream_t)stream);
 }
 
 extern "C" int moe_qmv_q6k(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
                            int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
     const int rc = check_moe_args(bank, x, x_div, ids, y, nslots, n, k, E);
     if (rc) return rc;
-    return launch_moe_q6k(static_cast<const uint8_t *>(bank), x, x_div, ids, y, nslots, n, k, E,
-                          (hipStream_t)stream);
+    return launch_moe<Q6KUnit>(gather_args(bank, nullptr, x, x_div, ids, y, nslots, n, k, E), (hipStream_t)stream);
 }
 
+// workspace: h f32[T*topk, inter]
 extern "C" int64_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter) {
     if (T < 1 || topk < 1 || hidden < 1 || inter < 1) return -1;
-    const int64_t ns = T * topk;
-    const int64_t h = div_up(ns * inter * 4, 256) * 256;
-    const int64_t d = div_up(ns * hidden * 4, 256) * 256;
-    return h + d;
+    return div_up(T * topk * inter * 4, 256) * 256;
 }
 
 extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
@@ -381,21 +716,27 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
     const int64_t need = moe_ffn_workspace_bytes(T, topk, hidden, inter);
     if (ws_bytes < need) return QMV_EINVAL;
     const int64_t ns = T * topk;
-    int rc = check_moe_args(gate, x, topk, ids, y, ns, inter, hidden, E);
+    int rc = check_moe_args(gate, x, topk, ids, y, ns, 2 * inter, hidden, E);
     if (rc) return rc;
     rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
     if (rc) return rc;
+    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
     if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 16)) return QMV_EALIGN;
     float *h = static_cast<float *>(ws);
-    float *d = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + div_up(ns * inter * 4, 256) * 256);
     hipStream_t s = (hipStream_t)stream;
-    rc = launch_moe_q4k(static_cast<const uint8_t *>(gate), static_cast<const uint8_t *>(up), x, topk, ids, h,
-                        ns, inter, hidden, E, s);
+    // h = silu(gate x) * (up x): one gather over interleaved gate/up rows
+    rc = launch_gate_up(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
     if (rc) return rc;
-    rc = launch_moe_q6k(static_cast<const uint8_t *>(down), h, 1, ids, d, ns, hidden, inter, E, s);
-    if (rc) return rc;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)div_up(T * hidden, 256)), dim3(256), 0, s, d, wts, y,
-                       (int)T, (int)topk, (int)hidden);
-    QMV_LAUNCH_CHECK();
-    return QMV_OK;
+    DownArgs dn{};
+    dn.bank = static_cast<const uint8_t *>(down);
+    dn.h = h;
+    dn.ids = ids;
+    dn.wts = wts;
+    dn.y = y;
+    dn.n = (int)hidden;
+    dn.k = (int)inter;
+    dn.E = (int)E;
+    dn.topk = (int)topk;
+    dn.chunk = down_chunk(inter, topk);
+    return launch_down(dn, T, s);
 }

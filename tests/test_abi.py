@@ -70,7 +70,8 @@ def test_host_validation_returns_before_launch(lib):
     assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 64, None) == QMV_EINVAL  # bm
     lib.moe_ffn_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.moe_ffn_workspace_bytes.restype = i64
-    assert lib.moe_ffn_workspace_bytes(16, 8, 2048, 768) == 16 * 8 * (2048 + 768) * 4
+    # h = silu(gate x) * (up x), f32 per slot
+    assert lib.moe_ffn_workspace_bytes(16, 8, 2048, 768) == 16 * 8 * 768 * 4
     lib.moe_ffn_q4k_q6k.argtypes = [vp] * 8 + [i64] * 6 + [vp]
     lib.moe_ffn_q4k_q6k.restype = i32
     assert lib.moe_ffn_q4k_q6k(fake, fake, fake, fake, fake, fake, fake, fake, 100, 16, 8, 2048, 768, 128,

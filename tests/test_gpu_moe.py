@@ -19,7 +19,9 @@ E, TOPK, HIDDEN, INTER = 128, 8, 2048, 768
 
 # ------------------------------------------------------------------ router
 @pytest.mark.parametrize("T,E_,topk", [(1, 128, 8), (4, 128, 8), (16, 128, 8), (33, 128, 8),
-                                       (5, 8, 2), (3, 64, 64), (7, 200, 5), (2, 4096, 16), (9, 1, 1)])
+                                       (5, 8, 2), (3, 64, 64), (7, 200, 5), (2, 4096, 16), (9, 1, 1),
+                                       (4, 2, 2), (3, 3, 1), (5, 5, 5), (2, 13, 4), (3, 16, 16), (2, 17, 3),
+                                       (2, 256, 64), (3, 257, 8), (2, 1000, 10)])
 def test_route_matches_oracle(T, E_, topk):
     announce(f"route T={T} E={E_} topk={topk}")
     lg = synth.normal(synth.SEED_LOGITS, T * E_).reshape(T, E_)
@@ -39,6 +41,28 @@ def test_route_ties_nan_and_inf():
     lg[4, 100] = 1.0
     lg[5, 7] = np.inf
     announce("route ties/nan/inf")
+    ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+    ids, w = qmv.moe_route(dev(lg), T, E_, topk)
+    assert np.array_equal(host(ids), ids_ref)
+    gw = host(w)
+    assert np.array_equal(np.isnan(gw), np.isnan(w_ref))
+    ok = ~np.isnan(w_ref)
+    assert np.abs(gw[ok] - w_ref[ok]).max() <= TOL
+
+
+@pytest.mark.parametrize("E_", [5, 37, 200, 1000])
+def test_route_ties_nan_other_sizes(E_):
+    """Ties, NaN and infinities on both router kernels (one workgroup per
+    token up to 256 experts, one wave per token above)."""
+    T, topk = 5, min(E_, 6)
+    lg = np.round(synth.normal(8, T * E_).reshape(T, E_)).astype(np.float32)
+    lg[1, :] = 1.0
+    lg[2, ::2] = np.nan
+    lg[3, :] = np.nan
+    lg[3, E_ - 1] = -np.inf
+    lg[4, :] = -0.0
+    lg[4, 1::2] = 0.0
+    announce(f"route ties/nan E={E_}")
     ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
     ids, w = qmv.moe_route(dev(lg), T, E_, topk)
     assert np.array_equal(host(ids), ids_ref)
@@ -148,6 +172,34 @@ def test_moe_layer_repeated_and_invalid_ids():
     d = b["dev"]
     y = qmv.moe_ffn_q4k_q6k(d["gate"], d["up"], d["down"], dev(x), dev(ids), dev(wts), T, TOPK, HIDDEN, INTER, E)
     assert scalerel(y_ref, host(y)) <= TOL
+
+
+def test_moe_layer_back_to_back_and_all_invalid():
+    """One workspace reused by consecutive layer calls with different routing
+    (the fused combine's per-block counters must start from zero each call),
+    then a call whose ids are all out of range (y must be all zero)."""
+    b = _banks()
+    d = b["dev"]
+    ws = torch.empty(qmv.moe_ffn_workspace_bytes(16, TOPK, HIDDEN, INTER), dtype=torch.uint8, device="cuda")
+    for T, seed in ((16, 60), (1, 61), (4, 62), (16, 63)):
+        announce(f"moe layer back-to-back T={T} seed={seed}")
+        lg = synth.normal(seed, T * E).reshape(T, E)
+        x = synth.normal(seed + 100, T * HIDDEN).reshape(T, HIDDEN)
+        ids_ref, w_ref = oracle.moe_route(lg, T, E, TOPK)
+        y_ref, _, _ = oracle.moe_ffn(b["gate"], b["up"], b["down"], x, ids_ref, w_ref.astype(np.float32),
+                                     T, TOPK, HIDDEN, INTER, E)
+        ids, w = qmv.moe_route(dev(lg), T, E, TOPK)
+        y = qmv.moe_ffn_q4k_q6k(d["gate"], d["up"], d["down"], dev(x), ids, w, T, TOPK, HIDDEN, INTER, E, ws=ws)
+        assert scalerel(y_ref, host(y)) <= TOL, scalerel(y_ref, host(y))
+    T = 2
+    announce("moe layer all ids invalid")
+    ids = np.full((T, TOPK), -1, dtype=np.int32)
+    ids[1, :] = E + 5
+    wts = np.full((T, TOPK), 0.125, dtype=np.float32)
+    x = synth.normal(64, T * HIDDEN).reshape(T, HIDDEN)
+    y = qmv.moe_ffn_q4k_q6k(d["gate"], d["up"], d["down"], dev(x), dev(ids), dev(wts), T, TOPK, HIDDEN, INTER, E,
+                            y=torch.full((T, HIDDEN), 7.0, device="cuda"), ws=ws)
+    assert np.array_equal(host(y), np.zeros((T, HIDDEN), dtype=np.float32))
 
 
 def test_moe_layer_small_shapes():
