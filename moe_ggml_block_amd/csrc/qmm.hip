@@ -1,168 +1,320 @@
-// Q4_K x q8-activation prefill GEMM on gfx950 int8 MFMA.
+// Q4_K x q8-activation prefill GEMM on gfx950 matrix cores.
 //
 // hanzo-ml `src/vulkan_backend.rs`, `mmq_q4k_rt_gpu` / `mmq_q4k_gpu`: affine
 // Q4_K weights decoded in-kernel, activation quantized to (xq, xs, xsum),
 // epilogue xs*(D*dot - M*xsum) per 32-value block; `mul_mm_q4k_tiled_dp4a`:
 // BM rows of the output per workgroup so cold weights are re-read m/BM times.
 //
-//   Y[i, r] = sum_b xs[i,b] * dsc[r,b] * S[i,r,b]  -  sum_b xsum[i,b] * dmn[r,b]
-//   S[i,r,b] = sum_{l<32} xq[i,32b+l] * q[r,32b+l]    (int32, exact)
-//   dsc = d*sc_j, dmn = dmin*m_j of the sub-block j holding q8 block b.
+//   Y[i, r] = sum_s d[r,s] * sum_{b in s} xs[i,b] * T[i,r,b]
+//           - sum_b xsum[i,b] * dmin[r,s(b)] * m[r,b]
+//   T[i,r,b] = sum_{l<32} xq[i,32b+l] * (sc[r,b] * q[r,32b+l])   (an integer)
 //
-// Each q8 block is one v_mfma_i32_16x16x32_i8 (K = 32, one block, so the
-// integer sum never mixes scales); its 16x16 int32 tile is converted and
-// scaled into an f32 accumulator by the VALU. The min term is a rank-(k/32)
-// f32 product done on v_mfma_f32_16x16x4_f32, four blocks per instruction.
+// T is formed on the f16 matrix cores (v_mfma_f32_16x16x32_f16), and it is
+// exact there: xq (|xq| <= 127) and sc*q (<= 63*15) are integers that f16
+// holds exactly, every product fits the f32 accumulator, and a sum of 32 of
+// them stays below 2^24. So one MFMA per 16x16 tile and q8 block gives the
+// block's integer dot with the weight's sub-block scale already folded in,
+// and the VALU only adds xs*T into a per-superblock accumulator (one FMA per
+// output and block) and d times that accumulator once per superblock. The
+// min term is a rank-8 f32 product per superblock on v_mfma_f32_16x16x4_f32,
+// accumulated straight into the output tile.
 //
-// Workgroup: 256 threads, tile BM x 32 of Y. The 32 weight rows of the
-// current superblock are decoded once into LDS as int8 codes (row stride
-// padded to 264 bytes against bank conflicts) plus dsc/dmn; activation codes
-// come straight from global memory (L2-resident); xs/xsum of the BM rows are
-// staged in LDS per superblock.
+// Workgroup: 512 threads (8 waves), output tile BM x BN, each wave MT x NT
+// 16x16 tiles. K advances by phases of KP through double-buffered LDS: after
+// a phase's matrix instructions are issued, the waves convert the next
+// phase's codes into the other buffer, so conversion and matrix work
+// overlap; the raw codes are loaded into registers two phases before they
+// are converted (two register sets), and the per-superblock scales are
+// double-buffered by superblock parity.
+//  - activation codes: int8 -> f16 through the 1024 + b half bit pattern
+//    (v_perm_b32 + v_pk_add_f16, exact);
+//  - weight codes: nibbles -> f16 the same way, then times sc with one
+//    v_pk_fma_f16 ((1024 + q) * sc - 1024 * sc is exact after the fused
+//    rounding because q * sc is);
+//  - LDS rows are padded by 8 halves (a 4-bank shift per row) so that the
+//    16-byte fragment reads of eight consecutive rows hit distinct banks;
+//    the staging writes go eight lanes to eight consecutive 16-byte units
+//    of a row (activations) or to one unit of eight rows (weights, xs), so
+//    they are conflict-free too.
 #include "blocks.hpp"
 
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-constexpr int BN = 32;
-constexpr int BSTRIDE = 264;  // bytes per decoded weight row in LDS
+constexpr int NTHREADS = 512;
 
-template <int BM>
-__global__ __launch_bounds__(256) void k_qmm_q4k(const uint8_t *__restrict__ w,
-                                                 const int8_t *__restrict__ xq,
-                                                 const float *__restrict__ xs,
-                                                 const float *__restrict__ xsum,
-                                                 float *__restrict__ Y, int m, int n, int k) {
-    constexpr int MT = BM / 64;  // 16-row m tiles per wave (4 waves split BM)
-    __shared__ __attribute__((aligned(16))) int8_t bq[BN * BSTRIDE];
-    __shared__ float dsc[8][BN], dmn[8][BN];
-    __shared__ __attribute__((aligned(16))) float sxs[8][BM], sxsum[8][BM];
+// bytes (0, 1) / (2, 3) of w as the low bytes of two halves 0x64bb
+QMV_DEV uint32_t half_bytes_lo(uint32_t w) { return __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u); }
+QMV_DEV uint32_t half_bytes_hi(uint32_t w) { return __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u); }
+QMV_DEV h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+QMV_DEV uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Four int8 codes (one dword) -> four f16 values, exact:
+// byte b ^ 0x80 = b + 128 -> half 1024 + 128 + b -> minus 1152.
+QMV_DEV uint2 i8x4_to_f16(uint32_t a) {
+    const h2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    a ^= 0x80808080u;
+    return make_uint2(as_u32(as_h2(half_bytes_lo(a)) + off), as_u32(as_h2(half_bytes_hi(a)) + off));
+}
+
+// Four 4-bit codes (one per byte) -> four f16 values sc * q, exact.
+QMV_DEV uint2 q4x4_to_f16(uint32_t c, h2 sc, h2 nsc) {
+    return make_uint2(as_u32(__builtin_elementwise_fma(as_h2(half_bytes_lo(c)), sc, nsc)),
+                      as_u32(__builtin_elementwise_fma(as_h2(half_bytes_hi(c)), sc, nsc)));
+}
+
+QMV_DEV h2 splat(float v) { return h2{(_Float16)v, (_Float16)v}; }
+
+template <int BM, int BN, int KP, int MT, int NT>
+__global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict__ w,
+                                                      const int8_t *__restrict__ xq,
+                                                      const float *__restrict__ xs,
+                                                      const float *__restrict__ xsum,
+                                                      float *__restrict__ Y, int m, int n, int k) {
+    constexpr int WM = 16 * MT, WN = 16 * NT;
+    constexpr int WGM = BM / WM, WGN = BN / WN;
+    static_assert(WGM * WGN == NTHREADS / 64, "eight waves tile the workgroup");
+    constexpr int ST = KP + 8;                     // halves per LDS row (4-bank shift per row)
+    constexpr int NBP = KP / 32;                   // q8 blocks per phase
+    constexpr int PPS = 256 / KP;                  // phases per superblock
+    static_assert(KP <= 128, "an even number of phases (the loop takes them in pairs)");
+    constexpr int AC = BM * KP / (8 * NTHREADS);   // 8-byte activation chunks per thread
+    constexpr int ACR = KP / 8;                    // activation chunks per row
+    constexpr int BCH = BN * KP / 16;              // 8-code-byte weight chunks per phase
+    constexpr int XC = (BM * NBP + NTHREADS - 1) / NTHREADS;  // xs values per thread
+    static_assert(AC * 8 * NTHREADS == BM * KP && BCH <= NTHREADS, "staging");
+    static_assert(XC * NTHREADS == BM * NBP || (XC == 1 && BM * NBP < NTHREADS), "xs staging");
+    static_assert(ACR >= 8, "eight lanes of a row per activation write");
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * ST];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * ST];
+    __shared__ __attribute__((aligned(16))) float sxs[2][NBP][BM];
+    __shared__ __attribute__((aligned(16))) float sxsum[2][8][BM];  // by superblock parity
+    __shared__ float sd[2][BN], sdmn[2][8][BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * BN;
-    const int mblk = blockIdx.y * BM;
-    const int mw = mblk + wave * (BM / 4);  // this wave's first row
-    const int kb = k / 32, nsb = k / 256;
-    const int row_bytes = nsb * 144;
+    const int wm = wave % WGM, wn = wave / WGM;
     const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int kb = k / 32;
+    const size_t row_bytes = (size_t)(k / 256) * 144;
 
-    v4f acc[MT][2];
-    v4f accm[MT][2];
-#pragma unroll
-    for (int a = 0; a < MT; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
-            accm[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
-        }
+    // weight staging role (rows fastest, so that eight lanes write eight
+    // rows at one offset): row brow, code bytes [8*bc, +8) of the phase's
+    // slice of the row's 128 code bytes
+    const bool bact = tid < BCH;
+    const int brow = tid % BN, bc = tid / BN;
+    const bool bvalid = bact && n0 + brow < n;
+    const uint8_t *wrow = w + (size_t)(bvalid ? n0 + brow : 0) * row_bytes;
 
-    for (int s = 0; s < nsb; ++s) {
-        __syncthreads();
-        // ---- decode 32 weight rows of superblock s into LDS: thread -> (row, chunk)
-        {
-            const int rr = tid >> 3, c = tid & 7;
-            const int r = n0 + rr;
-            uint4 q = make_uint4(0, 0, 0, 0), hd = make_uint4(0, 0, 0, 0);
-            if (r < n) {
-                const uint8_t *blk = w + (size_t)r * row_bytes + (size_t)s * 144;
-                q = ld16(blk + 16 + 16 * c);
-                hd = ld16(blk);
-            }
-            const int p = c >> 1, hh = c & 1;
-            uint4 lo, hi;
-            lo.x = q.x & 0x0F0F0F0Fu; lo.y = q.y & 0x0F0F0F0Fu; lo.z = q.z & 0x0F0F0F0Fu; lo.w = q.w & 0x0F0F0F0Fu;
-            hi.x = (q.x >> 4) & 0x0F0F0F0Fu; hi.y = (q.y >> 4) & 0x0F0F0F0Fu;
-            hi.z = (q.z >> 4) & 0x0F0F0F0Fu; hi.w = (q.w >> 4) & 0x0F0F0F0Fu;
-            // sub-block 2p gets the low nibbles at l = 16hh.., 2p+1 the high ones
-            uint32_t *dlo = reinterpret_cast<uint32_t *>(bq + rr * BSTRIDE + 32 * (2 * p) + 16 * hh);
-            uint32_t *dhi = reinterpret_cast<uint32_t *>(bq + rr * BSTRIDE + 32 * (2 * p + 1) + 16 * hh);
-            dlo[0] = lo.x; dlo[1] = lo.y; dlo[2] = lo.z; dlo[3] = lo.w;
-            dhi[0] = hi.x; dhi[1] = hi.y; dhi[2] = hi.z; dhi[3] = hi.w;
-            if (hh == 0) {
-                uint32_t sc2, mn2;
-                q4k_scales(hd.y, hd.z, hd.w, p, &sc2, &mn2);
-                const float d = h2f(hd.x), dm = h2f(hd.x >> 16);
-                dsc[2 * p][rr] = d * ubyte_f<0>(sc2);
-                dsc[2 * p + 1][rr] = d * ubyte_f<1>(sc2);
-                dmn[2 * p][rr] = dm * ubyte_f<0>(mn2);
-                dmn[2 * p + 1][rr] = dm * ubyte_f<1>(mn2);
-            }
-        }
-        // ---- stage xs / xsum of the BM rows for the 8 q8 blocks of superblock s
-        for (int i = tid; i < 8 * BM; i += 256) {
-            const int b = i / BM, mr = i % BM;
-            const int gm = mblk + mr;
-            float a = 0.f, z = 0.f;
-            if (gm < m) {
-                a = xs[(size_t)gm * kb + 8 * s + b];
-                z = xsum[(size_t)gm * kb + 8 * s + b];
-            }
-            sxs[b][mr] = a;
-            sxsum[b][mr] = z;
-        }
-        __syncthreads();
+    // two register sets of raw codes: phase p is loaded into set p % 2 two
+    // phases before it is converted
+    uint2 ra[2][AC];
+    uint2 rb[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+    uint4 rh[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    float rxs[2][XC], rxsum[2][XC];
+    uint32_t scp0 = 0, scp1 = 0;  // sc0..3, sc4..7 of the current superblock
 
-        // ---- 8 q8 blocks
-#pragma unroll 2
-        for (int b = 0; b < 8; ++b) {
-            long av[MT];
+    auto prefetch = [&](int ph, int q) {  // q == ph % 2, a constant
+        const int k0 = ph * KP, s = k0 / 256, half = ph % PPS;
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int gm = mw + 16 * t + li;
-                av[t] = gm < m ? *reinterpret_cast<const long *>(xq + (size_t)gm * k + 256 * s + 32 * b + 8 * lq) : 0;
-            }
-            long bv[2];
-            float ds[2];
+        for (int i = 0; i < AC; ++i) {
+            const int ch = tid + NTHREADS * i, row = ch / ACR, c8 = ch % ACR;
+            const int gm = m0 + row;
+            ra[q][i] = gm < m ? *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + k0 + 8 * c8)
+                              : make_uint2(0u, 0u);
+        }
+        if (bvalid) {
+            const uint8_t *blk = wrow + (size_t)s * 144;
+            rb[q] = *reinterpret_cast<const uint2 *>(blk + 16 + half * (KP / 2) + 8 * bc);
+            if (half == 0) rh[q] = ld16(blk);
+        }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bv[u] = *reinterpret_cast<const long *>(bq + (16 * u + li) * BSTRIDE + 32 * b + 8 * lq);
-                ds[u] = dsc[b][16 * u + li];
-            }
+        for (int i = 0; i < XC; ++i) {
+            const int idx = tid + NTHREADS * i, row = idx % BM, bl = idx / BM;
+            const int gm = m0 + row;
+            const bool ok = gm < m && idx < BM * NBP;
+            rxs[q][i] = ok ? xs[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
+            rxsum[q][i] = ok ? xsum[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
+        }
+    };
+
+    auto convert_store = [&](int ph, int buf, int q) {  // q == ph % 2
+        const int half = ph % PPS, j0 = half * NBP;  // first sub-block of the phase
+        const int sp = (ph / PPS) & 1;               // superblock parity
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const float4 x4 = *reinterpret_cast<const float4 *>(&sxs[b][wave * (BM / 4) + 16 * t + 4 * lq]);
+        for (int i = 0; i < AC; ++i) {
+            const int ch = tid + NTHREADS * i, row = ch / ACR, c8 = ch % ACR;
+            const uint2 h0 = i8x4_to_f16(ra[q][i].x), h1 = i8x4_to_f16(ra[q][i].y);
+            *reinterpret_cast<uint4 *>(&As[buf][row * ST + 8 * c8]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+        }
+        if (bact) {
+            if (half == 0) {
+                // the superblock's scales: sc bytes kept packed, d and dmin*m to LDS
+                uint32_t s01, m01, s23, m23, s45, m45, s67, m67;
+                const uint4 hd = rh[q];
+                q4k_scales(hd.y, hd.z, hd.w, 0, &s01, &m01);
+                q4k_scales(hd.y, hd.z, hd.w, 1, &s23, &m23);
+                q4k_scales(hd.y, hd.z, hd.w, 2, &s45, &m45);
+                q4k_scales(hd.y, hd.z, hd.w, 3, &s67, &m67);
+                scp0 = s01 | (s23 << 16);
+                scp1 = s45 | (s67 << 16);
+                if (bc == 0) {
+                    const uint32_t mp0 = m01 | (m23 << 16), mp1 = m45 | (m67 << 16);
+                    const float dm = h2f(hd.x >> 16);
+                    sd[sp][brow] = h2f(hd.x);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[t], bv[u], (v4i){0, 0, 0, 0}, 0, 0, 0);
-                    acc[t][u][0] = fmaf((float)S[0], x4.x * ds[u], acc[t][u][0]);
-                    acc[t][u][1] = fmaf((float)S[1], x4.y * ds[u], acc[t][u][1]);
-                    acc[t][u][2] = fmaf((float)S[2], x4.z * ds[u], acc[t][u][2]);
-                    acc[t][u][3] = fmaf((float)S[3], x4.w * ds[u], acc[t][u][3]);
+                    for (int jj = 0; jj < 8; ++jj)
+                        sdmn[sp][jj][brow] = dm * (float)(((jj < 4 ? mp0 : mp1) >> (8 * (jj & 3))) & 0xFFu);
                 }
             }
+            // code bytes [8bc, +8) of the slice: sub-blocks 2p (low nibbles)
+            // and 2p+1 (high) at positions l0..l0+7, p = (half*KP/2 + 8bc)/32
+            const int o0 = half * (KP / 2) + 8 * bc;
+            const int p = o0 / 32, l0 = o0 % 32;
+            const float sclo = (float)(((2 * p < 4 ? scp0 : scp1) >> (8 * ((2 * p) & 3))) & 0xFFu);
+            const float schi = (float)(((2 * p + 1 < 4 ? scp0 : scp1) >> (8 * ((2 * p + 1) & 3))) & 0xFFu);
+            const h2 slo = splat(sclo), nslo = splat(-1024.0f * sclo);
+            const h2 shi = splat(schi), nshi = splat(-1024.0f * schi);
+            const uint2 cw = rb[q];
+            const uint2 lo0 = q4x4_to_f16(cw.x & 0x0F0F0F0Fu, slo, nslo);
+            const uint2 lo1 = q4x4_to_f16(cw.y & 0x0F0F0F0Fu, slo, nslo);
+            const uint2 hi0 = q4x4_to_f16((cw.x >> 4) & 0x0F0F0F0Fu, shi, nshi);
+            const uint2 hi1 = q4x4_to_f16((cw.y >> 4) & 0x0F0F0F0Fu, shi, nshi);
+            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p - j0) + l0]) =
+                make_uint4(lo0.x, lo0.y, lo1.x, lo1.y);
+            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p + 1 - j0) + l0]) =
+                make_uint4(hi0.x, hi0.y, hi1.x, hi1.y);
         }
-        // ---- min term: two f32 MFMAs (K = 4 blocks each) per 16x16 tile
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int b = 4 * h + lq;
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const float a = sxsum[b][wave * (BM / 4) + 16 * t + li];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const float bb = dmn[b][16 * u + li];
-                    accm[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, accm[t][u], 0, 0, 0);
-                }
+        for (int i = 0; i < XC; ++i) {
+            const int idx = tid + NTHREADS * i, row = idx % BM, bl = idx / BM;
+            if (idx < BM * NBP) {
+                sxs[buf][bl][row] = rxs[q][i];
+                sxsum[sp][j0 + bl][row] = rxsum[q][i];
             }
         }
-    }
-    // ---- write Y: lane holds rows 4*lq + r, column li of each 16x16 tile
+    };
+
+    v4f acc[MT][NT], out[MT][NT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int col = n0 + 16 * u + li;
+        for (int u = 0; u < NT; ++u) {
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int nph = k / KP;  // even (k is a multiple of 256)
+    prefetch(0, 0);
+    convert_store(0, 0, 0);
+    prefetch(1, 1);
+    if (nph > 2) prefetch(2, 0);
+    __syncthreads();
+    for (int ph0 = 0; ph0 < nph; ph0 += 2) {
+#pragma unroll
+        for (int Q = 0; Q < 2; ++Q) {
+            const int ph = ph0 + Q;
+            const int buf = Q, half = ph % PPS, sp = (ph / PPS) & 1;
+            // software-pipelined over the phase's blocks: the MFMAs of block
+            // bl + 1 are in flight while block bl's results are scaled and summed
+            auto mma = [&](int bl, v4f (&T)[MT][NT]) {
+                h8 af[MT], bf[NT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    af[t] = *reinterpret_cast<const h8 *>(&As[buf][(wm * WM + 16 * t + li) * ST + 32 * bl + 8 * lq]);
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    bf[u] = *reinterpret_cast<const h8 *>(&Bs[buf][(wn * WN + 16 * u + li) * ST + 32 * bl + 8 * lq]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int u = 0; u < NT; ++u)
+                        T[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            };
+            v4f T0[MT][NT], T1[MT][NT];
+            mma(0, T0);
+#pragma unroll
+            for (int bl = 0; bl < NBP; ++bl) {
+                v4f (&Tc)[MT][NT] = (bl & 1) ? T1 : T0;
+                v4f (&Tn)[MT][NT] = (bl & 1) ? T0 : T1;
+                if (bl + 1 < NBP) mma(bl + 1, Tn);
+                v4f x4[MT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) x4[t] = *reinterpret_cast<const v4f *>(&sxs[buf][bl][wm * WM + 16 * t + 4 * lq]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) acc[t][u] = x4[t] * Tc[t][u] + acc[t][u];
+            }
+            if (half == PPS - 1) {
+                // superblock done: out += d * acc, then the min term on MFMA
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const float dcol = sd[sp][wn * WN + 16 * u + li];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        out[t][u] = dcol * acc[t][u] + out[t][u];
+                        acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int bb = 4 * h + lq;
+                    float am[MT], bmn[NT];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) am[t] = -sxsum[sp][bb][wm * WM + 16 * t + li];
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) bmn[u] = sdmn[sp][bb][wn * WN + 16 * u + li];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int u = 0; u < NT; ++u)
+                            out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[t], bmn[u], out[t][u], 0, 0, 0);
+                }
+            }
+            // the next phase goes into the other buffer (and the other
+            // superblock parity) while this one's matrix work drains; its
+            // register set is then refilled three phases ahead
+            if (ph + 1 < nph) {
+                convert_store(ph + 1, buf ^ 1, Q ^ 1);
+                if (ph + 3 < nph) prefetch(ph + 3, Q ^ 1);
+            }
+            __syncthreads();
+        }
+    }
+
+    // lane holds rows 4*lq + r, column li of each 16x16 tile
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int col = n0 + wn * WN + 16 * u + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = mw + 16 * t + 4 * lq + r;
-                if (row < m && col < n) Y[(size_t)row * n + col] = acc[t][u][r] - accm[t][u][r];
+                const int row = m0 + wm * WM + 16 * t + 4 * lq + r;
+                if (row < m && col < n) Y[(size_t)row * n + col] = out[t][u][r];
             }
         }
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile configurations (BM, BN, KP, MT, NT) for the two bm settings
+// (measured on the 512 x 4096 x 4096 shape).
+#ifndef QMM_CFG128
+#define QMM_CFG128 128, 64, 64, 2, 2
+#define QMM_CFG128_BM 128
+#define QMM_CFG128_BN 64
+#endif
+#ifndef QMM_CFG256
+#define QMM_CFG256 256, 32, 64, 2, 2
+#define QMM_CFG256_BM 256
+#define QMM_CFG256_BN 32
+#endif
 
 }  // namespace
 
@@ -173,13 +325,19 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
     if (m > (1 << 24) || n > (1 << 24) || k > (1 << 20) || (int64_t)m * k > ((int64_t)1 << 34)) return QMV_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(y, 4))
         return QMV_EALIGN;
-    const dim3 grid((unsigned)div_up(n, BN), (unsigned)div_up(m, bm));
     hipStream_t s = (hipStream_t)stream;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    if (bm == 128)
-        hipLaunchKernelGGL(k_qmm_q4k<128>, grid, dim3(256), 0, s, wb, xq, xs, xsum, y, (int)m, (int)n, (int)k);
-    else
-        hipLaunchKernelGGL(k_qmm_q4k<256>, grid, dim3(256), 0, s, wb, xq, xs, xsum, y, (int)m, (int)n, (int)k);
+    if (bm == 128) {
+        constexpr int BMv = QMM_CFG128_BM, BNv = QMM_CFG128_BN;
+        const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(NTHREADS), 0, s, wb, xq, xs, xsum, y, (int)m,
+                           (int)n, (int)k);
+    } else {
+        constexpr int BMv = QMM_CFG256_BM, BNv = QMM_CFG256_BN;
+        const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(NTHREADS), 0, s, wb, xq, xs, xsum, y, (int)m,
+                           (int)n, (int)k);
+    }
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
