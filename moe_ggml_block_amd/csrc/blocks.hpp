@@ -98,13 +98,13 @@ QMV_DEV void load_x_lds(UnitX &X, const float *xl, int u) {
 #define QMV_RING_Q8 1
 #endif
 #ifndef QMV_RING_Q4K
-#define QMV_RING_Q4K 2
+#define QMV_RING_Q4K 1
 #endif
 #ifndef QMV_RING_Q6K
 #define QMV_RING_Q6K 2
 #endif
 #ifndef QMV_RING_Q4KQ8
-#define QMV_RING_Q4KQ8 2
+#define QMV_RING_Q4KQ8 1
 #endif
 
 constexpr int STAGE_MAX = 8;

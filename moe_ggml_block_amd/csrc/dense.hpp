@@ -25,8 +25,9 @@
 // compiler waits for exactly the oldest pass (s_waitcnt vmcnt(N)) instead of
 // draining the ring. Partial sums are reduced across the G lanes with DPP.
 //
-// Launch shape: the grid is sized from the occupancy of the kernel so that
-// every wave is resident at once (one round, no tail).
+// Launch shape: the grid is sized from the occupancy of the kernel (capped
+// at MAX_WG_PER_CU workgroups per CU) so that every wave is resident at
+// once (one round, no tail).
 #pragma once
 
 #include "blocks.hpp"
@@ -34,6 +35,10 @@
 namespace qmv_dense {
 
 constexpr int WAVES_PER_BLOCK = 4;
+// Resident workgroups per CU used by a launch, at most: with more (and
+// more rows in flight) the cold-weight streams got slower, measured on all
+// four formats at their decode shapes.
+constexpr int MAX_WG_PER_CU = 3;
 
 template <class F, int G, int UPL>
 __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
@@ -141,6 +146,7 @@ int64_t resident_waves(K kernel, size_t lds) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
         per_cu = 2;
+    if (per_cu > MAX_WG_PER_CU) per_cu = MAX_WG_PER_CU;
     return (int64_t)per_cu * compute_units() * WAVES_PER_BLOCK;
 }
 
