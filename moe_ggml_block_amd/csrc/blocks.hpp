@@ -164,6 +164,7 @@ struct F32Act {
 struct Q8Unit : F32Act<Q8Unit> {
     static constexpr int BW = 32, BB = 34;
     static constexpr int RING = QMV_RING_Q8;  // row passes in flight per wave (measured best)
+    static constexpr int MAX_WG_PER_CU = 2;   // resident workgroups per CU at most (measured)
     static constexpr int UNITS_PER_BLOCKS = 2;  // informational
     struct Raw {
         uint32_t d[17];
@@ -229,6 +230,7 @@ QMV_DEV void q4k_scales(uint32_t m1, uint32_t m2, uint32_t m3, int p, uint32_t *
 struct Q4KUnit : F32Act<Q4KUnit> {
     static constexpr int BW = 256, BB = 144;
     static constexpr int RING = QMV_RING_Q4K;
+    static constexpr int MAX_WG_PER_CU = 3;
     struct Raw {
         uint4 q0, q1, m;
     };
@@ -294,6 +296,7 @@ QMV_DEV uint2 ld8u(const uint8_t *p) {
 struct Q6KUnit : F32Act<Q6KUnit> {
     static constexpr int BW = 256, BB = 210;
     static constexpr int RING = QMV_RING_Q6K;
+    static constexpr int MAX_WG_PER_CU = 2;
     struct Raw {
         uint4 a, b, h;
         uint2 sc;
@@ -386,6 +389,7 @@ QMV_DEV void q4k_q8_sums(const Q4KUnit::Raw &R, const int32_t *xq16, int32_t *sl
 struct Q4KQ8Unit {
     static constexpr int BW = 256, BB = 144;
     static constexpr int RING = QMV_RING_Q4KQ8;
+    static constexpr int MAX_WG_PER_CU = 3;
     static constexpr int ACT_STRIDE = 20;
     using Act = ActQ8;
     using X = UnitQ8;

@@ -26,7 +26,7 @@
 // draining the ring. Partial sums are reduced across the G lanes with DPP.
 //
 // Launch shape: the grid is sized from the occupancy of the kernel (capped
-// at MAX_WG_PER_CU workgroups per CU) so that every wave is resident at
+// at F::MAX_WG_PER_CU workgroups per CU) so that every wave is resident at
 // once (one round, no tail).
 #pragma once
 
@@ -35,10 +35,6 @@
 namespace qmv_dense {
 
 constexpr int WAVES_PER_BLOCK = 4;
-// Resident workgroups per CU used by a launch, at most: with more (and
-// more rows in flight) the cold-weight streams got slower, measured on all
-// four formats at their decode shapes.
-constexpr int MAX_WG_PER_CU = 3;
 
 template <class F, int G, int UPL>
 __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
@@ -140,13 +136,16 @@ inline int compute_units() {
     return info.cus;
 }
 
-// Resident waves of a kernel on the whole device (one full round).
+// Resident waves of a kernel on the device (one round), with at most
+// max_per_cu workgroups per CU: with more (and more rows in flight) the
+// cold-weight streams got slower (F::MAX_WG_PER_CU, measured per format at
+// its decode shape).
 template <class K>
-int64_t resident_waves(K kernel, size_t lds) {
+int64_t resident_waves(K kernel, size_t lds, int max_per_cu) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
         per_cu = 2;
-    if (per_cu > MAX_WG_PER_CU) per_cu = MAX_WG_PER_CU;
+    if (per_cu > max_per_cu) per_cu = max_per_cu;
     return (int64_t)per_cu * compute_units() * WAVES_PER_BLOCK;
 }
 
@@ -163,7 +162,7 @@ void launch(const uint8_t *w, typename F::Act act, float *y, int64_t n, int64_t 
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev != c_dev || lds != c_lds) {
-        c_target = resident_waves(k_dense<F, G, UPL>, lds);
+        c_target = resident_waves(k_dense<F, G, UPL>, lds, F::MAX_WG_PER_CU);
         c_dev = dev;
         c_lds = lds;
     }
