@@ -39,6 +39,9 @@ constexpr int MAX_E = 4096;
 constexpr int MAX_SLOTS = 2048;
 constexpr int WAVES = 4;
 constexpr int SMALL_E = 256;  // router: one workgroup per token up to this E
+// Row passes in flight per wave in the gathers: their row blocks are short
+// (a few passes per wave), so every pass of a block is requested up front.
+constexpr int MOE_RING = 2;
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     __shared__ uint32_t bitmap[MAX_E / 32];
     __shared__ int wprefix[MAX_E / 32];  // present experts in lower words
     __shared__ int sh[4];                // present, invalid, slot count, items
-    constexpr int NB = F::RING;
+    constexpr int NB = MOE_RING;
     constexpr int RPP = 64 / G;
     constexpr int STEP = WAVES * RPP;  // one pass per wave
     static_assert(!PAIR || RPP % 2 == 0, "pairs need an even number of rows per pass");

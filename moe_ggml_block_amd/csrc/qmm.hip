@@ -44,7 +44,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-constexpr int NTHREADS = 512;
 
 // bytes (0, 1) / (2, 3) of w as the low bytes of two halves 0x64bb
 QMV_DEV uint32_t half_bytes_lo(uint32_t w) { return __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u); }
@@ -68,7 +67,7 @@ QMV_DEV uint2 q4x4_to_f16(uint32_t c, h2 sc, h2 nsc) {
 
 QMV_DEV h2 splat(float v) { return h2{(_Float16)v, (_Float16)v}; }
 
-template <int BM, int BN, int KP, int MT, int NT>
+template <int BM, int BN, int KP, int MT, int NT, int NTHREADS>
 __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict__ w,
                                                       const int8_t *__restrict__ xq,
                                                       const float *__restrict__ xs,
@@ -76,7 +75,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
                                                       float *__restrict__ Y, int m, int n, int k) {
     constexpr int WM = 16 * MT, WN = 16 * NT;
     constexpr int WGM = BM / WM, WGN = BN / WN;
-    static_assert(WGM * WGN == NTHREADS / 64, "eight waves tile the workgroup");
+    static_assert(WGM * WGN == NTHREADS / 64, "the waves tile the workgroup");
     constexpr int ST = KP + 8;                     // halves per LDS row (4-bank shift per row)
     constexpr int NBP = KP / 32;                   // q8 blocks per phase
     constexpr int PPS = 256 / KP;                  // phases per superblock
@@ -84,8 +83,10 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
     constexpr int AC = BM * KP / (8 * NTHREADS);   // 8-byte activation chunks per thread
     constexpr int ACR = KP / 8;                    // activation chunks per row
     constexpr int BCH = BN * KP / 16;              // 8-code-byte weight chunks per phase
+    constexpr int BCT = BCH > NTHREADS ? BCH / NTHREADS : 1;  // weight chunks per thread
     constexpr int XC = (BM * NBP + NTHREADS - 1) / NTHREADS;  // xs values per thread
-    static_assert(AC * 8 * NTHREADS == BM * KP && BCH <= NTHREADS, "staging");
+    static_assert(AC * 8 * NTHREADS == BM * KP, "activation staging");
+    static_assert((BCH <= NTHREADS || BCH == BCT * NTHREADS) && NTHREADS % BN == 0, "weight staging");
     static_assert(XC * NTHREADS == BM * NBP || (XC == 1 && BM * NBP < NTHREADS), "xs staging");
     static_assert(ACR >= 8, "eight lanes of a row per activation write");
 
@@ -106,14 +107,14 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
     // rows at one offset): row brow, code bytes [8*bc, +8) of the phase's
     // slice of the row's 128 code bytes
     const bool bact = tid < BCH;
-    const int brow = tid % BN, bc = tid / BN;
+    const int brow = tid % BN, bc0 = tid / BN;  // chunk i has bc = bc0 + i*NTHREADS/BN
     const bool bvalid = bact && n0 + brow < n;
     const uint8_t *wrow = w + (size_t)(bvalid ? n0 + brow : 0) * row_bytes;
 
     // two register sets of raw codes: phase p is loaded into set p % 2 two
     // phases before it is converted
     uint2 ra[2][AC];
-    uint2 rb[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+    uint2 rb[2][BCT];
     uint4 rh[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
     float rxs[2][XC], rxsum[2][XC];
     uint32_t scp0 = 0, scp1 = 0;  // sc0..3, sc4..7 of the current superblock
@@ -129,7 +130,9 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
         }
         if (bvalid) {
             const uint8_t *blk = wrow + (size_t)s * 144;
-            rb[q] = *reinterpret_cast<const uint2 *>(blk + 16 + half * (KP / 2) + 8 * bc);
+#pragma unroll
+            for (int i = 0; i < BCT; ++i)
+                rb[q][i] = *reinterpret_cast<const uint2 *>(blk + 16 + half * (KP / 2) + 8 * (bc0 + i * (NTHREADS / BN)));
             if (half == 0) rh[q] = ld16(blk);
         }
 #pragma unroll
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
                 q4k_scales(hd.y, hd.z, hd.w, 3, &s67, &m67);
                 scp0 = s01 | (s23 << 16);
                 scp1 = s45 | (s67 << 16);
-                if (bc == 0) {
+                if (bc0 == 0) {
                     const uint32_t mp0 = m01 | (m23 << 16), mp1 = m45 | (m67 << 16);
                     const float dm = h2f(hd.x >> 16);
                     sd[sp][brow] = h2f(hd.x);
@@ -171,23 +174,27 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
                         sdmn[sp][jj][brow] = dm * (float)(((jj < 4 ? mp0 : mp1) >> (8 * (jj & 3))) & 0xFFu);
                 }
             }
-            // code bytes [8bc, +8) of the slice: sub-blocks 2p (low nibbles)
-            // and 2p+1 (high) at positions l0..l0+7, p = (half*KP/2 + 8bc)/32
-            const int o0 = half * (KP / 2) + 8 * bc;
-            const int p = o0 / 32, l0 = o0 % 32;
-            const float sclo = (float)(((2 * p < 4 ? scp0 : scp1) >> (8 * ((2 * p) & 3))) & 0xFFu);
-            const float schi = (float)(((2 * p + 1 < 4 ? scp0 : scp1) >> (8 * ((2 * p + 1) & 3))) & 0xFFu);
-            const h2 slo = splat(sclo), nslo = splat(-1024.0f * sclo);
-            const h2 shi = splat(schi), nshi = splat(-1024.0f * schi);
-            const uint2 cw = rb[q];
-            const uint2 lo0 = q4x4_to_f16(cw.x & 0x0F0F0F0Fu, slo, nslo);
-            const uint2 lo1 = q4x4_to_f16(cw.y & 0x0F0F0F0Fu, slo, nslo);
-            const uint2 hi0 = q4x4_to_f16((cw.x >> 4) & 0x0F0F0F0Fu, shi, nshi);
-            const uint2 hi1 = q4x4_to_f16((cw.y >> 4) & 0x0F0F0F0Fu, shi, nshi);
-            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p - j0) + l0]) =
-                make_uint4(lo0.x, lo0.y, lo1.x, lo1.y);
-            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p + 1 - j0) + l0]) =
-                make_uint4(hi0.x, hi0.y, hi1.x, hi1.y);
+#pragma unroll
+            for (int i = 0; i < BCT; ++i) {
+                // code bytes [8bc, +8) of the slice: sub-blocks 2p (low nibbles)
+                // and 2p+1 (high) at positions l0..l0+7, p = (half*KP/2 + 8bc)/32
+                const int bc = bc0 + i * (NTHREADS / BN);
+                const int o0 = half * (KP / 2) + 8 * bc;
+                const int p = o0 / 32, l0 = o0 % 32;
+                const float sclo = (float)(((2 * p < 4 ? scp0 : scp1) >> (8 * ((2 * p) & 3))) & 0xFFu);
+                const float schi = (float)(((2 * p + 1 < 4 ? scp0 : scp1) >> (8 * ((2 * p + 1) & 3))) & 0xFFu);
+                const h2 slo = splat(sclo), nslo = splat(-1024.0f * sclo);
+                const h2 shi = splat(schi), nshi = splat(-1024.0f * schi);
+                const uint2 cw = rb[q][i];
+                const uint2 lo0 = q4x4_to_f16(cw.x & 0x0F0F0F0Fu, slo, nslo);
+                const uint2 lo1 = q4x4_to_f16(cw.y & 0x0F0F0F0Fu, slo, nslo);
+                const uint2 hi0 = q4x4_to_f16((cw.x >> 4) & 0x0F0F0F0Fu, shi, nshi);
+                const uint2 hi1 = q4x4_to_f16((cw.y >> 4) & 0x0F0F0F0Fu, shi, nshi);
+                *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p - j0) + l0]) =
+                    make_uint4(lo0.x, lo0.y, lo1.x, lo1.y);
+                *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * (2 * p + 1 - j0) + l0]) =
+                    make_uint4(hi0.x, hi0.y, hi1.x, hi1.y);
+            }
         }
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
@@ -219,36 +226,41 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
         for (int Q = 0; Q < 2; ++Q) {
             const int ph = ph0 + Q;
             const int buf = Q, half = ph % PPS, sp = (ph / PPS) & 1;
-            // software-pipelined over the phase's blocks: the MFMAs of block
-            // bl + 1 are in flight while block bl's results are scaled and summed
-            auto mma = [&](int bl, v4f (&T)[MT][NT]) {
-                h8 af[MT], bf[NT];
+            // three-stage pipeline over the phase's blocks: the fragments of
+            // block bl + 2 are being read from LDS and the MFMAs of block
+            // bl + 1 are in flight while block bl's results are scaled and
+            // summed
+            h8 fa[NBP][MT], fb[NBP][NT];
+            v4f fx[NBP][MT], T[NBP][MT][NT];
+            auto load_frag = [&](int bl) {
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    af[t] = *reinterpret_cast<const h8 *>(&As[buf][(wm * WM + 16 * t + li) * ST + 32 * bl + 8 * lq]);
+                for (int t = 0; t < MT; ++t) {
+                    fa[bl][t] = *reinterpret_cast<const h8 *>(&As[buf][(wm * WM + 16 * t + li) * ST + 32 * bl + 8 * lq]);
+                    fx[bl][t] = *reinterpret_cast<const v4f *>(&sxs[buf][bl][wm * WM + 16 * t + 4 * lq]);
+                }
 #pragma unroll
                 for (int u = 0; u < NT; ++u)
-                    bf[u] = *reinterpret_cast<const h8 *>(&Bs[buf][(wn * WN + 16 * u + li) * ST + 32 * bl + 8 * lq]);
+                    fb[bl][u] = *reinterpret_cast<const h8 *>(&Bs[buf][(wn * WN + 16 * u + li) * ST + 32 * bl + 8 * lq]);
+            };
+            auto mma = [&](int bl) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
 #pragma unroll
                     for (int u = 0; u < NT; ++u)
-                        T[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        T[bl][t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[bl][t], fb[bl][u],
+                                                                             (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             };
-            v4f T0[MT][NT], T1[MT][NT];
-            mma(0, T0);
+            load_frag(0);
+            if (NBP > 1) load_frag(1);
+            mma(0);
 #pragma unroll
             for (int bl = 0; bl < NBP; ++bl) {
-                v4f (&Tc)[MT][NT] = (bl & 1) ? T1 : T0;
-                v4f (&Tn)[MT][NT] = (bl & 1) ? T0 : T1;
-                if (bl + 1 < NBP) mma(bl + 1, Tn);
-                v4f x4[MT];
-#pragma unroll
-                for (int t = 0; t < MT; ++t) x4[t] = *reinterpret_cast<const v4f *>(&sxs[buf][bl][wm * WM + 16 * t + 4 * lq]);
+                if (bl + 2 < NBP) load_frag(bl + 2);
+                if (bl + 1 < NBP) mma(bl + 1);
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
 #pragma unroll
-                    for (int u = 0; u < NT; ++u) acc[t][u] = x4[t] * Tc[t][u] + acc[t][u];
+                    for (int u = 0; u < NT; ++u) acc[t][u] = fx[bl][t] * T[bl][t][u] + acc[t][u];
             }
             if (half == PPS - 1) {
                 // superblock done: out += d * acc, then the min term on MFMA
@@ -303,17 +315,19 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile configurations (BM, BN, KP, MT, NT) for the two bm settings
+// Tile configurations (BM, BN, KP, MT, NT, threads) for the two bm settings
 // (measured on the 512 x 4096 x 4096 shape).
 #ifndef QMM_CFG128
-#define QMM_CFG128 128, 64, 64, 2, 2
+#define QMM_CFG128 128, 64, 128, 2, 2, 512
 #define QMM_CFG128_BM 128
 #define QMM_CFG128_BN 64
+#define QMM_CFG128_NT 512
 #endif
 #ifndef QMM_CFG256
-#define QMM_CFG256 256, 32, 64, 2, 2
+#define QMM_CFG256 256, 32, 64, 2, 2, 512
 #define QMM_CFG256_BM 256
 #define QMM_CFG256_BN 32
+#define QMM_CFG256_NT 512
 #endif
 
 }  // namespace
@@ -330,12 +344,12 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
     if (bm == 128) {
         constexpr int BMv = QMM_CFG128_BM, BNv = QMM_CFG128_BN;
         const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(NTHREADS), 0, s, wb, xq, xs, xsum, y, (int)m,
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(QMM_CFG128_NT), 0, s, wb, xq, xs, xsum, y, (int)m,
                            (int)n, (int)k);
     } else {
         constexpr int BMv = QMM_CFG256_BM, BNv = QMM_CFG256_BN;
         const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(NTHREADS), 0, s, wb, xq, xs, xsum, y, (int)m,
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(QMM_CFG256_NT), 0, s, wb, xq, xs, xsum, y, (int)m,
                            (int)n, (int)k);
     }
     QMV_LAUNCH_CHECK();
