@@ -53,9 +53,10 @@ def _load():
     lib.oracle_moe_qmv.argtypes = [i32, vp, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.oracle_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.oracle_qmm.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.oracle_gemv.argtypes = [vp, vp, i64, i64, i64, vp]
     for name in ("oracle_dequant", "oracle_matvec", "oracle_quantize_act_q8",
                  "oracle_blocksums_q4k_q8", "oracle_matvec_q8act", "oracle_moe_route",
-                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm"):
+                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -172,3 +173,23 @@ def qmm(fmt, w, xq, xs, m: int, n: int, k: int, mrows=None) -> np.ndarray:
     Y = np.empty((cnt, n), dtype=np.float64)
     _check(_load().oracle_qmm(fmt, _p(w), _p(xq), _p(xs), m, n, k, _p(r), cnt, _p(Y)), "qmm")
     return Y
+
+
+def gemv(w, x, T: int, E: int, hidden: int) -> np.ndarray:
+    """Router gate: f64 logits[T, E] = x Wr^T for Wr f32[E, hidden], x f32[T, hidden]."""
+    w, x = _c(w, np.float32), _c(x, np.float32)
+    out = np.empty((T, E), dtype=np.float64)
+    _check(_load().oracle_gemv(_p(w), _p(x), T, E, hidden, _p(out)), "gemv")
+    return out
+
+
+def gate_route(w, x, T: int, E: int, hidden: int, topk: int):
+    """Router gate then routing: (logits f64[T, E], ids int32[T, topk], wts f64[T, topk]).
+
+    The logits are routed as the f32 values the method stores (the f64 gate
+    output rounded to f32 once); softmax and renormalization are the f64
+    routing of `moe_route`.
+    """
+    lg = gemv(w, x, T, E, hidden)
+    ids, wts = moe_route(lg.astype(np.float32), T, E, topk)
+    return lg, ids, wts

@@ -24,6 +24,9 @@
  *  - router = softmax, top-k, renormalize: doc of `moe_route_vk`.
  *  - expert-gather matvec y[s,r] = sum_k W[ids[s],r,k] x[s,k]: doc of
  *    `moe_matvec_gpu`.
+ *  - router gate = plain f32 GEMV logits[t, e] = Wr[e, :] . x[t, :]: the
+ *    "gemv" kernel of `src/vulkan_backend.rs` and `check_gemv` of
+ *    hanzo-kernel `src/main.rs`.
  *
  * Compile with -ffp-contract=off (no FMA contraction) and without
  * -ffast-math.
@@ -403,5 +406,26 @@ int oracle_qmm(int fmt, const uint8_t *w, const int8_t *xq, const float *xs, int
     }
     free(wd);
     free(xd);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Router gate (hanzo-ml `src/vulkan_backend.rs`, the "gemv" entry of the  */
+/* kernel table; hanzo-kernel `src/main.rs`, `check_gemv`): the f32 GEMV   */
+/* that produces the router logits of a decode step, one output per        */
+/* router row, logits[t, e] = sum_c Wr[e, c] * x[t, c], here in f64.        */
+/* Wr: f32[E, hidden] row-major; x: f32[T, hidden]; out: f64[T, E].         */
+/* ---------------------------------------------------------------------- */
+int oracle_gemv(const float *w, const float *x, int64_t T, int64_t E, int64_t hidden, double *out) {
+    if (T < 0 || E < 1 || hidden < 1) return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *xt = x + t * hidden;
+        for (int64_t e = 0; e < E; ++e) {
+            const float *we = w + e * hidden;
+            double acc = 0.0;
+            for (int64_t c = 0; c < hidden; ++c) acc += (double)we[c] * (double)xt[c];
+            out[t * E + e] = acc;
+        }
+    }
     return 0;
 }

@@ -29,6 +29,7 @@ FMT_NAMES = {"q8_0": FMT_Q8_0, "q4k": FMT_Q4K, "q6k": FMT_Q6K}
 SEED_W, SEED_X, SEED_LOGITS = 1, 2, 3
 SEED_GATE, SEED_UP, SEED_DOWN = 10, 11, 12
 SEED_PREFILL_X = 20
+SEED_ROUTER = 30
 
 
 def build() -> None:
@@ -151,3 +152,10 @@ def moe_logits(T: int, E: int, rotation: int = 0) -> np.ndarray:
 def moe_bank(fmt: int, seed: int, E: int, n: int, k: int) -> np.ndarray:
     """Expert bank [E, n, k] encoded row-major: uint8[E*n, row_bytes]."""
     return weights(fmt, seed, E * n, k)
+
+
+def router_weights(E: int, hidden: int, seed: int = SEED_ROUTER) -> np.ndarray:
+    """float32[E, hidden] uniform in [-a, a), a = sqrt(3 / hidden): variance 1/hidden,
+    so the logits of an x ~ N(0, 1) are about N(0, 1), the routing workload's spread."""
+    a = np.float32(np.sqrt(3.0 / hidden))
+    return (uniform(seed, E * hidden) * a).reshape(E, hidden)

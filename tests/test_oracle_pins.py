@@ -312,6 +312,50 @@ def test_route_ties_and_nan():
 
 
 # ---------------------------------------------------------------------------
+# Router gate GEMV (logits = Wr . x per token) and gate + route
+# ---------------------------------------------------------------------------
+def test_gemv_integer_exact_non_square():
+    # small integers: every product and partial sum is exact in f64, so the
+    # oracle must equal the int64 matrix product exactly; E != hidden != T
+    # makes a transposed operand or a swapped index fail
+    rng = np.random.default_rng(41)
+    T, E, hidden = 3, 5, 12
+    W = rng.integers(-7, 8, size=(E, hidden))
+    X = rng.integers(-9, 10, size=(T, hidden))
+    lg = oracle.gemv(W.astype(np.float32), X.astype(np.float32), T, E, hidden)
+    assert lg.shape == (T, E)
+    assert np.array_equal(lg, (X @ W.T).astype(np.float64))
+
+
+def test_gemv_random_vs_numpy_f64():
+    T, E, hidden = 4, 128, 2048
+    W = synth.uniform(51, E * hidden).reshape(E, hidden)
+    X = synth.normal(52, T * hidden).reshape(T, hidden)
+    lg = oracle.gemv(W, X, T, E, hidden)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    np.testing.assert_allclose(lg, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_gate_route_one_hot_rows_select_inputs():
+    # row e of Wr picks coordinate perm[e] of x, so logits[t, e] = x[t, perm[e]]
+    # exactly and the route must rank those values (brute force over pairs)
+    rng = np.random.default_rng(43)
+    T, E, hidden, topk = 4, 9, 16, 3
+    perm = rng.permutation(hidden)[:E]
+    W = np.zeros((E, hidden), dtype=np.float32)
+    W[np.arange(E), perm] = 1.0
+    X = rng.standard_normal((T, hidden)).astype(np.float32)
+    lg, ids, w = oracle.gate_route(W, X, T, E, hidden, topk)
+    assert np.array_equal(lg, X[:, perm].astype(np.float64))
+    for t in range(T):
+        best = max(itertools.permutations(range(E), topk),
+                   key=lambda p: [(float(X[t, perm[i]]), -i) for i in p])
+        assert tuple(ids[t]) == best
+        p = np.exp(X[t, perm[list(best)]].astype(np.float64) - X[t, perm[best[0]]])
+        np.testing.assert_allclose(w[t], p / p.sum(), rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
 # MoE gather matvec and the FFN layer
 # ---------------------------------------------------------------------------
 def test_moe_qmv_is_per_slot_matvec():
