@@ -270,6 +270,19 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
                         "unique_experts": u, "gbs_unique_experts": round(u * per_expert / (ms * 1e-3) / 1e9, 1)}
     del bg, bu, bd, G, U, D
     torch.cuda.empty_cache()
+    # router gate GEMV + router from the activations (a cold router matrix per
+    # call: more copies than the last-level cache holds)
+    wr_host = synth.router_weights(E, hidden)
+    br, R = rotated(wr_host.view(np.uint8), 320)
+    for T in (1, 4, 16):
+        x = torch.from_numpy(synth.normal(synth.SEED_X, T * hidden)).cuda()
+        bufs = (torch.empty((T, E), device="cuda"), torch.empty((T, topk), dtype=torch.int32, device="cuda"),
+                torch.empty((T, topk), device="cuda"))
+        ms = time_graph(lambda i: qmv.moe_gate_route(R[i % 320], x, T, E, hidden, topk, out=bufs), 320, 5)
+        out[f"T{T}"]["gate_route_us"] = round(ms * 1e3, 3)
+        out[f"T{T}"]["gate_route_gbs"] = round(wr_host.nbytes / (ms * 1e-3) / 1e9, 1)
+    del br, R
+    torch.cuda.empty_cache()
     return out
 
 

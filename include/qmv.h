@@ -112,6 +112,22 @@ int moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t 
               qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * MoE router gate + router (the "gemv" kernel of hanzo-ml
+ * `src/vulkan_backend.rs`, used for the router gate at one token in place of
+ * the tiled GEMM; `check_gemv` of hanzo-kernel `src/main.rs`):
+ *   logits[t, e] = sum_c wr[e, c] * x[t, c]   (f32 accumulation),
+ * then moe_route(logits, ids, wts, T, E, topk) on the same stream.
+ * wr: f32[E, hidden] row-major (the router weight, resident); x: f32[T,
+ * hidden]; logits: f32[T, E] (written, caller-owned scratch that also serves
+ * as output); ids: int32[T, topk]; wts: f32[T, topk] as in moe_route.
+ * 4 <= hidden <= 8192, hidden % 4 == 0; 1 <= E <= 4096; 1 <= topk <=
+ * min(E, 64); 1 <= T <= 2^24. wr and x 16-byte aligned, the rest 4-byte.
+ * All checks run on the host before any launch; nothing is written on error.
+ * ---------------------------------------------------------------------- */
+int moe_gate_route(const float *wr, const float *x, float *logits, int32_t *ids, float *wts, int64_t T,
+                   int64_t E, int64_t hidden, int64_t topk, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Expert-gather matvec over a resident bank (`moe_matvec_gpu`):
  *   y[s, r] = sum_c W[ids[s], r, c] * x[s / x_div, c],  s < nslots, r < n.
  * bank: E*n*(k/B)*S bytes; x: f32[nslots/x_div rounded up, k];

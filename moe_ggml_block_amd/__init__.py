@@ -33,6 +33,7 @@ _SIGS = {
     "qmv_q4k_q8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_debug_blocksums_q4k_q8": [_vp, _vp, _vp, _i64, _i64, _vp],
     "moe_route": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "moe_gate_route": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q4k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q6k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
@@ -148,6 +149,23 @@ def moe_route(logits, T, E, topk, out=None, stream=None):
     ids, wts = out
     _check(_lib.moe_route(_p(logits), _p(ids), _p(wts), T, E, topk, _stream(stream)), "moe_route")
     return ids, wts
+
+
+def moe_gate_route(wr, x, T, E, hidden, topk, out=None, stream=None):
+    """Router gate GEMV (logits = x wr^T in f32) then moe_route: (logits, ids, wts)."""
+    _need(wr, 4 * E * hidden, "wr")
+    _need(x, 4 * T * hidden, "x")
+    if out is None:
+        out = (torch.empty((T, E), dtype=torch.float32, device=x.device),
+               torch.empty((T, topk), dtype=torch.int32, device=x.device),
+               torch.empty((T, topk), dtype=torch.float32, device=x.device))
+    logits, ids, wts = out
+    _need(logits, 4 * T * E, "logits")
+    _need(ids, 4 * T * topk, "ids")
+    _need(wts, 4 * T * topk, "wts")
+    _check(_lib.moe_gate_route(_p(wr), _p(x), _p(logits), _p(ids), _p(wts), T, E, hidden, topk,
+                               _stream(stream)), "moe_gate_route")
+    return logits, ids, wts
 
 
 def _moe(name, fmt, bank, x, x_div, ids, nslots, n, k, E, y, stream):

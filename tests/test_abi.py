@@ -65,6 +65,12 @@ def test_host_validation_returns_before_launch(lib):
     lib.moe_route.restype = i32
     assert lib.moe_route(fake, fake, fake, 2, 8, 9, None) == QMV_EINVAL   # topk > E
     assert lib.moe_route(fake, fake, fake, 2, 128, 0, None) == QMV_EINVAL
+    lib.moe_gate_route.argtypes = [vp] * 5 + [i64] * 4 + [vp]
+    lib.moe_gate_route.restype = i32
+    assert lib.moe_gate_route(fake, fake, fake, fake, fake, 2, 8, 64, 9, None) == QMV_EINVAL   # topk > E
+    assert lib.moe_gate_route(fake, fake, fake, fake, fake, 2, 8, 62, 2, None) == QMV_EINVAL   # hidden % 4
+    assert lib.moe_gate_route(fake, fake, fake, fake, fake, 2, 8, 8196, 2, None) == -4         # hidden > 8192
+    assert lib.moe_gate_route(odd, fake, fake, fake, fake, 2, 8, 64, 2, None) == QMV_EALIGN
     lib.qmm_q4k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.qmm_q4k.restype = i32
     assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 64, None) == QMV_EINVAL  # bm
