@@ -54,9 +54,10 @@ def _load():
     lib.oracle_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.oracle_qmm.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i64, vp]
     lib.oracle_gemv.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.oracle_moe_qmm.argtypes = [i32, vp, vp, vp, i64, vp, i64, i64, i64, i64, vp, i64, vp]
     for name in ("oracle_dequant", "oracle_matvec", "oracle_quantize_act_q8",
                  "oracle_blocksums_q4k_q8", "oracle_matvec_q8act", "oracle_moe_route",
-                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv"):
+                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv", "oracle_moe_qmm"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -193,3 +194,16 @@ def gate_route(w, x, T: int, E: int, hidden: int, topk: int):
     lg = gemv(w, x, T, E, hidden)
     ids, wts = moe_route(lg.astype(np.float32), T, E, topk)
     return lg, ids, wts
+
+
+def moe_qmm(fmt, bank, xq, xs, x_div: int, ids, nslots: int, n: int, k: int, E: int, slots=None) -> np.ndarray:
+    """Expert-indexed prefill GEMM on a q8 activation: f64 Y[rows, n] for all slots or the listed ones;
+    slot s uses expert ids[s] and activation row s // x_div (zero row for an expert outside [0, E))."""
+    fmt = _FMT[fmt]
+    bank, xq, xs, ids = _c(bank, np.uint8), _c(xq, np.int8), _c(xs, np.float32), _c(ids, np.int32)
+    sl = None if slots is None else _c(slots, np.int64)
+    cnt = nslots if sl is None else sl.size
+    Y = np.empty((cnt, n), dtype=np.float64)
+    _check(_load().oracle_moe_qmm(fmt, _p(bank), _p(xq), _p(xs), x_div, _p(ids), nslots, n, k, E, _p(sl), cnt,
+                                  _p(Y)), "moe_qmm")
+    return Y

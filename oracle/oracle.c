@@ -429,3 +429,41 @@ int oracle_gemv(const float *w, const float *x, int64_t T, int64_t E, int64_t hi
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Expert-indexed prefill GEMM on a q8 activation (hanzo-kernel            */
+/* `src/main.rs`, `check_mmq_q4k_id`: the expert-indexed Q4_K MMQ, the MoE  */
+/* prefill twin of the gather matvec): for slot s with expert e = ids[s],  */
+/*   Y[s, r] = sum_c W_deq[e, r, c] * xs[a, c/32] * xq[a, c],  a = s/x_div, */
+/* in f64, for the listed slots (all when `slots` is NULL); a slot whose   */
+/* expert is outside [0, E) has a zero row.                                 */
+/* ---------------------------------------------------------------------- */
+int oracle_moe_qmm(int fmt, const uint8_t *bank, const int8_t *xq, const float *xs, int64_t x_div,
+                   const int32_t *ids, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                   const int64_t *slots, int64_t nlist, double *Y) {
+    if (fmt < 0 || fmt > 2 || k % QK[fmt] || k % 32 || x_div < 1) return -1;
+    int64_t cnt = slots ? nlist : nslots;
+    double *wd = malloc(sizeof(double) * (size_t)k);
+    double *xd = malloc(sizeof(double) * (size_t)k);
+    if (!wd || !xd) { free(wd); free(xd); return -2; }
+    int64_t rb = row_bytes(fmt, k);
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t s = slots ? slots[i] : i;
+        int32_t e = ids[s];
+        if (e < 0 || e >= E) {
+            for (int64_t r = 0; r < n; ++r) Y[i * n + r] = 0.0;
+            continue;
+        }
+        int64_t a = s / x_div;
+        for (int64_t c = 0; c < k; ++c) xd[c] = (double)xs[a * (k / 32) + c / 32] * (double)xq[a * k + c];
+        for (int64_t r = 0; r < n; ++r) {
+            dec_row(fmt, bank + ((int64_t)e * n + r) * rb, k, wd);
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; ++c) acc += wd[c] * xd[c];
+            Y[i * n + r] = acc;
+        }
+    }
+    free(wd);
+    free(xd);
+    return 0;
+}

@@ -428,6 +428,38 @@ def test_qmm_rows_equal_q8act_matvec_and_numpy():
     np.testing.assert_array_equal(oracle.qmm("q4k", w, xq, xs, m, n, k, mrows=[4, 1]), Y[[4, 1]])
 
 
+def test_moe_qmm_single_expert_is_qmm():
+    m, n, k = 6, 10, 512
+    w = synth.weights(synth.FMT_Q4K, 53, n, k)
+    x = synth.normal(54, m * k).reshape(m, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, m, k)
+    ids = np.zeros(m, dtype=np.int32)
+    np.testing.assert_array_equal(oracle.moe_qmm("q4k", w, xq, xs, 1, ids, m, n, k, 1),
+                                  oracle.qmm("q4k", w, xq, xs, m, n, k))
+
+
+@pytest.mark.parametrize("fmt,sfmt", [("q4k", synth.FMT_Q4K), ("q6k", synth.FMT_Q6K)])
+def test_moe_qmm_slots_pick_expert_and_activation_row(fmt, sfmt):
+    # slot s multiplies expert ids[s]'s slice of the bank by activation row
+    # s // x_div; experts outside [0, E) give zero rows; E, n, k, T all differ
+    E, n, k, T, x_div = 4, 9, 512, 3, 2
+    bank = synth.weights(sfmt, 55, E * n, k)
+    x = synth.normal(56, T * k).reshape(T, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, T, k)
+    ids = np.array([3, 0, -1, 2, 3, 4], dtype=np.int32)
+    Y = oracle.moe_qmm(fmt, bank, xq, xs, x_div, ids, ids.size, n, k, E)
+    Wd = oracle.dequant(fmt, bank).reshape(E, n, k)
+    Xd = np.repeat(xs, 32, axis=1).astype(np.float64) * xq
+    for s_, e in enumerate(ids):
+        if 0 <= e < E:
+            ref = Wd[e] @ Xd[s_ // x_div]
+            np.testing.assert_allclose(Y[s_], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        else:
+            assert np.all(Y[s_] == 0.0)
+    np.testing.assert_array_equal(oracle.moe_qmm(fmt, bank, xq, xs, x_div, ids, ids.size, n, k, E,
+                                                 slots=[4, 0]), Y[[4, 0]])
+
+
 # ---------------------------------------------------------------------------
 # input encoders: round-trip bounds through the pinned decoders
 # ---------------------------------------------------------------------------
