@@ -307,7 +307,39 @@ def prefill_other(copies: int = 16):
     res["quantize_act_q8_us"] = round(qa * 1e3, 2)
     del big, W
     torch.cuda.empty_cache()
+    res["moe_qmm_q4k"] = moe_prefill_other()
     return res
+
+
+def moe_prefill_other(bank_copies: int = 3):
+    """Expert-indexed Q4_K prefill GEMM at the MoE layer's gate shape: 512
+    tokens routed top-8 over 128 experts (router on N(0,1) logits), experts
+    [768, 2048], one q8 activation row per token; banks rotate over cold copies."""
+    import numpy as np
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    T, topk, E, n, k = 512, 8, 128, 768, 2048
+    ns = T * topk
+    bank = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, n, k)
+    per_expert = bank.nbytes // E
+    bb, B = rotated(bank, bank_copies)
+    del bank
+    lg = torch.from_numpy(synth.moe_logits(T, E)).cuda()
+    ids, _ = qmv.moe_route(lg, T, E, topk)
+    uniq = len(np.unique(ids.cpu().numpy()))
+    x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, T * k)).cuda()
+    xq, xs, xsum = qmv.quantize_act_q8(x, T, k)
+    y = torch.empty((ns, n), device="cuda")
+    ms = time_graph(lambda i: qmv.moe_qmm_q4k(B[i % bank_copies], xq, xs, xsum, topk, ids, ns, n, k, E, y=y),
+                    4 * bank_copies, 5)
+    del bb, B
+    torch.cuda.empty_cache()
+    flops = 2.0 * ns * n * k
+    return {"shape": f"T{T} top{topk} E{E} {n}x{k}", "us": round(ms * 1e3, 2),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_f16_pct": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2),
+            "unique_experts": uniq, "gbs_unique_experts": round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)}
 
 
 def profile_run(copies: int, other_shapes: bool = False):

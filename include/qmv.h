@@ -171,6 +171,26 @@ int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const fl
 int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
             int64_t m, int64_t n, int64_t k, int bm, qmv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Expert-indexed Q4_K prefill GEMM on a q8 activation (the MoE prefill twin
+ * of moe_qmv_q4k: `check_mmq_q4k_id` of hanzo-kernel `src/main.rs`,
+ * expert-indexed MMQ with its slot grouping):
+ *   y[s, r] = sum_c W_deq[ids[s], r, c] * xs[a, c/32] * xq[a, c],
+ *   a = s / x_div (x_div = topk: one activation row per token),
+ * with the epilogue of qmm_q4k (f16 matrix cores on exact integer operands).
+ * bank: E*n*(k/256)*144 bytes, expert-major; xq: int8[ceil(nslots/x_div), k];
+ * xs, xsum: f32[ceil(nslots/x_div), k/32] (quantize_act_q8); ids:
+ * int32[nslots]; y: f32[nslots, n], every row written (a slot whose expert
+ * is outside [0, E) gets a zero row). Slots are grouped by expert on the
+ * device (each expert's rows are read once per tile of its slots); no
+ * workspace, no host synchronization.
+ * k % 256 == 0; 1 <= E <= 1024; 1 <= nslots <= 2^20; bank and xq 16-byte
+ * aligned, the rest 4-byte.
+ * ---------------------------------------------------------------------- */
+int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, const float *xsum, int64_t x_div,
+                const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                qmv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,6 +38,7 @@ _SIGS = {
     "moe_qmv_q6k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
+    "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -210,6 +211,22 @@ def qmm_q4k(w, xq, xs, xsum, m, n, k, bm=128, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     _check(_lib.qmm_q4k(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), m, n, k, bm, _stream(stream)), "qmm_q4k")
+    return y
+
+
+def moe_qmm_q4k(bank, xq, xs, xsum, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    """Expert-indexed Q4_K prefill GEMM: y[s] = W[ids[s]] . deq(xq, xs)[s // x_div]."""
+    rows = (nslots + x_div - 1) // x_div
+    _need(bank, E * n * row_bytes("q4k", k), "bank")
+    _need(xq, rows * k, "xq")
+    _need(xs, 4 * rows * (k // 32), "xs")
+    _need(xsum, 4 * rows * (k // 32), "xsum")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * nslots * n, "y")
+    _check(_lib.moe_qmm_q4k(_p(bank), _p(xq), _p(xs), _p(xsum), x_div, _p(ids), _p(y), nslots, n, k, E,
+                            _stream(stream)), "moe_qmm_q4k")
     return y
 
 

@@ -36,6 +36,8 @@
 //    the staging writes go eight lanes to eight consecutive 16-byte units
 //    of a row (activations) or to one unit of eight rows (weights, xs), so
 //    they are conflict-free too.
+#include <algorithm>
+
 #include "blocks.hpp"
 
 namespace {
@@ -67,12 +69,27 @@ QMV_DEV uint2 q4x4_to_f16(uint32_t c, h2 sc, h2 nsc) {
 
 QMV_DEV h2 splat(float v) { return h2{(_Float16)v, (_Float16)v}; }
 
-template <int BM, int BN, int KP, int MT, int NT, int NTHREADS>
-__global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict__ w,
-                                                      const int8_t *__restrict__ xq,
-                                                      const float *__restrict__ xs,
-                                                      const float *__restrict__ xsum,
-                                                      float *__restrict__ Y, int m, int n, int k) {
+struct QmmArgs {
+    const uint8_t *w;     // dense weight [n, k/256] blocks, or the expert bank [E, n, k/256]
+    const int8_t *xq;     // q8 activation rows
+    const float *xs, *xsum;
+    float *Y;
+    int m, n, k;          // dense: m activation rows; expert-indexed: m slots
+    const int32_t *ids;   // expert-indexed only: expert of each slot
+    int E, x_div;         // expert-indexed only: slot s reads activation row s / x_div
+};
+
+constexpr int QMM_ID_CHUNK = 4096;  // slot ids staged in LDS at a time (grouping)
+constexpr int QMM_MOE_MAX_E = 1024;
+
+template <int BM, int BN, int KP, int MT, int NT, int NTHREADS, bool MOE = false>
+__global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
+    const uint8_t *__restrict__ w = a.w;
+    const int8_t *__restrict__ xq = a.xq;
+    const float *__restrict__ xs = a.xs;
+    const float *__restrict__ xsum = a.xsum;
+    float *__restrict__ Y = a.Y;
+    const int m = a.m, n = a.n, k = a.k;
     constexpr int WM = 16 * MT, WN = 16 * NT;
     constexpr int WGM = BM / WM, WGN = BN / WN;
     static_assert(WGM * WGN == NTHREADS / 64, "the waves tile the workgroup");
@@ -103,13 +120,153 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
     const int kb = k / 32;
     const size_t row_bytes = (size_t)(k / 256) * 144;
 
+    // Expert-indexed mode: this workgroup's tile is row block r0 / BM of the
+    // esel-th expert's slots (experts in ascending order, each slot list in
+    // ascending slot order). Every workgroup derives it from ids itself:
+    // per-expert counts, a prefix of the tile counts, then a compaction of
+    // the slots of its expert. Workgroups past the last tile exit.
+    __shared__ int s_slot[MOE ? BM : 1];
+    int esel = 0;  // expert of this workgroup's tile
+    if constexpr (MOE) {
+        static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
+        constexpr int IPT = QMM_ID_CHUNK / NTHREADS;  // ids per thread per chunk
+        constexpr int NW = NTHREADS / 64;
+        int *s_ids = reinterpret_cast<int *>(&Bs[0][0]);  // staging buffers are free until the main loop
+        int *s_cnt = reinterpret_cast<int *>(&As[0][0]);
+        __shared__ int s_wsum[NW];
+        __shared__ int s_sel[3];
+        const int E = a.E;
+        auto stage_ids = [&](int c0) {  // ids[c0, c0 + QMM_ID_CHUNK) -> s_ids (-1 past the end)
+            int v[IPT];
+#pragma unroll
+            for (int i = 0; i < IPT; ++i) {
+                const int sl = c0 + tid + NTHREADS * i;
+                v[i] = sl < m ? a.ids[sl] : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < IPT; ++i) s_ids[tid + NTHREADS * i] = v[i];
+        };
+        for (int e = tid; e < E; e += NTHREADS) s_cnt[e] = 0;
+        for (int i = tid; i < BM; i += NTHREADS) s_slot[i] = -1;
+        for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
+            __syncthreads();  // counts zeroed / previous chunk counted
+            stage_ids(c0);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < IPT; ++i) {
+                const int e = s_ids[tid + NTHREADS * i];
+                if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns experts [l*EPL, l*EPL + EPL): tile counts, then an
+            // inclusive prefix over the lanes
+            constexpr int EPL = QMM_MOE_MAX_E / 64;
+            int tl = 0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                if (e < E) tl += (s_cnt[e] + BM - 1) / BM;
+            }
+            int inc = tl;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(inc, d);
+                if (lane >= d) inc += v;
+            }
+            const int tile = blockIdx.y;
+            int t = inc - tl;
+            if (tile >= t && tile < inc) {
+                for (int i = 0; i < EPL; ++i) {
+                    const int e = lane * EPL + i;
+                    const int nt = e < E ? (s_cnt[e] + BM - 1) / BM : 0;
+                    if (tile < t + nt) {
+                        s_sel[0] = e;
+                        s_sel[1] = (tile - t) * BM;
+                        break;
+                    }
+                    t += nt;
+                }
+            }
+            if (lane == 63) {
+                if (tile >= inc) s_sel[0] = -1;
+                s_sel[2] = inc;  // tiles in all
+            }
+        }
+        __syncthreads();
+        esel = s_sel[0];
+        if (esel < 0) {
+            // Past the last tile (uniform over the workgroup). The grid has
+            // more row blocks than tiles (each present expert adds less than
+            // one tile to nslots / BM), and these spare workgroups write the
+            // zero rows of slots whose expert is out of range: spare j of
+            // this column block takes slots [j*chunk, (j+1)*chunk).
+            const int ntot = s_sel[2], nspare = (int)gridDim.y - ntot, j = (int)blockIdx.y - ntot;
+            const int chunk = (m + nspare - 1) / nspare;
+            const int s0 = j * chunk, s1 = min(m, s0 + chunk);
+            for (int sl = s0 + tid; sl < s1; sl += NTHREADS) {
+                const int e = a.ids[sl];
+                if (e < 0 || e >= E)
+                    for (int c = n0; c < min(n0 + BN, n); ++c) Y[(size_t)sl * n + c] = 0.0f;
+            }
+            return;
+        }
+        const int r0 = s_sel[1];
+        // ascending compaction of the slots of expert esel: per chunk, wave w
+        // takes ids [w*CW, (w+1)*CW) in order; ranks are the running count
+        // plus the earlier waves' counts plus the ballot prefix
+        constexpr int CW = QMM_ID_CHUNK / NW;
+        int run = 0;
+        for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
+            __syncthreads();  // previous chunk's readers done
+            stage_ids(c0);
+            __syncthreads();
+            int cw = 0;
+            for (int b = 0; b < CW; b += 64) cw += __popcll(__ballot(s_ids[wave * CW + b + lane] == esel));
+            if (lane == 0) s_wsum[wave] = cw;
+            __syncthreads();
+            int base = run;
+            for (int v = 0; v < NW; ++v) {
+                if (v < wave) base += s_wsum[v];
+                run += s_wsum[v];
+            }
+            for (int b = 0; b < CW; b += 64) {
+                const bool hit = s_ids[wave * CW + b + lane] == esel;
+                const uint64_t bal = __ballot(hit);
+                const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+                if (hit && rank >= r0 && rank < r0 + BM) s_slot[rank - r0] = c0 + wave * CW + b + lane;
+                base += __popcll(bal);
+            }
+        }
+        __syncthreads();
+    }
+    // activation row of each staging role (-1: no row, zeros are staged)
+    auto act_row = [&](int row) -> int {
+        if constexpr (MOE) {
+            const int sl = s_slot[row];
+            return sl >= 0 ? sl / a.x_div : -1;
+        } else {
+            return m0 + row < m ? m0 + row : -1;
+        }
+    };
+
     // weight staging role (rows fastest, so that eight lanes write eight
     // rows at one offset): row brow, code bytes [8*bc, +8) of the phase's
     // slice of the row's 128 code bytes
     const bool bact = tid < BCH;
     const int brow = tid % BN, bc0 = tid / BN;  // chunk i has bc = bc0 + i*NTHREADS/BN
     const bool bvalid = bact && n0 + brow < n;
-    const uint8_t *wrow = w + (size_t)(bvalid ? n0 + brow : 0) * row_bytes;
+    const uint8_t *wrow = w + ((size_t)esel * n + (bvalid ? n0 + brow : 0)) * row_bytes;
+    // activation rows of this thread's activation chunks and xs entries
+    int arow[AC], xrow[XC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) arow[i] = act_row((tid + NTHREADS * i) / ACR);
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+        const int idx = tid + NTHREADS * i;
+        xrow[i] = idx < BM * NBP ? act_row(idx % BM) : -1;
+    }
 
     // two register sets of raw codes: phase p is loaded into set p % 2 two
     // phases before it is converted
@@ -123,9 +280,9 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
         const int k0 = ph * KP, s = k0 / 256, half = ph % PPS;
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
-            const int ch = tid + NTHREADS * i, row = ch / ACR, c8 = ch % ACR;
-            const int gm = m0 + row;
-            ra[q][i] = gm < m ? *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + k0 + 8 * c8)
+            const int c8 = (tid + NTHREADS * i) % ACR;
+            const int gm = arow[i];
+            ra[q][i] = gm >= 0 ? *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + k0 + 8 * c8)
                               : make_uint2(0u, 0u);
         }
         if (bvalid) {
@@ -137,9 +294,9 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
         }
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
-            const int idx = tid + NTHREADS * i, row = idx % BM, bl = idx / BM;
-            const int gm = m0 + row;
-            const bool ok = gm < m && idx < BM * NBP;
+            const int bl = (tid + NTHREADS * i) / BM;
+            const int gm = xrow[i];
+            const bool ok = gm >= 0;
             rxs[q][i] = ok ? xs[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
             rxsum[q][i] = ok ? xsum[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
         }
@@ -307,8 +464,11 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const uint8_t *__restrict_
             const int col = n0 + wn * WN + 16 * u + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * WM + 16 * t + 4 * lq + r;
-                if (row < m && col < n) Y[(size_t)row * n + col] = out[t][u][r];
+                const int tr = wm * WM + 16 * t + 4 * lq + r;
+                int row;
+                if constexpr (MOE) row = s_slot[tr];
+                else row = m0 + tr < m ? m0 + tr : -1;
+                if (row >= 0 && col < n) Y[(size_t)row * n + col] = out[t][u][r];
             }
         }
 }
@@ -329,6 +489,16 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 #define QMM_CFG256_BN 32
 #define QMM_CFG256_NT 512
 #endif
+// expert-indexed tiles: few rows per expert (BM 32 or 64), 128 columns
+#define QMM_MOE32 32, 128, 64, 2, 2, 256
+#define QMM_MOE32_BM 32
+#define QMM_MOE32_BN 128
+#define QMM_MOE32_NT 256
+#define QMM_MOE64 64, 128, 64, 2, 2, 512
+#define QMM_MOE64_BM 64
+#define QMM_MOE64_BN 128
+#define QMM_MOE64_NT 512
+constexpr int64_t QMM_MOE_MAX_SLOTS = 1 << 20;
 
 }  // namespace
 
@@ -340,17 +510,42 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(y, 4))
         return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
-    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    QmmArgs a{static_cast<const uint8_t *>(w), xq, xs, xsum, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
     if (bm == 128) {
-        constexpr int BMv = QMM_CFG128_BM, BNv = QMM_CFG128_BN;
-        const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(QMM_CFG128_NT), 0, s, wb, xq, xs, xsum, y, (int)m,
-                           (int)n, (int)k);
+        const dim3 grid((unsigned)div_up(n, QMM_CFG128_BN), (unsigned)div_up(m, QMM_CFG128_BM));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(QMM_CFG128_NT), 0, s, a);
     } else {
-        constexpr int BMv = QMM_CFG256_BM, BNv = QMM_CFG256_BN;
-        const dim3 grid((unsigned)div_up(n, BNv), (unsigned)div_up(m, BMv));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(QMM_CFG256_NT), 0, s, wb, xq, xs, xsum, y, (int)m,
-                           (int)n, (int)k);
+        const dim3 grid((unsigned)div_up(n, QMM_CFG256_BN), (unsigned)div_up(m, QMM_CFG256_BM));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(QMM_CFG256_NT), 0, s, a);
+    }
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, const float *xsum, int64_t x_div,
+                           const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                           qmv_stream_t stream) {
+    if (!bank || !xq || !xs || !xsum || !ids || !y || x_div < 1 || nslots < 1 || n < 1 || E < 1 || k < 256 ||
+        k % 256)
+        return QMV_EINVAL;
+    if (E > QMM_MOE_MAX_E || nslots > QMM_MOE_MAX_SLOTS || n > (1 << 24) || k > (1 << 20) ||
+        E * n * (k / 256) * 144 > ((int64_t)1 << 40))
+        return QMV_EUNSUPPORTED;
+    if (!aligned(bank, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(ids, 4) ||
+        !aligned(y, 4))
+        return QMV_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    QmmArgs a{static_cast<const uint8_t *>(bank), xq, xs, xsum, y, (int)nslots, (int)n, (int)k, ids, (int)E,
+              (int)x_div};
+    // rows per tile from the mean slots per expert; the grid covers the
+    // largest possible tile count (every expert adds at most one partial
+    // tile) and the spare workgroups exit after the grouping
+    if (nslots <= 48 * E) {
+        const dim3 grid((unsigned)div_up(n, QMM_MOE32_BN), (unsigned)(div_up(nslots, QMM_MOE32_BM) + std::min(E, nslots)));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true>), grid, dim3(QMM_MOE32_NT), 0, s, a);
+    } else {
+        const dim3 grid((unsigned)div_up(n, QMM_MOE64_BN), (unsigned)(div_up(nslots, QMM_MOE64_BM) + std::min(E, nslots)));
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
     }
     QMV_LAUNCH_CHECK();
     return QMV_OK;
