@@ -307,6 +307,16 @@ def prefill_other(copies: int = 16):
     res["quantize_act_q8_us"] = round(qa * 1e3, 2)
     del big, W
     torch.cuda.empty_cache()
+    # Q6_K prefill at the same shape (q8 activation)
+    w6 = synth.weights(synth.FMT_Q6K, synth.SEED_W, n, k)
+    big6, W6 = rotated(w6, copies)
+    del w6
+    y6 = torch.empty((m, n), device="cuda")
+    ms6 = time_graph(lambda i: qmv.qmm_q6k(W6[i % copies], xq, xs, m, n, k, y=y6), 2 * copies, 5)
+    res["q6k"] = {"us": round(ms6 * 1e3, 2), "tops": round(2.0 * m * n * k / (ms6 * 1e-3) / 1e12, 2),
+                  "mfma_f16_pct": round(2.0 * m * n * k / (ms6 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2)}
+    del big6, W6
+    torch.cuda.empty_cache()
     res["moe_qmm_q4k"] = moe_prefill_other()
     return res
 
@@ -335,11 +345,31 @@ def moe_prefill_other(bank_copies: int = 3):
                     4 * bank_copies, 5)
     del bb, B
     torch.cuda.empty_cache()
-    flops = 2.0 * ns * n * k
-    return {"shape": f"T{T} top{topk} E{E} {n}x{k}", "us": round(ms * 1e3, 2),
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_f16_pct": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2),
-            "unique_experts": uniq, "gbs_unique_experts": round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)}
+
+    def line(ms, n_, k_, per_exp, shape):
+        flops = 2.0 * ns * n_ * k_
+        return {"shape": shape, "us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "mfma_f16_pct": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2),
+                "unique_experts": uniq, "gbs_unique_experts": round(uniq * per_exp / (ms * 1e-3) / 1e9, 1)}
+
+    res = {"moe_qmm_q4k_gate": line(ms, n, k, per_expert, f"T{T} top{topk} E{E} {n}x{k}")}
+    # the down projection: Q6_K [2048, 768] experts on one f32 (and one q8) row per slot
+    dbank = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, k, n)
+    per_down = dbank.nbytes // E
+    bd, D = rotated(dbank, bank_copies)
+    del dbank
+    h = torch.from_numpy(synth.normal(synth.SEED_X, ns * n)).cuda()
+    hq, hs, _ = qmv.quantize_act_q8(h, ns, n)
+    yd = torch.empty((ns, k), device="cuda")
+    ms6 = time_graph(lambda i: qmv.moe_qmm_q6k_f32(D[i % bank_copies], h, 1, ids, ns, k, n, E, y=yd),
+                     4 * bank_copies, 5)
+    res["moe_qmm_q6k_f32_down"] = line(ms6, k, n, per_down, f"T{T} top{topk} E{E} {k}x{n}")
+    ms6q = time_graph(lambda i: qmv.moe_qmm_q6k(D[i % bank_copies], hq, hs, 1, ids, ns, k, n, E, y=yd),
+                      4 * bank_copies, 5)
+    res["moe_qmm_q6k_q8_down"] = line(ms6q, k, n, per_down, f"T{T} top{topk} E{E} {k}x{n}")
+    del bd, D
+    torch.cuda.empty_cache()
+    return res
 
 
 def profile_run(copies: int, other_shapes: bool = False):

@@ -191,6 +191,35 @@ int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, const float
                 const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
                 qmv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Q6_K prefill GEMM on a q8 activation (hanzo-ml `src/vulkan_backend.rs`,
+ * `matmul_q6k_gpu`: weights stay quantized, each decoded value serves a
+ * tile of rows; its int8 tile `mul_mm_q6k_tiled_dp4a` takes quantize_act_q8
+ * output):
+ *   y[i, r] = sum_c W_deq[r, c] * xs[i, c/32] * xq[i, c].
+ * w: n*(k/256)*210 bytes; xq: int8[m, k]; xs: f32[m, k/32]; y: f32[m, n].
+ * Each 16-value sub-block's integer dot runs on the f16 matrix cores, the
+ * int8 sub-scales and xs in an exact epilogue. k % 256 == 0; xq 16-byte
+ * aligned, w 2-byte, the rest 4-byte.
+ * ---------------------------------------------------------------------- */
+int qmm_q6k(const void *w, const int8_t *xq, const float *xs, float *y, int64_t m, int64_t n, int64_t k,
+            qmv_stream_t stream);
+
+/* Expert-indexed Q6_K prefill GEMM (the MoE down projection at m > 1;
+ * `matmul_q6k_gpu_off` on one expert's slice of a resident bank, slots
+ * grouped by expert on the device as in moe_qmm_q4k):
+ *   moe_qmm_q6k:     y[s, r] = sum_c W_deq[ids[s], r, c] * xs[a, c/32] * xq[a, c]
+ *   moe_qmm_q6k_f32: y[s, r] = sum_c W_deq[ids[s], r, c] * x[a, c]
+ * with a = s / x_div. The f32 form splits each activation (scaled by a power
+ * of two per 32 values) into two f16 halves on the matrix cores, which keeps
+ * f32 accuracy. bank: E*n*(k/256)*210 bytes; y: f32[nslots, n], every row
+ * written (zero for an expert outside [0, E)). k % 256 == 0; 1 <= E <= 1024;
+ * nslots <= 2^20; xq and x 16-byte aligned, bank 2-byte, the rest 4-byte. */
+int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids, float *y,
+                int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y, int64_t nslots,
+                    int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,9 @@ _SIGS = {
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "qmm_q6k": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "moe_qmm_q6k": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_qmm_q6k_f32": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -227,6 +230,47 @@ def moe_qmm_q4k(bank, xq, xs, xsum, x_div, ids, nslots, n, k, E, y=None, stream=
     _need(y, 4 * nslots * n, "y")
     _check(_lib.moe_qmm_q4k(_p(bank), _p(xq), _p(xs), _p(xsum), x_div, _p(ids), _p(y), nslots, n, k, E,
                             _stream(stream)), "moe_qmm_q4k")
+    return y
+
+
+def qmm_q6k(w, xq, xs, m, n, k, y=None, stream=None):
+    """Q6_K prefill GEMM on a q8 activation: y = deq(xq, xs) . W^T."""
+    _need(w, n * row_bytes("q6k", k), "w")
+    _need(xq, m * k, "xq")
+    _need(xs, 4 * m * (k // 32), "xs")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * m * n, "y")
+    _check(_lib.qmm_q6k(_p(w), _p(xq), _p(xs), _p(y), m, n, k, _stream(stream)), "qmm_q6k")
+    return y
+
+
+def moe_qmm_q6k(bank, xq, xs, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    """Expert-indexed Q6_K prefill GEMM on a q8 activation."""
+    rows = (nslots + x_div - 1) // x_div
+    _need(bank, E * n * row_bytes("q6k", k), "bank")
+    _need(xq, rows * k, "xq")
+    _need(xs, 4 * rows * (k // 32), "xs")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * nslots * n, "y")
+    _check(_lib.moe_qmm_q6k(_p(bank), _p(xq), _p(xs), x_div, _p(ids), _p(y), nslots, n, k, E, _stream(stream)),
+           "moe_qmm_q6k")
+    return y
+
+
+def moe_qmm_q6k_f32(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    """Expert-indexed Q6_K prefill GEMM on an f32 activation."""
+    rows = (nslots + x_div - 1) // x_div
+    _need(bank, E * n * row_bytes("q6k", k), "bank")
+    _need(x, 4 * rows * k, "x")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=x.device)
+    _need(y, 4 * nslots * n, "y")
+    _check(_lib.moe_qmm_q6k_f32(_p(bank), _p(x), x_div, _p(ids), _p(y), nslots, n, k, E, _stream(stream)),
+           "moe_qmm_q6k_f32")
     return y
 
 

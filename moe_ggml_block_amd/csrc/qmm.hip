@@ -37,6 +37,7 @@
 //    of a row (activations) or to one unit of eight rows (weights, xs), so
 //    they are conflict-free too.
 #include <algorithm>
+#include <type_traits>
 
 #include "blocks.hpp"
 
@@ -82,6 +83,129 @@ struct QmmArgs {
 constexpr int QMM_ID_CHUNK = 4096;  // slot ids staged in LDS at a time (grouping)
 constexpr int QMM_MOE_MAX_E = 1024;
 
+// Expert-indexed tiles. The tile of workgroup row block blockIdx.y is row
+// block r0 / BM of the esel-th expert's slots (experts in ascending order,
+// each expert's slots in ascending slot order). Every workgroup derives it
+// from ids itself: per-expert counts (LDS atomics over ids staged in chunks),
+// a wave prefix of the per-expert tile counts, then a ballot compaction of
+// its expert's slots into s_slot (-1 past the expert's count). Returns esel,
+// or -1 for a workgroup past the last tile: the grid has more row blocks
+// than tiles (each present expert adds less than one tile to nslots / BM),
+// and those spare workgroups write the zero rows (columns [n0, n0 + BN)) of
+// slots whose expert is outside [0, E), spare j taking slots
+// [j*chunk, (j+1)*chunk). s_ids (QMM_ID_CHUNK ints) and s_cnt (E ints) are
+// LDS scratch that the caller reuses afterwards; the function ends with a
+// barrier. Call from every thread of the workgroup.
+template <int BM, int BN, int NTHREADS>
+QMV_DEV int qmm_group(const int32_t *__restrict__ ids, int m, int E, int *s_ids, int *s_cnt, int *s_slot,
+                      float *__restrict__ Y, int n, int n0) {
+    constexpr int IPT = QMM_ID_CHUNK / NTHREADS;  // ids per thread per chunk
+    constexpr int NW = NTHREADS / 64;
+    __shared__ int s_wsum[NW];
+    __shared__ int s_sel[3];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto stage_ids = [&](int c0) {  // ids[c0, c0 + QMM_ID_CHUNK) -> s_ids (-1 past the end)
+        int v[IPT];
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int sl = c0 + tid + NTHREADS * i;
+            v[i] = sl < m ? ids[sl] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) s_ids[tid + NTHREADS * i] = v[i];
+    };
+    for (int e = tid; e < E; e += NTHREADS) s_cnt[e] = 0;
+    for (int i = tid; i < BM; i += NTHREADS) s_slot[i] = -1;
+    for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
+        __syncthreads();  // counts zeroed / previous chunk counted
+        stage_ids(c0);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int e = s_ids[tid + NTHREADS * i];
+            if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // lane l owns experts [l*EPL, l*EPL + EPL): tile counts, then an
+        // inclusive prefix over the lanes
+        constexpr int EPL = QMM_MOE_MAX_E / 64;
+        int tl = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            if (e < E) tl += (s_cnt[e] + BM - 1) / BM;
+        }
+        int inc = tl;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(inc, d);
+            if (lane >= d) inc += v;
+        }
+        const int tile = blockIdx.y;
+        int t = inc - tl;
+        if (tile >= t && tile < inc) {
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                const int nt = e < E ? (s_cnt[e] + BM - 1) / BM : 0;
+                if (tile < t + nt) {
+                    s_sel[0] = e;
+                    s_sel[1] = (tile - t) * BM;
+                    break;
+                }
+                t += nt;
+            }
+        }
+        if (lane == 63) {
+            if (tile >= inc) s_sel[0] = -1;
+            s_sel[2] = inc;  // tiles in all
+        }
+    }
+    __syncthreads();
+    const int esel = s_sel[0];
+    if (esel < 0) {
+        const int ntot = s_sel[2], nspare = (int)gridDim.y - ntot, j = (int)blockIdx.y - ntot;
+        const int chunk = (m + nspare - 1) / nspare;
+        const int s0 = j * chunk, s1 = min(m, s0 + chunk);
+        for (int sl = s0 + tid; sl < s1; sl += NTHREADS) {
+            const int e = ids[sl];
+            if (e < 0 || e >= E)
+                for (int c = n0; c < min(n0 + BN, n); ++c) Y[(size_t)sl * n + c] = 0.0f;
+        }
+        return -1;
+    }
+    const int r0 = s_sel[1];
+    // ascending compaction: per chunk, wave w takes ids [w*CW, (w+1)*CW) in
+    // order; a rank is the running count plus the earlier waves' counts plus
+    // the ballot prefix
+    constexpr int CW = QMM_ID_CHUNK / NW;
+    int run = 0;
+    for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
+        __syncthreads();  // previous chunk's readers done
+        stage_ids(c0);
+        __syncthreads();
+        int cw = 0;
+        for (int b = 0; b < CW; b += 64) cw += __popcll(__ballot(s_ids[wave * CW + b + lane] == esel));
+        if (lane == 0) s_wsum[wave] = cw;
+        __syncthreads();
+        int base = run;
+        for (int v = 0; v < NW; ++v) {
+            if (v < wave) base += s_wsum[v];
+            run += s_wsum[v];
+        }
+        for (int b = 0; b < CW; b += 64) {
+            const bool hit = s_ids[wave * CW + b + lane] == esel;
+            const uint64_t bal = __ballot(hit);
+            const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+            if (hit && rank >= r0 && rank < r0 + BM) s_slot[rank - r0] = c0 + wave * CW + b + lane;
+            base += __popcll(bal);
+        }
+    }
+    __syncthreads();
+    return esel;
+}
+
 template <int BM, int BN, int KP, int MT, int NT, int NTHREADS, bool MOE = false>
 __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
     const uint8_t *__restrict__ w = a.w;
@@ -120,126 +244,14 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
     const int kb = k / 32;
     const size_t row_bytes = (size_t)(k / 256) * 144;
 
-    // Expert-indexed mode: this workgroup's tile is row block r0 / BM of the
-    // esel-th expert's slots (experts in ascending order, each slot list in
-    // ascending slot order). Every workgroup derives it from ids itself:
-    // per-expert counts, a prefix of the tile counts, then a compaction of
-    // the slots of its expert. Workgroups past the last tile exit.
+    // Expert-indexed mode: this workgroup's tile (qmm_group)
     __shared__ int s_slot[MOE ? BM : 1];
     int esel = 0;  // expert of this workgroup's tile
     if constexpr (MOE) {
         static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
-        constexpr int IPT = QMM_ID_CHUNK / NTHREADS;  // ids per thread per chunk
-        constexpr int NW = NTHREADS / 64;
-        int *s_ids = reinterpret_cast<int *>(&Bs[0][0]);  // staging buffers are free until the main loop
-        int *s_cnt = reinterpret_cast<int *>(&As[0][0]);
-        __shared__ int s_wsum[NW];
-        __shared__ int s_sel[3];
-        const int E = a.E;
-        auto stage_ids = [&](int c0) {  // ids[c0, c0 + QMM_ID_CHUNK) -> s_ids (-1 past the end)
-            int v[IPT];
-#pragma unroll
-            for (int i = 0; i < IPT; ++i) {
-                const int sl = c0 + tid + NTHREADS * i;
-                v[i] = sl < m ? a.ids[sl] : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < IPT; ++i) s_ids[tid + NTHREADS * i] = v[i];
-        };
-        for (int e = tid; e < E; e += NTHREADS) s_cnt[e] = 0;
-        for (int i = tid; i < BM; i += NTHREADS) s_slot[i] = -1;
-        for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
-            __syncthreads();  // counts zeroed / previous chunk counted
-            stage_ids(c0);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < IPT; ++i) {
-                const int e = s_ids[tid + NTHREADS * i];
-                if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane l owns experts [l*EPL, l*EPL + EPL): tile counts, then an
-            // inclusive prefix over the lanes
-            constexpr int EPL = QMM_MOE_MAX_E / 64;
-            int tl = 0;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int e = lane * EPL + i;
-                if (e < E) tl += (s_cnt[e] + BM - 1) / BM;
-            }
-            int inc = tl;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int v = __shfl_up(inc, d);
-                if (lane >= d) inc += v;
-            }
-            const int tile = blockIdx.y;
-            int t = inc - tl;
-            if (tile >= t && tile < inc) {
-                for (int i = 0; i < EPL; ++i) {
-                    const int e = lane * EPL + i;
-                    const int nt = e < E ? (s_cnt[e] + BM - 1) / BM : 0;
-                    if (tile < t + nt) {
-                        s_sel[0] = e;
-                        s_sel[1] = (tile - t) * BM;
-                        break;
-                    }
-                    t += nt;
-                }
-            }
-            if (lane == 63) {
-                if (tile >= inc) s_sel[0] = -1;
-                s_sel[2] = inc;  // tiles in all
-            }
-        }
-        __syncthreads();
-        esel = s_sel[0];
-        if (esel < 0) {
-            // Past the last tile (uniform over the workgroup). The grid has
-            // more row blocks than tiles (each present expert adds less than
-            // one tile to nslots / BM), and these spare workgroups write the
-            // zero rows of slots whose expert is out of range: spare j of
-            // this column block takes slots [j*chunk, (j+1)*chunk).
-            const int ntot = s_sel[2], nspare = (int)gridDim.y - ntot, j = (int)blockIdx.y - ntot;
-            const int chunk = (m + nspare - 1) / nspare;
-            const int s0 = j * chunk, s1 = min(m, s0 + chunk);
-            for (int sl = s0 + tid; sl < s1; sl += NTHREADS) {
-                const int e = a.ids[sl];
-                if (e < 0 || e >= E)
-                    for (int c = n0; c < min(n0 + BN, n); ++c) Y[(size_t)sl * n + c] = 0.0f;
-            }
-            return;
-        }
-        const int r0 = s_sel[1];
-        // ascending compaction of the slots of expert esel: per chunk, wave w
-        // takes ids [w*CW, (w+1)*CW) in order; ranks are the running count
-        // plus the earlier waves' counts plus the ballot prefix
-        constexpr int CW = QMM_ID_CHUNK / NW;
-        int run = 0;
-        for (int c0 = 0; c0 < m; c0 += QMM_ID_CHUNK) {
-            __syncthreads();  // previous chunk's readers done
-            stage_ids(c0);
-            __syncthreads();
-            int cw = 0;
-            for (int b = 0; b < CW; b += 64) cw += __popcll(__ballot(s_ids[wave * CW + b + lane] == esel));
-            if (lane == 0) s_wsum[wave] = cw;
-            __syncthreads();
-            int base = run;
-            for (int v = 0; v < NW; ++v) {
-                if (v < wave) base += s_wsum[v];
-                run += s_wsum[v];
-            }
-            for (int b = 0; b < CW; b += 64) {
-                const bool hit = s_ids[wave * CW + b + lane] == esel;
-                const uint64_t bal = __ballot(hit);
-                const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
-                if (hit && rank >= r0 && rank < r0 + BM) s_slot[rank - r0] = c0 + wave * CW + b + lane;
-                base += __popcll(bal);
-            }
-        }
-        __syncthreads();
+        esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
+                                           reinterpret_cast<int *>(&As[0][0]), s_slot, Y, n, n0);
+        if (esel < 0) return;  // uniform over the workgroup
     }
     // activation row of each staging role (-1: no row, zeros are staged)
     auto act_row = [&](int row) -> int {
@@ -547,6 +559,375 @@ extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, 
         const dim3 grid((unsigned)div_up(n, QMM_MOE64_BN), (unsigned)(div_up(nslots, QMM_MOE64_BM) + std::min(E, nslots)));
         hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
     }
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+namespace {
+
+// ===================================================================== Q6_K
+// Q6_K prefill GEMM (hanzo-ml `src/vulkan_backend.rs`, `matmul_q6k_gpu`:
+// weights stay quantized and each decoded value is reused over a tile of
+// rows; `mul_mm_q6k_tiled_dp4a` on a q8 activation):
+//   Y[i, r] = sum_s d[r,s] * sum_{b in s} fx[i,b] * (sc[r,2b'] T[i,r,2b'] + sc[r,2b'+1] T[i,r,2b'+1])
+//   T[i,r,t] = sum_{l<16} a[i,16t+l] * (q[r,16t+l] - 32)
+// with one q8 block b = two 16-value sub-blocks t. q - 32 (|.| <= 32) is
+// exact in f16, but sc*(q - 32) (up to 4064) is not, so the sub-scale stays
+// out of the matrix product: each sub-block is one v_mfma_f32_16x16x16_f16
+// and the epilogue forms sc_a*T_a + sc_b*T_b per block.
+//  - q8 activation (ACT_Q8): a = xq, fx = xs. T is an integer below 2^16 and
+//    sc*T + sc*T an integer below 2^24, so the block sum is exact before the
+//    one FMA with xs, as in the Q4_K kernel.
+//  - f32 activation (ACT_F32): each 32-value block of a row is scaled by a
+//    power of two fx^-1 that puts its largest magnitude in [2^14, 2^15)
+//    (exact), split into a high f16 and the f16 of the remainder, and both
+//    halves go through the matrix cores (two MFMAs per sub-block); fx then
+//    undoes the scaling in the epilogue. The split keeps 22 bits of each
+//    value, so the product is as accurate as f32 arithmetic.
+// Code staging per row and phase of 64 values (a quarter superblock): the
+// phase's 64 ql bytes and 32 qh bytes give q = nibble | 2 bits << 4, turned
+// into the halves 1024 + q and then q - 32 exactly.
+enum { ACT_Q8 = 0, ACT_F32 = 1 };
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+struct Qmm6Args {
+    const uint8_t *w;    // dense weight [n, k/256] blocks of 210 bytes, or the bank [E, n, k/256]
+    const int8_t *xq;    // ACT_Q8: q8 activation rows
+    const float *xs;     // ACT_Q8: per-32 scales
+    const float *x;      // ACT_F32: f32 activation rows
+    float *Y;
+    int m, n, k;
+    const int32_t *ids;  // expert-indexed only
+    int E, x_div;
+};
+
+// four 6-bit codes (one per byte) -> four f16 values q - 32, exact
+QMV_DEV uint2 q6x4_to_f16(uint32_t c) {
+    const h2 off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+    return make_uint2(as_u32(as_h2(half_bytes_lo(c)) + off), as_u32(as_h2(half_bytes_hi(c)) + off));
+}
+
+template <int BM, int BN, int MT, int NT, int NTHREADS, int ACT, bool MOE>
+__global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
+    constexpr int KP = 64;                       // values per phase: a quarter superblock
+    constexpr int WM = 16 * MT, WN = 16 * NT;
+    constexpr int WGM = BM / WM, WGN = BN / WN;
+    static_assert(WGM * WGN == NTHREADS / 64, "the waves tile the workgroup");
+    constexpr int ST = KP + 8;                   // halves per LDS row
+    constexpr int NBP = KP / 32;                 // q8 blocks per phase
+    constexpr int NH = ACT == ACT_F32 ? 2 : 1;   // activation halves (high, low)
+    // activation staging: q8 -> 8-byte chunks (8 codes); f32 -> 16-byte chunks (4 values)
+    constexpr int AW = ACT == ACT_F32 ? 4 : 8;   // values per chunk
+    constexpr int ACR = KP / AW;                 // chunks per row
+    constexpr int AC = BM * ACR / NTHREADS;      // chunks per thread
+    static_assert(AC >= 1 && AC * NTHREADS == BM * ACR, "activation staging");
+    constexpr int BCH = BN * (KP / 8);           // 8-code weight chunks per phase
+    constexpr int BCT = BCH / NTHREADS;          // per thread
+    static_assert(BCT >= 1 && BCT * NTHREADS == BCH && NTHREADS % BN == 0, "weight staging");
+    constexpr int XC = (BM * NBP + NTHREADS - 1) / NTHREADS;  // xs values per thread (ACT_Q8)
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[NH][2][BM * ST];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * ST];
+    __shared__ __attribute__((aligned(16))) float sfx[2][NBP][BM];
+    __shared__ float ssc[2][16][BN], sd[2][BN];  // by superblock parity
+
+    const float *__restrict__ xsrc = a.x;
+    float *__restrict__ Y = a.Y;
+    const int m = a.m, n = a.n, k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int kb = k / 32;
+    const size_t row_bytes = (size_t)(k / 256) * 210;
+
+    __shared__ int s_slot[MOE ? BM : 1];
+    int esel = 0;
+    if constexpr (MOE) {
+        static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0][0]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
+        esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
+                                           reinterpret_cast<int *>(&As[0][0][0]), s_slot, Y, n, n0);
+        if (esel < 0) return;
+    }
+    auto act_row = [&](int row) -> int {
+        if constexpr (MOE) {
+            const int sl = s_slot[row];
+            return sl >= 0 ? sl / a.x_div : -1;
+        } else {
+            return m0 + row < m ? m0 + row : -1;
+        }
+    };
+
+    // weight staging role: row brow, chunks bc = bc0 + i*NTHREADS/BN (8 codes each)
+    const int brow = tid % BN, bc0 = tid / BN;
+    const bool bvalid = n0 + brow < n;
+    const uint8_t *wrow = a.w + ((size_t)esel * n + (bvalid ? n0 + brow : 0)) * row_bytes;
+    int arow[AC], xrow[XC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) arow[i] = act_row((tid + NTHREADS * i) / ACR);
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+        const int idx = tid + NTHREADS * i;
+        xrow[i] = idx < BM * NBP ? act_row(idx % BM) : -1;
+    }
+
+    using AReg = typename std::conditional<ACT == ACT_F32, float4, uint2>::type;
+    AReg ra[2][AC];
+    uint2 rql[2][BCT], rqh[2][BCT];
+    uint4 rsc[2];
+    uint32_t rd[2] = {0u, 0u};
+    float rxs[2][XC];
+
+    auto prefetch = [&](int ph, int q) {
+        const int k0 = ph * KP, s = k0 / 256, p4 = ph & 3, hh = p4 >> 1;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = (tid + NTHREADS * i) % ACR, gm = arow[i];
+            if constexpr (ACT == ACT_F32)
+                ra[q][i] = gm >= 0 ? *reinterpret_cast<const float4 *>(xsrc + (size_t)gm * k + k0 + 4 * c)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                ra[q][i] = gm >= 0 ? *reinterpret_cast<const uint2 *>(a.xq + (size_t)gm * k + k0 + 8 * c)
+                                   : make_uint2(0u, 0u);
+        }
+        if (bvalid) {
+            const uint8_t *blk = wrow + (size_t)s * 210;
+#pragma unroll
+            for (int i = 0; i < BCT; ++i) {
+                const int bc = bc0 + i * (NTHREADS / BN);  // 0..7
+                const int gl = bc >> 2, l0 = 8 * (bc & 3);
+                rql[q][i] = *reinterpret_cast<const uint2 *>(blk + 64 * hh + 32 * gl + l0);
+                rqh[q][i] = *reinterpret_cast<const uint2 *>(blk + 128 + 32 * hh + l0);
+            }
+            if (p4 == 0 && bc0 == 0) {
+                rsc[q] = *reinterpret_cast<const uint4 *>(blk + 192);
+                rd[q] = ld2(blk + 208);
+            }
+        }
+        if constexpr (ACT == ACT_Q8) {
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int bl = (tid + NTHREADS * i) / BM, gm = xrow[i];
+                rxs[q][i] = gm >= 0 ? a.xs[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
+            }
+        }
+    };
+
+    auto convert_store = [&](int ph, int buf, int q) {
+        const int p4 = ph & 3, odd = p4 & 1, sp = (ph >> 2) & 1;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int ch = tid + NTHREADS * i, row = ch / ACR, c = ch % ACR;
+            if constexpr (ACT == ACT_F32) {
+                // power-of-two block scale from the block's largest magnitude
+                // (8 consecutive lanes hold one 32-value block)
+                const float4 v = ra[q][i];
+                float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+                am = fmaxf(am, __shfl_xor(am, 1));
+                am = fmaxf(am, __shfl_xor(am, 2));
+                am = fmaxf(am, __shfl_xor(am, 4));
+                // e = exponent of am (am in [2^e, 2^(e+1))); scale 2^(14 - e)
+                const int e = am > 0.f ? ((int)((__float_as_uint(am) >> 23) & 0xFF) - 127) : 0;
+                const int ee = max(min(14 - e, 126), -126);  // 2^ee and 2^-ee are normal
+                const float sc = __uint_as_float((uint32_t)(ee + 127) << 23);
+                const float inv = __uint_as_float((uint32_t)(127 - ee) << 23);
+                const float y0 = v.x * sc, y1 = v.y * sc, y2 = v.z * sc, y3 = v.w * sc;
+                const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1, h2v = (_Float16)y2, h3 = (_Float16)y3;
+                const h4 hi = {h0, h1, h2v, h3};
+                const h4 lo = {(_Float16)(y0 - (float)h0), (_Float16)(y1 - (float)h1), (_Float16)(y2 - (float)h2v),
+                               (_Float16)(y3 - (float)h3)};
+                *reinterpret_cast<h4 *>(&As[0][buf][row * ST + 4 * c]) = hi;
+                *reinterpret_cast<h4 *>(&As[NH - 1][buf][row * ST + 4 * c]) = lo;
+                if ((c & 7) == 0) sfx[buf][c >> 3][row] = inv;
+            } else {
+                const uint2 h0 = i8x4_to_f16(ra[q][i].x), h1 = i8x4_to_f16(ra[q][i].y);
+                *reinterpret_cast<uint4 *>(&As[0][buf][row * ST + 8 * c]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            }
+        }
+        if (p4 == 0 && bc0 == 0) {
+            const uint4 s4 = rsc[q];
+            const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                ssc[sp][t][brow] = (float)(int8_t)((sw[t >> 2] >> (8 * (t & 3))) & 0xFFu);
+            sd[sp][brow] = h2f(rd[q]);
+        }
+#pragma unroll
+        for (int i = 0; i < BCT; ++i) {
+            const int bc = bc0 + i * (NTHREADS / BN);
+            const int gl = bc >> 2, l0 = 8 * (bc & 3);
+            const int sh = 4 * odd + 2 * gl;  // qh bit pair of this 32-run
+            const uint2 ql = rql[q][i], qh = rqh[q][i];
+            const uint32_t c0 = ((ql.x >> (4 * odd)) & 0x0F0F0F0Fu) | (((qh.x >> sh) & 0x03030303u) << 4);
+            const uint32_t c1 = ((ql.y >> (4 * odd)) & 0x0F0F0F0Fu) | (((qh.y >> sh) & 0x03030303u) << 4);
+            const uint2 f0 = q6x4_to_f16(c0), f1 = q6x4_to_f16(c1);
+            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * gl + l0]) = make_uint4(f0.x, f0.y, f1.x, f1.y);
+        }
+        if constexpr (ACT == ACT_Q8) {
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int idx = tid + NTHREADS * i, row = idx % BM, bl = idx / BM;
+                if (idx < BM * NBP) sfx[buf][bl][row] = rxs[q][i];
+            }
+        }
+    };
+
+    v4f acc[MT][NT], out[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int nph = k / KP;  // a multiple of 4
+    prefetch(0, 0);
+    convert_store(0, 0, 0);
+    prefetch(1, 1);
+    prefetch(2, 0);
+    __syncthreads();
+    for (int ph0 = 0; ph0 < nph; ph0 += 2) {
+#pragma unroll
+        for (int Q = 0; Q < 2; ++Q) {
+            const int ph = ph0 + Q, buf = Q, p4 = ph & 3, sp = (ph >> 2) & 1;
+#pragma unroll
+            for (int bl = 0; bl < NBP; ++bl) {
+                v4f T[2][MT][NT];
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int col = 32 * bl + 16 * sb + 4 * lq;
+                    h4 fa[NH][MT], fb[NT];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int hl = 0; hl < NH; ++hl)
+                            fa[hl][t] = *reinterpret_cast<const h4 *>(&As[hl][buf][(wm * WM + 16 * t + li) * ST + col]);
+#pragma unroll
+                    for (int u = 0; u < NT; ++u)
+                        fb[u] = *reinterpret_cast<const h4 *>(&Bs[buf][(wn * WN + 16 * u + li) * ST + col]);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int u = 0; u < NT; ++u) {
+                            v4f r = __builtin_amdgcn_mfma_f32_16x16x16f16(fa[0][t], fb[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            if constexpr (NH == 2) r = __builtin_amdgcn_mfma_f32_16x16x16f16(fa[1][t], fb[u], r, 0, 0, 0);
+                            T[sb][t][u] = r;
+                        }
+                }
+                const int sub = 4 * p4 + 2 * bl;  // first sub-block of this q8 block in the superblock
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const int c = wn * WN + 16 * u + li;
+                    const float sa = ssc[sp][sub][c], sbv = ssc[sp][sub + 1][c];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const v4f fx = *reinterpret_cast<const v4f *>(&sfx[buf][bl][wm * WM + 16 * t + 4 * lq]);
+                        const v4f S = sa * T[0][t][u] + sbv * T[1][t][u];
+                        acc[t][u] = fx * S + acc[t][u];
+                    }
+                }
+            }
+            if (p4 == 3) {
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const float dcol = sd[sp][wn * WN + 16 * u + li];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        out[t][u] = dcol * acc[t][u] + out[t][u];
+                        acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            }
+            if (ph + 1 < nph) {
+                convert_store(ph + 1, buf ^ 1, Q ^ 1);
+                if (ph + 3 < nph) prefetch(ph + 3, Q ^ 1);
+            }
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int col = n0 + wn * WN + 16 * u + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = wm * WM + 16 * t + 4 * lq + r;
+                int row;
+                if constexpr (MOE) row = s_slot[tr];
+                else row = m0 + tr < m ? m0 + tr : -1;
+                if (row >= 0 && col < n) Y[(size_t)row * n + col] = out[t][u][r];
+            }
+        }
+}
+
+// Q6_K tile configurations: dense (64 x 128, 512 threads) and expert-indexed
+// (32 x 128, 256 threads)
+#define QMM6_DENSE 64, 128, 2, 2, 512
+#define QMM6_MOE 32, 128, 2, 2, 256
+
+int check_q6k_shape(int64_t n, int64_t k) {
+    if (n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (n > (1 << 24) || k > (1 << 20)) return QMV_EUNSUPPORTED;
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" int qmm_q6k(const void *w, const int8_t *xq, const float *xs, float *y, int64_t m, int64_t n, int64_t k,
+                       qmv_stream_t stream) {
+    if (!w || !xq || !xs || !y || m < 1) return QMV_EINVAL;
+    int rc = check_q6k_shape(n, k);
+    if (rc != QMV_OK) return rc;
+    if (m > (1 << 24) || m * k > ((int64_t)1 << 34)) return QMV_EUNSUPPORTED;
+    if (!aligned(w, 2) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(y, 4)) return QMV_EALIGN;
+    Qmm6Args a{static_cast<const uint8_t *>(w), xq, xs, nullptr, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
+    const dim3 grid((unsigned)div_up(n, 128), (unsigned)div_up(m, 64));
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_DENSE, ACT_Q8, false>), grid, dim3(512), 0, (hipStream_t)stream, a);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+namespace {
+int check_moe6(const void *bank, const int32_t *ids, float *y, int64_t x_div, int64_t nslots, int64_t n, int64_t k,
+               int64_t E) {
+    if (!bank || !ids || !y || x_div < 1 || nslots < 1 || E < 1) return QMV_EINVAL;
+    int rc = check_q6k_shape(n, k);
+    if (rc != QMV_OK) return rc;
+    if (E > QMM_MOE_MAX_E || nslots > QMM_MOE_MAX_SLOTS || E * n * (k / 256) * 210 > ((int64_t)1 << 40))
+        return QMV_EUNSUPPORTED;
+    if (!aligned(bank, 2) || !aligned(ids, 4) || !aligned(y, 4)) return QMV_EALIGN;
+    return QMV_OK;
+}
+}  // namespace
+
+extern "C" int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids,
+                           float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
+    if (!xq || !xs) return QMV_EINVAL;
+    int rc = check_moe6(bank, ids, y, x_div, nslots, n, k, E);
+    if (rc != QMV_OK) return rc;
+    if (!aligned(xq, 16) || !aligned(xs, 4)) return QMV_EALIGN;
+    Qmm6Args a{static_cast<const uint8_t *>(bank), xq, xs, nullptr, y, (int)nslots, (int)n, (int)k, ids, (int)E,
+               (int)x_div};
+    const dim3 grid((unsigned)div_up(n, 128), (unsigned)(div_up(nslots, 32) + std::min(E, nslots)));
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_Q8, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
+                               int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
+    if (!x) return QMV_EINVAL;
+    int rc = check_moe6(bank, ids, y, x_div, nslots, n, k, E);
+    if (rc != QMV_OK) return rc;
+    if (!aligned(x, 16)) return QMV_EALIGN;
+    Qmm6Args a{static_cast<const uint8_t *>(bank), nullptr, nullptr, x, y, (int)nslots, (int)n, (int)k, ids, (int)E,
+               (int)x_div};
+    const dim3 grid((unsigned)div_up(n, 128), (unsigned)(div_up(nslots, 32) + std::min(E, nslots)));
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_F32, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

@@ -91,3 +91,83 @@ def test_moe_qmm_rejects_too_many_experts():
     i = torch.zeros(4, dtype=torch.int32, device="cuda")
     with pytest.raises(qmv.QmvError):
         qmv.moe_qmm_q4k(t, t, f, f, 1, i, 4, 1, 256, 1025)
+
+
+# ------------------------------------------------------------ Q6_K prefill
+@pytest.mark.parametrize("m,n,k", [(1, 16, 256), (70, 200, 512), (128, 256, 768), (300, 130, 2048)])
+def test_qmm_q6k_dense_small(m, n, k):
+    announce(f"qmm_q6k m={m} n={n} k={k}")
+    w = synth.weights(synth.FMT_Q6K, 90, n, k)
+    x = synth.normal(91, m * k).reshape(m, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q6k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q6k(dev(w), dev(xq), dev(xs), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_q6k_random_blocks_every_code_and_scale():
+    """Random raw Q6_K blocks: every 6-bit code and every int8 sub-scale
+    (including -128 and sc*(q-32) values that f16 cannot hold) occurs."""
+    m, n, k = 40, 64, 1024
+    announce("qmm_q6k random blocks")
+    w = synth.random_blocks(synth.FMT_Q6K, 92, n * k // 256).reshape(n, -1)
+    x = synth.normal(93, m * k).reshape(m, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q6k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q6k(dev(w), dev(xq), dev(xs), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def _check6(ids, n, k, E, x_div, seed, f32, sample=None):
+    ns = ids.size
+    rows_x = -(-ns // x_div)
+    bank = synth.moe_bank(synth.FMT_Q6K, seed, E, n, k)
+    x = synth.normal(seed + 1, rows_x * k).reshape(rows_x, k)
+    if f32:
+        got = host(qmv.moe_qmm_q6k_f32(dev(bank), dev(x), x_div, dev(ids), ns, n, k, E))
+        sl = np.arange(ns) if sample is None else np.asarray(sample)
+        ref = oracle.moe_qmv("q6k", bank, x, x_div, ids, ns, n, k, E)[sl]
+    else:
+        xq, xs, _ = oracle.quantize_act_q8(x, rows_x, k)
+        got = host(qmv.moe_qmm_q6k(dev(bank), dev(xq), dev(xs), x_div, dev(ids), ns, n, k, E))
+        sl = np.arange(ns) if sample is None else np.asarray(sample)
+        ref = oracle.moe_qmm("q6k", bank, xq, xs, x_div, ids, ns, n, k, E, slots=sample)
+    assert got.shape == (ns, n) and np.isfinite(got).all()
+    assert scalerel(ref, got[sl]) <= TOL, scalerel(ref, got[sl])
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(got[bad] == 0.0)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("case", ["pages", "ragged", "id_chunks"])
+def test_moe_qmm_q6k(case, f32):
+    if case == "pages":
+        # down shape [2048, 768], 32 tokens x top-8 over 16 experts, a row per slot
+        args = (_stride_ids(32, 8, 16), 2048, 768, 16, 1, 94)
+        sample = np.arange(0, 256, 5)
+    elif case == "ragged":
+        ids = np.array([2] * 45 + [-3] + [0] * 3 + [9], dtype=np.int32)
+        args = (ids, 130, 256, 3, 1, 96)
+        sample = None
+    else:
+        ids = ((np.arange(4500) * 5) % 11).astype(np.int32)
+        args = (ids, 48, 512, 11, 3, 98)
+        sample = np.array([0, 1, 4095, 4096, 4499])
+    announce(f"moe_qmm_q6k {case} f32={f32}")
+    _check6(*args, f32, sample=sample)
+
+
+def test_moe_qmm_q6k_f32_wide_dynamic_range():
+    """Activation blocks spanning many binades (1e-6 .. 1e4) and an all-zero
+    block: the per-block power-of-two scale and the two-half split keep f32
+    accuracy without f16 overflow."""
+    E, n, k, ns = 3, 64, 512, 12
+    bank = synth.moe_bank(synth.FMT_Q6K, 99, E, n, k)
+    x = synth.normal(100, ns * k).reshape(ns, k)
+    x *= np.float32(10.0) ** np.linspace(-6, 4, k, dtype=np.float32)[None, :]
+    x[3, 64:96] = 0.0
+    ids = (np.arange(ns) % E).astype(np.int32)
+    announce("moe_qmm_q6k_f32 dynamic range")
+    got = host(qmv.moe_qmm_q6k_f32(dev(bank), dev(x), 1, dev(ids), ns, n, k, E))
+    ref = oracle.moe_qmv("q6k", bank, x, 1, ids, ns, n, k, E)
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
