@@ -55,9 +55,10 @@ def _load():
     lib.oracle_qmm.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i64, vp]
     lib.oracle_gemv.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.oracle_moe_qmm.argtypes = [i32, vp, vp, vp, i64, vp, i64, i64, i64, i64, vp, i64, vp]
+    lib.oracle_moe_ffn_q8x.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp]
     for name in ("oracle_dequant", "oracle_matvec", "oracle_quantize_act_q8",
                  "oracle_blocksums_q4k_q8", "oracle_matvec_q8act", "oracle_moe_route",
-                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv", "oracle_moe_qmm"):
+                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv", "oracle_moe_qmm", "oracle_moe_ffn_q8x"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -207,3 +208,17 @@ def moe_qmm(fmt, bank, xq, xs, x_div: int, ids, nslots: int, n: int, k: int, E: 
     _check(_load().oracle_moe_qmm(fmt, _p(bank), _p(xq), _p(xs), x_div, _p(ids), nslots, n, k, E, _p(sl), cnt,
                                   _p(Y)), "moe_qmm")
     return Y
+
+
+def moe_ffn_q8x(gate, up, down, xq, xs, ids, wts, T: int, topk: int, hidden: int, inter: int, E: int,
+                toks=None) -> np.ndarray:
+    """MoE layer on a q8 activation (prefill): f64 y rows of all tokens or the listed ones."""
+    gate, up, down = _c(gate, np.uint8), _c(up, np.uint8), _c(down, np.uint8)
+    xq, xs = _c(xq, np.int8), _c(xs, np.float32)
+    ids, wts = _c(ids, np.int32), _c(wts, np.float32)
+    tl = None if toks is None else _c(toks, np.int64)
+    cnt = T if tl is None else tl.size
+    y = np.empty((cnt, hidden), dtype=np.float64)
+    _check(_load().oracle_moe_ffn_q8x(_p(gate), _p(up), _p(down), _p(xq), _p(xs), _p(ids), _p(wts), T, topk,
+                                      hidden, inter, E, _p(tl), cnt, _p(y)), "moe_ffn_q8x")
+    return y

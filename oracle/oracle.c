@@ -467,3 +467,55 @@ int oracle_moe_qmm(int fmt, const uint8_t *bank, const int8_t *xq, const float *
     free(xd);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* MoE layer at prefill on a q8 activation (the prefill twin of             */
+/* oracle_moe_ffn: the expert-indexed MMQ takes quantize_act_q8 output,     */
+/* hanzo-kernel `src/main.rs` `check_mmq_q4k_id`; `matmul_q6k_gpu_off` runs  */
+/* the down projection on one expert of the bank): x_deq[t, c] =            */
+/* xs[t, c/32] * xq[t, c] exactly in f64, then per slot s = topk*t + j,     */
+/* e = ids[s] in [0, E): g = Wg[e] x_deq[t], u = Wu[e] x_deq[t],            */
+/* h = g / (1 + exp(-g)) * u, d = Wd[e] h; y[t] = sum_j wts[t, j] d_s (a    */
+/* slot outside [0, E) adds nothing). y rows of the listed tokens (all when */
+/* `toks` is NULL), f64.                                                    */
+/* ---------------------------------------------------------------------- */
+int oracle_moe_ffn_q8x(const uint8_t *gate, const uint8_t *up, const uint8_t *down, const int8_t *xq,
+                       const float *xs, const int32_t *ids, const float *wts, int64_t T, int64_t topk,
+                       int64_t hidden, int64_t inter, int64_t E, const int64_t *toks, int64_t ntok, double *y) {
+    if (hidden % 256 || inter % 256) return -1;
+    int64_t cnt = toks ? ntok : T;
+    double *xd = malloc(sizeof(double) * (size_t)hidden);
+    double *h = malloc(sizeof(double) * (size_t)inter);
+    double *wd = malloc(sizeof(double) * (size_t)(hidden > inter ? hidden : inter));
+    if (!xd || !h || !wd) { free(xd); free(h); free(wd); return -2; }
+    int64_t rb_gu = row_bytes(ORACLE_Q4K, hidden), rb_dn = row_bytes(ORACLE_Q6K, inter);
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t t = toks ? toks[i] : i;
+        for (int64_t c = 0; c < hidden; ++c)
+            xd[c] = (double)xs[t * (hidden / 32) + c / 32] * (double)xq[t * hidden + c];
+        for (int64_t r = 0; r < hidden; ++r) y[i * hidden + r] = 0.0;
+        for (int64_t j = 0; j < topk; ++j) {
+            int32_t e = ids[t * topk + j];
+            if (e < 0 || e >= E) continue;
+            for (int64_t r = 0; r < inter; ++r) {
+                double g = 0.0, u = 0.0;
+                dec_row(ORACLE_Q4K, gate + ((int64_t)e * inter + r) * rb_gu, hidden, wd);
+                for (int64_t c = 0; c < hidden; ++c) g += wd[c] * xd[c];
+                dec_row(ORACLE_Q4K, up + ((int64_t)e * inter + r) * rb_gu, hidden, wd);
+                for (int64_t c = 0; c < hidden; ++c) u += wd[c] * xd[c];
+                h[r] = g / (1.0 + exp(-g)) * u;
+            }
+            double wj = (double)wts[t * topk + j];
+            for (int64_t r = 0; r < hidden; ++r) {
+                dec_row(ORACLE_Q6K, down + ((int64_t)e * hidden + r) * rb_dn, inter, wd);
+                double acc = 0.0;
+                for (int64_t c = 0; c < inter; ++c) acc += wd[c] * h[c];
+                y[i * hidden + r] += wj * acc;
+            }
+        }
+    }
+    free(xd);
+    free(h);
+    free(wd);
+    return 0;
+}

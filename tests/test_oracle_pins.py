@@ -460,6 +460,26 @@ def test_moe_qmm_slots_pick_expert_and_activation_row(fmt, sfmt):
                                                  slots=[4, 0]), Y[[4, 0]])
 
 
+def test_moe_ffn_q8x_equals_f32_layer_on_exact_dequantized_x():
+    # with power-of-two scales xs * xq is exact in f32, so the q8 layer must
+    # equal the f32 layer (pinned above) on x = xs * xq, token by token
+    E, hidden, inter, T, topk = 5, 512, 256, 4, 3
+    gate = synth.weights(synth.FMT_Q4K, 61, E * inter, hidden)
+    up = synth.weights(synth.FMT_Q4K, 62, E * inter, hidden)
+    down = synth.weights(synth.FMT_Q6K, 63, E * hidden, inter)
+    rng = np.random.default_rng(64)
+    xq = rng.integers(-127, 128, size=(T, hidden)).astype(np.int8)
+    xs = (2.0 ** rng.integers(-9, -4, size=(T, hidden // 32))).astype(np.float32)
+    x = (np.repeat(xs, 32, axis=1) * xq).astype(np.float32)
+    ids = np.array([[4, 0, 2], [1, -1, 3], [2, 2, 0], [0, 5, 4]], dtype=np.int32)  # repeats, out of range
+    wts = rng.random((T, topk)).astype(np.float32)
+    y = oracle.moe_ffn_q8x(gate, up, down, xq, xs, ids, wts, T, topk, hidden, inter, E)
+    ref, _, _ = oracle.moe_ffn(gate, up, down, x, ids, wts, T, topk, hidden, inter, E)
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    np.testing.assert_array_equal(oracle.moe_ffn_q8x(gate, up, down, xq, xs, ids, wts, T, topk, hidden, inter,
+                                                     E, toks=[3, 1]), y[[3, 1]])
+
+
 # ---------------------------------------------------------------------------
 # input encoders: round-trip bounds through the pinned decoders
 # ---------------------------------------------------------------------------
