@@ -367,7 +367,29 @@ def moe_prefill_other(bank_copies: int = 3):
     ms6q = time_graph(lambda i: qmv.moe_qmm_q6k(D[i % bank_copies], hq, hs, 1, ids, ns, k, n, E, y=yd),
                       4 * bank_copies, 5)
     res["moe_qmm_q6k_q8_down"] = line(ms6q, k, n, per_down, f"T{T} top{topk} E{E} {k}x{n}")
-    del bd, D
+    # the whole prefill layer (quantize, grouping, paired gate/up + SiLU, down, combine)
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, n, k)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, n, k)
+    bg, G = rotated(gate, bank_copies)
+    bu, U = rotated(up, bank_copies)
+    per_layer = (gate.nbytes + up.nbytes) // E + per_down
+    del gate, up
+    for TT in (128, 512, 2048):
+        lgT = torch.from_numpy(synth.moe_logits(TT, E)).cuda()
+        idsT, wT = qmv.moe_route(lgT, TT, E, topk)
+        uT = len(np.unique(idsT.cpu().numpy()))
+        xT = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, TT * k)).cuda()
+        yT = torch.empty((TT, k), device="cuda")
+        wsT = torch.empty(qmv.moe_ffn_prefill_workspace_bytes(TT, topk, k, n, E), dtype=torch.uint8, device="cuda")
+        msL = time_graph(lambda i: qmv.moe_ffn_prefill_q4k_q6k(G[i % bank_copies], U[i % bank_copies],
+                                                               D[i % bank_copies], xT, idsT, wT, TT, topk, k, n, E,
+                                                               y=yT, ws=wsT), 2 * bank_copies, 3)
+        res[f"layer_T{TT}"] = {"us": round(msL * 1e3, 1), "tokens_per_s": round(TT / (msL * 1e-3), 0),
+                               "unique_experts": uT,
+                               "gbs_unique_experts": round(uT * per_layer / (msL * 1e-3) / 1e9, 1),
+                               "tflops": round(2.0 * TT * topk * 3 * n * k / (msL * 1e-3) / 1e12, 2)}
+        del wsT
+    del bd, D, bg, G, bu, U
     torch.cuda.empty_cache()
     return res
 

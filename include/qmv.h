@@ -220,6 +220,28 @@ int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, int64_t x_d
 int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y, int64_t nslots,
                     int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * MoE layer at prefill (the same layer as moe_ffn_q4k_q6k at m > 1, on the
+ * pages' prefill path: the token activations are quantized to q8 once and
+ * the expert-indexed MMQ runs gate and up, `check_mmq_q4k_id` of
+ * hanzo-kernel `src/main.rs`; the down projection is the Q6_K prefill GEMM
+ * on one expert of the bank, `matmul_q6k_gpu_off` of hanzo-ml
+ * `src/vulkan_backend.rs`):
+ *   x_deq = quantize_act_q8(x) dequantized; for slot s = topk*t + j with
+ *   e = ids[t, j] in [0, E): h = silu(Wg[e] x_deq[t]) * (Wu[e] x_deq[t]),
+ *   d = Wd[e] h (h kept in f32); y[t] = sum_j wts[t, j] * d_s.
+ * Same operands as moe_ffn_q4k_q6k; ws: moe_ffn_prefill_workspace_bytes()
+ * bytes of device scratch (q8 activation, tile table, h, d), 256-byte
+ * aligned, caller-owned, contents undefined after the call. Slots are
+ * grouped by expert on the device; nothing is synchronized with the host.
+ * hidden, inter: multiples of 256 (<= 65536); 1 <= E <= 1024; T <= 65535;
+ * T*topk <= 2^20. gate, up, x, y 16-byte aligned; down 2-byte; rest 4-byte.
+ * ---------------------------------------------------------------------- */
+int64_t moe_ffn_prefill_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E);
+int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
+                            const float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,
+                            int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

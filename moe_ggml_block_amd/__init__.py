@@ -42,6 +42,7 @@ _SIGS = {
     "qmm_q6k": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "moe_qmm_q6k": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q6k_f32": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_ffn_prefill_q4k_q6k": [_vp] * 8 + [_i64] * 6 + [_vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -49,11 +50,14 @@ for _name, _args in _SIGS.items():
     _f.restype = _i32
 _lib.moe_ffn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
 _lib.moe_ffn_workspace_bytes.restype = _i64
+_lib.moe_ffn_prefill_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
+_lib.moe_ffn_prefill_workspace_bytes.restype = _i64
 _lib.qmv_version.restype = ctypes.c_char_p
 _lib.qmv_strerror.argtypes = [_i32]
 _lib.qmv_strerror.restype = ctypes.c_char_p
 
-EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "qmv_version", "qmv_strerror")
+EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "moe_ffn_prefill_workspace_bytes", "qmv_version",
+                          "qmv_strerror")
 
 BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210)}
 
@@ -271,6 +275,31 @@ def moe_qmm_q6k_f32(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
     _need(y, 4 * nslots * n, "y")
     _check(_lib.moe_qmm_q6k_f32(_p(bank), _p(x), x_div, _p(ids), _p(y), nslots, n, k, E, _stream(stream)),
            "moe_qmm_q6k_f32")
+    return y
+
+
+def moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E) -> int:
+    return int(_lib.moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E))
+
+
+def moe_ffn_prefill_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=None, ws=None,
+                            stream=None):
+    """MoE layer at prefill: q8 activation, expert-grouped gate/up and down GEMMs, weighted combine."""
+    nb = moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _need(x, 4 * T * hidden, "x")
+    _need(ids, 4 * T * topk, "ids")
+    _need(wts, 4 * T * topk, "wts")
+    _need(y, 4 * T * hidden, "y")
+    _check(_lib.moe_ffn_prefill_q4k_q6k(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), _p(ws),
+                                        ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
+                                        _stream(stream)), "moe_ffn_prefill_q4k_q6k")
     return y
 
 

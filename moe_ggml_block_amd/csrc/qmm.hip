@@ -78,6 +78,10 @@ struct QmmArgs {
     int m, n, k;          // dense: m activation rows; expert-indexed: m slots
     const int32_t *ids;   // expert-indexed only: expert of each slot
     int E, x_div;         // expert-indexed only: slot s reads activation row s / x_div
+    // tile table (expert-indexed, built once per layer by k_group_tiles):
+    // tile i is expert tile_e[i] on slots tile_slots[BM*i .. BM*i + BM) (-1: none)
+    const int *ntiles, *tile_e, *tile_slots;
+    const uint8_t *w2;    // PAIR: the up bank (w is the gate bank); Y is then h [nslots, n]
 };
 
 constexpr int QMM_ID_CHUNK = 4096;  // slot ids staged in LDS at a time (grouping)
@@ -206,8 +210,26 @@ QMV_DEV int qmm_group(const int32_t *__restrict__ ids, int m, int E, int *s_ids,
     return esel;
 }
 
-template <int BM, int BN, int KP, int MT, int NT, int NTHREADS, bool MOE = false>
+// Expert-indexed tile of this workgroup from the tile table: returns the
+// expert (s_slot filled, then a barrier) or -1 past the table's last tile.
+template <int BM, int NTHREADS>
+QMV_DEV int table_tile(const int *__restrict__ ntiles, const int *__restrict__ tile_e,
+                       const int *__restrict__ tile_slots, int *s_slot) {
+    if ((int)blockIdx.y >= *ntiles) return -1;
+    for (int i = threadIdx.x; i < BM; i += NTHREADS) s_slot[i] = tile_slots[(size_t)blockIdx.y * BM + i];
+    __syncthreads();
+    return tile_e[blockIdx.y];
+}
+
+// MOE: expert-indexed rows (TABLE: from the tile table, else grouped here).
+// PAIR (expert-indexed, NT == 2): the tile's columns interleave gate and up
+// rows by 16 -- wave column block w holds gate rows and then up rows
+// [BN/2 * blockIdx.x + 16 w, +16) -- so one lane holds both dots of an
+// output and writes h = silu(gate) * up.
+template <int BM, int BN, int KP, int MT, int NT, int NTHREADS, bool MOE = false, bool TABLE = false,
+          bool PAIR = false>
 __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
+    static_assert(!PAIR || (MOE && NT == 2), "paired gate/up tiles");
     const uint8_t *__restrict__ w = a.w;
     const int8_t *__restrict__ xq = a.xq;
     const float *__restrict__ xs = a.xs;
@@ -244,13 +266,18 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
     const int kb = k / 32;
     const size_t row_bytes = (size_t)(k / 256) * 144;
 
-    // Expert-indexed mode: this workgroup's tile (qmm_group)
+    // Expert-indexed mode: this workgroup's tile
     __shared__ int s_slot[MOE ? BM : 1];
     int esel = 0;  // expert of this workgroup's tile
     if constexpr (MOE) {
-        static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
-        esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
-                                           reinterpret_cast<int *>(&As[0][0]), s_slot, Y, n, n0);
+        if constexpr (TABLE) {
+            esel = table_tile<BM, NTHREADS>(a.ntiles, a.tile_e, a.tile_slots, s_slot);
+        } else {
+            static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0]) >= QMM_MOE_MAX_E * 4,
+                          "grouping scratch");
+            esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
+                                               reinterpret_cast<int *>(&As[0][0]), s_slot, Y, n, n0);
+        }
         if (esel < 0) return;  // uniform over the workgroup
     }
     // activation row of each staging role (-1: no row, zeros are staged)
@@ -268,8 +295,16 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
     // slice of the row's 128 code bytes
     const bool bact = tid < BCH;
     const int brow = tid % BN, bc0 = tid / BN;  // chunk i has bc = bc0 + i*NTHREADS/BN
-    const bool bvalid = bact && n0 + brow < n;
-    const uint8_t *wrow = w + ((size_t)esel * n + (bvalid ? n0 + brow : 0)) * row_bytes;
+    // weight row of the staging role: row n0 + brow, or for PAIR the gate /
+    // up row of the interleaved column brow
+    int wr_row = n0 + brow;
+    const uint8_t *wsrc = w;
+    if constexpr (PAIR) {
+        wr_row = (BN / 2) * blockIdx.x + 16 * (brow / 32) + brow % 16;
+        if ((brow / 16) & 1) wsrc = a.w2;
+    }
+    const bool bvalid = bact && wr_row < n;
+    const uint8_t *wrow = wsrc + ((size_t)esel * n + (bvalid ? wr_row : 0)) * row_bytes;
     // activation rows of this thread's activation chunks and xs entries
     int arow[AC], xrow[XC];
 #pragma unroll
@@ -468,6 +503,18 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
         }
     }
 
+    if constexpr (PAIR) {
+        // out[t][0] = gate, out[t][1] = up for the same slot and h column
+        const int col = (BN / 2) * blockIdx.x + 16 * wn + li;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = s_slot[wm * WM + 16 * t + 4 * lq + r];
+                if (row >= 0 && col < n) Y[(size_t)row * n + col] = silu(out[t][0][r]) * out[t][1][r];
+            }
+        return;
+    }
     // lane holds rows 4*lq + r, column li of each 16x16 tile
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -600,6 +647,7 @@ struct Qmm6Args {
     int m, n, k;
     const int32_t *ids;  // expert-indexed only
     int E, x_div;
+    const int *ntiles, *tile_e, *tile_slots;  // tile table (see QmmArgs)
 };
 
 // four 6-bit codes (one per byte) -> four f16 values q - 32, exact
@@ -608,7 +656,7 @@ QMV_DEV uint2 q6x4_to_f16(uint32_t c) {
     return make_uint2(as_u32(as_h2(half_bytes_lo(c)) + off), as_u32(as_h2(half_bytes_hi(c)) + off));
 }
 
-template <int BM, int BN, int MT, int NT, int NTHREADS, int ACT, bool MOE>
+template <int BM, int BN, int MT, int NT, int NTHREADS, int ACT, bool MOE, bool TABLE = false>
 __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
     constexpr int KP = 64;                       // values per phase: a quarter superblock
     constexpr int WM = 16 * MT, WN = 16 * NT;
@@ -645,9 +693,14 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
     __shared__ int s_slot[MOE ? BM : 1];
     int esel = 0;
     if constexpr (MOE) {
-        static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0][0]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
-        esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
-                                           reinterpret_cast<int *>(&As[0][0][0]), s_slot, Y, n, n0);
+        if constexpr (TABLE) {
+            esel = table_tile<BM, NTHREADS>(a.ntiles, a.tile_e, a.tile_slots, s_slot);
+        } else {
+            static_assert(sizeof(Bs[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[0][0]) >= QMM_MOE_MAX_E * 4,
+                          "grouping scratch");
+            esel = qmm_group<BM, BN, NTHREADS>(a.ids, m, a.E, reinterpret_cast<int *>(&Bs[0][0]),
+                                               reinterpret_cast<int *>(&As[0][0][0]), s_slot, Y, n, n0);
+        }
         if (esel < 0) return;
     }
     auto act_row = [&](int row) -> int {
@@ -928,6 +981,165 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
                (int)x_div};
     const dim3 grid((unsigned)div_up(n, 128), (unsigned)(div_up(nslots, 32) + std::min(E, nslots)));
     hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_F32, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+// ============================================================ prefill layer
+// The MoE layer at m > 1 (the prefill twin of moe_ffn_q4k_q6k): the token
+// activations are quantized once (quantize_act_q8), the slots are grouped
+// by expert once into a table of 32-slot tiles shared by both projections,
+// gate and up run as one paired expert-indexed Q4_K GEMM whose epilogue
+// writes h = silu(gate) * up per slot, the down projection is the f32-
+// activation Q6_K GEMM on h, and the weighted combine sums each token's
+// slots in slot order.
+namespace {
+
+constexpr int PF_BM = 32;  // slots per tile in the layer
+
+// One workgroup builds the tile table: per-expert slot counts (LDS
+// atomics), an exclusive prefix of the per-expert tile counts, the tile ->
+// expert map with the pad of each expert's last tile set to -1, then every
+// valid slot is placed in its expert's tiles. The order of an expert's slots
+// within its tiles follows the atomics and may differ between runs; every
+// output row depends only on its own slot, so the results do not.
+template <int BM>
+__global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict__ ids, int S, int E,
+                                                      int *__restrict__ ntiles, int *__restrict__ tile_e,
+                                                      int *__restrict__ tile_slots) {
+    __shared__ int s_cnt[QMM_MOE_MAX_E], s_off[QMM_MOE_MAX_E], s_wtot[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += 1024) {
+        const int e = ids[sl];
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    const int cnt = tid < E ? s_cnt[tid] : 0;
+    const int nt = (cnt + BM - 1) / BM;
+    int inc = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d);
+        if (lane >= d) inc += v;
+    }
+    if (lane == 63) s_wtot[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wtot[w];
+    const int off = base + inc - nt;
+    if (tid < E) {
+        s_off[tid] = off;
+        for (int i = 0; i < nt; ++i) tile_e[off + i] = tid;
+        for (int j = cnt; j < nt * BM; ++j) tile_slots[(size_t)off * BM + j] = -1;
+        s_cnt[tid] = 0;  // now the running position of the expert's slots
+    }
+    if (tid == 1023) ntiles[0] = base + inc;
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += 1024) {
+        const int e = ids[sl];
+        if (e >= 0 && e < E) {
+            const int pos = atomicAdd(&s_cnt[e], 1);
+            tile_slots[(size_t)s_off[e] * BM + pos] = sl;
+        }
+    }
+}
+
+// y[t, :] = sum_j wts[t, j] * d[t*topk + j, :] over the slots whose expert is
+// in [0, E), in slot order; four columns per thread.
+__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ d, const int32_t *__restrict__ ids,
+                                                     const float *__restrict__ wts, float *__restrict__ y,
+                                                     int topk, int hidden, int E) {
+    const int t = blockIdx.y;
+    const int c4 = blockIdx.x * 256 + threadIdx.x;
+    if (4 * c4 >= hidden) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < topk; ++j) {
+        const int e = ids[t * topk + j];
+        if (e < 0 || e >= E) continue;
+        const float w = wts[t * topk + j];
+        const float4 v = *reinterpret_cast<const float4 *>(d + (size_t)(t * topk + j) * hidden + 4 * c4);
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+    }
+    *reinterpret_cast<float4 *>(y + (size_t)t * hidden + 4 * c4) = acc;
+}
+
+struct PrefillWs {
+    int8_t *xq;
+    float *xs, *xsum, *h, *d;
+    int *ntiles, *tile_e, *tile_slots;
+    int64_t bytes;
+};
+
+int64_t pf_max_tiles(int64_t S, int64_t E) { return div_up(S, PF_BM) + std::min(E, S); }
+
+PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E) {
+    const int64_t S = T * topk, mt = pf_max_tiles(S, E);
+    PrefillWs w{};
+    int64_t o = 0;
+    auto take = [&](int64_t nbytes) {
+        uint8_t *p = base ? base + o : nullptr;
+        o += div_up(nbytes, 256) * 256;
+        return p;
+    };
+    w.xq = reinterpret_cast<int8_t *>(take(T * hidden));
+    w.xs = reinterpret_cast<float *>(take(4 * T * (hidden / 32)));
+    w.xsum = reinterpret_cast<float *>(take(4 * T * (hidden / 32)));
+    w.ntiles = reinterpret_cast<int *>(take(4));
+    w.tile_e = reinterpret_cast<int *>(take(4 * mt));
+    w.tile_slots = reinterpret_cast<int *>(take(4 * mt * PF_BM));
+    w.h = reinterpret_cast<float *>(take(4 * S * inter));
+    w.d = reinterpret_cast<float *>(take(4 * S * hidden));
+    w.bytes = o;
+    return w;
+}
+
+}  // namespace
+
+extern "C" int64_t moe_ffn_prefill_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter,
+                                                   int64_t E) {
+    if (T < 1 || topk < 1 || hidden < 1 || inter < 1 || E < 1) return 0;
+    return prefill_ws(nullptr, T, topk, hidden, inter, E).bytes;
+}
+
+extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
+                                       const int32_t *ids, const float *wts, float *y, void *ws, int64_t ws_bytes,
+                                       int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
+                                       qmv_stream_t stream) {
+    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
+    if (T < 1 || topk < 1 || E < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
+    if (ws_bytes < moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E)) return QMV_EINVAL;
+    const int64_t S = T * topk;
+    if (E > QMM_MOE_MAX_E || S > QMM_MOE_MAX_SLOTS || T > 65535 || hidden > 65536 || inter > 65536 ||
+        E * inter * (hidden / 256) * 144 > ((int64_t)1 << 40) || E * hidden * (inter / 256) * 210 > ((int64_t)1 << 40))
+        return QMV_EUNSUPPORTED;
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(down, 2) || !aligned(x, 16) || !aligned(ids, 4) ||
+        !aligned(wts, 4) || !aligned(y, 16) || !aligned(ws, 256))
+        return QMV_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const PrefillWs w = prefill_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter, E);
+    const int64_t mt = pf_max_tiles(S, E);
+    int rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
+    if (rc != QMV_OK) return rc;
+    hipLaunchKernelGGL((k_group_tiles<PF_BM>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
+                       w.tile_slots);
+    QMV_LAUNCH_CHECK();
+    QmmArgs gu{static_cast<const uint8_t *>(gate), w.xq, w.xs, w.xsum, w.h, (int)S, (int)inter, (int)hidden, ids,
+               (int)E, (int)topk, w.ntiles, w.tile_e, w.tile_slots, static_cast<const uint8_t *>(up)};
+    hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, QMM_MOE32_BN / 2),
+                       (unsigned)mt), dim3(QMM_MOE32_NT), 0, s, gu);
+    QMV_LAUNCH_CHECK();
+    Qmm6Args dn{static_cast<const uint8_t *>(down), nullptr, nullptr, w.h, w.d, (int)S, (int)hidden, (int)inter, ids,
+                (int)E, 1, w.ntiles, w.tile_e, w.tile_slots};
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 128), (unsigned)mt),
+                       dim3(256), 0, s, dn);
+    QMV_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)div_up(hidden, 1024), (unsigned)T), dim3(256), 0, s, w.d, ids,
+                       wts, y, (int)topk, (int)hidden, (int)E);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

@@ -171,3 +171,62 @@ def test_moe_qmm_q6k_f32_wide_dynamic_range():
     got = host(qmv.moe_qmm_q6k_f32(dev(bank), dev(x), 1, dev(ids), ns, n, k, E))
     ref = oracle.moe_qmv("q6k", bank, x, 1, ids, ns, n, k, E)
     assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+# ------------------------------------------------------------ prefill layer
+def _layer(T, topk, E, hidden, inter, seed, ids=None, sample=None):
+    gate = synth.moe_bank(synth.FMT_Q4K, seed, E, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, seed + 1, E, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, seed + 2, E, hidden, inter)
+    x = synth.normal(seed + 3, T * hidden).reshape(T, hidden)
+    if ids is None:
+        ids, wts = oracle.moe_route(synth.moe_logits(T, E, seed % 7), T, E, topk)
+        wts = wts.astype(np.float32)
+    else:
+        wts = np.random.default_rng(seed).random(ids.shape).astype(np.float32)
+    got = host(qmv.moe_ffn_prefill_q4k_q6k(dev(gate), dev(up), dev(down), dev(x), dev(ids), dev(wts), T, topk,
+                                           hidden, inter, E))
+    assert got.shape == (T, hidden) and np.isfinite(got).all()
+    xq, xs, _ = oracle.quantize_act_q8(x, T, hidden)
+    ref = oracle.moe_ffn_q8x(gate, up, down, xq, xs, ids, wts, T, topk, hidden, inter, E, toks=sample)
+    g = got if sample is None else got[sample]
+    assert scalerel(ref, g) <= TOL, scalerel(ref, g)
+    return gate, up, down, x, ids, wts, got
+
+
+def test_moe_prefill_layer_small_full_output():
+    T, topk, E, hidden, inter = 64, 8, 16, 512, 256
+    announce(f"moe prefill layer T={T} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 110)
+
+
+def test_moe_prefill_layer_full_shape_sampled_tokens():
+    """512 tokens routed top-8 over 128 experts, gate/up [768, 2048], down
+    [2048, 768]: every output column of 12 sampled tokens."""
+    T, topk, E, hidden, inter = 512, 8, 128, 2048, 768
+    announce(f"moe prefill layer T={T} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 120, sample=np.array([0, 1, 2, 63, 64, 200, 255, 256, 300, 450, 510, 511]))
+
+
+def test_moe_prefill_layer_repeats_and_out_of_range_experts():
+    T, topk, E, hidden, inter = 9, 3, 5, 256, 256
+    ids = np.array([[4, 0, 2], [1, -1, 3], [2, 2, 0], [0, 5, 4], [3, 3, 3], [-2, -2, -2], [1, 2, 3], [0, 0, 1],
+                    [4, 4, 0]], dtype=np.int32)
+    announce("moe prefill layer repeats / out of range")
+    got = _layer(T, topk, E, hidden, inter, 130, ids=ids)[-1]
+    assert np.all(got[5] == 0.0)  # every slot of token 5 out of range
+
+
+def test_moe_prefill_layer_workspace_reuse_smaller_second_call():
+    import torch
+    T, topk, E, hidden, inter = 40, 4, 8, 512, 256
+    announce("moe prefill layer workspace reuse")
+    gate, up, down, x, ids, wts, first = _layer(T, topk, E, hidden, inter, 140)
+    ws = torch.empty(qmv.moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E), dtype=torch.uint8,
+                     device="cuda")
+    G, U, D = dev(gate), dev(up), dev(down)
+    a = host(qmv.moe_ffn_prefill_q4k_q6k(G, U, D, dev(x), dev(ids), dev(wts), T, topk, hidden, inter, E, ws=ws))
+    b = host(qmv.moe_ffn_prefill_q4k_q6k(G, U, D, dev(x[:7]), dev(ids[:7]), dev(wts[:7]), 7, topk, hidden, inter,
+                                         E, ws=ws))
+    assert np.array_equal(a, first)   # same inputs, same bits (grouping order does not matter)
+    assert np.array_equal(b, first[:7])
