@@ -56,9 +56,10 @@ def _load():
     lib.oracle_gemv.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.oracle_moe_qmm.argtypes = [i32, vp, vp, vp, i64, vp, i64, i64, i64, i64, vp, i64, vp]
     lib.oracle_moe_ffn_q8x.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp]
+    lib.oracle_moe_ffn_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     for name in ("oracle_dequant", "oracle_matvec", "oracle_quantize_act_q8",
                  "oracle_blocksums_q4k_q8", "oracle_matvec_q8act", "oracle_moe_route",
-                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv", "oracle_moe_qmm", "oracle_moe_ffn_q8x"):
+                 "oracle_moe_qmv", "oracle_moe_ffn", "oracle_qmm", "oracle_gemv", "oracle_moe_qmm", "oracle_moe_ffn_q8x", "oracle_moe_ffn_q8"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -222,3 +223,20 @@ def moe_ffn_q8x(gate, up, down, xq, xs, ids, wts, T: int, topk: int, hidden: int
     _check(_load().oracle_moe_ffn_q8x(_p(gate), _p(up), _p(down), _p(xq), _p(xs), _p(ids), _p(wts), T, topk,
                                       hidden, inter, E, _p(tl), cnt, _p(y)), "moe_ffn_q8x")
     return y
+
+
+def moe_ffn_q8(gate, up, down, xq, xs, ids, wts, T: int, topk: int, hidden: int, inter: int, E: int, toks=None):
+    """MoE layer with q8 activations on both projections: (y f64 [rows, hidden], h f64 [rows*topk, inter],
+    hq int8 [rows*topk, inter], hs f32 [rows*topk, inter/32]) for all tokens or the listed ones."""
+    gate, up, down = _c(gate, np.uint8), _c(up, np.uint8), _c(down, np.uint8)
+    xq, xs = _c(xq, np.int8), _c(xs, np.float32)
+    ids, wts = _c(ids, np.int32), _c(wts, np.float32)
+    tl = None if toks is None else _c(toks, np.int64)
+    cnt = T if tl is None else tl.size
+    y = np.empty((cnt, hidden), dtype=np.float64)
+    h = np.empty((cnt * topk, inter), dtype=np.float64)
+    hq = np.empty((cnt * topk, inter), dtype=np.int8)
+    hs = np.empty((cnt * topk, inter // 32), dtype=np.float32)
+    _check(_load().oracle_moe_ffn_q8(_p(gate), _p(up), _p(down), _p(xq), _p(xs), _p(ids), _p(wts), T, topk,
+                                     hidden, inter, E, _p(tl), cnt, _p(y), _p(h), _p(hq), _p(hs)), "moe_ffn_q8")
+    return y, h, hq, hs

@@ -519,3 +519,73 @@ int oracle_moe_ffn_q8x(const uint8_t *gate, const uint8_t *up, const uint8_t *do
     free(wd);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* MoE layer with q8 activations on both projections (the pages' int8-dot  */
+/* MoE decode path: hanzo-ml `src/vulkan_backend.rs` quantizes the         */
+/* activation once with `quantize_act_q8` and runs the dp4a gate/up and    */
+/* down gathers; the down activation h is quantized the same way): per    */
+/* token t, x_deq = xs * xq; per slot s = topk*t + j with e = ids[s] in     */
+/* [0, E): h = silu(Wg[e] x_deq) * (Wu[e] x_deq) in f64, rounded to f32 and */
+/* quantized by oracle_quantize_act_q8 (hq, hs), d = Wd[e] (hs * hq);       */
+/* y[t] = sum_j wts[t, j] d. For the listed tokens (all when `toks` is      */
+/* NULL): y rows, and when the pointers are non-NULL the f64 h, hq and hs   */
+/* of their slots (zero rows for a slot outside [0, E)).                    */
+/* ---------------------------------------------------------------------- */
+int oracle_moe_ffn_q8(const uint8_t *gate, const uint8_t *up, const uint8_t *down, const int8_t *xq,
+                      const float *xs, const int32_t *ids, const float *wts, int64_t T, int64_t topk,
+                      int64_t hidden, int64_t inter, int64_t E, const int64_t *toks, int64_t ntok, double *y,
+                      double *h_out, int8_t *hq_out, float *hs_out) {
+    if (hidden % 256 || inter % 256) return -1;
+    int64_t cnt = toks ? ntok : T;
+    double *xd = malloc(sizeof(double) * (size_t)hidden);
+    double *h = malloc(sizeof(double) * (size_t)inter);
+    float *hf = malloc(sizeof(float) * (size_t)inter);
+    int8_t *hq = malloc((size_t)inter);
+    float *hs = malloc(sizeof(float) * (size_t)(inter / 32));
+    float *hsum = malloc(sizeof(float) * (size_t)(inter / 32));
+    double *wd = malloc(sizeof(double) * (size_t)(hidden > inter ? hidden : inter));
+    if (!xd || !h || !hf || !hq || !hs || !hsum || !wd) {
+        free(xd); free(h); free(hf); free(hq); free(hs); free(hsum); free(wd);
+        return -2;
+    }
+    int64_t rb_gu = row_bytes(ORACLE_Q4K, hidden), rb_dn = row_bytes(ORACLE_Q6K, inter);
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t t = toks ? toks[i] : i;
+        for (int64_t c = 0; c < hidden; ++c)
+            xd[c] = (double)xs[t * (hidden / 32) + c / 32] * (double)xq[t * hidden + c];
+        for (int64_t r = 0; r < hidden; ++r) y[i * hidden + r] = 0.0;
+        for (int64_t j = 0; j < topk; ++j) {
+            int64_t o = i * topk + j;  /* slot row of the outputs */
+            int32_t e = ids[t * topk + j];
+            if (e < 0 || e >= E) {
+                if (h_out) for (int64_t r = 0; r < inter; ++r) h_out[o * inter + r] = 0.0;
+                if (hq_out) memset(hq_out + o * inter, 0, (size_t)inter);
+                if (hs_out) for (int64_t b = 0; b < inter / 32; ++b) hs_out[o * (inter / 32) + b] = 0.0f;
+                continue;
+            }
+            for (int64_t r = 0; r < inter; ++r) {
+                double g = 0.0, u = 0.0;
+                dec_row(ORACLE_Q4K, gate + ((int64_t)e * inter + r) * rb_gu, hidden, wd);
+                for (int64_t c = 0; c < hidden; ++c) g += wd[c] * xd[c];
+                dec_row(ORACLE_Q4K, up + ((int64_t)e * inter + r) * rb_gu, hidden, wd);
+                for (int64_t c = 0; c < hidden; ++c) u += wd[c] * xd[c];
+                h[r] = g / (1.0 + exp(-g)) * u;
+                hf[r] = (float)h[r];
+            }
+            oracle_quantize_act_q8(hf, 1, inter, hq, hs, hsum);
+            if (h_out) memcpy(h_out + o * inter, h, sizeof(double) * (size_t)inter);
+            if (hq_out) memcpy(hq_out + o * inter, hq, (size_t)inter);
+            if (hs_out) memcpy(hs_out + o * (inter / 32), hs, sizeof(float) * (size_t)(inter / 32));
+            double wj = (double)wts[t * topk + j];
+            for (int64_t r = 0; r < hidden; ++r) {
+                dec_row(ORACLE_Q6K, down + ((int64_t)e * hidden + r) * rb_dn, inter, wd);
+                double acc = 0.0;
+                for (int64_t c = 0; c < inter; ++c) acc += wd[c] * (double)hs[c / 32] * (double)hq[c];
+                y[i * hidden + r] += wj * acc;
+            }
+        }
+    }
+    free(xd); free(h); free(hf); free(hq); free(hs); free(hsum); free(wd);
+    return 0;
+}

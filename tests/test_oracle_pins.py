@@ -480,6 +480,39 @@ def test_moe_ffn_q8x_equals_f32_layer_on_exact_dequantized_x():
                                                      E, toks=[3, 1]), y[[3, 1]])
 
 
+def test_moe_ffn_q8_is_quantized_swiglu_per_slot():
+    # each slot: h from numpy on the decoded expert slices, quantized by the
+    # pinned quantizer, then the decoded down slice times the dequantized h;
+    # repeats and out-of-range experts included
+    E, hidden, inter, T, topk = 4, 512, 256, 3, 3
+    gate = synth.weights(synth.FMT_Q4K, 65, E * inter, hidden)
+    up = synth.weights(synth.FMT_Q4K, 66, E * inter, hidden)
+    down = synth.weights(synth.FMT_Q6K, 67, E * hidden, inter)
+    x = synth.normal(68, T * hidden).reshape(T, hidden)
+    xq, xs, _ = oracle.quantize_act_q8(x, T, hidden)
+    ids = np.array([[3, 0, 3], [1, -1, 2], [0, 4, 2]], dtype=np.int32)
+    wts = np.array([[0.5, 0.3, 0.2], [0.6, 0.1, 0.3], [0.25, 0.25, 0.5]], dtype=np.float32)
+    y, h, hq, hs = oracle.moe_ffn_q8(gate, up, down, xq, xs, ids, wts, T, topk, hidden, inter, E)
+    G = oracle.dequant("q4k", gate).reshape(E, inter, hidden)
+    U = oracle.dequant("q4k", up).reshape(E, inter, hidden)
+    D = oracle.dequant("q6k", down).reshape(E, hidden, inter)
+    Xd = np.repeat(xs, 32, axis=1).astype(np.float64) * xq
+    for t in range(T):
+        ref = np.zeros(hidden)
+        for j in range(topk):
+            s_, e = t * topk + j, ids[t, j]
+            if not 0 <= e < E:
+                assert np.all(h[s_] == 0) and np.all(hq[s_] == 0)
+                continue
+            g = G[e] @ Xd[t]
+            hh = g * scipy.special.expit(g) * (U[e] @ Xd[t])
+            np.testing.assert_allclose(h[s_], hh, rtol=1e-12, atol=1e-12 * np.abs(hh).max())
+            q, sc, _ = oracle.quantize_act_q8(hh.astype(np.float32), 1, inter)
+            assert np.array_equal(hq[s_], q[0]) and np.array_equal(hs[s_], sc[0])
+            ref += float(wts[t, j]) * (D[e] @ (np.repeat(sc[0], 32).astype(np.float64) * q[0]))
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 # ---------------------------------------------------------------------------
 # input encoders: round-trip bounds through the pinned decoders
 # ---------------------------------------------------------------------------
