@@ -160,6 +160,33 @@ int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const fl
                     qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * q8-activation MoE decode variant (the int8-dot gathers of hanzo-ml
+ * `src/vulkan_backend.rs`: activation quantized once by quantize_act_q8,
+ * dp4a gate/up and down over resident banks, ids on the device):
+ *   moe_qmv_q4k_q8: y[s, r] = sum_c W_deq[ids[s], r, c] * xs[a, c/32] * xq[a, c]
+ *                   (integer block sums of codes x xq, as in qmv_q4k_q8)
+ *   moe_qmv_q6k_q8: the same over a Q6_K bank; q - 32 enters the int8 dot
+ *                   as a signed byte (xsum is not needed)
+ * a = s / x_div. Layout, limits and errors as moe_qmv_q4k / moe_qmv_q6k;
+ * xq 16-byte aligned, xs / xsum 4-byte.
+ * ---------------------------------------------------------------------- */
+int moe_qmv_q4k_q8(const void *bank, const int8_t *xq, const float *xs, const float *xsum, int64_t x_div,
+                   const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                   qmv_stream_t stream);
+int moe_qmv_q6k_q8(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids,
+                   float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+
+/* The MoE layer with q8 activations on both projections: x quantized once,
+ * h = silu(gate) * up from int8 dots (f32), h quantized (quantize_act_q8
+ * per 32 values of each slot row), down on int8 dots with the weighted
+ * combine -- four launches. Same operands as moe_ffn_q4k_q6k; ws:
+ * moe_ffn_q8_workspace_bytes() bytes (q8 x, h, q8 h), 256-byte aligned. */
+int64_t moe_ffn_q8_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter);
+int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
+                       const float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,
+                       int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Q4_K prefill GEMM on int8 MFMA (`mmq_q4k_rt_gpu`: affine Q4_K x q8
  * activation, epilogue xs*(D*dot - M*xsum)):
  *   Y[i, r] = sum_b ( xs[i,b]*d_r*sc_rj*S[i,r,b] - xsum[i,b]*dmin_r*m_rj ),

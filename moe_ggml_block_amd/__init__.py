@@ -43,6 +43,9 @@ _SIGS = {
     "moe_qmm_q6k": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q6k_f32": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_prefill_q4k_q6k": [_vp] * 8 + [_i64] * 6 + [_vp],
+    "moe_qmv_q4k_q8": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_qmv_q6k_q8": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_ffn_q4k_q6k_q8": [_vp] * 8 + [_i64] * 6 + [_vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -52,12 +55,14 @@ _lib.moe_ffn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
 _lib.moe_ffn_workspace_bytes.restype = _i64
 _lib.moe_ffn_prefill_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
 _lib.moe_ffn_prefill_workspace_bytes.restype = _i64
+_lib.moe_ffn_q8_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.moe_ffn_q8_workspace_bytes.restype = _i64
 _lib.qmv_version.restype = ctypes.c_char_p
 _lib.qmv_strerror.argtypes = [_i32]
 _lib.qmv_strerror.restype = ctypes.c_char_p
 
-EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "moe_ffn_prefill_workspace_bytes", "qmv_version",
-                          "qmv_strerror")
+EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "moe_ffn_prefill_workspace_bytes",
+                          "moe_ffn_q8_workspace_bytes", "qmv_version", "qmv_strerror")
 
 BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210)}
 
@@ -300,6 +305,61 @@ def moe_ffn_prefill_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter,
     _check(_lib.moe_ffn_prefill_q4k_q6k(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), _p(ws),
                                         ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
                                         _stream(stream)), "moe_ffn_prefill_q4k_q6k")
+    return y
+
+
+def moe_qmv_q4k_q8(bank, xq, xs, xsum, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    """Expert-gather Q4_K matvec on a q8 activation (int8 dot products)."""
+    rows = (nslots + x_div - 1) // x_div
+    _need(bank, E * n * row_bytes("q4k", k), "bank")
+    _need(xq, rows * k, "xq")
+    _need(xs, 4 * rows * (k // 32), "xs")
+    _need(xsum, 4 * rows * (k // 32), "xsum")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * nslots * n, "y")
+    _check(_lib.moe_qmv_q4k_q8(_p(bank), _p(xq), _p(xs), _p(xsum), x_div, _p(ids), _p(y), nslots, n, k, E,
+                               _stream(stream)), "moe_qmv_q4k_q8")
+    return y
+
+
+def moe_qmv_q6k_q8(bank, xq, xs, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    """Expert-gather Q6_K matvec on a q8 activation (int8 dot products)."""
+    rows = (nslots + x_div - 1) // x_div
+    _need(bank, E * n * row_bytes("q6k", k), "bank")
+    _need(xq, rows * k, "xq")
+    _need(xs, 4 * rows * (k // 32), "xs")
+    _need(ids, 4 * nslots, "ids")
+    if y is None:
+        y = torch.empty((nslots, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * nslots * n, "y")
+    _check(_lib.moe_qmv_q6k_q8(_p(bank), _p(xq), _p(xs), x_div, _p(ids), _p(y), nslots, n, k, E,
+                               _stream(stream)), "moe_qmv_q6k_q8")
+    return y
+
+
+def moe_ffn_q8_workspace_bytes(T, topk, hidden, inter) -> int:
+    return int(_lib.moe_ffn_q8_workspace_bytes(T, topk, hidden, inter))
+
+
+def moe_ffn_q4k_q6k_q8(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=None, ws=None, stream=None):
+    """MoE layer with q8 activations on both projections (int8 dot products)."""
+    nb = moe_ffn_q8_workspace_bytes(T, topk, hidden, inter)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _need(x, 4 * T * hidden, "x")
+    _need(ids, 4 * T * topk, "ids")
+    _need(wts, 4 * T * topk, "wts")
+    _need(y, 4 * T * hidden, "y")
+    _check(_lib.moe_ffn_q4k_q6k_q8(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), _p(ws),
+                                   ws.numel() * ws.element_size(), T, topk, hidden, inter, E, _stream(stream)),
+           "moe_ffn_q4k_q6k_q8")
     return y
 
 

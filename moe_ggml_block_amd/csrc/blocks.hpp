@@ -149,6 +149,7 @@ struct ActF32 {
 
 template <class F>
 struct F32Act {
+    static constexpr bool Q8 = false;  // activation: f32 rows
     using Act = ActF32;
     using X = UnitX;
     using Stage = StageRegs;
@@ -387,6 +388,7 @@ QMV_DEV void q4k_q8_sums(const Q4KUnit::Raw &R, const int32_t *xq16, int32_t *sl
 }
 
 struct Q4KQ8Unit {
+    static constexpr bool Q8 = true;  // activation: q8 rows (xq, xs, xsum)
     static constexpr int BW = 256, BB = 144;
     static constexpr int RING = QMV_RING_Q4KQ8;
     static constexpr int MAX_WG_PER_CU = 3;
@@ -445,5 +447,108 @@ struct Q4KQ8Unit {
         r = fmaf(-(dmin * ubyte_f<0>(mn2)), X.xsum[0], r);
         r = fmaf(-(dmin * ubyte_f<1>(mn2)), X.xsum[1], r);
         return r;
+    }
+};
+
+// ------------------------------------------------------ Q6_K x q8 (dot4) ---
+// A Q6_K unit (64 weights of one superblock, Q6KUnit) against a q8
+// activation. Its values are four runs of 16: run g covers values
+// 128h + 32g + 16lh + [0, 16) of the superblock, half of q8 block
+// 8s + 4h + g. q - 32 (in [-32, 31]) becomes a signed byte: r = q ^ 0x20 is
+// q - 32 modulo 64, and setting the top two bits where bit 5 of r is set
+// sign-extends it. Each run's integer dot S_g = sum (q - 32) * xq is one
+// v_dot4 chain (exact), and the unit adds d * sc_g * xs_g * S_g for its four
+// runs (sc_g: the run's int8 sub-scale).
+struct UnitQ8x4 {
+    int32_t q[16];  // dwords 4g..4g+3: xq of run g
+    float xs[4];    // xs of run g's q8 block
+};
+
+struct Q6KQ8Unit {
+    static constexpr bool Q8 = true;
+    static constexpr int BW = 256, BB = 210;
+    static constexpr int RING = QMV_RING_Q6K;
+    static constexpr int MAX_WG_PER_CU = 2;
+    static constexpr int ACT_STRIDE = 20;  // 16 dwords of xq + 4 scales per unit
+    using Act = ActQ8;                     // (xsum is not read)
+    using X = UnitQ8x4;
+    using Raw = Q6KUnit::Raw;
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) { Q6KUnit::load(R, row, u); }
+    // 16-value granule i of a row (xq bytes 16i..16i+15) -> its unit and run
+    static __device__ __forceinline__ int granule_unit(int i, int *g) {
+        *g = (i >> 1) & 3;
+        return 4 * (i >> 4) + 2 * ((i >> 3) & 1) + (i & 1);
+    }
+    // q8 block b -> the first of the two units (lh = 0, 1) that read it, and its run
+    static __device__ __forceinline__ int block_unit(int b, int *g) {
+        *g = b & 3;
+        return 4 * (b >> 3) + 2 * ((b >> 2) & 1);
+    }
+    typedef u32x4 Stage[3];  // granules tid and tid + 256, then {xs, -, -, -}
+    template <int NS>
+    static __device__ __forceinline__ void fetch(Stage &S, ActQ8 a, int k) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(a.xq);
+        const int lastq = k / 16 - 1, lastb = k / 32 - 1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) S[m] = q[min((int)threadIdx.x + 256 * m, lastq)];
+        S[2].x = __float_as_uint(a.xs[min((int)threadIdx.x, lastb)]);
+    }
+    template <int NS>
+    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) {
+        uint32_t *l = reinterpret_cast<uint32_t *>(xl);
+        const int lastq = k / 16 - 1, lastb = k / 32 - 1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = min((int)threadIdx.x + 256 * m, lastq);
+            int g;
+            const int u = granule_unit(i, &g);
+            *reinterpret_cast<u32x4 *>(l + ACT_STRIDE * u + 4 * g) = S[m];
+        }
+        int g;
+        const int u = block_unit(min((int)threadIdx.x, lastb), &g);
+        xl[ACT_STRIDE * u + 16 + g] = __uint_as_float(S[2].x);
+        xl[ACT_STRIDE * (u + 1) + 16 + g] = __uint_as_float(S[2].x);
+    }
+    static __device__ __forceinline__ void load_lds(UnitQ8x4 &X, const float *xl, int u) {
+        const int4 *p = reinterpret_cast<const int4 *>(xl + ACT_STRIDE * u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int4 v = p[t];
+            X.q[4 * t] = v.x; X.q[4 * t + 1] = v.y; X.q[4 * t + 2] = v.z; X.q[4 * t + 3] = v.w;
+        }
+        const float4 f = reinterpret_cast<const float4 *>(xl + ACT_STRIDE * u)[4];
+        X.xs[0] = f.x; X.xs[1] = f.y; X.xs[2] = f.z; X.xs[3] = f.w;
+    }
+    // four 6-bit codes (one per byte) -> four signed bytes q - 32
+    static __device__ __forceinline__ int centred(uint32_t q) {
+        const uint32_t r = q ^ 0x20202020u;
+        return (int)(r | (((r >> 5) & 0x01010101u) * 0xC0u));
+    }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8x4 &X, int u) {
+        const uint32_t A[4] = {R.a.x, R.a.y, R.a.z, R.a.w};
+        const uint32_t B[4] = {R.b.x, R.b.y, R.b.z, R.b.w};
+        const uint32_t H[4] = {R.h.x, R.h.y, R.h.z, R.h.w};
+        int S[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t q0 = (A[t] & 0x0F0F0F0Fu) | ((H[t] << 4) & 0x30303030u);
+            const uint32_t q1 = (B[t] & 0x0F0F0F0Fu) | ((H[t] << 2) & 0x30303030u);
+            const uint32_t q2 = ((A[t] >> 4) & 0x0F0F0F0Fu) | (H[t] & 0x30303030u);
+            const uint32_t q3 = ((B[t] >> 4) & 0x0F0F0F0Fu) | ((H[t] >> 2) & 0x30303030u);
+            S[0] = __builtin_amdgcn_sdot4(centred(q0), X.q[t], S[0], false);
+            S[1] = __builtin_amdgcn_sdot4(centred(q1), X.q[4 + t], S[1], false);
+            S[2] = __builtin_amdgcn_sdot4(centred(q2), X.q[8 + t], S[2], false);
+            S[3] = __builtin_amdgcn_sdot4(centred(q3), X.q[12 + t], S[3], false);
+        }
+        // sub-scale of run g: byte 2g + lh of the 8 scale bytes of half h
+        const int lh = u & 1;
+        const uint32_t s0 = R.sc.x >> (8 * lh), s1 = R.sc.y >> (8 * lh);
+        const float c0 = sbyte_f<0>(s0), c1 = sbyte_f<2>(s0), c2 = sbyte_f<0>(s1), c3 = sbyte_f<2>(s1);
+        float r = c0 * (X.xs[0] * (float)S[0]);
+        r = fmaf(c1, X.xs[1] * (float)S[1], r);
+        r = fmaf(c2, X.xs[2] * (float)S[2], r);
+        r = fmaf(c3, X.xs[3] * (float)S[3], r);
+        return h2f(R.d) * r;
     }
 };

@@ -171,7 +171,9 @@ __global__ __launch_bounds__(256) void k_route_wave(const float *__restrict__ lo
 struct MoeArgs {
     const uint8_t *bank;   // [E, n, k]; PAIR: the gate bank [E, n/2, k]
     const uint8_t *bank2;  // PAIR: the up bank [E, n/2, k]
-    const float *x;
+    const float *x;        // f32 activation rows (units with F::Q8 false)
+    const int8_t *xq;      // q8 activation rows (F::Q8): xq [rows, k], xs / xsum [rows, k/32]
+    const float *xs, *xsum;
     int x_div;
     const int32_t *ids;
     float *y;  // [nslots, n]; PAIR: [nslots, n/2]
@@ -197,6 +199,17 @@ size_t moe_lds_bytes(int k, int act_stride, int nslots, int E) {
 // PAIR: virtual row 2i is gate row i and 2i+1 is up row i; a pass holds
 // whole pairs (64/G even), and the lane group of the up row writes
 // y[s, i] = silu(gate . x) * (up . x).
+// The activation row `row` in the unit's form.
+template <class F>
+QMV_DEV typename F::Act moe_act(const MoeArgs &a, int row) {
+    if constexpr (F::Q8) {
+        const size_t kb = (size_t)(a.k / 32) * row;
+        return ActQ8{a.xq + (size_t)row * a.k, a.xs + kb, a.xsum ? a.xsum + kb : nullptr};
+    } else {
+        return ActF32{a.x + (size_t)row * a.k};
+    }
+}
+
 template <class F, int G, int UPL, bool PAIR>
 __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     extern __shared__ float4 dyn4[];
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
         for (int c = 0; c < count; ++c) {
             const int slot = slot_list[c];
             typename F::Stage S;
-            F::template fetch<stage_granules(G, UPL)>(S, ActF32{a.x + (size_t)(slot / a.x_div) * a.k}, a.k);
+            F::template fetch<stage_granules(G, UPL)>(S, moe_act<F>(a, slot / a.x_div), a.k);
             Raw R[NB][UPL];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
@@ -416,7 +429,9 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
 // not depend on timing). Slots whose id is out of range contribute nothing.
 struct DownArgs {
     const uint8_t *bank;  // Q6_K [E, n, k]
-    const float *h;       // [T*topk, k]
+    const float *h;       // [T*topk, k] (units with F::Q8 false)
+    const int8_t *hq;     // F::Q8: q8 h rows [T*topk, k], scales hs [T*topk, k/32]
+    const float *hs;
     const int32_t *ids;
     const float *wts;
     float *y;  // [T, n]
@@ -474,13 +489,34 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();  // the previous chunk's LDS reads are done
-        const int k4 = a.k / 4;
-        for (int i = tid; i < nch * k4; i += 256) {
-            const int j = i / k4, c4 = i - j * k4;
-            const f32x4 hv = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j0 + j) * a.k + 4 * c4);
-            int jj;
-            const int u = F::xslot(4 * c4, &jj);
-            *reinterpret_cast<f32x4 *>(hlds + j * ust + F::ACT_STRIDE * u + jj) = hv;
+        if constexpr (F::Q8) {
+            // q8 rows: 16-value granules to their unit's run, each block's
+            // scale to the two units that read it
+            const int k16 = a.k / 16, k32 = a.k / 32;
+            for (int i = tid; i < nch * k16; i += 256) {
+                const int j = i / k16, gi = i - j * k16;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(a.hq + ((size_t)t * a.topk + j0 + j) * a.k + 16 * gi);
+                int g;
+                const int u = F::granule_unit(gi, &g);
+                *reinterpret_cast<u32x4 *>(hlds + j * ust + F::ACT_STRIDE * u + 4 * g) = v;
+            }
+            for (int i = tid; i < nch * k32; i += 256) {
+                const int j = i / k32, b = i - j * k32;
+                const float sc = a.hs[((size_t)t * a.topk + j0 + j) * k32 + b];
+                int g;
+                const int u = F::block_unit(b, &g);
+                hlds[j * ust + F::ACT_STRIDE * u + 16 + g] = sc;
+                hlds[j * ust + F::ACT_STRIDE * (u + 1) + 16 + g] = sc;
+            }
+        } else {
+            const int k4 = a.k / 4;
+            for (int i = tid; i < nch * k4; i += 256) {
+                const int j = i / k4, c4 = i - j * k4;
+                const f32x4 hv = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j0 + j) * a.k + 4 * c4);
+                int jj;
+                const int u = F::xslot(4 * c4, &jj);
+                *reinterpret_cast<f32x4 *>(hlds + j * ust + F::ACT_STRIDE * u + jj) = hv;
+            }
         }
         __syncthreads();
         int cur = -1;
@@ -576,37 +612,39 @@ int launch_moe(MoeArgs a, hipStream_t s) {
 
 // gate/up of the layer: pairs need 64/G even, so G <= 32 (two units per
 // lane above k = 2048)
+template <class F>
 int launch_gate_up(MoeArgs a, hipStream_t s) {
     const int64_t U = a.k / 64;
     switch (next_pow2_le64(U)) {
-        case 1: return launch_moe_t<Q4KUnit, 1, 1, true>(a, s);
-        case 2: return launch_moe_t<Q4KUnit, 2, 1, true>(a, s);
-        case 4: return launch_moe_t<Q4KUnit, 4, 1, true>(a, s);
-        case 8: return launch_moe_t<Q4KUnit, 8, 1, true>(a, s);
-        case 16: return launch_moe_t<Q4KUnit, 16, 1, true>(a, s);
-        case 32: return launch_moe_t<Q4KUnit, 32, 1, true>(a, s);
+        case 1: return launch_moe_t<F, 1, 1, true>(a, s);
+        case 2: return launch_moe_t<F, 2, 1, true>(a, s);
+        case 4: return launch_moe_t<F, 4, 1, true>(a, s);
+        case 8: return launch_moe_t<F, 8, 1, true>(a, s);
+        case 16: return launch_moe_t<F, 16, 1, true>(a, s);
+        case 32: return launch_moe_t<F, 32, 1, true>(a, s);
         default:
-            if (U <= 64) return launch_moe_t<Q4KUnit, 32, 2, true>(a, s);
+            if (U <= 64) return launch_moe_t<F, 32, 2, true>(a, s);
             return QMV_EUNSUPPORTED;
     }
 }
 
 // Slots staged at once by the down pass: as many as fit 48 KB of LDS, <= 8.
+template <class F>
 int down_chunk(int64_t k, int64_t topk) {
-    const int64_t per = (k / 64) * XSTRIDE * 4;
+    const int64_t per = (k / 64) * F::ACT_STRIDE * 4;
     int64_t c = 49152 / per;
     if (c > 8) c = 8;
     if (c < 1) c = 1;
     return (int)(c < topk ? c : topk);
 }
 
-template <int G>
+template <class F, int G>
 int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
     constexpr int RPP = 64 / G;
-    const size_t lds0 = (size_t)a.chunk * (a.k / 64) * XSTRIDE * 4;
+    const size_t lds0 = (size_t)a.chunk * (a.k / 64) * F::ACT_STRIDE * 4;
     static thread_local int64_t cache[2] = {-1, -1};
     if (cache[0] != (int64_t)lds0) {
-        cache[1] = resident_wgs(k_moe_down<Q6KUnit, G>, lds0 + WAVES * 64 * 4);
+        cache[1] = resident_wgs(k_moe_down<F, G>, lds0 + WAVES * 64 * 4);
         cache[0] = (int64_t)lds0;
     }
     // rows per workgroup: within one round of resident workgroups, and
@@ -619,18 +657,19 @@ int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
     a.rblk = rblk;
     const size_t lds = lds0 + (size_t)WAVES * a.rblk * 4;
     const dim3 grid((unsigned)div_up(a.n, a.rblk), (unsigned)T);
-    hipLaunchKernelGGL((k_moe_down<Q6KUnit, G>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_moe_down<F, G>), grid, dim3(256), lds, s, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
 
+template <class F>
 int launch_down(DownArgs a, int64_t T, hipStream_t s) {
     switch (next_pow2_le64(a.k / 64)) {
-        case 4: return launch_down_g<4>(a, T, s);
-        case 8: return launch_down_g<8>(a, T, s);
-        case 16: return launch_down_g<16>(a, T, s);
-        case 32: return launch_down_g<32>(a, T, s);
-        case 64: return launch_down_g<64>(a, T, s);
+        case 4: return launch_down_g<F, 4>(a, T, s);
+        case 8: return launch_down_g<F, 8>(a, T, s);
+        case 16: return launch_down_g<F, 16>(a, T, s);
+        case 32: return launch_down_g<F, 32>(a, T, s);
+        case 64: return launch_down_g<F, 64>(a, T, s);
         default: return QMV_EUNSUPPORTED;  // k / 64 <= 64 (inter <= 4096) on this path
     }
 }
@@ -728,7 +767,7 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
     float *h = static_cast<float *>(ws);
     hipStream_t s = (hipStream_t)stream;
     // h = silu(gate x) * (up x): one gather over interleaved gate/up rows
-    rc = launch_gate_up(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
+    rc = launch_gate_up<Q4KUnit>(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
     if (rc) return rc;
     DownArgs dn{};
     dn.bank = static_cast<const uint8_t *>(down);
@@ -740,6 +779,111 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
     dn.k = (int)inter;
     dn.E = (int)E;
     dn.topk = (int)topk;
-    dn.chunk = down_chunk(inter, topk);
-    return launch_down(dn, T, s);
+    dn.chunk = down_chunk<Q6KUnit>(inter, topk);
+    return launch_down<Q6KUnit>(dn, T, s);
+}
+
+// ------------------------------------------------- q8-activation variants ---
+// The gathers and the layer with int8 dot products: activations quantized
+// to q8 once (quantize_act_q8), Q4_K codes against xq through v_dot4
+// (Q4KQ8Unit), Q6_K codes as signed q - 32 bytes against xq (Q6KQ8Unit).
+extern "C" int moe_qmv_q4k_q8(const void *bank, const int8_t *xq, const float *xs, const float *xsum, int64_t x_div,
+                              const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
+                              qmv_stream_t stream) {
+    if (!xs || !xsum) return QMV_EINVAL;
+    const int rc = check_moe_args(bank, reinterpret_cast<const float *>(xq), x_div, ids, y, nslots, n, k, E);
+    if (rc) return rc;
+    if (!aligned(xs, 4) || !aligned(xsum, 4)) return QMV_EALIGN;
+    MoeArgs a = gather_args(bank, nullptr, nullptr, x_div, ids, y, nslots, n, k, E);
+    a.xq = xq;
+    a.xs = xs;
+    a.xsum = xsum;
+    return launch_moe<Q4KQ8Unit>(a, (hipStream_t)stream);
+}
+
+extern "C" int moe_qmv_q6k_q8(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids,
+                              float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
+    if (!xs) return QMV_EINVAL;
+    const int rc = check_moe_args(bank, reinterpret_cast<const float *>(xq), x_div, ids, y, nslots, n, k, E);
+    if (rc) return rc;
+    if (!aligned(xs, 4)) return QMV_EALIGN;
+    MoeArgs a = gather_args(bank, nullptr, nullptr, x_div, ids, y, nslots, n, k, E);
+    a.xq = xq;
+    a.xs = xs;
+    return launch_moe<Q6KQ8Unit>(a, (hipStream_t)stream);
+}
+
+namespace {
+struct Q8LayerWs {
+    int8_t *xq, *hq;
+    float *xs, *xsum, *h, *hs, *hsum;
+    int64_t bytes;
+};
+
+Q8LayerWs q8_layer_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int64_t inter) {
+    const int64_t S = T * topk;
+    Q8LayerWs w{};
+    int64_t o = 0;
+    auto take = [&](int64_t nbytes) {
+        uint8_t *p = base ? base + o : nullptr;
+        o += div_up(nbytes, 256) * 256;
+        return p;
+    };
+    w.xq = reinterpret_cast<int8_t *>(take(T * hidden));
+    w.xs = reinterpret_cast<float *>(take(4 * T * (hidden / 32)));
+    w.xsum = reinterpret_cast<float *>(take(4 * T * (hidden / 32)));
+    w.h = reinterpret_cast<float *>(take(4 * S * inter));
+    w.hq = reinterpret_cast<int8_t *>(take(S * inter));
+    w.hs = reinterpret_cast<float *>(take(4 * S * (inter / 32)));
+    w.hsum = reinterpret_cast<float *>(take(4 * S * (inter / 32)));
+    w.bytes = o;
+    return w;
+}
+}  // namespace
+
+extern "C" int64_t moe_ffn_q8_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter) {
+    if (T < 1 || topk < 1 || hidden < 1 || inter < 1) return -1;
+    return q8_layer_ws(nullptr, T, topk, hidden, inter).bytes;
+}
+
+extern "C" int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const float *x,
+                                  const int32_t *ids, const float *wts, float *y, void *ws, int64_t ws_bytes,
+                                  int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
+                                  qmv_stream_t stream) {
+    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
+    if (T < 1 || topk < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
+    if (ws_bytes < moe_ffn_q8_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
+    const int64_t ns = T * topk;
+    int rc = check_moe_args(gate, x, topk, ids, y, ns, 2 * inter, hidden, E);
+    if (rc) return rc;
+    rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
+    if (rc) return rc;
+    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 256)) return QMV_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const Q8LayerWs w = q8_layer_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter);
+    // x -> q8 once; h = silu(gate x) * (up x) on int8 dots; h -> q8; down on int8 dots + combine
+    rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
+    if (rc) return rc;
+    MoeArgs gu = gather_args(gate, up, nullptr, topk, ids, w.h, ns, 2 * inter, hidden, E);
+    gu.xq = w.xq;
+    gu.xs = w.xs;
+    gu.xsum = w.xsum;
+    rc = launch_gate_up<Q4KQ8Unit>(gu, s);
+    if (rc) return rc;
+    rc = quantize_act_q8(w.h, w.hq, w.hs, w.hsum, ns, inter, stream);
+    if (rc) return rc;
+    DownArgs dn{};
+    dn.bank = static_cast<const uint8_t *>(down);
+    dn.hq = w.hq;
+    dn.hs = w.hs;
+    dn.ids = ids;
+    dn.wts = wts;
+    dn.y = y;
+    dn.n = (int)hidden;
+    dn.k = (int)inter;
+    dn.E = (int)E;
+    dn.topk = (int)topk;
+    dn.chunk = down_chunk<Q6KQ8Unit>(inter, topk);
+    return launch_down<Q6KQ8Unit>(dn, T, s);
 }
