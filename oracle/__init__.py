@@ -19,10 +19,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-Q8_0, Q4K, Q6K = 0, 1, 2
-_FMT = {"q8_0": Q8_0, "q4k": Q4K, "q6k": Q6K, Q8_0: Q8_0, Q4K: Q4K, Q6K: Q6K}
-BLOCK_WEIGHTS = {Q8_0: 32, Q4K: 256, Q6K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4K: 144, Q6K: 210}
+Q8_0, Q4K, Q6K, Q4_0, Q5K = 0, 1, 2, 3, 4
+_FMT = {"q8_0": Q8_0, "q4k": Q4K, "q6k": Q6K, "q4_0": Q4_0, "q5k": Q5K,
+        Q8_0: Q8_0, Q4K: Q4K, Q6K: Q6K, Q4_0: Q4_0, Q5K: Q5K}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4K: 256, Q6K: 256, Q4_0: 32, Q5K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4K: 144, Q6K: 210, Q4_0: 18, Q5K: 176}
 
 
 def build() -> None:

@@ -16,7 +16,9 @@
  *  - block field order: Q8_0 = f16 scale + 32 int8 (`quantize_q8_blocks`);
  *    Q4_K = d, dmin, scales[12], qs[128] (`quantize_q4k_split`);
  *    Q6_K = ql[128], qh[64], scales[16] int8, d (`quantize_q6k`,
- *    `quantize_q6k_split`). The bit packing inside the fields is not printed
+ *    `quantize_q6k_split`); Q4_0 = f16 d + 16 code bytes (`matvec_q4_0_gpu`);
+ *    Q5_K = d, dmin, scales[12], qh[32], qs[128] (`quantize_q5k`). The bit
+ *    packing inside the fields is not printed
  *    on the pages; the public GGML k-quant packing is used (see the decoder
  *    comments).
  *  - q8 activation triple (xq, xs, xsum = dequantized block sum) per 32
@@ -36,10 +38,10 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_Q6K = 2 };
+enum { ORACLE_Q8_0 = 0, ORACLE_Q4K = 1, ORACLE_Q6K = 2, ORACLE_Q4_0 = 3, ORACLE_Q5K = 4, ORACLE_NFMT = 5 };
 
-static const int64_t QK[3] = {32, 256, 256};
-static const int64_t QB[3] = {34, 144, 210};
+static const int64_t QK[ORACLE_NFMT] = {32, 256, 256, 32, 256};
+static const int64_t QB[ORACLE_NFMT] = {34, 144, 210, 18, 176};
 
 /* ---------------------------------------------------------------------- */
 /* O1: IEEE binary16 -> f64, exact, subnormals included. The pages stress  */
@@ -126,14 +128,47 @@ static void dec_q6k(const uint8_t *b, double *out) {
     }
 }
 
+/* Q4_0 (hanzo-ml `src/vulkan_backend.rs`, `matvec_q4_0_gpu`: the native
+ * 18-byte block, f16 d then 16 code bytes): w = d * (q - 8), q 4 bit; byte j
+ * holds weight j (low nibble) and weight j + 16 (high nibble), the public
+ * GGML order. */
+static void dec_q4_0(const uint8_t *b, double *out) {
+    double d = oracle_half(rd16(b));
+    for (int j = 0; j < 16; ++j) {
+        out[j] = d * (double)((b[2 + j] & 15) - 8);
+        out[j + 16] = d * (double)((b[2 + j] >> 4) - 8);
+    }
+}
+
+/* Q5_K (hanzo-ml `src/vulkan_backend.rs`, `quantize_q5k`: d, dmin, 12 scale
+ * bytes, 32 qh bytes, 128 qs bytes): w = d*sc_j*q - dmin*m_j with a 5-bit q;
+ * scales as Q4_K; sub-block j takes its low 4 bits as Q4_K does from qs and
+ * its bit 4 from bit j of qh[l] (public GGML packing). */
+static void dec_q5k(const uint8_t *b, double *out) {
+    double d = oracle_half(rd16(b));
+    double dmin = oracle_half(rd16(b + 2));
+    const uint8_t *sc = b + 4, *qh = b + 16, *qs = b + 48;
+    for (int j = 0; j < 8; ++j) {
+        int s, m;
+        q4k_scale_min(sc, j, &s, &m);
+        for (int l = 0; l < 32; ++l) {
+            uint8_t byte = qs[32 * (j / 2) + l];
+            int q = ((j & 1) ? (byte >> 4) : (byte & 15)) | (((qh[l] >> j) & 1) << 4);
+            out[32 * j + l] = d * (double)s * (double)q - dmin * (double)m;
+        }
+    }
+}
+
 static void dec_block(int fmt, const uint8_t *b, double *out) {
     if (fmt == ORACLE_Q8_0) dec_q8_0(b, out);
     else if (fmt == ORACLE_Q4K) dec_q4k(b, out);
-    else dec_q6k(b, out);
+    else if (fmt == ORACLE_Q6K) dec_q6k(b, out);
+    else if (fmt == ORACLE_Q4_0) dec_q4_0(b, out);
+    else dec_q5k(b, out);
 }
 
 int oracle_dequant(int fmt, const uint8_t *blocks, int64_t nblocks, double *out) {
-    if (fmt < 0 || fmt > 2) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT) return -1;
     for (int64_t b = 0; b < nblocks; ++b) dec_block(fmt, blocks + b * QB[fmt], out + b * QK[fmt]);
     return 0;
 }
@@ -151,7 +186,7 @@ static int64_t row_bytes(int fmt, int64_t k) { return k / QK[fmt] * QB[fmt]; }
 /* ---------------------------------------------------------------------- */
 int oracle_matvec(int fmt, const uint8_t *w, const float *x, int64_t n, int64_t k,
                   const int64_t *rows, int64_t nrows, double *y) {
-    if (fmt < 0 || fmt > 2 || k % QK[fmt]) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT || k % QK[fmt]) return -1;
     double *wd = malloc(sizeof(double) * (size_t)k);
     if (!wd) return -2;
     int64_t cnt = rows ? nrows : n;
@@ -236,7 +271,7 @@ int oracle_blocksums_q4k_q8(const uint8_t *w, const int8_t *xq, int64_t n, int64
 /* ---------------------------------------------------------------------- */
 int oracle_matvec_q8act(int fmt, const uint8_t *w, const int8_t *xq, const float *xs, int64_t n,
                         int64_t k, const int64_t *rows, int64_t nrows, double *y) {
-    if (fmt < 0 || fmt > 2 || k % QK[fmt] || k % 32) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT || k % QK[fmt] || k % 32) return -1;
     double *wd = malloc(sizeof(double) * (size_t)k);
     double *xd = malloc(sizeof(double) * (size_t)k);
     if (!wd || !xd) { free(wd); free(xd); return -2; }
@@ -308,7 +343,7 @@ int oracle_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, in
 /* ---------------------------------------------------------------------- */
 int oracle_moe_qmv(int fmt, const uint8_t *bank, const float *x, int64_t x_div, const int32_t *ids,
                    int64_t nslots, int64_t n, int64_t k, int64_t E, double *y) {
-    if (fmt < 0 || fmt > 2 || k % QK[fmt] || x_div < 1) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT || k % QK[fmt] || x_div < 1) return -1;
     double *wd = malloc(sizeof(double) * (size_t)k);
     if (!wd) return -2;
     int64_t rb = row_bytes(fmt, k);
@@ -388,7 +423,7 @@ int oracle_moe_ffn(const uint8_t *gate, const uint8_t *up, const uint8_t *down, 
 /* ---------------------------------------------------------------------- */
 int oracle_qmm(int fmt, const uint8_t *w, const int8_t *xq, const float *xs, int64_t m, int64_t n,
                int64_t k, const int64_t *mrows, int64_t nm, double *Y) {
-    if (fmt < 0 || fmt > 2 || k % QK[fmt] || k % 32) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT || k % QK[fmt] || k % 32) return -1;
     int64_t cnt = mrows ? nm : m;
     double *wd = malloc(sizeof(double) * (size_t)(n * k));
     double *xd = malloc(sizeof(double) * (size_t)k);
@@ -441,7 +476,7 @@ int oracle_gemv(const float *w, const float *x, int64_t T, int64_t E, int64_t hi
 int oracle_moe_qmm(int fmt, const uint8_t *bank, const int8_t *xq, const float *xs, int64_t x_div,
                    const int32_t *ids, int64_t nslots, int64_t n, int64_t k, int64_t E,
                    const int64_t *slots, int64_t nlist, double *Y) {
-    if (fmt < 0 || fmt > 2 || k % QK[fmt] || k % 32 || x_div < 1) return -1;
+    if (fmt < 0 || fmt >= ORACLE_NFMT || k % QK[fmt] || k % 32 || x_div < 1) return -1;
     int64_t cnt = slots ? nlist : nslots;
     double *wd = malloc(sizeof(double) * (size_t)k);
     double *xd = malloc(sizeof(double) * (size_t)k);

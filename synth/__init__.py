@@ -20,10 +20,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
-FMT_Q8_0, FMT_Q4K, FMT_Q6K = 0, 1, 2
-BLOCK_WEIGHTS = {FMT_Q8_0: 32, FMT_Q4K: 256, FMT_Q6K: 256}
-BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4K: 144, FMT_Q6K: 210}
-FMT_NAMES = {"q8_0": FMT_Q8_0, "q4k": FMT_Q4K, "q6k": FMT_Q6K}
+FMT_Q8_0, FMT_Q4K, FMT_Q6K, FMT_Q4_0, FMT_Q5K = 0, 1, 2, 3, 4
+BLOCK_WEIGHTS = {FMT_Q8_0: 32, FMT_Q4K: 256, FMT_Q6K: 256, FMT_Q4_0: 32, FMT_Q5K: 256}
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4K: 144, FMT_Q6K: 210, FMT_Q4_0: 18, FMT_Q5K: 176}
+FMT_NAMES = {"q8_0": FMT_Q8_0, "q4k": FMT_Q4K, "q6k": FMT_Q6K, "q4_0": FMT_Q4_0, "q5k": FMT_Q5K}
 
 # Stream seeds for the workloads (one stream per input, rotations offset by 100).
 SEED_W, SEED_X, SEED_LOGITS = 1, 2, 3
@@ -54,7 +54,8 @@ def _load():
     lib.synth_normal.argtypes = [u64, u64, i64, vp]
     lib.synth_f32_to_f16.argtypes = [ctypes.c_float]
     lib.synth_f32_to_f16.restype = ctypes.c_uint16
-    for f in (lib.synth_encode_q8_0, lib.synth_encode_q4k, lib.synth_encode_q6k):
+    for f in (lib.synth_encode_q8_0, lib.synth_encode_q4k, lib.synth_encode_q6k, lib.synth_encode_q4_0,
+              lib.synth_encode_q5k):
         f.argtypes = [vp, i64, i64, vp]
         f.restype = i32
     lib.synth_row_bytes.argtypes = [i32, i64]
@@ -101,7 +102,8 @@ def encode(fmt: int, w: np.ndarray) -> np.ndarray:
     rows, k = w.shape
     out = np.empty((rows, row_bytes(fmt, k)), dtype=np.uint8)
     fn = {FMT_Q8_0: _load().synth_encode_q8_0, FMT_Q4K: _load().synth_encode_q4k,
-          FMT_Q6K: _load().synth_encode_q6k}[fmt]
+          FMT_Q6K: _load().synth_encode_q6k, FMT_Q4_0: _load().synth_encode_q4_0,
+          FMT_Q5K: _load().synth_encode_q5k}[fmt]
     if fn(_ptr(w), rows, k, _ptr(out)) != 0:
         raise ValueError(f"k={k} not a multiple of {BLOCK_WEIGHTS[fmt]}")
     return out

@@ -15,7 +15,8 @@
  *  - Q8_0 encoder: `VulkanDevice::quantize_q8` in `src/vulkan_backend.rs`
  *    (per 32 weights: amax, inv = 127/amax, q = round(w*inv) clamped to
  *    +-127, scale = amax/127 stored as f16, all-zero block stores 1.0).
- *  - Q4_K / Q6_K encoders: the pages only name `QTensor::quantize`; the
+ *  - Q4_K / Q6_K / Q5_K / Q4_0 encoders: the pages only name the block
+ *    layouts (`quantize_q5k`, `matvec_q4_0_gpu`) or `QTensor::quantize`; the
  *    encoders below are plain min/max quantizers producing valid blocks of
  *    the public GGML k-quant byte layout (parity is on the bytes, so any
  *    valid encoder serves).
@@ -260,16 +261,102 @@ int synth_encode_q6k(const float *w, int64_t rows, int64_t k, uint8_t *out) {
 }
 
 /* ---------------------------------------------------------------------- */
+/* Q4_0: 18 bytes per 32 weights = f16 d, 16 bytes of 4-bit codes; byte j   */
+/* holds weight j (low nibble) and weight j + 16 (high nibble),             */
+/* w = d * (q - 8). Encoder: the weight of largest magnitude m (with its    */
+/* sign) maps to code 0, d = m / -8; q = clamp(round(w / d) + 8, 0, 15).     */
+/* ---------------------------------------------------------------------- */
+static void enc_q4_0(const float *w, uint8_t *b) {
+    float m = 0.0f;
+    for (int i = 0; i < 32; ++i)
+        if (fabsf(w[i]) > fabsf(m)) m = w[i];
+    uint16_t dh = synth_f32_to_f16(m / -8.0f);
+    float d = h2f(dh);
+    b[0] = (uint8_t)(dh & 0xFF); b[1] = (uint8_t)(dh >> 8);
+    for (int j = 0; j < 16; ++j) {
+        int q0 = d != 0.0f ? clampi((int)rnd(w[j] / d) + 8, 0, 15) : 8;
+        int q1 = d != 0.0f ? clampi((int)rnd(w[j + 16] / d) + 8, 0, 15) : 8;
+        b[2 + j] = (uint8_t)(q0 | (q1 << 4));
+    }
+}
+
+int synth_encode_q4_0(const float *w, int64_t rows, int64_t k, uint8_t *out) {
+    if (k % 32) return -1;
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) enc_q4_0(w + r * k + b * 32, out + (r * nb + b) * 18);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Q5_K: 176 bytes per 256 weights                                         */
+/*   [0,2) d f16, [2,4) dmin f16, [4,16) scales as Q4_K, [16,48) qh,        */
+/*   [48,176) qs. Sub-block j: low 4 bits of weight 32j+l from              */
+/*   qs[32*(j/2)+l] (low nibble for even j, high for odd), bit 4 from bit j */
+/*   of qh[l]; w = d*sc_j*q - dmin*m_j, q in [0, 31]. Encoder: the Q4_K     */
+/*   min/max quantizer with 31 levels.                                      */
+/* ---------------------------------------------------------------------- */
+static void enc_q5k(const float *w, uint8_t *b) {
+    float scale[8], minv[8];
+    float maxscale = 0.0f, maxmin = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        float lo = 0.0f, hi = -INFINITY;
+        for (int l = 0; l < 32; ++l) {
+            float v = w[32 * j + l];
+            if (v < lo) lo = v;
+            if (v > hi) hi = v;
+        }
+        scale[j] = (hi - lo) / 31.0f;
+        minv[j] = -lo;
+        if (scale[j] > maxscale) maxscale = scale[j];
+        if (minv[j] > maxmin) maxmin = minv[j];
+    }
+    uint16_t dh = synth_f32_to_f16(maxscale / 63.0f);
+    uint16_t mh = synth_f32_to_f16(maxmin / 63.0f);
+    float d = h2f(dh), dmin = h2f(mh);
+    uint8_t sc[8], mn[8];
+    for (int j = 0; j < 8; ++j) {
+        sc[j] = (uint8_t)(d > 0.0f ? clampi((int)rnd(scale[j] / d), 0, 63) : 0);
+        mn[j] = (uint8_t)(dmin > 0.0f ? clampi((int)rnd(minv[j] / dmin), 0, 63) : 0);
+    }
+    b[0] = (uint8_t)(dh & 0xFF); b[1] = (uint8_t)(dh >> 8);
+    b[2] = (uint8_t)(mh & 0xFF); b[3] = (uint8_t)(mh >> 8);
+    synth_pack_q4k_scales(sc, mn, b + 4);
+    uint8_t *qh = b + 16, *qs = b + 48;
+    memset(qh, 0, 32);
+    memset(qs, 0, 128);
+    for (int j = 0; j < 8; ++j) {
+        float ds = d * (float)sc[j];
+        float dm = dmin * (float)mn[j];
+        for (int l = 0; l < 32; ++l) {
+            int q = ds > 0.0f ? clampi((int)rnd((w[32 * j + l] + dm) / ds), 0, 31) : 0;
+            qs[32 * (j / 2) + l] |= (uint8_t)((j & 1) ? ((q & 15) << 4) : (q & 15));
+            qh[l] |= (uint8_t)((q >> 4) << j);
+        }
+    }
+}
+
+int synth_encode_q5k(const float *w, int64_t rows, int64_t k, uint8_t *out) {
+    if (k % 256) return -1;
+    int64_t nb = k / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) enc_q5k(w + r * k + b * 256, out + (r * nb + b) * 176);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Whole weight matrices straight from the seed, row-chunked so that no     */
 /* full f32 copy of a large matrix is ever held. Element (r, c) of a        */
 /* [rows, k] matrix is uniform counter r*k + c of stream `seed`.            */
-/* fmt: 0 = Q8_0, 1 = Q4_K, 2 = Q6_K.                                       */
+/* fmt: 0 = Q8_0, 1 = Q4_K, 2 = Q6_K, 3 = Q4_0, 4 = Q5_K.                   */
 /* ---------------------------------------------------------------------- */
-static const int64_t BLK_W[3] = {32, 256, 256};
-static const int64_t BLK_B[3] = {34, 144, 210};
+static const int64_t BLK_W[5] = {32, 256, 256, 32, 256};
+static const int64_t BLK_B[5] = {34, 144, 210, 18, 176};
 
 int64_t synth_row_bytes(int fmt, int64_t k) {
-    if (fmt < 0 || fmt > 2 || k % BLK_W[fmt]) return -1;
+    if (fmt < 0 || fmt > 4 || k % BLK_W[fmt]) return -1;
     return k / BLK_W[fmt] * BLK_B[fmt];
 }
 
@@ -290,7 +377,9 @@ int synth_weights(int fmt, uint64_t seed, int64_t rows, int64_t k, uint8_t *out)
                     const float *wb = buf + b * BLK_W[fmt];
                     if (fmt == 0) enc_q8_0(wb, o + b * 34);
                     else if (fmt == 1) enc_q4k(wb, o + b * 144);
-                    else enc_q6k(wb, o + b * 210);
+                    else if (fmt == 2) enc_q6k(wb, o + b * 210);
+                    else if (fmt == 3) enc_q4_0(wb, o + b * 18);
+                    else enc_q5k(wb, o + b * 176);
                 }
             }
         }
@@ -314,7 +403,7 @@ static uint16_t rand_half(uint64_t c, int subnormal) {
 }
 
 int synth_random_blocks(int fmt, uint64_t seed, int64_t nblocks, int subnormal_every, uint8_t *out) {
-    if (fmt < 0 || fmt > 2) return -1;
+    if (fmt < 0 || fmt > 4) return -1;
     int64_t bb = BLK_B[fmt];
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblocks; ++b) {
@@ -322,10 +411,10 @@ int synth_random_blocks(int fmt, uint64_t seed, int64_t nblocks, int subnormal_e
         for (int64_t i = 0; i < bb; ++i) o[i] = (uint8_t)(mix64(ctr(seed, (uint64_t)(b * bb + i))) >> 56);
         int sub = subnormal_every > 0 && (b % subnormal_every) == 0;
         uint64_t c = ctr(seed ^ 0x5A5Aull, (uint64_t)b * 2);
-        if (fmt == 0) {
+        if (fmt == 0 || fmt == 3) {
             uint16_t h = rand_half(c, sub);
             o[0] = (uint8_t)h; o[1] = (uint8_t)(h >> 8);
-        } else if (fmt == 1) {
+        } else if (fmt == 1 || fmt == 4) {
             uint16_t h0 = rand_half(c, sub), h1 = rand_half(c + 1, sub);
             h0 &= 0x7FFF; h1 &= 0x7FFF; /* d and dmin non-negative as an encoder would emit */
             o[0] = (uint8_t)h0; o[1] = (uint8_t)(h0 >> 8);

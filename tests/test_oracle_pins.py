@@ -131,6 +131,80 @@ def test_q6k_packer_matches_hand_bytes():
     assert bytes(ql) == hexbytes(f["ql"]) and bytes(qh) == hexbytes(f["qh"])
 
 
+def _q4_0_fixture():
+    f = read_fixture("q4_0_block.txt")
+    blk = hexbytes(f["d"]) + hexbytes(f["qs"])
+    assert len(blk) == 18
+    q = [(5 * j + 3 * (j // 16)) % 16 for j in range(32)]
+    return np.frombuffer(blk, dtype=np.uint8), np.array([0.5 * (v - 8) for v in q])
+
+
+def _q5k_fixture():
+    f = read_fixture("q5k_block.txt")
+    blk = hexbytes(f["d"]) + hexbytes(f["dmin"]) + hexbytes(f["scales"]) + hexbytes(f["qh"]) + hexbytes(f["qs"])
+    assert len(blk) == 176
+    sc = [int(v) for v in f["sc"]]
+    m = [int(v) for v in f["m"]]
+    q = [((97 * i) % 251) % 32 for i in range(256)]
+    expect = np.array([1.0 * sc[i // 32] * q[i] - 0.5 * m[i // 32] for i in range(256)])
+    return np.frombuffer(blk, dtype=np.uint8), sc, m, q, expect
+
+
+def test_q4_0_hand_block_and_one_hot_columns():
+    blk, expect = _q4_0_fixture()
+    assert np.array_equal(oracle.dequant("q4_0", blk), expect)
+    for c in range(32):  # nibble order: weight j low nibble, j + 16 high nibble of byte j
+        x = np.zeros(32, dtype=np.float32)
+        x[c] = 1.0
+        assert oracle.matvec("q4_0", blk, x, 1, 32)[0] == expect[c]
+
+
+def test_q4_0_subnormal_scale_and_zero_code_offset():
+    blk, expect = _q4_0_fixture()
+    b = blk.copy()
+    b[0:2] = [0x03, 0x80]  # d = -3 * 2^-24
+    assert np.array_equal(oracle.dequant("q4_0", b), expect / 0.5 * (-3 * 2.0 ** -24))
+    b[2:] = 0x88           # every code 8: every weight exactly 0
+    assert np.all(oracle.dequant("q4_0", b) == 0.0)
+
+
+def test_q5k_hand_block_and_one_hot_columns():
+    blk, _, _, _, expect = _q5k_fixture()
+    assert np.array_equal(oracle.dequant("q5k", blk), expect)
+    for c in range(0, 256, 3):
+        x = np.zeros(256, dtype=np.float32)
+        x[c] = 1.0
+        assert oracle.matvec("q5k", blk, x, 1, 256)[0] == expect[c]
+
+
+def test_q5k_high_bit_and_subnormal_scales():
+    blk, sc, m, q, _ = _q5k_fixture()
+    b = blk.copy()
+    b[16:48] = 0           # clear every bit 4: codes reduce to their low nibbles
+    expect = np.array([1.0 * sc[i // 32] * (q[i] & 15) - 0.5 * m[i // 32] for i in range(256)])
+    assert np.array_equal(oracle.dequant("q5k", b), expect)
+    b = blk.copy()
+    b[0:2] = [0x01, 0x00]  # d = 2^-24
+    b[2:4] = [0xFF, 0x03]  # dmin = 1023 * 2^-24
+    expect = np.array([2.0 ** -24 * sc[i // 32] * q[i] - 1023 * 2.0 ** -24 * m[i // 32] for i in range(256)])
+    assert np.array_equal(oracle.dequant("q5k", b), expect)
+
+
+def test_q4_0_q5k_encoder_roundtrip_bound():
+    n, k = 32, 1024
+    wf = synth.weight_matrix_f32(8, n, k).astype(np.float64)
+    # Q4_0: 16 levels d*(q-8) with d = -(largest weight)/8 -- the step is
+    # about 1/8 and the far end of the range is one step short (codes -8..7),
+    # so the max error is about one step; Q5_K: 32 levels over a sub-block's
+    # range, half a step of about 2/31 plus the 6-bit scale rounding.
+    for fmt, f, lim in (("q4_0", synth.FMT_Q4_0, 0.13), ("q5k", synth.FMT_Q5K, 0.05)):
+        wd = oracle.dequant(fmt, synth.weights(f, 8, n, k)).reshape(n, k)
+        err = np.abs(wd - wf)
+        assert err.max() < lim, (fmt, err.max())
+        rel = np.sqrt((err ** 2).mean() / (wf ** 2).mean())
+        assert rel < (0.07 if fmt == "q4_0" else 0.035), (fmt, rel)
+
+
 def test_q8_0_hand_block():
     blk, q = _q8_0_fixture()
     assert np.array_equal(oracle.dequant("q8_0", blk), q)
@@ -169,7 +243,7 @@ def test_matvec_q8_0_integer_exact():
     assert np.array_equal(y, (q @ x).astype(np.float64))
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k", "q4_0", "q5k"])
 def test_matvec_vs_numpy_f64_on_random_blocks(fmt):
     f = synth.FMT_NAMES[fmt]
     n, k = 19, 512
