@@ -213,8 +213,8 @@ def dense_other(fmt: str, n: int, k: int, copies: int):
     import torch
     import moe_ggml_block_amd as qmv
     import synth
-    f = {"q8_0": synth.FMT_Q8_0, "q6k": synth.FMT_Q6K}[fmt]
-    fn = {"q8_0": qmv.qmv_q8_0, "q6k": qmv.qmv_q6k}[fmt]
+    f = {"q8_0": synth.FMT_Q8_0, "q6k": synth.FMT_Q6K, "q4_0": synth.FMT_Q4_0, "q5k": synth.FMT_Q5K}[fmt]
+    fn = {"q8_0": qmv.qmv_q8_0, "q6k": qmv.qmv_q6k, "q4_0": qmv.qmv_q4_0, "q5k": qmv.qmv_q5k}[fmt]
     w_host = synth.weights(f, synth.SEED_W, n, k)
     nbytes = w_host.nbytes
     big, W = rotated(w_host, copies)
@@ -545,6 +545,9 @@ def main():
         others["q8_0_4096x4096"] = dense_other("q8_0", 4096, 4096, 64)
         log("others: q6k")
         others["q6k_128256x4096"] = dense_other("q6k", 128256, 4096, 3)
+        log("others: q4_0, q5k")
+        others["q4_0_14336x4096"] = dense_other("q4_0", 14336, 4096, 32)
+        others["q5k_14336x4096"] = dense_other("q5k", 14336, 4096, 32)
         log("others: moe")
         others["moe_layer"] = moe_other()
         log("others: prefill")

@@ -69,6 +69,17 @@ int qmv_q8_0(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_
 int qmv_q4k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
 int qmv_q6k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
 
+/* More formats on the same decode skeleton (hanzo-ml `src/vulkan_backend.rs`):
+ *   qmv_q4_0: native 18-byte Q4_0 blocks (`matvec_q4_0_gpu`: f16 d + 16 code
+ *             bytes, w = d*(q - 8)); w: n*(k/32)*18 bytes, k % 32 == 0.
+ *   qmv_q5k:  176-byte Q5_K superblocks (`quantize_q5k` / `matvec_q5k_gpu`: d,
+ *             dmin, 12 scale bytes, 32 qh bytes, 128 qs bytes, w =
+ *             d*sc_j*q - dmin*m_j with a 5-bit q); w: n*(k/256)*176 bytes,
+ *             k % 256 == 0.
+ * x: f32[k]; y: f32[n]; blocks read verbatim; w and x 16-byte aligned. */
+int qmv_q4_0(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+int qmv_q5k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * q8 activation quantizer (`quantize_act_q8`: xq int8, xs f32 scale, xsum
  * f32 dequantized block sum, per 32 consecutive values of each row).

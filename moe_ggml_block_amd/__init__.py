@@ -29,6 +29,8 @@ _SIGS = {
     "qmv_q8_0": [_vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q4k": [_vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q6k": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q4_0": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q5k": [_vp, _vp, _vp, _i64, _i64, _vp],
     "quantize_act_q8": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q4k_q8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_debug_blocksums_q4k_q8": [_vp, _vp, _vp, _i64, _i64, _vp],
@@ -64,7 +66,7 @@ _lib.qmv_strerror.restype = ctypes.c_char_p
 EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "moe_ffn_prefill_workspace_bytes",
                           "moe_ffn_q8_workspace_bytes", "qmv_version", "qmv_strerror")
 
-BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210)}
+BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210), "q4_0": (32, 18), "q5k": (256, 176)}
 
 
 class QmvError(RuntimeError):
@@ -125,6 +127,14 @@ def qmv_q4k(w, x, n, k, y=None, stream=None):
 
 def qmv_q6k(w, x, n, k, y=None, stream=None):
     return _dense("qmv_q6k", "q6k", w, x, n, k, y, stream)
+
+
+def qmv_q4_0(w, x, n, k, y=None, stream=None):
+    return _dense("qmv_q4_0", "q4_0", w, x, n, k, y, stream)
+
+
+def qmv_q5k(w, x, n, k, y=None, stream=None):
+    return _dense("qmv_q5k", "q5k", w, x, n, k, y, stream)
 
 
 def quantize_act_q8(x, m, k, out=None, stream=None):

@@ -283,6 +283,130 @@ struct Q4KUnit : F32Act<Q4KUnit> {
     }
 };
 
+// ---------------------------------------------------------------- Q4_0 ---
+// Native 18-byte blocks (f16 d, 16 code bytes; byte j holds weight j in its
+// low nibble and weight j + 16 in its high nibble), w = d * (q - 8). A unit
+// is two blocks (36 bytes, 4-byte aligned in a row of k % 64 == 0); the
+// nibbles go through the exact fp8 path of the Q4_K unit (q * 2^-9) and the
+// offset is folded as d * (sum q*x - 8 * sum x) with the run sums of x.
+struct Q40Unit : F32Act<Q40Unit> {
+    static constexpr int BW = 32, BB = 18;
+    static constexpr int RING = QMV_RING_Q8;
+    static constexpr int MAX_WG_PER_CU = 2;
+    struct Raw {
+        uint32_t d[9];
+    };
+    static __device__ __forceinline__ int units_per_row(int k) { return k / 64; }
+    static __device__ __forceinline__ void load_x(UnitX &X, const float *x, int u) {
+        load_x_runs(X, x, 64 * u, 64 * u + 16, 64 * u + 32, 64 * u + 48);
+    }
+    static __device__ __forceinline__ int xslot(int i, int *j) {
+        *j = i & 63;
+        return i >> 6;
+    }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) {
+        const uint8_t *p = row + 36 * u;
+        const v4u_a4 *v = reinterpret_cast<const v4u_a4 *>(p);
+        const v4u_a4 a = v[0], b = v[1];
+        R.d[0] = a.x; R.d[1] = a.y; R.d[2] = a.z; R.d[3] = a.w;
+        R.d[4] = b.x; R.d[5] = b.y; R.d[6] = b.z; R.d[7] = b.w;
+        R.d[8] = reinterpret_cast<const uint32_t *>(p)[8];
+    }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitX &X, int) {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t qa = funnel(R.d[t + 1], R.d[t], 2);  // block A codes: bytes 2..17
+            const uint32_t qb = R.d[5 + t];                     // block B codes: bytes 20..35
+            const uint32_t al = qa & 0x0F0F0F0Fu, ah = (qa >> 4) & 0x0F0F0F0Fu;
+            const uint32_t bl = qb & 0x0F0F0F0Fu, bh = (qb >> 4) & 0x0F0F0F0Fu;
+            const float2 al0 = nib2f_lo(al), al1 = nib2f_hi(al), ah0 = nib2f_lo(ah), ah1 = nib2f_hi(ah);
+            const float2 bl0 = nib2f_lo(bl), bl1 = nib2f_hi(bl), bh0 = nib2f_lo(bh), bh1 = nib2f_hi(bh);
+            a = fmaf(al0.x, X.v[4 * t + 0], a);
+            a = fmaf(al0.y, X.v[4 * t + 1], a);
+            a = fmaf(al1.x, X.v[4 * t + 2], a);
+            a = fmaf(al1.y, X.v[4 * t + 3], a);
+            a = fmaf(ah0.x, X.v[16 + 4 * t + 0], a);
+            a = fmaf(ah0.y, X.v[16 + 4 * t + 1], a);
+            a = fmaf(ah1.x, X.v[16 + 4 * t + 2], a);
+            a = fmaf(ah1.y, X.v[16 + 4 * t + 3], a);
+            b = fmaf(bl0.x, X.v[32 + 4 * t + 0], b);
+            b = fmaf(bl0.y, X.v[32 + 4 * t + 1], b);
+            b = fmaf(bl1.x, X.v[32 + 4 * t + 2], b);
+            b = fmaf(bl1.y, X.v[32 + 4 * t + 3], b);
+            b = fmaf(bh0.x, X.v[48 + 4 * t + 0], b);
+            b = fmaf(bh0.y, X.v[48 + 4 * t + 1], b);
+            b = fmaf(bh1.x, X.v[48 + 4 * t + 2], b);
+            b = fmaf(bh1.y, X.v[48 + 4 * t + 3], b);
+        }
+        const float da = h2f(R.d[0]), db = h2f(R.d[4] >> 16);
+        float r = (da * 512.0f) * a;  // undo the 2^-9 of the fp8 read
+        r = fmaf(-8.0f * da, X.s[0] + X.s[1], r);
+        r = fmaf(db * 512.0f, b, r);
+        r = fmaf(-8.0f * db, X.s[2] + X.s[3], r);
+        return r;
+    }
+};
+
+// ---------------------------------------------------------------- Q5_K ---
+// 176-byte superblocks: d, dmin, scales[12] (as Q4_K), qh[32], qs[128]. A
+// unit is a quarter superblock (sub-blocks 2p, 2p+1): the 5-bit code of
+// weight l of sub-block j is its Q4_K nibble plus bit j of qh[l] as bit 4,
+// w = d*sc_j*q - dmin*m_j.
+struct Q5KUnit : F32Act<Q5KUnit> {
+    static constexpr int BW = 256, BB = 176;
+    static constexpr int RING = QMV_RING_Q4K;
+    static constexpr int MAX_WG_PER_CU = 3;
+    struct Raw {
+        uint4 q0, q1, h0, h1, m;
+    };
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load_x(UnitX &X, const float *x, int u) {
+        const int b = 256 * (u >> 2) + 64 * (u & 3);
+        load_x_runs(X, x, b, b + 16, b + 32, b + 48);
+    }
+    static __device__ __forceinline__ int xslot(int i, int *j) {
+        *j = i & 63;
+        return i >> 6;
+    }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) {
+        const uint8_t *blk = row + (size_t)(u >> 2) * 176;
+        const int p = u & 3;
+        R.q0 = ld16(blk + 48 + 32 * p);
+        R.q1 = ld16(blk + 64 + 32 * p);
+        R.h0 = ld16(blk + 16);
+        R.h1 = ld16(blk + 32);
+        R.m = ld16(blk);
+    }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitX &X, int u) {
+        const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+        const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
+        const int jl = 2 * (u & 3);  // sub-blocks jl (low nibbles) and jl + 1 (high)
+        float alo = 0.0f, ahi = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t lo = (qw[t] & 0x0F0F0F0Fu) | (((hw[t] >> jl) & 0x01010101u) << 4);
+            const uint32_t hi = ((qw[t] >> 4) & 0x0F0F0F0Fu) | (((hw[t] >> (jl + 1)) & 0x01010101u) << 4);
+            alo = fmaf(ubyte_f<0>(lo), X.v[4 * t + 0], alo);
+            alo = fmaf(ubyte_f<1>(lo), X.v[4 * t + 1], alo);
+            alo = fmaf(ubyte_f<2>(lo), X.v[4 * t + 2], alo);
+            alo = fmaf(ubyte_f<3>(lo), X.v[4 * t + 3], alo);
+            ahi = fmaf(ubyte_f<0>(hi), X.v[32 + 4 * t + 0], ahi);
+            ahi = fmaf(ubyte_f<1>(hi), X.v[32 + 4 * t + 1], ahi);
+            ahi = fmaf(ubyte_f<2>(hi), X.v[32 + 4 * t + 2], ahi);
+            ahi = fmaf(ubyte_f<3>(hi), X.v[32 + 4 * t + 3], ahi);
+        }
+        uint32_t sc2, mn2;
+        q4k_scales(R.m.y, R.m.z, R.m.w, u & 3, &sc2, &mn2);
+        const float d = h2f(R.m.x), dmin = h2f(R.m.x >> 16);
+        float r = (d * ubyte_f<0>(sc2)) * alo;
+        r = fmaf(d * ubyte_f<1>(sc2), ahi, r);
+        r = fmaf(-(dmin * ubyte_f<0>(mn2)), X.s[0] + X.s[1], r);
+        r = fmaf(-(dmin * ubyte_f<1>(mn2)), X.s[2] + X.s[3], r);
+        return r;
+    }
+};
+
 // ---------------------------------------------------------------- Q6_K ---
 // 16 / 8 bytes at an even address, one global load each (see file comment).
 QMV_DEV uint4 ld16u(const uint8_t *p) {

@@ -1,4 +1,5 @@
-// Dense decode matvecs y = W_deq x over raw Q8_0 / Q4_K / Q6_K rows (gfx950).
+// Dense decode matvecs y = W_deq x over raw Q8_0 / Q4_K / Q6_K / Q4_0 / Q5_K
+// rows (gfx950).
 //
 // Defined by hanzo-ml `src/vulkan_backend.rs`: `matvec_q8_0_gpu`,
 // `matvec_q4k_gpu_off` and `matvec_q6k_gpu_off` (y[nout] = Wq * x[k], blocks
@@ -45,6 +46,37 @@ __device__ float block_dot_generic(int fmt, const uint8_t *b, const float *x) {
         }
         return acc;
     }
+    if (fmt == 3) {
+        float d = h2f(b[0] | (b[1] << 8));
+        for (int j = 0; j < 16; ++j) {
+            acc = fmaf((float)((b[2 + j] & 15) - 8), x[j], acc);
+            acc = fmaf((float)((b[2 + j] >> 4) - 8), x[j + 16], acc);
+        }
+        return d * acc;
+    }
+    if (fmt == 4) {
+        float d = h2f(b[0] | (b[1] << 8)), dmin = h2f(b[2] | (b[3] << 8));
+        const uint8_t *s = b + 4, *qh = b + 16, *qs = b + 48;
+        for (int j = 0; j < 8; ++j) {
+            int sc, m;
+            if (j < 4) {
+                sc = s[j] & 63;
+                m = s[j + 4] & 63;
+            } else {
+                sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+                m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+            }
+            float a = 0.0f, xs = 0.0f;
+            for (int l = 0; l < 32; ++l) {
+                uint8_t v = qs[32 * (j >> 1) + l];
+                int q = ((j & 1) ? (v >> 4) : (v & 15)) | (((qh[l] >> j) & 1) << 4);
+                a = fmaf((float)q, x[32 * j + l], a);
+                xs += x[32 * j + l];
+            }
+            acc += d * (float)sc * a - dmin * (float)m * xs;
+        }
+        return acc;
+    }
     const uint8_t *ql = b, *qh = b + 128;
     const int8_t *sc = reinterpret_cast<const int8_t *>(b + 192);
     float d = h2f(b[208] | (b[209] << 8));
@@ -70,7 +102,8 @@ __global__ __launch_bounds__(256) void k_qmv_generic(int fmt, const uint8_t *__r
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
     if (r >= n) return;
-    const int bw = fmt == 0 ? 32 : 256, bb = fmt == 0 ? 34 : (fmt == 1 ? 144 : 210);
+    const int bw = (fmt == 0 || fmt == 3) ? 32 : 256;
+    const int bb = fmt == 0 ? 34 : fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 18 : 176;
     const int64_t nb = k / bw;
     float acc = 0.0f;
     for (int64_t b = lane; b < nb; b += 64) acc += block_dot_generic(fmt, w + r * row_bytes + b * bb, x + b * bw);
@@ -83,7 +116,7 @@ template <class F>
 int launch_dense(const uint8_t *w, const float *x, float *y, int64_t n, int64_t k, hipStream_t s) {
     const int64_t row_bytes = k / F::BW * F::BB;
     const bool tiled = (k % 64 == 0) && k <= 8192;  // units of 64 weights, x fits LDS
-    const int fmt = F::BB == 34 ? 0 : (F::BB == 144 ? 1 : 2);
+    const int fmt = F::BB == 34 ? 0 : F::BB == 144 ? 1 : F::BB == 210 ? 2 : F::BB == 18 ? 3 : 4;
     if (!tiled) {
         const dim3 grid((unsigned)((n + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
         hipLaunchKernelGGL(k_qmv_generic, grid, dim3(256), 0, s, fmt, w, x, y, n, k, row_bytes);
@@ -113,4 +146,10 @@ extern "C" int qmv_q4k(const void *w, const float *x, float *y, int64_t n, int64
 }
 extern "C" int qmv_q6k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
     return dense_entry<Q6KUnit>(w, x, y, n, k, s);
+}
+extern "C" int qmv_q4_0(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
+    return dense_entry<Q40Unit>(w, x, y, n, k, s);
+}
+extern "C" int qmv_q5k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
+    return dense_entry<Q5KUnit>(w, x, y, n, k, s);
 }

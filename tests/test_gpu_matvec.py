@@ -16,8 +16,9 @@ from gpu_util import TOL, announce, dev, host, scalerel
 
 pytestmark = pytest.mark.gpu
 
-FMTS = {"q8_0": synth.FMT_Q8_0, "q4k": synth.FMT_Q4K, "q6k": synth.FMT_Q6K}
-FN = {"q8_0": qmv.qmv_q8_0, "q4k": qmv.qmv_q4k, "q6k": qmv.qmv_q6k}
+FMTS = {"q8_0": synth.FMT_Q8_0, "q4k": synth.FMT_Q4K, "q6k": synth.FMT_Q6K, "q4_0": synth.FMT_Q4_0,
+        "q5k": synth.FMT_Q5K}
+FN = {"q8_0": qmv.qmv_q8_0, "q4k": qmv.qmv_q4k, "q6k": qmv.qmv_q6k, "q4_0": qmv.qmv_q4_0, "q5k": qmv.qmv_q5k}
 
 
 def _run_dense(fmt, w, x, n, k):
@@ -31,10 +32,12 @@ SMALL = {
     "q8_0": [(1, 32), (37, 96), (5, 64), (130, 512), (67, 2048), (29, 4096), (33, 8192), (9, 16384)],
     "q4k": [(1, 256), (37, 256), (70, 768), (65, 2048), (33, 4096), (17, 8192), (5, 12288), (3, 20480)],
     "q6k": [(1, 256), (37, 256), (70, 768), (65, 2048), (33, 4096), (17, 8192), (5, 12288), (3, 20480)],
+    "q4_0": [(1, 32), (37, 96), (5, 64), (130, 512), (67, 2048), (29, 4096), (33, 8192), (9, 16384)],
+    "q5k": [(1, 256), (37, 256), (70, 768), (65, 2048), (33, 4096), (17, 8192), (5, 12288), (3, 20480)],
 }
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k", "q4_0", "q5k"])
 def test_dense_small_shapes(fmt):
     for n, k in SMALL[fmt]:
         announce(f"dense {fmt} n={n} k={k}")
@@ -45,7 +48,7 @@ def test_dense_small_shapes(fmt):
         assert scalerel(ref, got) <= TOL, (fmt, n, k, scalerel(ref, got))
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4k", "q6k", "q4_0", "q5k"])
 def test_dense_random_blocks(fmt):
     """Random raw bytes: every code, every 6-bit scale/min, negative Q6_K
     sub-scales, subnormal f16 scales in every 3rd block."""
@@ -60,7 +63,7 @@ def test_dense_random_blocks(fmt):
 
 
 def test_dense_subnormal_only_scales():
-    for fmt in ("q4k", "q6k", "q8_0"):
+    for fmt in ("q4k", "q6k", "q8_0", "q4_0", "q5k"):
         f = FMTS[fmt]
         n, k = 16, 1024
         announce(f"dense subnormal {fmt}")
@@ -71,7 +74,8 @@ def test_dense_subnormal_only_scales():
         assert scalerel(ref, got) <= TOL, (fmt, scalerel(ref, got))
 
 
-@pytest.mark.parametrize("fmt,n,k", [("q8_0", 4096, 4096), ("q4k", 14336, 4096), ("q6k", 128256, 4096)])
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 4096, 4096), ("q4k", 14336, 4096), ("q6k", 128256, 4096),
+                                     ("q4_0", 14336, 4096), ("q5k", 14336, 4096)])
 def test_dense_full_config(fmt, n, k):
     """The full workload shapes, in the launch configuration the benchmark times."""
     announce(f"dense full {fmt} n={n} k={k}")
