@@ -41,7 +41,7 @@ Q4K_LAUNCH_BYTES = Q4K_BYTES + 4 * N2 + 4 * K2  # 33,103,872
 CALIB_BYTES = 64 << 20                         # the counter-calibration copy
 TRAFFIC_JSON = os.path.join("profiles", "qmv_q4k_14336x4096_traffic.json")
 METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
-KERNEL_SOURCES = ["include/qmv.h", "moe_ggml_block_amd/csrc/common.hpp",
+KERNEL_SOURCES = ["moe_ggml_block_amd/csrc/common.hpp",
                   "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/dense.hpp",
                   "moe_ggml_block_amd/csrc/qmv_dense.hip"]
 
