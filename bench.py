@@ -268,6 +268,13 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
             qmv.moe_ffn_q4k_q6k_q8(G[b], U[b], D[b], x, ids, wts, T, topk, hidden, inter, E, y=y, ws=wsq)
 
         ms_q8 = time_graph(layer_q8, 2 * logit_sets, 5)
+
+        def layer_routed(i):
+            b = i % bank_copies
+            qmv.moe_ffn_routed_q4k_q6k(G[b], U[b], D[b], x, lg[i % logit_sets], T, topk, hidden, inter, E,
+                                       out=(y, ids, wts), ws=ws)
+
+        ms_rt = time_graph(layer_routed, 2 * logit_sets, 5)
         # unique experts actually routed, averaged over the logit sets
         uniq = []
         for r in range(logit_sets):
@@ -276,6 +283,8 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
         u = float(np.mean(uniq))
         out[f"T{T}"] = {"tokens_per_s": round(T / (ms * 1e-3), 1), "layer_us": round(ms * 1e3, 3),
                         "q8_layer_us": round(ms_q8 * 1e3, 3), "q8_tokens_per_s": round(T / (ms_q8 * 1e-3), 1),
+                        "routed_layer_us": round(ms_rt * 1e3, 3),
+                        "routed_tokens_per_s": round(T / (ms_rt * 1e-3), 1),
                         "unique_experts": u, "gbs_unique_experts": round(u * per_expert / (ms * 1e-3) / 1e9, 1)}
     del bg, bu, bd, G, U, D
     torch.cuda.empty_cache()

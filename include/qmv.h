@@ -170,6 +170,19 @@ int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const fl
                     int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
                     qmv_stream_t stream);
 
+/* The same layer with the router fused into the gate/up gather (the
+ * indexed-MoE design of hanzo-ml `src/vulkan_backend.rs`: `moe_route_vk`
+ * softmax + top-k + renormalize feeding `moe_matvec_gpu` with ids kept on
+ * the device): every workgroup of the gather routes logits f32[T, E] itself
+ * (moe_route semantics: ties to the lower expert, NaN below every number)
+ * and groups the slots by expert; ids int32[T, topk] and wts f32[T, topk]
+ * are written as outputs and read by the down pass. For E > 256 or T > 8
+ * the router runs as its own kernel first (same ids; measured faster there). Operands otherwise as
+ * moe_ffn_q4k_q6k (same workspace). */
+int moe_ffn_routed_q4k_q6k(const void *gate, const void *up, const void *down, const float *x, const float *logits,
+                           int32_t *ids, float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,
+                           int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * q8-activation MoE decode variant (the int8-dot gathers of hanzo-ml
  * `src/vulkan_backend.rs`: activation quantized once by quantize_act_q8,

@@ -48,6 +48,7 @@ _SIGS = {
     "moe_qmv_q4k_q8": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q6k_q8": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k_q8": [_vp] * 8 + [_i64] * 6 + [_vp],
+    "moe_ffn_routed_q4k_q6k": [_vp] * 9 + [_i64] * 6 + [_vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -316,6 +317,31 @@ def moe_ffn_prefill_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter,
                                         ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
                                         _stream(stream)), "moe_ffn_prefill_q4k_q6k")
     return y
+
+
+def moe_ffn_routed_q4k_q6k(gate, up, down, x, logits, T, topk, hidden, inter, E, out=None, ws=None,
+                           stream=None):
+    """MoE layer with the router fused into the gate/up gather: (y, ids, wts)."""
+    nb = moe_ffn_workspace_bytes(T, topk, hidden, inter)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = (torch.empty((T, hidden), dtype=torch.float32, device=x.device),
+               torch.empty((T, topk), dtype=torch.int32, device=x.device),
+               torch.empty((T, topk), dtype=torch.float32, device=x.device))
+    y, ids, wts = out
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _need(x, 4 * T * hidden, "x")
+    _need(logits, 4 * T * E, "logits")
+    _need(ids, 4 * T * topk, "ids")
+    _need(wts, 4 * T * topk, "wts")
+    _need(y, 4 * T * hidden, "y")
+    _check(_lib.moe_ffn_routed_q4k_q6k(_p(gate), _p(up), _p(down), _p(x), _p(logits), _p(ids), _p(wts), _p(y),
+                                       _p(ws), ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
+                                       _stream(stream)), "moe_ffn_routed_q4k_q6k")
+    return y, ids, wts
 
 
 def moe_qmv_q4k_q8(bank, xq, xs, xsum, x_div, ids, nslots, n, k, E, y=None, stream=None):

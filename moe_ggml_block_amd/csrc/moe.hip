@@ -39,6 +39,10 @@ constexpr int MAX_E = 4096;
 constexpr int MAX_SLOTS = 2048;
 constexpr int WAVES = 4;
 constexpr int SMALL_E = 256;  // router: one workgroup per token up to this E
+constexpr int ROUTE_FUSED_E = 256;  // routing fused into the gather up to this E
+// and up to this many tokens: every workgroup routes every token, which
+// beat a separate router launch at 1 and 4 tokens and lost at 16 (measured)
+constexpr int ROUTE_FUSED_T = 8;
 // Row passes in flight per wave in the gathers: their row blocks are short
 // (a few passes per wave), so every pass of a block is requested up front.
 constexpr int MOE_RING = 2;
@@ -120,8 +124,71 @@ __global__ __launch_bounds__(256) void k_route_small(const float *__restrict__ l
     }
 }
 
-// Any E <= 4096: one wave per token, VPL keys per lane (lane l holds
-// experts l + 64 v); topk rounds of a wave-wide maximum of the keys.
+// Wave-wide maximum of an unsigned value through DPP row operations (the
+// reduction pattern of group_sum_last: the result lands in lane 63, then a
+// readlane makes it wave-uniform). 0 is the identity. Whole wave only.
+template <int CTRL, int ROW_MASK>
+QMV_DEV uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+    return v > t ? v : t;
+}
+QMV_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_u32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_u32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_u32<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max_u32<0x140, 0xF>(v);  // row_mirror
+    v = dpp_max_u32<0x142, 0xA>(v);  // row_bcast15 into rows 1, 3
+    v = dpp_max_u32<0x143, 0xC>(v);  // row_bcast31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One token routed by one wave (E <= 64 * VPL): lane l holds the order keys
+// (route_key's upper half: logit order, NaN as -inf, -0 as +0) of experts
+// l + 64 v. Each of the topk rounds takes the wave maximum of the keys, then
+// the lowest expert holding it (a maximum of the complemented index), and
+// removes that key; lane j keeps the j-th pick. Lane j < topk returns the
+// j-th expert and its renormalized weight. Call with the whole wave.
+template <int VPL>
+QMV_DEV void route_token_wave(const float *__restrict__ lg, int E, int topk, int lane, int *out_e, float *out_w) {
+    uint32_t ord[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + 64 * i;
+        ord[i] = e < E ? (uint32_t)(route_key(lg[e], e) >> 32) : 0u;  // padding below every key
+    }
+    uint32_t my_e = 0, my_ord = 0;
+    for (int j = 0; j < topk; ++j) {
+        uint32_t mo = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) mo = ord[i] > mo ? ord[i] : mo;
+        const uint32_t M = wave_max_u32(mo);
+        uint32_t c = 0;  // ~(lowest expert of this lane with key M)
+#pragma unroll
+        for (int i = VPL - 1; i >= 0; --i)
+            if (ord[i] == M) c = ~(uint32_t)(lane + 64 * i);
+        const uint32_t W = ~wave_max_u32(c);
+        if ((int)(W & 63) == lane) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                if ((int)(W >> 6) == i) ord[i] = 0;
+        }
+        if (lane == j) {
+            my_e = W;
+            my_ord = M;
+        }
+    }
+    // back from the order key to the logit
+    const uint32_t bits = (my_ord & 0x80000000u) ? (my_ord & 0x7FFFFFFFu) : ~my_ord;
+    const float my_v = __uint_as_float(bits);
+    const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    float p = 0.0f;
+    if (lane < topk) p = (lmax == -INFINITY) ? 1.0f : expf(my_v - lmax);
+    const float den = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum_last<64>(p)), 63));
+    *out_e = (int)my_e;
+    *out_w = p / den;
+}
+
+// Any E <= 4096: one wave per token.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_route_wave(const float *__restrict__ logits,
                                                     int32_t *__restrict__ ids,
@@ -129,41 +196,12 @@ __global__ __launch_bounds__(256) void k_route_wave(const float *__restrict__ lo
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (t >= T) return;
-    uint64_t key[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? route_key(logits[(size_t)t * E + e], e) : 0;
-    }
-    uint64_t my = 0;
-    for (int j = 0; j < topk; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint64_t o = __shfl_xor(best, off);
-            best = o > best ? o : best;
-        }
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (key[i] == best) key[i] = 0;  // keys are unique: only the winner
-        if (lane == j) my = best;
-    }
-    // back from the key to (expert, logit)
-    const int my_e = (int)~(uint32_t)my;
-    const uint32_t ord = (uint32_t)(my >> 32);
-    const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-    const float my_v = __uint_as_float(bits);
-    const float lmax = __shfl(my_v, 0);
-    float p = 0.0f;
-    if (lane < topk) p = (lmax == -INFINITY) ? 1.0f : expf(my_v - lmax);
-    float den = p;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    int e;
+    float w;
+    route_token_wave<VPL>(logits + (size_t)t * E, E, topk, lane, &e, &w);
     if (lane < topk) {
-        ids[(size_t)t * topk + lane] = my_e;
-        wts[(size_t)t * topk + lane] = p / den;
+        ids[(size_t)t * topk + lane] = e;
+        wts[(size_t)t * topk + lane] = w;
     }
 }
 
@@ -178,6 +216,12 @@ struct MoeArgs {
     const int32_t *ids;
     float *y;  // [nslots, n]; PAIR: [nslots, n/2]
     int nslots, n, k, E;
+    // fused routing (ids == nullptr): logits [nslots / topk, E] are routed
+    // here (E <= ROUTE_FUSED_E); workgroup 0 writes ids_out / wts_out
+    const float *logits;
+    int topk;
+    int32_t *ids_out;
+    float *wts_out;
 };
 
 // Dynamic LDS of k_moe: activation staging, ids (int16, -1 = out of
@@ -237,12 +281,32 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     for (int i = tid; i < pmax; i += 256) cnt[i] = 0;
     if (tid == 0) sh[1] = 0;
     __syncthreads();
-    for (int s = tid; s < a.nslots; s += 256) {
-        const int e = a.ids[s];
-        const bool ok = e >= 0 && e < a.E;
-        s_ids[s] = (int16_t)(ok ? e : -1);
-        if (ok) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-        else atomicAdd(&sh[1], 1);
+    if (a.logits) {
+        // fused routing: wave w routes tokens w, w + WAVES, ... (every
+        // workgroup routes all tokens; workgroup 0 publishes the result)
+        const int T = a.nslots / a.topk;
+        for (int t = wave; t < T; t += WAVES) {
+            int e;
+            float w;
+            route_token_wave<ROUTE_FUSED_E / 64>(a.logits + (size_t)t * a.E, a.E, a.topk, lane, &e, &w);
+            if (lane < a.topk) {
+                const int s = t * a.topk + lane;
+                s_ids[s] = (int16_t)e;
+                atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+                if (blockIdx.x == 0) {
+                    a.ids_out[s] = e;
+                    a.wts_out[s] = w;
+                }
+            }
+        }
+    } else {
+        for (int s = tid; s < a.nslots; s += 256) {
+            const int e = a.ids[s];
+            const bool ok = e >= 0 && e < a.E;
+            s_ids[s] = (int16_t)(ok ? e : -1);
+            if (ok) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+            else atomicAdd(&sh[1], 1);
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -768,6 +832,57 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
     hipStream_t s = (hipStream_t)stream;
     // h = silu(gate x) * (up x): one gather over interleaved gate/up rows
     rc = launch_gate_up<Q4KUnit>(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
+    if (rc) return rc;
+    DownArgs dn{};
+    dn.bank = static_cast<const uint8_t *>(down);
+    dn.h = h;
+    dn.ids = ids;
+    dn.wts = wts;
+    dn.y = y;
+    dn.n = (int)hidden;
+    dn.k = (int)inter;
+    dn.E = (int)E;
+    dn.topk = (int)topk;
+    dn.chunk = down_chunk<Q6KUnit>(inter, topk);
+    return launch_down<Q6KUnit>(dn, T, s);
+}
+
+// The layer with the router fused into the gate/up gather: every workgroup
+// of the gather routes the logits itself (softmax + top-k + renormalize,
+// the moe_route semantics, one wave per token) before it groups the slots by
+// expert, and workgroup 0 writes ids and wts for the down pass and the
+// caller. Above ROUTE_FUSED_E experts or ROUTE_FUSED_T tokens the router
+// runs as its own kernel first.
+extern "C" int moe_ffn_routed_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
+                                      const float *logits, int32_t *ids, float *wts, float *y, void *ws,
+                                      int64_t ws_bytes, int64_t T, int64_t topk, int64_t hidden, int64_t inter,
+                                      int64_t E, qmv_stream_t stream) {
+    if (!logits || topk > E || topk > 64) return QMV_EINVAL;
+    if (!aligned(logits, 4)) return QMV_EALIGN;
+    if (E > ROUTE_FUSED_E || T > ROUTE_FUSED_T) {
+        if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
+        const int rc = moe_route(logits, ids, wts, T, E, topk, stream);
+        if (rc) return rc;
+        return moe_ffn_q4k_q6k(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden, inter, E, stream);
+    }
+    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
+    if (T < 1 || topk < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
+    if (ws_bytes < moe_ffn_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
+    const int64_t ns = T * topk;
+    int rc = check_moe_args(gate, x, topk, ids, y, ns, 2 * inter, hidden, E);
+    if (rc) return rc;
+    rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
+    if (rc) return rc;
+    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 16)) return QMV_EALIGN;
+    float *h = static_cast<float *>(ws);
+    hipStream_t s = (hipStream_t)stream;
+    MoeArgs gu = gather_args(gate, up, x, topk, nullptr, h, ns, 2 * inter, hidden, E);
+    gu.logits = logits;
+    gu.topk = (int)topk;
+    gu.ids_out = ids;
+    gu.wts_out = wts;
+    rc = launch_gate_up<Q4KUnit>(gu, s);
     if (rc) return rc;
     DownArgs dn{};
     dn.bank = static_cast<const uint8_t *>(down);

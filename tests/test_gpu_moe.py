@@ -248,3 +248,46 @@ def test_qmm_full_config_sampled_rows(bm):
     ref = oracle.qmm("q4k", w, rq, rs, m, n, k, mrows=rows)
     assert scalerel(ref, Y[rows]) <= TOL, scalerel(ref, Y[rows])
     assert np.isfinite(Y).all()
+
+
+# ------------------------------------------------- router fused in the layer
+@pytest.mark.parametrize("T,E_,topk", [(1, 128, 8), (4, 128, 8), (8, 128, 8), (16, 128, 8), (33, 128, 8),
+                                       (3, 256, 64), (5, 300, 6), (2, 7, 7)])
+def test_routed_layer_matches_oracle(T, E_, topk):
+    """Router fused into the gate/up gather (E <= 256 and T <= 8; E = 300 and
+    T > 8 take the separate router): ids bit-exact, weights and y within 1e-4
+    of the oracle composition route -> layer."""
+    announce(f"routed layer T={T} E={E_} topk={topk}")
+    hidden, inter = (HIDDEN, INTER) if E_ == E else (512, 256)
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E_, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E_, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E_, hidden, inter)
+    x = synth.normal(synth.SEED_X, T * hidden).reshape(T, hidden)
+    lg = synth.moe_logits(T, E_, 2)
+    ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+    y_ref, _, _ = oracle.moe_ffn(gate, up, down, x, ids_ref, w_ref.astype(np.float32), T, topk, hidden, inter, E_)
+    y, ids, w = qmv.moe_ffn_routed_q4k_q6k(dev(gate), dev(up), dev(down), dev(x), dev(lg), T, topk, hidden, inter, E_)
+    assert np.array_equal(host(ids), ids_ref)
+    assert scalerel(w_ref, host(w)) <= TOL
+    assert scalerel(y_ref, host(y)) <= TOL, scalerel(y_ref, host(y))
+
+
+def test_routed_layer_ties_and_nan_logits():
+    T, E_, topk, hidden, inter = 6, 64, 4, 256, 256
+    gate = synth.moe_bank(synth.FMT_Q4K, 40, E_, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, 41, E_, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, 42, E_, hidden, inter)
+    x = synth.normal(43, T * hidden).reshape(T, hidden)
+    lg = np.round(synth.normal(44, T * E_).reshape(T, E_)).astype(np.float32)  # ties
+    lg[1, :] = 0.0
+    lg[2, ::3] = np.nan
+    lg[3, :] = -np.inf
+    lg[4, :] = -0.0
+    lg[4, 1::2] = 0.0
+    announce("routed layer ties/nan")
+    ids_ref, w_ref = oracle.moe_route(lg, T, E_, topk)
+    y_ref, _, _ = oracle.moe_ffn(gate, up, down, x, ids_ref, w_ref.astype(np.float32), T, topk, hidden, inter, E_)
+    y, ids, w = qmv.moe_ffn_routed_q4k_q6k(dev(gate), dev(up), dev(down), dev(x), dev(lg), T, topk, hidden, inter, E_)
+    assert np.array_equal(host(ids), ids_ref)
+    assert np.abs(host(w) - w_ref).max() <= TOL
+    assert scalerel(y_ref, host(y)) <= TOL
