@@ -548,11 +548,9 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 #define QMM_CFG256_BN 32
 #define QMM_CFG256_NT 512
 #endif
-// expert-indexed tiles: few rows per expert (BM 32 or 64), 128 columns
+// expert-indexed tiles: 64 rows (slots), 128 columns, eight waves; the
+// prefill layer also takes 32-row tiles at few slots per expert
 #define QMM_MOE32 32, 128, 64, 2, 2, 256
-#define QMM_MOE32_BM 32
-#define QMM_MOE32_BN 128
-#define QMM_MOE32_NT 256
 #define QMM_MOE64 64, 128, 64, 2, 2, 512
 #define QMM_MOE64_BM 64
 #define QMM_MOE64_BN 128
@@ -596,16 +594,12 @@ extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, 
     hipStream_t s = (hipStream_t)stream;
     QmmArgs a{static_cast<const uint8_t *>(bank), xq, xs, xsum, y, (int)nslots, (int)n, (int)k, ids, (int)E,
               (int)x_div};
-    // rows per tile from the mean slots per expert; the grid covers the
-    // largest possible tile count (every expert adds at most one partial
-    // tile) and the spare workgroups exit after the grouping
-    if (nslots <= 48 * E) {
-        const dim3 grid((unsigned)div_up(n, QMM_MOE32_BN), (unsigned)(div_up(nslots, QMM_MOE32_BM) + std::min(E, nslots)));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true>), grid, dim3(QMM_MOE32_NT), 0, s, a);
-    } else {
-        const dim3 grid((unsigned)div_up(n, QMM_MOE64_BN), (unsigned)(div_up(nslots, QMM_MOE64_BM) + std::min(E, nslots)));
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
-    }
+    // 64-row tiles (eight waves; faster than 32-row four-wave tiles even at
+    // 32 slots per expert, measured); the grid covers the largest possible
+    // tile count (every expert adds at most one partial tile) and the spare
+    // workgroups exit after the grouping
+    const dim3 grid((unsigned)div_up(n, QMM_MOE64_BN), (unsigned)(div_up(nslots, QMM_MOE64_BM) + std::min(E, nslots)));
+    hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
@@ -656,9 +650,11 @@ QMV_DEV uint2 q6x4_to_f16(uint32_t c) {
     return make_uint2(as_u32(as_h2(half_bytes_lo(c)) + off), as_u32(as_h2(half_bytes_hi(c)) + off));
 }
 
-template <int BM, int BN, int MT, int NT, int NTHREADS, int ACT, bool MOE, bool TABLE = false>
+template <int BM, int BN, int MT, int NT, int NTHREADS, int ACT, bool MOE, bool TABLE = false, int KP = 64>
 __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
-    constexpr int KP = 64;                       // values per phase: a quarter superblock
+    // KP values per phase: a quarter (64) or half (128) superblock
+    static_assert(KP == 64 || KP == 128, "phase length");
+    constexpr int PPS = 256 / KP;                // phases per superblock
     constexpr int WM = 16 * MT, WN = 16 * NT;
     constexpr int WGM = BM / WM, WGN = BN / WN;
     static_assert(WGM * WGN == NTHREADS / 64, "the waves tile the workgroup");
@@ -733,7 +729,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
     float rxs[2][XC];
 
     auto prefetch = [&](int ph, int q) {
-        const int k0 = ph * KP, s = k0 / 256, p4 = ph & 3, hh = p4 >> 1;
+        const int k0 = ph * KP, s = k0 / 256, pi = ph % PPS;
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int c = (tid + NTHREADS * i) % ACR, gm = arow[i];
@@ -748,12 +744,13 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
             const uint8_t *blk = wrow + (size_t)s * 210;
 #pragma unroll
             for (int i = 0; i < BCT; ++i) {
-                const int bc = bc0 + i * (NTHREADS / BN);  // 0..7
-                const int gl = bc >> 2, l0 = 8 * (bc & 3);
-                rql[q][i] = *reinterpret_cast<const uint2 *>(blk + 64 * hh + 32 * gl + l0);
-                rqh[q][i] = *reinterpret_cast<const uint2 *>(blk + 128 + 32 * hh + l0);
+                // values e0..e0+7 of the superblock: half h, 32-run g, position l0
+                const int e0 = KP * pi + 8 * (bc0 + i * (NTHREADS / BN));
+                const int h = e0 >> 7, g = (e0 >> 5) & 3, l0 = e0 & 31;
+                rql[q][i] = *reinterpret_cast<const uint2 *>(blk + 64 * h + 32 * (g & 1) + l0);
+                rqh[q][i] = *reinterpret_cast<const uint2 *>(blk + 128 + 32 * h + l0);
             }
-            if (p4 == 0 && bc0 == 0) {
+            if (pi == 0 && bc0 == 0) {
                 rsc[q] = *reinterpret_cast<const uint4 *>(blk + 192);
                 rd[q] = ld2(blk + 208);
             }
@@ -768,7 +765,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
     };
 
     auto convert_store = [&](int ph, int buf, int q) {
-        const int p4 = ph & 3, odd = p4 & 1, sp = (ph >> 2) & 1;
+        const int pi = ph % PPS, sp = (ph / PPS) & 1;
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int ch = tid + NTHREADS * i, row = ch / ACR, c = ch % ACR;
@@ -798,7 +795,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
                 *reinterpret_cast<uint4 *>(&As[0][buf][row * ST + 8 * c]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
             }
         }
-        if (p4 == 0 && bc0 == 0) {
+        if (pi == 0 && bc0 == 0) {
             const uint4 s4 = rsc[q];
             const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -808,14 +805,14 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
         }
 #pragma unroll
         for (int i = 0; i < BCT; ++i) {
-            const int bc = bc0 + i * (NTHREADS / BN);
-            const int gl = bc >> 2, l0 = 8 * (bc & 3);
-            const int sh = 4 * odd + 2 * gl;  // qh bit pair of this 32-run
+            const int el = 8 * (bc0 + i * (NTHREADS / BN));  // position in the phase
+            const int g = ((KP * pi + el) >> 5) & 3;
+            const int nsh = 4 * (g >> 1), sh = 2 * g;  // nibble of ql, bit pair of qh for run g
             const uint2 ql = rql[q][i], qh = rqh[q][i];
-            const uint32_t c0 = ((ql.x >> (4 * odd)) & 0x0F0F0F0Fu) | (((qh.x >> sh) & 0x03030303u) << 4);
-            const uint32_t c1 = ((ql.y >> (4 * odd)) & 0x0F0F0F0Fu) | (((qh.y >> sh) & 0x03030303u) << 4);
+            const uint32_t c0 = ((ql.x >> nsh) & 0x0F0F0F0Fu) | (((qh.x >> sh) & 0x03030303u) << 4);
+            const uint32_t c1 = ((ql.y >> nsh) & 0x0F0F0F0Fu) | (((qh.y >> sh) & 0x03030303u) << 4);
             const uint2 f0 = q6x4_to_f16(c0), f1 = q6x4_to_f16(c1);
-            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 32 * gl + l0]) = make_uint4(f0.x, f0.y, f1.x, f1.y);
+            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + el]) = make_uint4(f0.x, f0.y, f1.x, f1.y);
         }
         if constexpr (ACT == ACT_Q8) {
 #pragma unroll
@@ -835,16 +832,16 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
             out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
 
-    const int nph = k / KP;  // a multiple of 4
+    const int nph = k / KP;  // even
     prefetch(0, 0);
     convert_store(0, 0, 0);
     prefetch(1, 1);
-    prefetch(2, 0);
+    if (nph > 2) prefetch(2, 0);
     __syncthreads();
     for (int ph0 = 0; ph0 < nph; ph0 += 2) {
 #pragma unroll
         for (int Q = 0; Q < 2; ++Q) {
-            const int ph = ph0 + Q, buf = Q, p4 = ph & 3, sp = (ph >> 2) & 1;
+            const int ph = ph0 + Q, buf = Q, pi = ph % PPS, sp = (ph / PPS) & 1;
 #pragma unroll
             for (int bl = 0; bl < NBP; ++bl) {
                 v4f T[2][MT][NT];
@@ -869,7 +866,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
                             T[sb][t][u] = r;
                         }
                 }
-                const int sub = 4 * p4 + 2 * bl;  // first sub-block of this q8 block in the superblock
+                const int sub = (KP * pi) / 16 + 2 * bl;  // first sub-block of this q8 block in the superblock
 #pragma unroll
                 for (int u = 0; u < NT; ++u) {
                     const int c = wn * WN + 16 * u + li;
@@ -882,7 +879,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
                     }
                 }
             }
-            if (p4 == 3) {
+            if (pi == PPS - 1) {
 #pragma unroll
                 for (int u = 0; u < NT; ++u) {
                     const float dcol = sd[sp][wn * WN + 16 * u + li];
@@ -917,10 +914,24 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
         }
 }
 
-// Q6_K tile configurations: dense (64 x 128, 512 threads) and expert-indexed
-// (32 x 128, 256 threads)
+// Q6_K tile configurations (BM, BN, MT, NT, threads), measured at the MoE
+// prefill down shape (4,096 slots, [2048, 768] experts): eight-wave tiles
+// were 1.4x faster than four-wave 32 x 128 tiles, and 128-value phases
+// slower than 64-value ones.
 #define QMM6_DENSE 64, 128, 2, 2, 512
-#define QMM6_MOE 32, 128, 2, 2, 256
+#define QMM6_MOE 64, 128, 2, 2, 512    // expert-indexed, q8 activation
+#define QMM6_MOE_BM 64
+#define QMM6_MOE_BN 128
+#define QMM6_MOE_NT 512
+#ifndef QMM6_MOEF                       // expert-indexed, f32 activation
+#define QMM6_MOEF 64, 128, 2, 2, 512
+#define QMM6_MOEF_BM 64
+#define QMM6_MOEF_BN 128
+#define QMM6_MOEF_NT 512
+#define QMM6_MOEF_KP 64
+#endif
+#define QMM6_PF64 64, 128, 2, 2, 512   // the prefill layer's down projection, 64-slot tiles
+#define QMM6_PF32 32, 256, 2, 2, 512   // and 32-slot tiles
 
 int check_q6k_shape(int64_t n, int64_t k) {
     if (n < 1 || k < 256 || k % 256) return QMV_EINVAL;
@@ -965,8 +976,8 @@ extern "C" int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, 
     if (!aligned(xq, 16) || !aligned(xs, 4)) return QMV_EALIGN;
     Qmm6Args a{static_cast<const uint8_t *>(bank), xq, xs, nullptr, y, (int)nslots, (int)n, (int)k, ids, (int)E,
                (int)x_div};
-    const dim3 grid((unsigned)div_up(n, 128), (unsigned)(div_up(nslots, 32) + std::min(E, nslots)));
-    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_Q8, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    const dim3 grid((unsigned)div_up(n, QMM6_MOE_BN), (unsigned)(div_up(nslots, QMM6_MOE_BM) + std::min(E, nslots)));
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_Q8, true>), grid, dim3(QMM6_MOE_NT), 0, (hipStream_t)stream, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
@@ -979,8 +990,9 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
     if (!aligned(x, 16)) return QMV_EALIGN;
     Qmm6Args a{static_cast<const uint8_t *>(bank), nullptr, nullptr, x, y, (int)nslots, (int)n, (int)k, ids, (int)E,
                (int)x_div};
-    const dim3 grid((unsigned)div_up(n, 128), (unsigned)(div_up(nslots, 32) + std::min(E, nslots)));
-    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_F32, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    const dim3 grid((unsigned)div_up(n, QMM6_MOEF_BN), (unsigned)(div_up(nslots, QMM6_MOEF_BM) + std::min(E, nslots)));
+    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOEF, ACT_F32, true, false, QMM6_MOEF_KP>), grid, dim3(QMM6_MOEF_NT), 0,
+                       (hipStream_t)stream, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
@@ -995,7 +1007,10 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
 // slots in slot order.
 namespace {
 
-constexpr int PF_BM = 32;  // slots per tile in the layer
+// Slots per tile in the layer (both projections share the tile table): 32
+// below a mean of 32 slots per expert, else 64 (measured: the 64-slot
+// eight-wave tiles were faster from 32 slots per expert up, the 32-slot ones
+// at 8).
 
 // One workgroup builds the tile table: per-expert slot counts (LDS
 // atomics), an exclusive prefix of the per-expert tile counts, the tile ->
@@ -1075,10 +1090,11 @@ struct PrefillWs {
     int64_t bytes;
 };
 
-int64_t pf_max_tiles(int64_t S, int64_t E) { return div_up(S, PF_BM) + std::min(E, S); }
+int pf_bm(int64_t S, int64_t E) { return S < 32 * E ? 32 : 64; }
+int64_t pf_max_tiles(int64_t S, int64_t E, int bm) { return div_up(S, bm) + std::min(E, S); }
 
 PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E) {
-    const int64_t S = T * topk, mt = pf_max_tiles(S, E);
+    const int64_t S = T * topk, bm = pf_bm(S, E), mt = pf_max_tiles(S, E, (int)bm);
     PrefillWs w{};
     int64_t o = 0;
     auto take = [&](int64_t nbytes) {
@@ -1091,7 +1107,7 @@ PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int
     w.xsum = reinterpret_cast<float *>(take(4 * T * (hidden / 32)));
     w.ntiles = reinterpret_cast<int *>(take(4));
     w.tile_e = reinterpret_cast<int *>(take(4 * mt));
-    w.tile_slots = reinterpret_cast<int *>(take(4 * mt * PF_BM));
+    w.tile_slots = reinterpret_cast<int *>(take(4 * mt * bm));
     w.h = reinterpret_cast<float *>(take(4 * S * inter));
     w.d = reinterpret_cast<float *>(take(4 * S * hidden));
     w.bytes = o;
@@ -1122,21 +1138,33 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
     const PrefillWs w = prefill_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter, E);
-    const int64_t mt = pf_max_tiles(S, E);
+    const int bm = pf_bm(S, E);
+    const int64_t mt = pf_max_tiles(S, E, bm);
     int rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
     if (rc != QMV_OK) return rc;
-    hipLaunchKernelGGL((k_group_tiles<PF_BM>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                       w.tile_slots);
-    QMV_LAUNCH_CHECK();
     QmmArgs gu{static_cast<const uint8_t *>(gate), w.xq, w.xs, w.xsum, w.h, (int)S, (int)inter, (int)hidden, ids,
                (int)E, (int)topk, w.ntiles, w.tile_e, w.tile_slots, static_cast<const uint8_t *>(up)};
-    hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, QMM_MOE32_BN / 2),
-                       (unsigned)mt), dim3(QMM_MOE32_NT), 0, s, gu);
-    QMV_LAUNCH_CHECK();
     Qmm6Args dn{static_cast<const uint8_t *>(down), nullptr, nullptr, w.h, w.d, (int)S, (int)hidden, (int)inter, ids,
                 (int)E, 1, w.ntiles, w.tile_e, w.tile_slots};
-    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 128), (unsigned)mt),
-                       dim3(256), 0, s, dn);
+    if (bm == 32) {
+        hipLaunchKernelGGL((k_group_tiles<32>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
+                           w.tile_slots);
+        QMV_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt),
+                           dim3(256), 0, s, gu);
+        QMV_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF32, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 256), (unsigned)mt),
+                           dim3(512), 0, s, dn);
+    } else {
+        hipLaunchKernelGGL((k_group_tiles<64>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
+                           w.tile_slots);
+        QMV_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true, true, true>), dim3((unsigned)div_up(inter, QMM_MOE64_BN / 2),
+                           (unsigned)mt), dim3(QMM_MOE64_NT), 0, s, gu);
+        QMV_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF64, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 128), (unsigned)mt),
+                           dim3(512), 0, s, dn);
+    }
     QMV_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)div_up(hidden, 1024), (unsigned)T), dim3(256), 0, s, w.d, ids,
                        wts, y, (int)topk, (int)hidden, (int)E);

@@ -61,7 +61,7 @@ def test_moe_qmm_prefill_layer_shape_routed():
 @pytest.mark.parametrize("case", ["one_expert_many_tiles", "id_chunks", "bm64", "max_experts", "single"])
 def test_moe_qmm_edges(case):
     if case == "one_expert_many_tiles":
-        # 70 slots of one expert (three row tiles, the last ragged), two
+        # 70 slots of one expert (two 64-row tiles, the last ragged), two
         # out-of-range ids, ragged columns
         ids = np.array([3] * 33 + [-1] + [3] * 37 + [5], dtype=np.int32)
         args = (ids, 200, 256, 5, 1, 74)
@@ -70,7 +70,7 @@ def test_moe_qmm_edges(case):
         ids = ((np.arange(5000) * 3) % 7).astype(np.int32)
         args = (ids, 64, 512, 7, 2, 76)
     elif case == "bm64":
-        # many slots per expert: the 64-row tiles
+        # many slots per expert: several full 64-row tiles per expert
         ids = (np.arange(256) % 4).astype(np.int32)[::-1].copy()
         args = (ids, 128, 512, 4, 1, 78)
     elif case == "max_experts":
