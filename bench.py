@@ -286,10 +286,9 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
                         "routed_layer_us": round(ms_rt * 1e3, 3),
                         "routed_tokens_per_s": round(T / (ms_rt * 1e-3), 1),
                         "unique_experts": u, "gbs_unique_experts": round(u * per_expert / (ms * 1e-3) / 1e9, 1)}
-    del bg, bu, bd, G, U, D
-    torch.cuda.empty_cache()
     # router gate GEMV + router from the activations (a cold router matrix per
-    # call: more copies than the last-level cache holds)
+    # call: more copies than the last-level cache holds), and the whole MoE
+    # block from the hidden state (gate GEMV + layer with the fused router)
     wr_host = synth.router_weights(E, hidden)
     br, R = rotated(wr_host.view(np.uint8), 320)
     for T in (1, 4, 16):
@@ -299,7 +298,15 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
         ms = time_graph(lambda i: qmv.moe_gate_route(R[i % 320], x, T, E, hidden, topk, out=bufs), 320, 5)
         out[f"T{T}"]["gate_route_us"] = round(ms * 1e3, 3)
         out[f"T{T}"]["gate_route_gbs"] = round(wr_host.nbytes / (ms * 1e-3) / 1e9, 1)
-    del br, R
+        y = torch.empty((T, hidden), device="cuda")
+        ws = torch.empty(qmv.moe_ffn_workspace_bytes(T, topk, hidden, inter), dtype=torch.uint8, device="cuda")
+        blk = (y,) + bufs
+        ms_b = time_graph(lambda i: qmv.moe_block_q4k_q6k(R[i % 320], G[i % bank_copies], U[i % bank_copies],
+                                                          D[i % bank_copies], x, T, topk, hidden, inter, E, out=blk,
+                                                          ws=ws), 2 * 48, 5)
+        out[f"T{T}"]["block_us"] = round(ms_b * 1e3, 3)
+        out[f"T{T}"]["block_tokens_per_s"] = round(T / (ms_b * 1e-3), 1)
+    del br, R, bg, bu, bd, G, U, D
     torch.cuda.empty_cache()
     return out
 

@@ -138,6 +138,16 @@ int moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t 
 int moe_gate_route(const float *wr, const float *x, float *logits, int32_t *ids, float *wts, int64_t T,
                    int64_t E, int64_t hidden, int64_t topk, qmv_stream_t stream);
 
+/* The MoE block from the hidden state: the router gate GEMV above (logits
+ * written to `logits`), then moe_ffn_routed_q4k_q6k on those logits (router
+ * fused into the gate/up gather; ids, wts written). Three launches. Operands
+ * and limits as moe_gate_route and moe_ffn_q4k_q6k (hidden is both the
+ * router's and the layer's input width; ws: moe_ffn_workspace_bytes()). All
+ * checks run before the first launch. */
+int moe_block_q4k_q6k(const float *wr, const void *gate, const void *up, const void *down, const float *x,
+                      float *logits, int32_t *ids, float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T,
+                      int64_t topk, int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Expert-gather matvec over a resident bank (`moe_matvec_gpu`):
  *   y[s, r] = sum_c W[ids[s], r, c] * x[s / x_div, c],  s < nslots, r < n.

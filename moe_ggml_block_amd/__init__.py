@@ -49,6 +49,7 @@ _SIGS = {
     "moe_qmv_q6k_q8": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k_q8": [_vp] * 8 + [_i64] * 6 + [_vp],
     "moe_ffn_routed_q4k_q6k": [_vp] * 9 + [_i64] * 6 + [_vp],
+    "moe_block_q4k_q6k": [_vp] * 10 + [_i64] * 6 + [_vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -342,6 +343,31 @@ def moe_ffn_routed_q4k_q6k(gate, up, down, x, logits, T, topk, hidden, inter, E,
                                        _p(ws), ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
                                        _stream(stream)), "moe_ffn_routed_q4k_q6k")
     return y, ids, wts
+
+
+def moe_block_q4k_q6k(wr, gate, up, down, x, T, topk, hidden, inter, E, out=None, ws=None, stream=None):
+    """The MoE block from the hidden state: router gate GEMV + routed layer -> (y, logits, ids, wts)."""
+    nb = moe_ffn_workspace_bytes(T, topk, hidden, inter)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = (torch.empty((T, hidden), dtype=torch.float32, device=x.device),
+               torch.empty((T, E), dtype=torch.float32, device=x.device),
+               torch.empty((T, topk), dtype=torch.int32, device=x.device),
+               torch.empty((T, topk), dtype=torch.float32, device=x.device))
+    y, logits, ids, wts = out
+    _need(wr, 4 * E * hidden, "wr")
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _need(x, 4 * T * hidden, "x")
+    for t_, nbytes, nm in ((logits, 4 * T * E, "logits"), (ids, 4 * T * topk, "ids"), (wts, 4 * T * topk, "wts"),
+                           (y, 4 * T * hidden, "y")):
+        _need(t_, nbytes, nm)
+    _check(_lib.moe_block_q4k_q6k(_p(wr), _p(gate), _p(up), _p(down), _p(x), _p(logits), _p(ids), _p(wts), _p(y),
+                                  _p(ws), ws.numel() * ws.element_size(), T, topk, hidden, inter, E,
+                                  _stream(stream)), "moe_block_q4k_q6k")
+    return y, logits, ids, wts
 
 
 def moe_qmv_q4k_q8(bank, xq, xs, xsum, x_div, ids, nslots, n, k, E, y=None, stream=None):

@@ -144,17 +144,8 @@ void launch_gate(const float *w, const float *x, float *logits, int64_t T, int64
                        (int)E, (int)hidden, (int)tc, (int)nchunks);
 }
 
-}  // namespace
-
-extern "C" int moe_gate_route(const float *wr, const float *x, float *logits, int32_t *ids, float *wts,
-                              int64_t T, int64_t E, int64_t hidden, int64_t topk, qmv_stream_t stream) {
-    if (!wr || !x || !logits || !ids || !wts || T < 1 || E < 1 || hidden < 4 || hidden % 4 || topk < 1 ||
-        topk > E || topk > 64)
-        return QMV_EINVAL;
-    if (E > GATE_MAX_E || hidden > GATE_MAX_HIDDEN || T > (1 << 24)) return QMV_EUNSUPPORTED;
-    if (!aligned(wr, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(wts, 4))
-        return QMV_EALIGN;
-    hipStream_t s = (hipStream_t)stream;
+// logits = x Wr^T (all checks done by the caller)
+int launch_logits(const float *wr, const float *x, float *logits, int64_t T, int64_t E, int64_t hidden, hipStream_t s) {
     const int64_t nv64 = (hidden / 4 + 63) / 64;  // float4s per lane
     if (nv64 <= 1) launch_gate<1>(wr, x, logits, T, E, hidden, s);
     else if (nv64 <= 2) launch_gate<2>(wr, x, logits, T, E, hidden, s);
@@ -163,5 +154,46 @@ extern "C" int moe_gate_route(const float *wr, const float *x, float *logits, in
     else if (nv64 <= 16) launch_gate<16>(wr, x, logits, T, E, hidden, s);
     else launch_gate<32>(wr, x, logits, T, E, hidden, s);
     QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+int check_gate(const float *wr, const float *x, const float *logits, const int32_t *ids, const float *wts, int64_t T,
+               int64_t E, int64_t hidden, int64_t topk) {
+    if (!wr || !x || !logits || !ids || !wts || T < 1 || E < 1 || hidden < 4 || hidden % 4 || topk < 1 ||
+        topk > E || topk > 64)
+        return QMV_EINVAL;
+    if (E > GATE_MAX_E || hidden > GATE_MAX_HIDDEN || T > (1 << 24)) return QMV_EUNSUPPORTED;
+    if (!aligned(wr, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(wts, 4))
+        return QMV_EALIGN;
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_gate_route(const float *wr, const float *x, float *logits, int32_t *ids, float *wts,
+                              int64_t T, int64_t E, int64_t hidden, int64_t topk, qmv_stream_t stream) {
+    int rc = check_gate(wr, x, logits, ids, wts, T, E, hidden, topk);
+    if (rc) return rc;
+    rc = launch_logits(wr, x, logits, T, E, hidden, (hipStream_t)stream);
+    if (rc) return rc;
     return moe_route(logits, ids, wts, T, E, topk, stream);
+}
+
+// The MoE block from the hidden state: router gate GEMV, then the layer with
+// the router fused into its gate/up gather (moe_ffn_routed_q4k_q6k).
+extern "C" int moe_block_q4k_q6k(const float *wr, const void *gate, const void *up, const void *down, const float *x,
+                                 float *logits, int32_t *ids, float *wts, float *y, void *ws, int64_t ws_bytes,
+                                 int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
+                                 qmv_stream_t stream) {
+    int rc = check_gate(wr, x, logits, ids, wts, T, E, hidden, topk);
+    if (rc) return rc;
+    // the layer's own checks before anything is launched
+    if (!gate || !up || !down || !y || !ws || hidden < 256 || inter < 256 || hidden % 256 || inter % 256)
+        return QMV_EINVAL;
+    if (ws_bytes < moe_ffn_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
+    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    rc = launch_logits(wr, x, logits, T, E, hidden, (hipStream_t)stream);
+    if (rc) return rc;
+    return moe_ffn_routed_q4k_q6k(gate, up, down, x, logits, ids, wts, y, ws, ws_bytes, T, topk, hidden, inter, E,
+                                  stream);
 }

@@ -130,3 +130,35 @@ def test_gate_route_rejects_bad_arguments():
         qmv.moe_gate_route(W, X, 2, 8, 64, 9)  # topk > E
     with pytest.raises(qmv.QmvError):
         qmv.moe_gate_route(W, X, 2, 8, 62, 2)  # hidden % 4
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_moe_block_from_hidden_state(T):
+    """Router gate GEMV + the layer with the fused router (three launches)
+    against the oracle chain gemv -> route -> layer. Ids: identical to the
+    router kernel on the device's own logits; against the oracle wherever the
+    logit gaps exceed twice the summation bound (then y too, per token)."""
+    E, hidden, inter, topk = 128, 2048, 768, 8
+    announce(f"moe block T={T}")
+    W = synth.router_weights(E, hidden)
+    X = synth.normal(synth.SEED_X, T * hidden).reshape(T, hidden)
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, hidden, inter)
+    y, lg, ids, w = qmv.moe_block_q4k_q6k(dev(W), dev(gate), dev(up), dev(down), dev(X), T, topk, hidden, inter, E)
+    g_y, g_lg, g_ids = host(y), host(lg), host(ids)
+    lg_ref, ids_ref, w_ref = oracle.gate_route(W, X, T, E, hidden, topk)
+    assert scalerel(lg_ref, g_lg) <= TOL
+    ids2, _ = qmv.moe_route(lg, T, E, topk)
+    assert np.array_equal(host(ids2), g_ids)
+    bnd = _bound(W, X)
+    y_ref, _, _ = oracle.moe_ffn(gate, up, down, X, ids_ref, w_ref.astype(np.float32), T, topk, hidden, inter, E)
+    compared = 0
+    for t in range(T):
+        tol = 2.0 * bnd[t].max() + 2.0 * np.spacing(np.float32(np.abs(lg_ref[t]).max()))
+        nxt = np.sort(lg_ref[t])[::-1][: topk + 1]
+        if (-np.diff(nxt)).min() > tol:
+            assert np.array_equal(g_ids[t], ids_ref[t])
+            assert scalerel(y_ref[t], g_y[t]) <= TOL
+            compared += 1
+    assert compared >= (T + 1) // 2
