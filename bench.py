@@ -160,10 +160,17 @@ def headline(steps: int, warmup: int, copies: int):
     xsum = torch.empty(K2 // 32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    # a step: the f32-activation matvec, the q8 activation quantizer and the
+    # int8-dot matvec; the same work with the quantizer inside the int8
+    # matvec's kernel (qmv_q4k_q8x, one launch) is timed below as well
     def step(i):
         qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
         qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum))
         qmv.qmv_q4k_q8(W[(i + copies // 2) % copies], xq, xs, xsum, N2, K2, y=y8)
+
+    def step_fused(i):
+        qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
+        qmv.qmv_q4k_q8x(W[(i + copies // 2) % copies], x, N2, K2, y=y8)
 
     # one graph holds `copies` steps (every weight copy once per matvec);
     # the timed region replays it until exactly `steps` steps have run.
@@ -190,6 +197,8 @@ def headline(steps: int, warmup: int, copies: int):
     k_f32 = q4k_ms
     k_qa = time_graph(lambda i: qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum)), 128, 10)
     k_q8 = time_graph(lambda i: qmv.qmv_q4k_q8(W[i % copies], xq, xs, xsum, N2, K2, y=y8), 4 * copies, 10)
+    k_q8x = time_graph(lambda i: qmv.qmv_q4k_q8x(W[i % copies], x, N2, K2, y=y8), 4 * copies, 10)
+    ms_fused = time_graph(step_fused, copies, 10)
     k_f32_warm = time_graph(lambda i: qmv.qmv_q4k(W[0], x, N2, K2, y=y), 128, 10)
     k_q8_warm = time_graph(lambda i: qmv.qmv_q4k_q8(W[0], xq, xs, xsum, N2, K2, y=y8), 128, 10)
     del big, W
@@ -205,6 +214,9 @@ def headline(steps: int, warmup: int, copies: int):
             "qmv_q4k_q8_cold_us": round(k_q8 * 1e3, 3),
             "qmv_q4k_q8_cold_gbs": round(Q4K_BYTES / k_q8 / 1e6, 1),
             "qmv_q4k_q8_warm_gbs": round(Q4K_BYTES / k_q8_warm / 1e6, 1),
+            "qmv_q4k_q8x_cold_us": round(k_q8x * 1e3, 3),
+            "qmv_q4k_q8x_cold_gbs": round(Q4K_BYTES / k_q8x / 1e6, 1),
+            "step_with_quantizer_in_kernel_us": round(ms_fused * 1e3, 3),
         },
     }
 

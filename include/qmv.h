@@ -104,6 +104,15 @@ int quantize_act_q8(const float *x, int8_t *xq, float *xs, float *xsum, int64_t 
 int qmv_q4k_q8(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
                int64_t n, int64_t k, qmv_stream_t stream);
 
+/* The same int8-dot Q4_K matvec from an f32 activation in one launch: every
+ * workgroup quantizes x itself (the steps of quantize_act_q8, so the codes
+ * and scales are the same bits) while staging it, then decodes as
+ * qmv_q4k_q8 -- y is bit-identical to quantize_act_q8 followed by
+ * qmv_q4k_q8 (`matvec_q4k_gpu_off` quantizes x once per call and runs the
+ * int8-dot decode). w: n*(k/256)*144 bytes; x: f32[k]; y: f32[n];
+ * k % 256 == 0, k <= 8192; w and x 16-byte aligned. */
+int qmv_q4k_q8x(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream);
+
 /* Debug export of the integer part of qmv_q4k_q8: sums[r, b] = S[r, b]
  * (int32[n, k/32]) computed by the same dot4 sequence as qmv_q4k_q8. */
 int qmv_debug_blocksums_q4k_q8(const void *w, const int8_t *xq, int32_t *sums, int64_t n,

@@ -33,6 +33,7 @@ _SIGS = {
     "qmv_q5k": [_vp, _vp, _vp, _i64, _i64, _vp],
     "quantize_act_q8": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q4k_q8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q4k_q8x": [_vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_debug_blocksums_q4k_q8": [_vp, _vp, _vp, _i64, _i64, _vp],
     "moe_route": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "moe_gate_route": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
@@ -156,6 +157,11 @@ def qmv_q4k_q8(w, xq, xs, xsum, n, k, y=None, stream=None):
         y = torch.empty(n, dtype=torch.float32, device=xq.device)
     _check(_lib.qmv_q4k_q8(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), n, k, _stream(stream)), "qmv_q4k_q8")
     return y
+
+
+def qmv_q4k_q8x(w, x, n, k, y=None, stream=None):
+    """int8-dot Q4_K matvec from an f32 activation, quantized inside the kernel."""
+    return _dense("qmv_q4k_q8x", "q4k", w, x, n, k, y, stream)
 
 
 def qmv_debug_blocksums_q4k_q8(w, xq, n, k, stream=None):

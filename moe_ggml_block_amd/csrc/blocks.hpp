@@ -526,6 +526,61 @@ QMV_DEV void q4k_q8_sums(const Q4KUnit::Raw &R, const int32_t *xq16, int32_t *sl
     *shi = b;
 }
 
+// q8 activation quantizer, one lane's four values of a 32-value block held
+// by eight consecutive lanes (lane groups aligned to 8; every lane of the
+// wave must call it). Every f32 step is one IEEE operation with
+// round-to-nearest (correctly rounded division, the product x*inv rounded to
+// f32 before the half-away rounding), so codes and scales equal any IEEE
+// implementation's. Returns the four codes packed in a dword; *scale and
+// *xsum are the block's xs and xs * sum(xq).
+// Reductions over aligned groups of 8 lanes with DPP (no LDS crossbar):
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], then row_half_mirror, which
+// pairs each lane with one of the other quad; every lane gets the result.
+// fmaxf ignores NaN in any order, so the maximum does not depend on it.
+template <int CTRL>
+QMV_DEV float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+QMV_DEV int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+QMV_DEV float group8_max(float a) {
+    a = fmaxf(a, dpp_f<0xB1>(a));
+    a = fmaxf(a, dpp_f<0x4E>(a));
+    return fmaxf(a, dpp_f<0x141>(a));
+}
+QMV_DEV int group8_sum(int s) {
+    s += dpp_i<0xB1>(s);
+    s += dpp_i<0x4E>(s);
+    return s + dpp_i<0x141>(s);
+}
+
+QMV_DEV uint32_t quantize_q8_lanes(float4 v, float *scale, float *xsum) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = group8_max(a);
+    float inv = 0.0f, sc = 1.0f;
+    if (a > 0.0f) {
+        inv = __fdiv_rn(127.0f, a);
+        sc = __fdiv_rn(a, 127.0f);
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    int q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float prod = __fmul_rn(vv[i], inv);
+        asm volatile("" : "+v"(prod));  // materialize the rounded f32 product
+        float r = roundf(prod);         // half away from zero
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q[i] = (int)r;
+    }
+    const int s = group8_sum((q[0] + q[1]) + (q[2] + q[3]));
+    *scale = sc;
+    *xsum = __fmul_rn(sc, (float)s);
+    return (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+           ((uint32_t)(q[3] & 0xFF) << 24);
+}
+
 struct Q4KQ8Unit {
     static constexpr bool Q8 = true;  // activation: q8 rows (xq, xs, xsum)
     static constexpr int BW = 256, BB = 144;
@@ -690,4 +745,50 @@ struct Q6KQ8Unit {
         r = fmaf(c3, X.xs[3] * (float)S[3], r);
         return h2f(R.d) * r;
     }
+};
+
+// ---------------------------------------- Q4_K x q8, quantizing in-kernel ---
+// The Q4KQ8Unit decode with the activation given in f32: every workgroup
+// quantizes x itself while staging it (the same IEEE steps as
+// quantize_act_q8, so the codes and scales are the same bits) straight into
+// the q8 unit layout in LDS. One launch instead of quantizer + matvec.
+struct Q4KQ8XUnit {
+    static constexpr bool Q8 = false;  // takes f32 rows
+    static constexpr int BW = 256, BB = 144;
+    static constexpr int RING = QMV_RING_Q4KQ8;
+    static constexpr int MAX_WG_PER_CU = 3;
+    static constexpr int ACT_STRIDE = Q4KQ8Unit::ACT_STRIDE;
+    using Act = ActF32;
+    using X = UnitQ8;
+    using Raw = Q4KUnit::Raw;
+    using Stage = StageRegs;
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) { Q4KUnit::load(R, row, u); }
+    template <int NS>
+    static __device__ __forceinline__ void fetch(Stage &S, ActF32 a, int k) { fetch_x<NS>(S, a.x, k); }
+    // float4 i of x (values 4i..4i+3) -> codes at dword i % 16 of unit i / 16;
+    // the block b = i / 8 scale and dequantized sum at slots 16 + b % 2 and
+    // 18 + b % 2 of unit b / 2 (the Q4KQ8Unit layout)
+    template <int NS>
+    static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) {
+        uint32_t *l = reinterpret_cast<uint32_t *>(xl);
+        const int n4 = k / 4;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int i = (int)threadIdx.x + 256 * m;  // lanes past n4 form whole groups of 8
+            float sc, xsum;
+            const f32x4 v = S[m];
+            const uint32_t packed = quantize_q8_lanes(make_float4(v.x, v.y, v.z, v.w), &sc, &xsum);
+            if (i < n4) {
+                l[ACT_STRIDE * (i >> 4) + (i & 15)] = packed;
+                if ((i & 7) == 0) {
+                    const int b = i >> 3;
+                    xl[ACT_STRIDE * (b >> 1) + 16 + (b & 1)] = sc;
+                    xl[ACT_STRIDE * (b >> 1) + 18 + (b & 1)] = xsum;
+                }
+            }
+        }
+    }
+    static __device__ __forceinline__ void load_lds(UnitQ8 &X, const float *xl, int u) { Q4KQ8Unit::load_lds(X, xl, u); }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8 &X, int u) { return Q4KQ8Unit::dot(R, X, u); }
 };

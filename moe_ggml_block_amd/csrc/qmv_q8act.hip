@@ -10,53 +10,28 @@
 namespace {
 
 // ------------------------------------------------------------ quantizer ---
-// Eight lanes per 32-value block, four values each. Every f32 step is one
-// IEEE operation with round-to-nearest (no contraction, correctly rounded
-// division), so the codes and scales equal any IEEE implementation's. In
-// particular the product x*inv is rounded to f32 before it is rounded to an
-// integer: were it fused into the fraction test of the half-away rounding, a
-// product that rounds to k+0.5 but lies just below it would go the other way.
+// Eight lanes per 32-value block, four values each (quantize_q8_lanes in
+// blocks.hpp: every f32 step one IEEE operation; in particular the product
+// x*inv is rounded to f32 before it is rounded to an integer -- were it fused
+// into the fraction test of the half-away rounding, a product that rounds to
+// k+0.5 but lies just below it would go the other way).
 __global__ __launch_bounds__(256) void k_quantize_act_q8(const float *__restrict__ x,
                                                          int8_t *__restrict__ xq,
                                                          float *__restrict__ xs,
                                                          float *__restrict__ xsum, int64_t nblocks) {
-#pragma clang fp contract(off)
     const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t b = tid >> 3;
     const int sub = (int)(tid & 7);
     const bool valid = b < nblocks;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) v = *reinterpret_cast<const float4 *>(x + b * 32 + sub * 4);
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, __shfl_xor(a, 1));
-    a = fmaxf(a, __shfl_xor(a, 2));
-    a = fmaxf(a, __shfl_xor(a, 4));
-    float inv = 0.0f, scale = 1.0f;
-    if (a > 0.0f) {
-        inv = __fdiv_rn(127.0f, a);
-        scale = __fdiv_rn(a, 127.0f);
-    }
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    int q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float prod = vv[i] * inv;
-        asm volatile("" : "+v"(prod));  // materialize the rounded f32 product
-        float r = roundf(prod);         // half away from zero
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        q[i] = (int)r;
-    }
-    int s = (q[0] + q[1]) + (q[2] + q[3]);
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
+    float scale, sum;
+    const uint32_t packed = quantize_q8_lanes(v, &scale, &sum);
     if (valid) {
-        const uint32_t packed = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) |
-                                ((uint32_t)(q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
         *reinterpret_cast<uint32_t *>(xq + b * 32 + sub * 4) = packed;
         if (sub == 0) {
             xs[b] = scale;
-            xsum[b] = __fmul_rn(scale, (float)s);
+            xsum[b] = sum;
         }
     }
 }
@@ -131,6 +106,15 @@ extern "C" int qmv_debug_blocksums_q4k_q8(const void *w, const int8_t *xq, int32
     hipLaunchKernelGGL(k_blocksums_q4k_q8, dim3((unsigned)div_up(n, WAVES_PER_BLOCK)), dim3(256), 0,
                        (hipStream_t)stream, static_cast<const uint8_t *>(w), xq, sums, (int)n, U,
                        (int)((k / 256) * 144));
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+extern "C" int qmv_q4k_q8x(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t stream) {
+    if (!w || !x || !y || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (n > (1 << 30) || k > 8192) return QMV_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMV_EALIGN;
+    qmv_dense::launch_tiled<Q4KQ8XUnit>(static_cast<const uint8_t *>(w), ActF32{x}, y, n, k, (hipStream_t)stream);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

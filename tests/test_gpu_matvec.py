@@ -172,3 +172,21 @@ def test_q4k_q8_end_to_end_from_f32():
     assert np.array_equal(host(xq), rq)
     y_ref = oracle.matvec_q8act("q4k", w, rq, rs, n, k)
     assert scalerel(y_ref, y) <= TOL
+
+
+@pytest.mark.parametrize("n,k", [(37, 256), (65, 768), (33, 2048), (70, 4096), (9, 8192), (14336, 4096)])
+def test_q4k_q8x_fused_quantize_matches_two_step(n, k):
+    """qmv_q4k_q8x quantizes x inside the kernel: bit-identical to
+    quantize_act_q8 + qmv_q4k_q8, and within 1e-4 of the oracle."""
+    announce(f"q4k q8x fused n={n} k={k}")
+    w = synth.weights(synth.FMT_Q4K, 11, n, k)
+    x = synth.normal(12, k)
+    x[::37] *= 100.0  # blocks with a wide spread of magnitudes
+    W, X = dev(w), dev(x)
+    fused = host(qmv.qmv_q4k_q8x(W, X, n, k))
+    xq, xs, xsum = qmv.quantize_act_q8(X, 1, k)
+    two = host(qmv.qmv_q4k_q8(W, xq, xs, xsum, n, k))
+    assert np.array_equal(fused, two)
+    oq, os_, _ = oracle.quantize_act_q8(x, 1, k)
+    ref = oracle.matvec_q8act("q4k", w, oq[0], os_[0], n, k)
+    assert scalerel(ref, fused) <= TOL
