@@ -170,6 +170,11 @@ int moe_qmv_q4k(const void *bank, const float *x, int64_t x_div, const int32_t *
                 int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
 int moe_qmv_q6k(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
                 int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
+/* The same gather over a bank of native Q8_0 blocks (34 bytes per 32
+ * weights; `moe_matvec_gpu` takes any resident bank format): bank
+ * E*n*(k/32)*34 bytes, 2-byte aligned; limits as moe_qmv_q4k. */
+int moe_qmv_q8_0(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y, int64_t nslots,
+                 int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * MoE FFN layer over routed slots s = topk*t + j, e = ids[s]

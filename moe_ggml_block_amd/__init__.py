@@ -39,6 +39,7 @@ _SIGS = {
     "moe_gate_route": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q4k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q6k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
+    "moe_qmv_q8_0": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
@@ -214,6 +215,10 @@ def moe_qmv_q4k(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
 
 def moe_qmv_q6k(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
     return _moe("moe_qmv_q6k", "q6k", bank, x, x_div, ids, nslots, n, k, E, y, stream)
+
+
+def moe_qmv_q8_0(bank, x, x_div, ids, nslots, n, k, E, y=None, stream=None):
+    return _moe("moe_qmv_q8_0", "q8_0", bank, x, x_div, ids, nslots, n, k, E, y, stream)
 
 
 def moe_ffn_workspace_bytes(T, topk, hidden, inter) -> int:

@@ -808,6 +808,13 @@ extern "C" int moe_qmv_q6k(const void *bank, const float *x, int64_t x_div, cons
 }
 
 // workspace: h f32[T*topk, inter]
+extern "C" int moe_qmv_q8_0(const void *bank, const float *x, int64_t x_div, const int32_t *ids, float *y,
+                            int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream) {
+    const int rc = check_moe_args(bank, x, x_div, ids, y, nslots, n, k, E);
+    if (rc) return rc;
+    return launch_moe<Q8Unit>(gather_args(bank, nullptr, x, x_div, ids, y, nslots, n, k, E), (hipStream_t)stream);
+}
+
 extern "C" int64_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter) {
     if (T < 1 || topk < 1 || hidden < 1 || inter < 1) return -1;
     return div_up(T * topk * inter * 4, 256) * 256;

@@ -78,34 +78,34 @@ def _ids(T, topk, E_, seed=0):
     return np.array([(i * 7 + 3 + seed) % E_ for i in range(T * topk)], dtype=np.int32)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "q8_0"])
 @pytest.mark.parametrize("E_,n,k,nslots,x_div", [(8, 256, 256, 4, 2), (16, 512, 256, 12, 4),
                                                  (4, 768, 512, 2, 1), (128, 768, 2048, 8, 8),
                                                  (128, 2048, 768, 16, 1), (5, 100, 1024, 9, 3)])
 def test_moe_qmv_matches_oracle(fmt, E_, n, k, nslots, x_div):
     announce(f"moe_qmv {fmt} E={E_} n={n} k={k} nslots={nslots}")
-    f = synth.FMT_Q4K if fmt == "q4k" else synth.FMT_Q6K
+    f = synth.FMT_NAMES[fmt]
     bank = synth.moe_bank(f, 30, E_, n, k)
     rows = (nslots + x_div - 1) // x_div
     x = synth.normal(31, rows * k).reshape(rows, k)
     ids = _ids(nslots, 1, E_)
     ids[nslots // 2] = ids[0]  # repeated expert
     ref = oracle.moe_qmv(fmt, bank, x, x_div, ids, nslots, n, k, E_)
-    fn = qmv.moe_qmv_q4k if fmt == "q4k" else qmv.moe_qmv_q6k
+    fn = {"q4k": qmv.moe_qmv_q4k, "q6k": qmv.moe_qmv_q6k, "q8_0": qmv.moe_qmv_q8_0}[fmt]
     got = host(fn(dev(bank), dev(x), x_div, dev(ids), nslots, n, k, E_))
     assert scalerel(ref, got) <= TOL
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "q8_0"])
 def test_moe_qmv_invalid_ids_zero_rows(fmt):
     E_, n, k, nslots = 6, 64, 512, 7
-    f = synth.FMT_Q4K if fmt == "q4k" else synth.FMT_Q6K
+    f = synth.FMT_NAMES[fmt]
     bank = synth.moe_bank(f, 32, E_, n, k)
     x = synth.normal(33, nslots * k).reshape(nslots, k)
     ids = np.array([2, -1, 5, 6, 2, 100, 0], dtype=np.int32)
     announce(f"moe_qmv invalid ids {fmt}")
     ref = oracle.moe_qmv(fmt, bank, x, 1, ids, nslots, n, k, E_)
-    fn = qmv.moe_qmv_q4k if fmt == "q4k" else qmv.moe_qmv_q6k
+    fn = {"q4k": qmv.moe_qmv_q4k, "q6k": qmv.moe_qmv_q6k, "q8_0": qmv.moe_qmv_q8_0}[fmt]
     y = torch.full((nslots, n), float("nan"), device="cuda")
     fn(dev(bank), dev(x), 1, dev(ids), nslots, n, k, E_, y=y)
     got = host(y)
