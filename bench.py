@@ -354,6 +354,15 @@ def prefill_other(copies: int = 16):
                   "mfma_f16_pct": round(2.0 * m * n * k / (ms6 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2)}
     del big6, W6
     torch.cuda.empty_cache()
+    # Q8_0 prefill at the same shape
+    w8 = synth.weights(synth.FMT_Q8_0, synth.SEED_W, n, k)
+    big8, W8 = rotated(w8, copies)
+    del w8
+    ms8 = time_graph(lambda i: qmv.qmm_q8_0(W8[i % copies], xq, xs, m, n, k, y=y6), 2 * copies, 5)
+    res["q8_0"] = {"us": round(ms8 * 1e3, 2), "tops": round(2.0 * m * n * k / (ms8 * 1e-3) / 1e12, 2),
+                   "mfma_f16_pct": round(2.0 * m * n * k / (ms8 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS * 100, 2)}
+    del big8, W8
+    torch.cuda.empty_cache()
     res["moe_qmm_q4k"] = moe_prefill_other()
     return res
 

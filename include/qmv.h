@@ -280,6 +280,22 @@ int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, const float
 int qmm_q6k(const void *w, const int8_t *xq, const float *xs, float *y, int64_t m, int64_t n, int64_t k,
             qmv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Q8_0 prefill GEMM on a q8 activation (hanzo-ml `src/vulkan_backend.rs`:
+ * the native Q8_0 blocks of `matvec_q8_0_gpu`, kept quantized at m > 1 as
+ * `matmul_q4_0_gpu` keeps Q4_0):
+ *   y[i, r] = sum_c W_deq[r, c] * xs[i, c/32] * xq[i, c].
+ * w: n*(k/32)*34 bytes (f16 d, then 32 int8 codes per block); xq: int8[m, k];
+ * xs: f32[m, k/32] (quantize_act_q8); y: f32[m, n], every element written.
+ * The integer dot of each 32-value block runs exactly on the f16 matrix
+ * cores; d and xs scale it in the epilogue. k % 256 == 0; xq 16-byte
+ * aligned, w 2-byte, the rest 4-byte. Errors: QMV_EINVAL (null pointer,
+ * m or n < 1, bad k), QMV_EUNSUPPORTED (m, n > 2^24, k > 2^20 or
+ * m*k > 2^34), QMV_EALIGN; nothing is launched on an error.
+ * ---------------------------------------------------------------------- */
+int qmm_q8_0(const void *w, const int8_t *xq, const float *xs, float *y, int64_t m, int64_t n, int64_t k,
+             qmv_stream_t stream);
+
 /* Expert-indexed Q6_K prefill GEMM (the MoE down projection at m > 1;
  * `matmul_q6k_gpu_off` on one expert's slice of a resident bank, slots
  * grouped by expert on the device as in moe_qmm_q4k):

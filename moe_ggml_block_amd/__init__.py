@@ -44,6 +44,7 @@ _SIGS = {
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "qmm_q6k": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "qmm_q8_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "moe_qmm_q6k": [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q6k_f32": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_prefill_q4k_q6k": [_vp] * 8 + [_i64] * 6 + [_vp],
@@ -274,6 +275,18 @@ def qmm_q6k(w, xq, xs, m, n, k, y=None, stream=None):
         y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     _need(y, 4 * m * n, "y")
     _check(_lib.qmm_q6k(_p(w), _p(xq), _p(xs), _p(y), m, n, k, _stream(stream)), "qmm_q6k")
+    return y
+
+
+def qmm_q8_0(w, xq, xs, m, n, k, y=None, stream=None):
+    """Q8_0 prefill GEMM on a q8 activation: y = deq(xq, xs) . W^T."""
+    _need(w, n * row_bytes("q8_0", k), "w")
+    _need(xq, m * k, "xq")
+    _need(xs, 4 * m * (k // 32), "xs")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * m * n, "y")
+    _check(_lib.qmm_q8_0(_p(w), _p(xq), _p(xs), _p(y), m, n, k, _stream(stream)), "qmm_q8_0")
     return y
 
 

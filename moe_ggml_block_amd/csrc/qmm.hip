@@ -1171,3 +1171,182 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
+
+// ==================================================================== Q8_0
+// Q8_0 prefill GEMM on a q8 activation (hanzo-ml `src/vulkan_backend.rs`: the
+// native Q8_0 blocks of `matvec_q8_0_gpu`, prefill as `matmul_q4_0_gpu` does
+// for Q4_0 -- weights stay quantized, each decoded value serves a tile of
+// rows):
+//   Y[i, r] = sum_b xs[i, b] * d[r, b] * T[i, r, b],  T = sum_{l<32} xq * q.
+// Both codes are int8, exact in f16, and T (|T| <= 32*127*128) is exact on
+// the f16 matrix cores (one v_mfma_f32_16x16x32_f16 per 16x16 tile and
+// block); the epilogue is d * T, then one FMA with xs, per output and block.
+// Tiles of 64 x 128 on eight waves, phases of 64 values (two blocks), the
+// double-buffered staging of the Q6_K kernel; rows of 34-byte blocks are
+// 2-byte aligned and read with 8-byte loads.
+namespace {
+
+template <int BM, int BN, int MT, int NT, int NTHREADS>
+__global__ __launch_bounds__(NTHREADS) void k_qmm_q8_0(const uint8_t *__restrict__ w, const int8_t *__restrict__ xq,
+                                                       const float *__restrict__ xs, float *__restrict__ Y, int m,
+                                                       int n, int k) {
+    constexpr int KP = 64, NBP = 2;              // values and blocks per phase
+    constexpr int WM = 16 * MT, WN = 16 * NT;
+    constexpr int WGM = BM / WM, WGN = BN / WN;
+    static_assert(WGM * WGN == NTHREADS / 64, "the waves tile the workgroup");
+    constexpr int ST = KP + 8;
+    constexpr int ACR = KP / 8;                  // 8-code activation chunks per row
+    constexpr int AC = BM * ACR / NTHREADS;
+    static_assert(AC >= 1 && AC * NTHREADS == BM * ACR, "activation staging");
+    constexpr int BCH = BN * (KP / 8);           // 8-code weight chunks per phase
+    constexpr int BCT = BCH / NTHREADS;
+    static_assert(BCT >= 1 && BCT * NTHREADS == BCH && NTHREADS % BN == 0, "weight staging");
+    constexpr int XC = (BM * NBP + NTHREADS - 1) / NTHREADS;
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * ST];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * ST];
+    __shared__ __attribute__((aligned(16))) float sfx[2][NBP][BM];
+    __shared__ float sdq[2][NBP][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int kb = k / 32;
+    const size_t row_bytes = (size_t)kb * 34;
+    const int brow = tid % BN, bc0 = tid / BN;
+    const bool bvalid = n0 + brow < n;
+    const uint8_t *wrow = w + (size_t)(bvalid ? n0 + brow : 0) * row_bytes;
+    int arow[AC], xrow[XC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int r = (tid + NTHREADS * i) / ACR;
+        arow[i] = m0 + r < m ? m0 + r : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+        const int idx = tid + NTHREADS * i, r = idx % BM;
+        xrow[i] = (idx < BM * NBP && m0 + r < m) ? m0 + r : -1;
+    }
+
+    uint2 ra[2][AC], rb[2][BCT];
+    uint32_t rd[2][BCT];
+    float rxs[2][XC];
+
+    auto prefetch = [&](int ph, int q) {
+        const int k0 = ph * KP;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = (tid + NTHREADS * i) % ACR, gm = arow[i];
+            ra[q][i] = gm >= 0 ? *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + k0 + 8 * c)
+                               : make_uint2(0u, 0u);
+        }
+        if (bvalid) {
+#pragma unroll
+            for (int i = 0; i < BCT; ++i) {
+                const int bc = bc0 + i * (NTHREADS / BN);  // block bc / 4 of the phase, codes 8 (bc % 4) ..
+                const uint8_t *blk = wrow + (size_t)(2 * ph + (bc >> 2)) * 34;
+                rb[q][i] = *reinterpret_cast<const uint2 *>(blk + 2 + 8 * (bc & 3));
+                rd[q][i] = ld2(blk);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < BCT; ++i) rb[q][i] = make_uint2(0u, 0u), rd[q][i] = 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int bl = (tid + NTHREADS * i) / BM, gm = xrow[i];
+            rxs[q][i] = gm >= 0 ? xs[(size_t)gm * kb + k0 / 32 + bl] : 0.f;
+        }
+    };
+    auto convert_store = [&](int buf, int q) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int ch = tid + NTHREADS * i, row = ch / ACR, c = ch % ACR;
+            const uint2 h0 = i8x4_to_f16(ra[q][i].x), h1 = i8x4_to_f16(ra[q][i].y);
+            *reinterpret_cast<uint4 *>(&As[buf][row * ST + 8 * c]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+        }
+#pragma unroll
+        for (int i = 0; i < BCT; ++i) {
+            const int bc = bc0 + i * (NTHREADS / BN);
+            const uint2 c0 = i8x4_to_f16(rb[q][i].x), c1 = i8x4_to_f16(rb[q][i].y);
+            *reinterpret_cast<uint4 *>(&Bs[buf][brow * ST + 8 * bc]) = make_uint4(c0.x, c0.y, c1.x, c1.y);
+            if ((bc & 3) == 0) sdq[buf][bc >> 2][brow] = h2f(rd[q][i]);
+        }
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int idx = tid + NTHREADS * i, row = idx % BM, bl = idx / BM;
+            if (idx < BM * NBP) sfx[buf][bl][row] = rxs[q][i];
+        }
+    };
+
+    v4f acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    const int nph = k / KP;  // even (k % 256 == 0)
+    prefetch(0, 0);
+    convert_store(0, 0);
+    prefetch(1, 1);
+    if (nph > 2) prefetch(2, 0);
+    __syncthreads();
+    for (int ph0 = 0; ph0 < nph; ph0 += 2) {
+#pragma unroll
+        for (int Q = 0; Q < 2; ++Q) {
+            const int ph = ph0 + Q, buf = Q;
+#pragma unroll
+            for (int bl = 0; bl < NBP; ++bl) {
+                h8 fa[MT], fb[NT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    fa[t] = *reinterpret_cast<const h8 *>(&As[buf][(wm * WM + 16 * t + li) * ST + 32 * bl + 8 * lq]);
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    fb[u] = *reinterpret_cast<const h8 *>(&Bs[buf][(wn * WN + 16 * u + li) * ST + 32 * bl + 8 * lq]);
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const float dcol = sdq[buf][bl][wn * WN + 16 * u + li];
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const v4f T = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[t], fb[u], (v4f){0.f, 0.f, 0.f, 0.f},
+                                                                             0, 0, 0);
+                        const v4f fx = *reinterpret_cast<const v4f *>(&sfx[buf][bl][wm * WM + 16 * t + 4 * lq]);
+                        acc[t][u] = fx * (dcol * T) + acc[t][u];
+                    }
+                }
+            }
+            if (ph + 1 < nph) {
+                convert_store(buf ^ 1, Q ^ 1);
+                if (ph + 3 < nph) prefetch(ph + 3, Q ^ 1);
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int col = n0 + wn * WN + 16 * u + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * WM + 16 * t + 4 * lq + r;
+                if (row < m && col < n) Y[(size_t)row * n + col] = acc[t][u][r];
+            }
+        }
+}
+
+}  // namespace
+
+extern "C" int qmm_q8_0(const void *w, const int8_t *xq, const float *xs, float *y, int64_t m, int64_t n, int64_t k,
+                        qmv_stream_t stream) {
+    if (!w || !xq || !xs || !y || m < 1 || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (m > (1 << 24) || n > (1 << 24) || k > (1 << 20) || m * k > ((int64_t)1 << 34)) return QMV_EUNSUPPORTED;
+    if (!aligned(w, 2) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(y, 4)) return QMV_EALIGN;
+    const dim3 grid((unsigned)div_up(n, 128), (unsigned)div_up(m, 64));
+    hipLaunchKernelGGL((k_qmm_q8_0<64, 128, 2, 2, 512>), grid, dim3(512), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t *>(w), xq, xs, y, (int)m, (int)n, (int)k);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}

@@ -74,6 +74,11 @@ def test_host_validation_returns_before_launch(lib):
     lib.qmm_q4k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.qmm_q4k.restype = i32
     assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 64, None) == QMV_EINVAL  # bm
+    lib.qmm_q8_0.argtypes = [vp] * 4 + [i64] * 3 + [vp]
+    lib.qmm_q8_0.restype = i32
+    assert lib.qmm_q8_0(fake, fake, fake, fake, 4, 64, 224, None) == QMV_EINVAL   # k % 256
+    assert lib.qmm_q8_0(fake, fake, fake, fake, 0, 64, 256, None) == QMV_EINVAL   # m < 1
+    assert lib.qmm_q8_0(fake, odd, fake, fake, 4, 64, 256, None) == QMV_EALIGN    # xq
     lib.moe_ffn_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.moe_ffn_workspace_bytes.restype = i64
     # h = silu(gate x) * (up x), f32 per slot

@@ -118,6 +118,48 @@ def test_qmm_q6k_random_blocks_every_code_and_scale():
     assert scalerel(ref, got) <= TOL, scalerel(ref, got)
 
 
+# ------------------------------------------------------------ Q8_0 prefill
+@pytest.mark.parametrize("m,n,k", [(1, 16, 256), (70, 200, 512), (128, 256, 768), (300, 130, 2048)])
+def test_qmm_q8_0_dense_small(m, n, k):
+    announce(f"qmm_q8_0 m={m} n={n} k={k}")
+    w = synth.weights(synth.FMT_Q8_0, 94, n, k)
+    x = synth.normal(95, m * k).reshape(m, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q8_0", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q8_0(dev(w), dev(xq), dev(xs), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_q8_0_random_blocks_every_code():
+    """Random raw Q8_0 blocks: every int8 code (-128 included) and scales
+    across the f16 range."""
+    m, n, k = 40, 64, 1024
+    announce("qmm_q8_0 random blocks")
+    w = synth.random_blocks(synth.FMT_Q8_0, 96, n * k // 32).reshape(n, -1)
+    x = synth.normal(97, m * k).reshape(m, k)
+    xq, xs, _ = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q8_0", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q8_0(dev(w), dev(xq), dev(xs), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_q8_0_full_config_sampled_rows():
+    """m=512 tokens x W[4096, 4096] in Q8_0: every output column of sampled
+    rows (first/last tiles and interior) against the oracle."""
+    m, n, k = 512, 4096, 4096
+    announce("qmm_q8_0 full")
+    w = synth.weights(synth.FMT_Q8_0, synth.SEED_W, n, k)
+    x = synth.normal(synth.SEED_PREFILL_X, m * k).reshape(m, k)
+    xq, xs, _ = qmv.quantize_act_q8(dev(x), m, k)
+    rq, rs, _ = oracle.quantize_act_q8(x, m, k)
+    assert np.array_equal(host(xq), rq)
+    Y = host(qmv.qmm_q8_0(dev(w), xq, xs, m, n, k))
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 128, 255, 256, 300, 383, 384, 450, 480, 509, 511])
+    ref = oracle.qmm("q8_0", w, rq, rs, m, n, k, mrows=rows)
+    assert scalerel(ref, Y[rows]) <= TOL, scalerel(ref, Y[rows])
+    assert np.isfinite(Y).all()
+
+
 def _check6(ids, n, k, E, x_div, seed, f32, sample=None):
     ns = ids.size
     rows_x = -(-ns // x_div)
