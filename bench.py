@@ -333,7 +333,7 @@ def prefill_other(copies: int = 16):
     x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, m * k)).cuda()
     xq, xs, xsum = qmv.quantize_act_q8(x, m, k)
     res = {}
-    for bm in (128, 256):
+    for bm in (64, 128, 256):
         y = torch.empty((m, n), device="cuda")
         ms = time_graph(lambda i: qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y), 2 * copies, 5)
         tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12

@@ -235,12 +235,16 @@ int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const
                        int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * Q4_K prefill GEMM on int8 MFMA (`mmq_q4k_rt_gpu`: affine Q4_K x q8
- * activation, epilogue xs*(D*dot - M*xsum)):
+ * Q4_K prefill GEMM (`mmq_q4k_rt_gpu`: affine Q4_K x q8 activation,
+ * epilogue xs*(D*dot - M*xsum)):
  *   Y[i, r] = sum_b ( xs[i,b]*d_r*sc_rj*S[i,r,b] - xsum[i,b]*dmin_r*m_rj ),
- *   S[i,r,b] = sum_{l<32} xq[i, 32b+l] * q[r, 32b+l]  (int32, exact),
+ *   S[i,r,b] = sum_{l<32} xq[i, 32b+l] * q[r, 32b+l]  (an integer, exact),
+ * each block's integer dot (with sc folded in) formed on the f16 matrix
+ * cores, which hold the integer operands exactly.
  * w: n*(k/256)*144 bytes; xq: int8[m, k]; xs, xsum: f32[m, k/32];
- * Y: f32[m, n]. bm = rows of Y per workgroup tile, 128 or 256.
+ * Y: f32[m, n]. bm = rows of Y per workgroup tile: 64 (weights decoded
+ * straight into matrix fragments, activations staged once per tile; the
+ * fastest at m = 512), 128 or 256 (weights and activations both staged).
  * k % 256 == 0; m, n >= 1 (ragged tiles are masked).
  * ---------------------------------------------------------------------- */
 int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,

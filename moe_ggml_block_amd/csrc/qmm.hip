@@ -532,6 +532,290 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
         }
 }
 
+// ------------------------------------------------- Q4_K prefill, weight-side
+// Same contraction as k_qmm_q4k with the matrix roles swapped: the weights
+// are the A operand (16 rows x 32 values per fragment) and the activations
+// the B operand, so a lane of a 16x16 result holds four weight rows
+// (4*lq + r) of one activation row (li), and that row's xs for a block is a
+// single scalar per lane. The weight fragments never pass through LDS: a
+// lane loads, per 32-value block, the 8 code bytes its fragment needs (the
+// low nibbles of bytes 8*lq..8*lq+7 of a 32-byte pair are values 8*lq.. of
+// the even sub-block, the high nibbles those of the odd one) and turns them
+// into f16 sc*q in registers. Only the activations are staged, once per
+// workgroup and superblock, as f16 in LDS (double-buffered, one barrier per
+// superblock).
+//
+// Eight waves: NG groups of 32 weight rows x MG groups of 64 activation rows
+// x KS parts of each superblock's eight blocks (KS = 2: blocks 0-3 and 4-7,
+// summed through LDS at the end). Tile: BN = 32*NG weight rows x
+// BM = 64*MG activation rows. Per superblock a wave forms, for each of its
+// blocks, the 2x4 fragment products T (one v_mfma_f32_16x16x32_f16 each),
+// adds xs*T into acc, then out += d*acc and the min term of its blocks
+// (-dmin*m x xsum, one v_mfma_f32_16x16x4_f32 per four blocks).
+template <int NG, int MG, int KS>
+__global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store) {
+    static_assert(NG * MG * KS == 8 && (KS == 1 || KS == 2), "eight waves");
+    constexpr int BN = 32 * NG, BM = 64 * MG;
+    constexpr int ST = 256 + 8;          // halves per LDS activation row (4-bank shift per row)
+    constexpr int NBW = 8 / KS;          // blocks of a superblock per wave
+    constexpr int NPW = NBW / 2;         // code-byte pairs per wave
+    constexpr int AC = BM * 32 / 512;    // 8-byte activation chunks per thread and superblock
+    constexpr int XV = BM * 8 / 512;     // xs (and xsum) values per thread and superblock
+    static_assert(AC >= 1 && XV >= 1, "staging");
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * ST];
+    constexpr int XST = 12;              // floats per xs row: 16-byte reads of 16 rows conflict-free
+    __shared__ __attribute__((aligned(16))) float sxs[2][BM * XST];
+    __shared__ __attribute__((aligned(16))) float sxsum[2][BM * XST];
+
+    const uint8_t *__restrict__ w = a.w;
+    const int8_t *__restrict__ xq = a.xq;
+    const float *__restrict__ xs = a.xs;
+    const float *__restrict__ xsum = a.xsum;
+    const int m = a.m, n = a.n, k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index in a scalar register: every role test below is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = wave % KS, g = (wave / KS) % NG, mg = wave / (KS * NG);
+    const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int nsb = k / 256, kb = k / 32;
+    const size_t row_bytes = (size_t)nsb * 144;
+
+    // this lane's two weight rows (clamped for the loads; stores are masked)
+    const uint8_t *wrow[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) wrow[t] = w + (size_t)min(n0 + 32 * g + 16 * t + li, n - 1) * row_bytes;
+
+    // Raw superblock codes of this lane (header and NPW 8-byte pieces per
+    // row) and the staged activation chunks come in two register sets: the
+    // loads of superblock s + 2 are issued at the top of superblock s into
+    // the set that s used, so every load has two superblocks of work to land.
+    struct WSet {
+        uint4 hdr[2];
+        uint2 qc[2][NPW];
+    };
+    auto load_w = [&](int s, WSet &W) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint8_t *blk = wrow[t] + (size_t)s * 144;
+            W.hdr[t] = ld16(blk);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp)
+                W.qc[t][pp] = *reinterpret_cast<const uint2 *>(blk + 16 + 32 * (NPW * h + pp) + 8 * lq);
+        }
+    };
+    // Activation staging: chunk c = tid + 512*i is row c/32, bytes 8*(c%32)
+    // (8-byte pieces, so that consecutive lanes write consecutive 16-byte f16
+    // units: conflict-free). The loads read clamped rows unconditionally;
+    // rows past m are zeroed when stored, so nothing consumes a loaded value
+    // before the store (a select right after the loads would make the
+    // compiler wait for them there).
+    struct ASet {
+        uint2 q[AC];
+        float xs[XV], xsum[XV];
+    };
+    auto load_act = [&](int s, ASet &A) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
+            const int gm = min(m0 + row, m - 1);
+            A.q[i] = *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + 256 * s + 8 * c8);
+        }
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int c = tid + 512 * i, row = c >> 3, j = c & 7;
+            const int gm = min(m0 + row, m - 1);
+            A.xs[i] = xs[(size_t)gm * kb + 8 * s + j];
+            A.xsum[i] = xsum[(size_t)gm * kb + 8 * s + j];
+        }
+    };
+    auto store_act = [&](int buf, const ASet &A) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
+            const uint2 v = m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
+            const uint2 h0 = i8x4_to_f16(v.x), h1 = i8x4_to_f16(v.y);
+            *reinterpret_cast<uint4 *>(&As[buf][row * ST + 8 * c8]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+        }
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int c = tid + 512 * i, row = c >> 3, j = c & 7;
+            const bool ok = m0 + row < m;
+            sxs[buf][row * XST + j] = ok ? A.xs[i] : 0.f;
+            sxsum[buf][row * XST + j] = ok ? A.xsum[i] : 0.f;
+        }
+    };
+
+    v4f acc[2][4], out[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+
+    WSet wset[2];
+    ASet aset[2];
+    // Every load and store below is unconditional: superblock indices past
+    // the end are clamped to the last one (its data is loaded again and
+    // never used). A branch around them would make the compiler's wait
+    // counts assume the shorter path and wait for every load in flight.
+    load_w(0, wset[0]);
+    load_act(0, aset[0]);
+    load_w(min(1, nsb - 1), wset[1]);
+    load_act(min(1, nsb - 1), aset[1]);
+    store_act(0, aset[0]);
+    __syncthreads();
+
+    // one superblock: P = s % 2 names its register set and LDS buffer
+    auto superblock = [&](int s, auto Pc) {
+        constexpr int P = decltype(Pc)::value;
+        // this superblock's scales: sc of the wave's blocks as f16 splats,
+        // -dmin*m of the min-term operand, d of the lane's output rows
+        h2 scl[2][NBW], nscl[2][NBW];
+        float amn[2][KS == 1 ? 2 : 1], dout[2][4];
+        uint2 q[2][NPW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint4 hd = wset[P].hdr[t];
+            const float dmin = h2f(hd.x >> 16);
+            uint32_t sc2[NPW], mn2[NPW];
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q4k_scales(hd.y, hd.z, hd.w, NPW * h + pp, &sc2[pp], &mn2[pp]);
+#pragma unroll
+            for (int bl = 0; bl < NBW; ++bl) {
+                const float sc = (float)((sc2[bl / 2] >> (8 * (bl & 1))) & 0xFFu);
+                scl[t][bl] = splat(sc);
+                nscl[t][bl] = splat(-1024.0f * sc);
+            }
+            // min-term operand: block 4*i + lq of the wave's blocks (lanes
+            // lq = 2, 3 take the second pair; bit arithmetic rather than an
+            // indexed array, which the compiler would place in LDS)
+#pragma unroll
+            for (int i = 0; i < (KS == 1 ? 2 : 1); ++i) {
+                const uint32_t lo = mn2[2 * i], hi = mn2[2 * i + 1];
+                const uint32_t pr = lo ^ ((lo ^ hi) & (0u - (uint32_t)(lq >> 1)));
+                amn[t][i] = -dmin * (float)((pr >> (8 * (lq & 1))) & 0xFFu);
+            }
+            const float down = h2f(hd.x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[P].qc[t][pp];
+        }
+        // superblock s + 2 goes into the registers just read
+        load_w(min(s + 2, nsb - 1), wset[P]);
+        load_act(min(s + 2, nsb - 1), aset[P]);
+        // xs of the lane's activation rows for the wave's blocks
+        float xv[4][NBW];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *p = &sxs[P][(64 * mg + 16 * u + li) * XST + NBW * h];
+#pragma unroll
+            for (int c = 0; c < NBW / 4; ++c) {
+                const v4f v = *reinterpret_cast<const v4f *>(p + 4 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[u][4 * c + e] = v[e];
+            }
+        }
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+            const int jb = NBW * h + bl;  // block within the superblock
+            h8 bf[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                bf[u] = *reinterpret_cast<const h8 *>(&As[P][(64 * mg + 16 * u + li) * ST + 32 * jb + 8 * lq]);
+            v4f T[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint2 cw = q[t][bl / 2];
+                const uint32_t c0 = (bl & 1) ? (cw.x >> 4) : cw.x, c1 = (bl & 1) ? (cw.y >> 4) : cw.y;
+                const uint2 v0 = q4x4_to_f16(c0 & 0x0F0F0F0Fu, scl[t][bl], nscl[t][bl]);
+                const uint2 v1 = q4x4_to_f16(c1 & 0x0F0F0F0Fu, scl[t][bl], nscl[t][bl]);
+                const h8 af = __builtin_bit_cast(h8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    T[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[t][u] = xv[u][bl] * T[t][u] + acc[t][u];
+        }
+        // superblock done: out += d*acc, then the min term of the wave's blocks
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[t][u][r] = dout[t][r] * acc[t][u][r] + out[t][u][r];
+                acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int i = 0; i < (KS == 1 ? 2 : 1); ++i) {
+            float xb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xb[u] = sxsum[P][(64 * mg + 16 * u + li) * XST + NBW * h + 4 * i + lq];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(amn[t][i], xb[u], out[t][u], 0, 0, 0);
+        }
+        // superblock s + 1's activations (loaded a superblock ago) into the
+        // other buffer, which every wave finished reading before the last
+        // barrier (after the last superblock this stores unused data)
+        store_act(P ^ 1, aset[P ^ 1]);
+        __syncthreads();
+    };
+    for (int s = 0; s < nsb; s += 2) {
+        superblock(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nsb) superblock(s + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (KS == 2) {
+        // the second half of each superblock's blocks adds in through LDS
+        // (the activation buffers are free after the loop's last barrier)
+        float *red = reinterpret_cast<float *>(&As[0][0]);
+        const int pair = g + NG * mg;
+        if (h == 1) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((pair * 32) + 16 * t + 4 * u + r) * 64 + lane] = out[t][u][r];
+        }
+        __syncthreads();
+        if (h == 1) return;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[t][u][r] += red[((pair * 32) + 16 * t + 4 * u + r) * 64 + lane];
+    }
+    // lane holds weight rows 4*lq + r of each 16x16 result, activation row li
+    float *__restrict__ Y = a.Y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = m0 + 64 * mg + 16 * u + li;
+        if (row >= m) continue;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = n0 + 32 * g + 16 * t + 4 * lq;
+            float *dst = Y + (size_t)row * n + col;
+            if (vec_store && col + 3 < n) {
+                *reinterpret_cast<v4f *>(dst) = out[t][u];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < n) dst[r] = out[t][u][r];
+            }
+        }
+    }
+}
+
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile configurations (BM, BN, KP, MT, NT, threads) for the two bm settings
@@ -548,6 +832,15 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 #define QMM_CFG256_BN 32
 #define QMM_CFG256_NT 512
 #endif
+// weight-side kernel at bm = 64: four groups of 32 weight rows, one group of
+// 64 activation rows, each superblock's blocks split over two waves (the
+// 128-row form (2, 2, 2) spills registers with two superblocks of loads in
+// flight and measured slower than k_qmm_q4k at bm = 128)
+#ifndef QMM2_BM64_NG
+#define QMM2_BM64_NG 4
+#define QMM2_BM64_MG 1
+#define QMM2_BM64_KS 2
+#endif
 // expert-indexed tiles: 64 rows (slots), 128 columns, eight waves; the
 // prefill layer also takes 32-row tiles at few slots per expert
 #define QMM_MOE32 32, 128, 64, 2, 2, 256
@@ -562,13 +855,17 @@ constexpr int64_t QMM_MOE_MAX_SLOTS = 1 << 20;
 extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
                        int64_t m, int64_t n, int64_t k, int bm, qmv_stream_t stream) {
     if (!w || !xq || !xs || !xsum || !y || m < 1 || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
-    if (bm != 128 && bm != 256) return QMV_EINVAL;
+    if (bm != 64 && bm != 128 && bm != 256) return QMV_EINVAL;
     if (m > (1 << 24) || n > (1 << 24) || k > (1 << 20) || (int64_t)m * k > ((int64_t)1 << 34)) return QMV_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(y, 4))
         return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
     QmmArgs a{static_cast<const uint8_t *>(w), xq, xs, xsum, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
-    if (bm == 128) {
+    const int vec = aligned(y, 16) && n % 4 == 0;
+    if (bm == 64) {
+        const dim3 grid((unsigned)div_up(n, 32 * QMM2_BM64_NG), (unsigned)div_up(m, 64 * QMM2_BM64_MG));
+        hipLaunchKernelGGL((k_qmm2_q4k<QMM2_BM64_NG, QMM2_BM64_MG, QMM2_BM64_KS>), grid, dim3(512), 0, s, a, vec);
+    } else if (bm == 128) {
         const dim3 grid((unsigned)div_up(n, QMM_CFG128_BN), (unsigned)div_up(m, QMM_CFG128_BM));
         hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(QMM_CFG128_NT), 0, s, a);
     } else {

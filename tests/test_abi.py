@@ -73,7 +73,7 @@ def test_host_validation_returns_before_launch(lib):
     assert lib.moe_gate_route(odd, fake, fake, fake, fake, 2, 8, 64, 2, None) == QMV_EALIGN
     lib.qmm_q4k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.qmm_q4k.restype = i32
-    assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 64, None) == QMV_EINVAL  # bm
+    assert lib.qmm_q4k(fake, fake, fake, fake, fake, 512, 4096, 4096, 32, None) == QMV_EINVAL  # bm
     lib.qmm_q8_0.argtypes = [vp] * 4 + [i64] * 3 + [vp]
     lib.qmm_q8_0.restype = i32
     assert lib.qmm_q8_0(fake, fake, fake, fake, 4, 64, 224, None) == QMV_EINVAL   # k % 256

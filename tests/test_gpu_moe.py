@@ -219,7 +219,9 @@ def test_moe_layer_small_shapes():
 
 # ------------------------------------------------------------------ prefill
 @pytest.mark.parametrize("m,n,k,bm", [(1, 32, 256, 128), (40, 70, 512, 128), (130, 96, 1024, 256),
-                                      (257, 33, 2048, 256), (128, 64, 4096, 128)])
+                                      (257, 33, 2048, 256), (128, 64, 4096, 128),
+                                      (1, 32, 256, 64), (40, 70, 512, 64), (65, 130, 768, 64),
+                                      (200, 257, 1024, 64), (129, 131, 512, 128), (64, 128, 2048, 64)])
 def test_qmm_small_shapes(m, n, k, bm):
     announce(f"qmm m={m} n={n} k={k} bm={bm}")
     w = synth.weights(synth.FMT_Q4K, 60, n, k)
@@ -230,7 +232,7 @@ def test_qmm_small_shapes(m, n, k, bm):
     assert scalerel(ref, got) <= TOL, scalerel(ref, got)
 
 
-@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("bm", [64, 128, 256])
 def test_qmm_full_config_sampled_rows(bm):
     """m=512 tokens x W[4096, 4096]: every output column of 24 sampled rows
     (first/last tiles and interior) against the oracle."""
