@@ -581,10 +581,18 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     const int nsb = k / 256, kb = k / 32;
     const size_t row_bytes = (size_t)nsb * 144;
 
-    // this lane's two weight rows (clamped for the loads; stores are masked)
-    const uint8_t *wrow[2];
+    // Load addresses are a uniform base (the superblock's offset folded in,
+    // scalar registers) plus a per-lane 32-bit offset fixed for the whole
+    // loop (the host routes shapes whose offsets could pass 2^32 elsewhere).
+    // This lane's two weight rows are clamped for the loads (stores are
+    // masked); its code bytes of pair NPW*h + pp sit at 16 + 32*pair + 8*lq.
+    uint32_t woff[2], qoff[2][NPW];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) wrow[t] = w + (size_t)min(n0 + 32 * g + 16 * t + li, n - 1) * row_bytes;
+    for (int t = 0; t < 2; ++t) {
+        woff[t] = (uint32_t)((size_t)min(n0 + 32 * g + 16 * t + li, n - 1) * row_bytes);
+#pragma unroll
+        for (int pp = 0; pp < NPW; ++pp) qoff[t][pp] = woff[t] + 16 + 32 * (NPW * h + pp) + 8 * lq;
+    }
 
     // Raw superblock codes of this lane (header and NPW 8-byte pieces per
     // row) and the staged activation chunks come in two register sets: the
@@ -595,13 +603,12 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         uint2 qc[2][NPW];
     };
     auto load_w = [&](int s, WSet &W) {
+        const uint8_t *wsb = w + (size_t)s * 144;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint8_t *blk = wrow[t] + (size_t)s * 144;
-            W.hdr[t] = ld16(blk);
+            W.hdr[t] = ld16(wsb + woff[t]);
 #pragma unroll
-            for (int pp = 0; pp < NPW; ++pp)
-                W.qc[t][pp] = *reinterpret_cast<const uint2 *>(blk + 16 + 32 * (NPW * h + pp) + 8 * lq);
+            for (int pp = 0; pp < NPW; ++pp) W.qc[t][pp] = *reinterpret_cast<const uint2 *>(wsb + qoff[t][pp]);
         }
     };
     // Activation staging: chunk c = tid + 512*i is row c/32, bytes 8*(c%32)
@@ -614,19 +621,26 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         uint2 q[AC];
         float xs[XV], xsum[XV];
     };
-    auto load_act = [&](int s, ASet &A) {
+    uint32_t aoff[AC], xoff[XV];
 #pragma unroll
-        for (int i = 0; i < AC; ++i) {
-            const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
-            const int gm = min(m0 + row, m - 1);
-            A.q[i] = *reinterpret_cast<const uint2 *>(xq + (size_t)gm * k + 256 * s + 8 * c8);
-        }
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 512 * i;
+        aoff[i] = (uint32_t)((size_t)min(m0 + (c >> 5), m - 1) * k + 8 * (c & 31));
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        const int c = tid + 512 * i;
+        xoff[i] = (uint32_t)((size_t)min(m0 + (c >> 3), m - 1) * kb + (c & 7));
+    }
+    auto load_act = [&](int s, ASet &A) {
+        const int8_t *xqs = xq + (size_t)s * 256;
+        const float *xss = xs + (size_t)s * 8, *xms = xsum + (size_t)s * 8;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) A.q[i] = *reinterpret_cast<const uint2 *>(xqs + aoff[i]);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int c = tid + 512 * i, row = c >> 3, j = c & 7;
-            const int gm = min(m0 + row, m - 1);
-            A.xs[i] = xs[(size_t)gm * kb + 8 * s + j];
-            A.xsum[i] = xsum[(size_t)gm * kb + 8 * s + j];
+            A.xs[i] = xss[xoff[i]];
+            A.xsum[i] = xms[xoff[i]];
         }
     };
     auto store_act = [&](int buf, const ASet &A) {
@@ -673,7 +687,7 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         constexpr int P = decltype(Pc)::value;
         // this superblock's scales: sc of the wave's blocks as f16 splats,
         // -dmin*m of the min-term operand, d of the lane's output rows
-        h2 scl[2][NBW], nscl[2][NBW];
+        uint32_t scpk[2][NPW];
         float amn[2][KS == 1 ? 2 : 1], dout[2][4];
         uint2 q[2][NPW];
 #pragma unroll
@@ -684,11 +698,7 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
             for (int pp = 0; pp < NPW; ++pp) q4k_scales(hd.y, hd.z, hd.w, NPW * h + pp, &sc2[pp], &mn2[pp]);
 #pragma unroll
-            for (int bl = 0; bl < NBW; ++bl) {
-                const float sc = (float)((sc2[bl / 2] >> (8 * (bl & 1))) & 0xFFu);
-                scl[t][bl] = splat(sc);
-                nscl[t][bl] = splat(-1024.0f * sc);
-            }
+            for (int pp = 0; pp < NPW; ++pp) scpk[t][pp] = sc2[pp];
             // min-term operand: block 4*i + lq of the wave's blocks (lanes
             // lq = 2, 3 take the second pair; bit arithmetic rather than an
             // indexed array, which the compiler would place in LDS)
@@ -719,30 +729,41 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
                 for (int e = 0; e < 4; ++e) xv[u][4 * c + e] = v[e];
             }
         }
-#pragma unroll
-        for (int bl = 0; bl < NBW; ++bl) {
+        auto mma = [&](int bl, v4f (&R)[2][4]) {
             const int jb = NBW * h + bl;  // block within the superblock
             h8 bf[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 bf[u] = *reinterpret_cast<const h8 *>(&As[P][(64 * mg + 16 * u + li) * ST + 32 * jb + 8 * lq]);
-            v4f T[2][4];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                // the block's sc as an f16 pair (exact: the half 1024 + sc,
+                // minus 1024); the high nibbles stay in place (16*q), which
+                // the scale pair absorbs: (1024 + 16q)*(sc/16) - 64*sc = q*sc
+                const uint32_t sb = __builtin_amdgcn_perm(0x64646464u, scpk[t][bl / 2], (bl & 1) ? 0x04010401u : 0x04000400u);
+                const h2 sch = as_h2(sb) + splat(-1024.0f);
+                const h2 mul = (bl & 1) ? sch * splat(0.0625f) : sch;
+                const h2 add = sch * splat((bl & 1) ? -64.0f : -1024.0f);
                 const uint2 cw = q[t][bl / 2];
-                const uint32_t c0 = (bl & 1) ? (cw.x >> 4) : cw.x, c1 = (bl & 1) ? (cw.y >> 4) : cw.y;
-                const uint2 v0 = q4x4_to_f16(c0 & 0x0F0F0F0Fu, scl[t][bl], nscl[t][bl]);
-                const uint2 v1 = q4x4_to_f16(c1 & 0x0F0F0F0Fu, scl[t][bl], nscl[t][bl]);
+                const uint32_t msk = (bl & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+                const uint2 v0 = q4x4_to_f16(cw.x & msk, mul, add);
+                const uint2 v1 = q4x4_to_f16(cw.y & msk, mul, add);
                 const h8 af = __builtin_bit_cast(h8, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    T[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    R[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             }
+        };
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+            v4f T[2][4];
+            mma(bl, T);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[t][u] = xv[u][bl] * T[t][u] + acc[t][u];
+                for (int u = 0; u < 4; ++u) acc[t][u] = bl == 0 ? xv[u][bl] * T[t][u] : xv[u][bl] * T[t][u] + acc[t][u];
         }
+
         // superblock done: out += d*acc, then the min term of the wave's blocks
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -750,7 +771,6 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
             for (int u = 0; u < 4; ++u) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[t][u][r] = dout[t][r] * acc[t][u][r] + out[t][u][r];
-                acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
         for (int i = 0; i < (KS == 1 ? 2 : 1); ++i) {
@@ -862,6 +882,9 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
     hipStream_t s = (hipStream_t)stream;
     QmmArgs a{static_cast<const uint8_t *>(w), xq, xs, xsum, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
     const int vec = aligned(y, 16) && n % 4 == 0;
+    // the bm = 64 kernel addresses with 32-bit per-lane offsets
+    const bool off32 = n * (k / 256) * 144 < ((int64_t)1 << 32) && m * k < ((int64_t)1 << 32);
+    if (bm == 64 && !off32) bm = 128;
     if (bm == 64) {
         const dim3 grid((unsigned)div_up(n, 32 * QMM2_BM64_NG), (unsigned)div_up(m, 64 * QMM2_BM64_MG));
         hipLaunchKernelGGL((k_qmm2_q4k<QMM2_BM64_NG, QMM2_BM64_MG, QMM2_BM64_KS>), grid, dim3(512), 0, s, a, vec);
