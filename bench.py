@@ -479,6 +479,30 @@ def profile_run(copies: int, other_shapes: bool = False):
                       "q4k_bytes": Q4K_BYTES, "copy_bytes": CALIB_BYTES}))
 
 
+def profile_prefill_run(copies: int = 16):
+    """Short eager run for rocprofv3 counters of the Q4_K prefill GEMM:
+    m=512 x W[4096, 4096], 20 launches each at bm = 64 and bm = 128 over
+    rotating weight copies, then the 64 MiB calibration copy (torch neg x8)."""
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    m, n, k = 512, 4096, 4096
+    big, W = rotated(synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k), copies)
+    x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, m * k)).cuda()
+    xq, xs, xsum = qmv.quantize_act_q8(x, m, k)
+    y = torch.empty((m, n), device="cuda")
+    for bm in (64, 128):
+        for i in range(20):
+            qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y)
+    a = torch.ones(CALIB_BYTES // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(8):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": "qmm_q4k 512x4096x4096 bm=64 x20, bm=128 x20, neg 64MiB x8",
+                      "copy_bytes": CALIB_BYTES}))
+
+
 def counter_rows(csv_path: str, counter: str):
     """{kernel name: [value per dispatch]} for one counter of a rocprofv3
     counter_collection.csv."""
@@ -527,6 +551,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--profile", action="store_true", help="short eager run for rocprofv3")
     ap.add_argument("--profile-all", action="store_true", help="--profile plus the Q8_0 and Q6_K shapes")
+    ap.add_argument("--profile-prefill", action="store_true", help="short eager prefill run for rocprofv3")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc runs of --profile into the traffic file, then exit")
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,6 +578,9 @@ def main():
 
     if a.profile or a.profile_all:
         profile_run(a.copies, a.profile_all)
+        return
+    if a.profile_prefill:
+        profile_prefill_run()
         return
     khash = source_hash(KERNEL_SOURCES)
     h = headline(a.steps, a.warmup, a.copies)
