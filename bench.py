@@ -340,6 +340,13 @@ def prefill_other(copies: int = 16):
         res[f"bm{bm}"] = {"us": round(ms * 1e3, 2), "tops": round(tops, 2),
                           "mfma_f16_pct": round(tops / MFMA_F16_PEAK_TFLOPS * 100, 2),
                           "int8_peak_pct": round(tops / MFMA_I8_PEAK_TOPS * 100, 2)}
+    ws = torch.empty(qmv.qmm_q4k_split_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    ms = time_graph(lambda i: qmv.qmm_q4k_split(W[i % copies], xq, xs, xsum, m, n, k, y=y, ws=ws), 2 * copies, 5)
+    tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    res["split"] = {"us": round(ms * 1e3, 2), "tops": round(tops, 2),
+                    "mfma_f16_pct": round(tops / MFMA_F16_PEAK_TFLOPS * 100, 2),
+                    "note": "qmm_q4k_split: activation pre-pass + GEMM, both launches"}
+    del ws
     qa = time_graph(lambda i: qmv.quantize_act_q8(x, m, k, out=(xq, xs, xsum)), 32, 5)
     res["quantize_act_q8_us"] = round(qa * 1e3, 2)
     del big, W
@@ -481,8 +488,9 @@ def profile_run(copies: int, other_shapes: bool = False):
 
 def profile_prefill_run(copies: int = 16):
     """Short eager run for rocprofv3 counters of the Q4_K prefill GEMM:
-    m=512 x W[4096, 4096], 20 launches each at bm = 64 and bm = 128 over
-    rotating weight copies, then the 64 MiB calibration copy (torch neg x8)."""
+    m=512 x W[4096, 4096], 20 launches each of qmm_q4k at bm = 64 and
+    bm = 128 and of qmm_q4k_split over rotating weight copies, then the
+    64 MiB calibration copy (torch neg x8)."""
     import torch
     import moe_ggml_block_amd as qmv
     import synth
@@ -494,12 +502,15 @@ def profile_prefill_run(copies: int = 16):
     for bm in (64, 128):
         for i in range(20):
             qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y)
+    ws = torch.empty(qmv.qmm_q4k_split_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    for i in range(20):
+        qmv.qmm_q4k_split(W[i % copies], xq, xs, xsum, m, n, k, y=y, ws=ws)
     a = torch.ones(CALIB_BYTES // 4, device="cuda")
     b = torch.empty_like(a)
     for _ in range(8):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": "qmm_q4k 512x4096x4096 bm=64 x20, bm=128 x20, neg 64MiB x8",
+    print(json.dumps({"profile_run": "qmm_q4k 512x4096x4096 bm=64 x20, bm=128 x20, qmm_q4k_split x20, neg 64MiB x8",
                       "copy_bytes": CALIB_BYTES}))
 
 

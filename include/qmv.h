@@ -251,6 +251,24 @@ int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum,
             int64_t m, int64_t n, int64_t k, int bm, qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The same Q4_K prefill product (`mmq_q4k_rt_gpu` on its q8 activation),
+ *   Y[i, r] = sum_c W_deq[r, c] * xs[i, c/32] * xq[i, c],
+ * formed from the dequantized activation instead of the integer block dots:
+ * a pre-pass writes each row of xs*xq, scaled by a power of two that puts
+ * the row's largest magnitude in [2^14, 2^15), as two f16 halves (high part
+ * and the f16 of the remainder: 22 bits of each value) into ws, then one
+ * GEMM accumulates whole superblocks on the f16 matrix cores (two MFMAs per
+ * block, no per-block epilogue) and undoes the row scale exactly. Same
+ * operands and results as qmm_q4k to f32 accuracy; two launches.
+ * ws: qmm_q4k_split_workspace_bytes(m, k) bytes (m*k*4 plus row scales),
+ * 256-byte aligned, caller-owned, overwritten. k % 256 == 0; m*k*2 and
+ * n*(k/256)*144 below 2^32 (else QMV_EUNSUPPORTED); w and xq 16-byte
+ * aligned, the rest 4-byte. */
+int64_t qmm_q4k_split_workspace_bytes(int64_t m, int64_t k); /* -1 for invalid shapes */
+int qmm_q4k_split(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y, void *ws,
+                  int64_t ws_bytes, int64_t m, int64_t n, int64_t k, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Expert-indexed Q4_K prefill GEMM on a q8 activation (the MoE prefill twin
  * of moe_qmv_q4k: `check_mmq_q4k_id` of hanzo-kernel `src/main.rs`,
  * expert-indexed MMQ with its slot grouping):

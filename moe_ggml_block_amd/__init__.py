@@ -42,6 +42,7 @@ _SIGS = {
     "moe_qmv_q8_0": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
+    "qmm_q4k_split": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "qmm_q6k": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "qmm_q8_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
@@ -64,12 +65,15 @@ _lib.moe_ffn_prefill_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
 _lib.moe_ffn_prefill_workspace_bytes.restype = _i64
 _lib.moe_ffn_q8_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
 _lib.moe_ffn_q8_workspace_bytes.restype = _i64
+_lib.qmm_q4k_split_workspace_bytes.argtypes = [_i64, _i64]
+_lib.qmm_q4k_split_workspace_bytes.restype = _i64
 _lib.qmv_version.restype = ctypes.c_char_p
 _lib.qmv_strerror.argtypes = [_i32]
 _lib.qmv_strerror.restype = ctypes.c_char_p
 
 EXPORTS = tuple(_SIGS) + ("moe_ffn_workspace_bytes", "moe_ffn_prefill_workspace_bytes",
-                          "moe_ffn_q8_workspace_bytes", "qmv_version", "qmv_strerror")
+                          "moe_ffn_q8_workspace_bytes", "qmm_q4k_split_workspace_bytes", "qmv_version",
+                          "qmv_strerror")
 
 BLOCK = {"q8_0": (32, 34), "q4k": (256, 144), "q6k": (256, 210), "q4_0": (32, 18), "q5k": (256, 176)}
 
@@ -247,6 +251,28 @@ def qmm_q4k(w, xq, xs, xsum, m, n, k, bm=128, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     _check(_lib.qmm_q4k(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), m, n, k, bm, _stream(stream)), "qmm_q4k")
+    return y
+
+
+def qmm_q4k_split_workspace_bytes(m, k) -> int:
+    return int(_lib.qmm_q4k_split_workspace_bytes(m, k))
+
+
+def qmm_q4k_split(w, xq, xs, xsum, m, n, k, y=None, ws=None, stream=None):
+    """Q4_K prefill GEMM on the dequantized q8 activation split into two f16
+    halves (pre-pass into ws, then one GEMM): y = deq(xq, xs) . W^T."""
+    _need(w, n * row_bytes("q4k", k), "w")
+    _need(xq, m * k, "xq")
+    _need(xs, 4 * m * (k // 32), "xs")
+    _need(xsum, 4 * m * (k // 32), "xsum")
+    nb = qmm_q4k_split_workspace_bytes(m, k)
+    if ws is None:
+        ws = torch.empty(nb, dtype=torch.uint8, device=xq.device)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _need(y, 4 * m * n, "y")
+    _check(_lib.qmm_q4k_split(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), _p(ws), ws.numel() * ws.element_size(),
+                              m, n, k, _stream(stream)), "qmm_q4k_split")
     return y
 
 

@@ -836,6 +836,294 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     }
 }
 
+// ------------------------------------ Q4_K prefill on a split f16 activation
+// Y = W_deq x_deq with x_deq = xs * xq (the q8 activation, dequantized):
+// a pre-pass writes each row of x_deq, scaled by a power of two rs that puts
+// the row's largest magnitude (xs*127 of its largest block) in [2^14, 2^15),
+// as two f16 halves: hi = f16(v), lo = f16(v - hi), v = rs * xs * xq. Their
+// sum keeps 22 bits of v (the f32 product itself is within 2^-24), so
+//   Y[i, r] = (1/rs_i) * sum_s d[r,s] * sum_{c in s} (sc*q)[r, c] * (hi + lo)[i, c]
+//             - sum_b xsum[i,b] * dmin[r,s(b)] * m[r,b]
+// needs no per-block epilogue: the matrix cores accumulate a whole
+// superblock (two MFMAs per block, hi then lo), and the vector ALU only adds
+// d times that sum once per superblock. The min term takes rs*xsum (exact)
+// so that it lands in the same scaled units, and the epilogue multiplies by
+// 1/rs (exact).
+//
+// Pre-pass: one 256-thread workgroup per activation row.
+QMV_DEV float group_max_wave(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__global__ __launch_bounds__(256) void k_act_split(const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                   _Float16 *__restrict__ hi, _Float16 *__restrict__ lo,
+                                                   float *__restrict__ rs, float *__restrict__ rinv, int k) {
+    const int row = blockIdx.x, tid = threadIdx.x, kb = k / 32;
+    const float *xr = xs + (size_t)row * kb;
+    float am = 0.f;
+    for (int b = tid; b < kb; b += 256) am = fmaxf(am, xr[b]);
+    __shared__ float red[4];
+    am = group_max_wave(am);
+    if ((tid & 63) == 0) red[tid >> 6] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * 127.0f;
+    // am in [2^e, 2^(e+1)): scale 2^(14 - e), kept normal both ways
+    const int e = am > 0.f ? ((int)((__float_as_uint(am) >> 23) & 0xFF) - 127) : 0;
+    const int ee = max(min(14 - e, 126), -126);
+    const float sc = __uint_as_float((uint32_t)(ee + 127) << 23);
+    if (tid == 0) {
+        rs[row] = sc;
+        rinv[row] = __uint_as_float((uint32_t)(127 - ee) << 23);
+    }
+    const int8_t *qr = xq + (size_t)row * k;
+    for (int c = 8 * tid; c < k; c += 8 * 256) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(qr + c);
+        const float f = xr[c / 32] * sc;  // exact scaling of xs
+        _Float16 h[8], l[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int qv = (int)(int8_t)(((j < 4 ? q.x : q.y) >> (8 * (j & 3))) & 0xFFu);
+            const float v = f * (float)qv;
+            h[j] = (_Float16)v;
+            l[j] = (_Float16)(v - (float)h[j]);
+        }
+        *reinterpret_cast<h8 *>(hi + (size_t)row * k + c) = h8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+        *reinterpret_cast<h8 *>(lo + (size_t)row * k + c) = h8{l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]};
+    }
+}
+
+// The GEMM: the weight-side tile of k_qmm2_q4k (four groups of 32 weight
+// rows, 64 activation rows, the blocks of each superblock split 4 + 4 over
+// two waves), with hi and lo staged in LDS as they are (one superblock
+// ahead in registers) and each block's fragment products accumulated on the
+// matrix cores.
+__global__ __launch_bounds__(512) void k_qmm4_q4k(const QmmArgs a, const _Float16 *__restrict__ xhi,
+                                                  const _Float16 *__restrict__ xlo, const float *__restrict__ rs,
+                                                  const float *__restrict__ rinv, int vec_store) {
+    constexpr int BN = 128, BM = 64, NPW = 2;
+    constexpr int ST = 256 + 8;  // halves per LDS row (4-bank shift per row)
+    constexpr int XST = 12;
+    constexpr int AC = BM * 32 / 512;  // 16-byte (8-half) chunks of hi (and of lo) per thread
+    __shared__ __attribute__((aligned(16))) _Float16 Ah[2][BM * ST];
+    __shared__ __attribute__((aligned(16))) _Float16 Al[2][BM * ST];
+    __shared__ __attribute__((aligned(16))) float sxsum[2][BM * XST];
+
+    const uint8_t *__restrict__ w = a.w;
+    const float *__restrict__ xsum = a.xsum;
+    const int m = a.m, n = a.n, k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = wave & 1, g = wave >> 1;
+    const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int nsb = k / 256, kb = k / 32;
+    const size_t row_bytes = (size_t)nsb * 144;
+
+    uint32_t woff[2], qoff[2][NPW];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        woff[t] = (uint32_t)((size_t)min(n0 + 32 * g + 16 * t + li, n - 1) * row_bytes);
+#pragma unroll
+        for (int pp = 0; pp < NPW; ++pp) qoff[t][pp] = woff[t] + 16 + 32 * (NPW * h + pp) + 8 * lq;
+    }
+    struct WSet {
+        uint4 hdr[2];
+        uint2 qc[2][NPW];
+    };
+    auto load_w = [&](int s, WSet &W) {
+        const uint8_t *wsb = w + (size_t)s * 144;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            W.hdr[t] = ld16(wsb + woff[t]);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) W.qc[t][pp] = *reinterpret_cast<const uint2 *>(wsb + qoff[t][pp]);
+        }
+    };
+    // staging: chunk c = tid + 512*i is row c/32, halves 8*(c%32) of the
+    // superblock (consecutive lanes write consecutive 16-byte units)
+    uint32_t aoff[AC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 512 * i;
+        aoff[i] = (uint32_t)((size_t)min(m0 + (c >> 5), m - 1) * k + 8 * (c & 31));
+    }
+    const int xrow = tid >> 3, xj = tid & 7;
+    const int xgm = min(m0 + xrow, m - 1);
+    const uint32_t xoff = (uint32_t)((size_t)xgm * kb + xj);
+    const float xrs = rs[xgm];
+    // native vectors (a HIP uint4 copy is a struct memcpy that the compiler
+    // left in scratch memory)
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    struct ASet {
+        u4 h[AC], l[AC];
+        float xsum;
+    };
+    auto load_act = [&](int s, ASet &A) {
+        const _Float16 *hs = xhi + (size_t)s * 256, *ls = xlo + (size_t)s * 256;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            A.h[i] = *reinterpret_cast<const u4 *>(hs + aoff[i]);
+            A.l[i] = *reinterpret_cast<const u4 *>(ls + aoff[i]);
+        }
+        A.xsum = xsum[(size_t)s * 8 + xoff];
+    };
+    // Rows past m hold row m - 1's (finite) data: an activation row only
+    // feeds its own output row, which is not stored, so nothing is zeroed
+    // (a select on the loaded values let the compiler sink those loads to
+    // the store and wait for them there).
+    auto store_act = [&](int buf, const ASet &A) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
+            *reinterpret_cast<u4 *>(&Ah[buf][row * ST + 8 * c8]) = A.h[i];
+            *reinterpret_cast<u4 *>(&Al[buf][row * ST + 8 * c8]) = A.l[i];
+        }
+        sxsum[buf][xrow * XST + xj] = A.xsum * xrs;
+    };
+
+    v4f out[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // unconditional loads, indices past the end clamped (exact wait counts)
+    WSet wset[2];
+    {
+        ASet a0;
+        load_w(0, wset[0]);
+        load_act(0, a0);
+        load_w(min(1, nsb - 1), wset[1]);
+        store_act(0, a0);
+    }
+    __syncthreads();
+
+    auto superblock = [&](int s, auto Pc) {
+        constexpr int P = decltype(Pc)::value;
+        uint32_t scpk[2][NPW];
+        float amn[2], dout[2][4];
+        uint2 q[2][NPW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint4 hd = wset[P].hdr[t];
+            const float dmin = h2f(hd.x >> 16);
+            uint32_t mn2[NPW];
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q4k_scales(hd.y, hd.z, hd.w, NPW * h + pp, &scpk[t][pp], &mn2[pp]);
+            const uint32_t pr = mn2[0] ^ ((mn2[0] ^ mn2[1]) & (0u - (uint32_t)(lq >> 1)));
+            amn[t] = -dmin * (float)((pr >> (8 * (lq & 1))) & 0xFFu);
+            const float down = h2f(hd.x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[P].qc[t][pp];
+        }
+        // the activations (stored at the end of this superblock) are
+        // requested before the weights (used two superblocks on), so that
+        // their wait leaves the weight loads in flight
+        ASet aset;  // lives within this superblock only (kept in registers)
+        load_act(min(s + 1, nsb - 1), aset);
+        load_w(min(s + 2, nsb - 1), wset[P]);
+        v4f acc[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+            const int jb = 4 * h + bl;
+            h8 bh[4], bo[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bh[u] = *reinterpret_cast<const h8 *>(&Ah[P][(16 * u + li) * ST + 32 * jb + 8 * lq]);
+                bo[u] = *reinterpret_cast<const h8 *>(&Al[P][(16 * u + li) * ST + 32 * jb + 8 * lq]);
+            }
+            h8 af[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // sc*q in f16 (exact), the high nibbles in place as in k_qmm2_q4k
+                const uint32_t sb = __builtin_amdgcn_perm(0x64646464u, scpk[t][bl / 2], (bl & 1) ? 0x04010401u : 0x04000400u);
+                const h2 sch = as_h2(sb) + splat(-1024.0f);
+                const h2 mul = (bl & 1) ? sch * splat(0.0625f) : sch;
+                const h2 add = sch * splat((bl & 1) ? -64.0f : -1024.0f);
+                const uint2 cw = q[t][bl / 2];
+                const uint32_t msk = (bl & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+                const uint2 v0 = q4x4_to_f16(cw.x & msk, mul, add);
+                const uint2 v1 = q4x4_to_f16(cw.y & msk, mul, add);
+                af[t] = __builtin_bit_cast(h8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], bh[u], acc[t][u], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], bo[u], acc[t][u], 0, 0, 0);
+        }
+        // out += d*acc, then the min term of the wave's blocks (rs*xsum)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[t][u][r] = dout[t][r] * acc[t][u][r] + out[t][u][r];
+        float xb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xb[u] = sxsum[P][(16 * u + li) * XST + 4 * h + lq];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(amn[t], xb[u], out[t][u], 0, 0, 0);
+        // superblock s + 1 into the other buffer (every wave finished
+        // reading it before the last barrier; after the last superblock this
+        // stores unused data)
+        store_act(P ^ 1, aset);
+        __syncthreads();
+    };
+    for (int s = 0; s < nsb; s += 2) {
+        superblock(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nsb) superblock(s + 1, std::integral_constant<int, 1>{});
+    }
+
+    // the second half of each superblock's blocks adds in through LDS
+    float *red = reinterpret_cast<float *>(&Ah[0][0]);
+    if (h == 1) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[((g * 32) + 16 * t + 4 * u + r) * 64 + lane] = out[t][u][r];
+    }
+    __syncthreads();
+    if (h == 1) return;
+    float *__restrict__ Y = a.Y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = m0 + 16 * u + li;
+        if (row >= m) continue;
+        const float ri = rinv[row];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            v4f o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (out[t][u][r] + red[((g * 32) + 16 * t + 4 * u + r) * 64 + lane]) * ri;
+            const int col = n0 + 32 * g + 16 * t + 4 * lq;
+            float *dst = Y + (size_t)row * n + col;
+            if (vec_store && col + 3 < n) {
+                *reinterpret_cast<v4f *>(dst) = o;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < n) dst[r] = o[r];
+            }
+        }
+    }
+}
+
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile configurations (BM, BN, KP, MT, NT, threads) for the two bm settings
@@ -895,6 +1183,48 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
         const dim3 grid((unsigned)div_up(n, QMM_CFG256_BN), (unsigned)div_up(m, QMM_CFG256_BM));
         hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(QMM_CFG256_NT), 0, s, a);
     }
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+// workspace of qmm_q4k_split: hi and lo halves of the scaled activation,
+// then the row scales and their inverses (each part 256-byte aligned)
+static int64_t split_ws_parts(int64_t m, int64_t k, int64_t *o_lo, int64_t *o_rs, int64_t *o_ri) {
+    auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
+    const int64_t half = up(m * k * 2);
+    *o_lo = half;
+    *o_rs = 2 * half;
+    *o_ri = 2 * half + up(m * 4);
+    return 2 * half + 2 * up(m * 4);
+}
+
+extern "C" int64_t qmm_q4k_split_workspace_bytes(int64_t m, int64_t k) {
+    if (m < 1 || k < 256 || k % 256) return -1;
+    int64_t a, b, c;
+    return split_ws_parts(m, k, &a, &b, &c);
+}
+
+extern "C" int qmm_q4k_split(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
+                             void *ws, int64_t ws_bytes, int64_t m, int64_t n, int64_t k, qmv_stream_t stream) {
+    if (!w || !xq || !xs || !xsum || !y || !ws || m < 1 || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (m > (1 << 24) || n > (1 << 24) || k > (1 << 20) || n * (k / 256) * 144 >= ((int64_t)1 << 32) ||
+        m * k * 2 >= ((int64_t)1 << 32))
+        return QMV_EUNSUPPORTED;
+    int64_t olo, ors, ori;
+    if (ws_bytes < split_ws_parts(m, k, &olo, &ors, &ori)) return QMV_EINVAL;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(y, 4) ||
+        !aligned(ws, 256))
+        return QMV_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    _Float16 *hi = reinterpret_cast<_Float16 *>(base), *lo = reinterpret_cast<_Float16 *>(base + olo);
+    float *rs = reinterpret_cast<float *>(base + ors), *ri = reinterpret_cast<float *>(base + ori);
+    hipLaunchKernelGGL(k_act_split, dim3((unsigned)m), dim3(256), 0, s, xq, xs, hi, lo, rs, ri, (int)k);
+    QMV_LAUNCH_CHECK();
+    QmmArgs a{static_cast<const uint8_t *>(w), xq, xs, xsum, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
+    const int vec = aligned(y, 16) && n % 4 == 0;
+    hipLaunchKernelGGL(k_qmm4_q4k, dim3((unsigned)div_up(n, 128), (unsigned)div_up(m, 64)), dim3(512), 0, s, a, hi,
+                       lo, rs, ri, vec);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

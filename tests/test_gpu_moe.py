@@ -252,6 +252,62 @@ def test_qmm_full_config_sampled_rows(bm):
     assert np.isfinite(Y).all()
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 32, 256), (40, 70, 512), (65, 130, 768), (200, 257, 1024),
+                                   (64, 128, 2048), (129, 131, 512), (257, 33, 2048)])
+def test_qmm_split_small_shapes(m, n, k):
+    """qmm_q4k_split (dequantized activation as two f16 halves) against the
+    same oracle as qmm_q4k, with ragged row and column tiles."""
+    announce(f"qmm_split m={m} n={n} k={k}")
+    w = synth.weights(synth.FMT_Q4K, 62, n, k)
+    x = synth.normal(63, m * k).reshape(m, k)
+    xq, xs, xsum = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q4k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q4k_split(dev(w), dev(xq), dev(xs), dev(xsum), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_split_row_magnitudes():
+    """Rows spanning 60 orders of magnitude, an all-zero row and a row with one
+    large block among tiny ones: the per-row power-of-two scale keeps each
+    row's two halves in the f16 range (checked per row against the oracle)."""
+    m, n, k = 6, 96, 1024
+    announce("qmm_split row magnitudes")
+    w = synth.weights(synth.FMT_Q4K, 64, n, k)
+    x = synth.normal(65, m * k).reshape(m, k)
+    x[0] *= 1e-30
+    x[1] *= 1e30
+    x[2] = 0.0
+    x[3, :32] *= 1e6
+    x[4, 32:] *= 1e-12
+    xq, xs, xsum = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q4k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q4k_split(dev(w), dev(xq), dev(xs), dev(xsum), m, n, k))
+    assert np.isfinite(got).all()
+    assert np.array_equal(got[2], np.zeros(n, dtype=np.float32))
+    for i in (0, 1, 3, 4, 5):
+        assert scalerel(ref[i], got[i]) <= TOL, (i, scalerel(ref[i], got[i]))
+
+
+def test_qmm_split_full_config_sampled_rows():
+    """m=512 tokens x W[4096, 4096] through the split path: 24 sampled rows
+    against the oracle, the rest finite and equal to qmm_q4k within 1e-4."""
+    m, n, k = 512, 4096, 4096
+    announce("qmm_split full")
+    w = synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k)
+    x = synth.normal(synth.SEED_PREFILL_X, m * k).reshape(m, k)
+    xq, xs, xsum = qmv.quantize_act_q8(dev(x), m, k)
+    rq, rs, _ = oracle.quantize_act_q8(x, m, k)
+    wd = dev(w)
+    Y = host(qmv.qmm_q4k_split(wd, xq, xs, xsum, m, n, k))
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 128, 129, 200, 255, 256, 300, 383, 384, 400, 450,
+                     479, 480, 495, 500, 509, 510, 511])
+    ref = oracle.qmm("q4k", w, rq, rs, m, n, k, mrows=rows)
+    assert scalerel(ref, Y[rows]) <= TOL, scalerel(ref, Y[rows])
+    assert np.isfinite(Y).all()
+    Y64 = host(qmv.qmm_q4k(wd, xq, xs, xsum, m, n, k, bm=64))
+    assert scalerel(Y64, Y) <= TOL
+
+
 # ------------------------------------------------- router fused in the layer
 @pytest.mark.parametrize("T,E_,topk", [(1, 128, 8), (4, 128, 8), (8, 128, 8), (16, 128, 8), (33, 128, 8),
                                        (3, 256, 64), (5, 300, 6), (2, 7, 7)])
