@@ -552,7 +552,14 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
 // blocks, the 2x4 fragment products T (one v_mfma_f32_16x16x32_f16 each),
 // adds xs*T into acc, then out += d*acc and the min term of its blocks
 // (-dmin*m x xsum, one v_mfma_f32_16x16x4_f32 per four blocks).
-template <int NG, int MG, int KS>
+//
+// PAIRT: the MoE prefill gate/up GEMM on the tile table (k_group_tiles):
+// workgroup row block blockIdx.y is table tile blockIdx.y (its expert and 64
+// slots, -1 past the expert's count; spare tiles exit), activation row of
+// slot s is s / x_div, and the wave's two 16-row fragments are gate row i
+// (t = 0) and up row i (t = 1) of the same h column, so a lane holds both
+// dots of its outputs and writes h = silu(gate) * up.
+template <int NG, int MG, int KS, bool PAIRT = false>
 __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store) {
     static_assert(NG * MG * KS == 8 && (KS == 1 || KS == 2), "eight waves");
     constexpr int BN = 32 * NG, BM = 64 * MG;
@@ -580,6 +587,29 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nsb = k / 256, kb = k / 32;
     const size_t row_bytes = (size_t)nsb * 144;
+    static_assert(!PAIRT || (MG == 1 && KS == 2), "paired tiles: one 64-slot group, split blocks");
+
+    // weight banks of the two fragments (gate and up for PAIRT) and the
+    // tile's slots
+    __shared__ int s_slot[PAIRT ? BM : 1];
+    const uint8_t *wb[2] = {w, w};
+    if constexpr (PAIRT) {
+        const int esel = __builtin_amdgcn_readfirstlane(table_tile<BM, 512>(a.ntiles, a.tile_e, a.tile_slots, s_slot));
+        if (esel < 0) return;  // uniform: past the last tile
+        wb[0] = a.w + (size_t)esel * n * row_bytes;
+        wb[1] = a.w2 + (size_t)esel * n * row_bytes;
+    }
+    // PAIRT: h columns [hb, hb + BN/2) of the workgroup, 16 per wave group
+    const int hb = blockIdx.x * (BN / 2);
+    // activation row of staging row `row` (always a valid row to read)
+    auto act_row = [&](int row) -> int {
+        if constexpr (PAIRT) {
+            const int sl = s_slot[row];
+            return sl >= 0 ? sl / a.x_div : 0;
+        } else {
+            return min(m0 + row, m - 1);
+        }
+    };
 
     // Load addresses are a uniform base (the superblock's offset folded in,
     // scalar registers) plus a per-lane 32-bit offset fixed for the whole
@@ -589,7 +619,8 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     uint32_t woff[2], qoff[2][NPW];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        woff[t] = (uint32_t)((size_t)min(n0 + 32 * g + 16 * t + li, n - 1) * row_bytes);
+        const int wr = PAIRT ? hb + 16 * g + li : n0 + 32 * g + 16 * t + li;
+        woff[t] = (uint32_t)((size_t)min(wr, n - 1) * row_bytes);
 #pragma unroll
         for (int pp = 0; pp < NPW; ++pp) qoff[t][pp] = woff[t] + 16 + 32 * (NPW * h + pp) + 8 * lq;
     }
@@ -603,9 +634,9 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         uint2 qc[2][NPW];
     };
     auto load_w = [&](int s, WSet &W) {
-        const uint8_t *wsb = w + (size_t)s * 144;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            const uint8_t *wsb = wb[t] + (size_t)s * 144;
             W.hdr[t] = ld16(wsb + woff[t]);
 #pragma unroll
             for (int pp = 0; pp < NPW; ++pp) W.qc[t][pp] = *reinterpret_cast<const uint2 *>(wsb + qoff[t][pp]);
@@ -625,12 +656,12 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
         const int c = tid + 512 * i;
-        aoff[i] = (uint32_t)((size_t)min(m0 + (c >> 5), m - 1) * k + 8 * (c & 31));
+        aoff[i] = (uint32_t)((size_t)act_row(c >> 5) * k + 8 * (c & 31));
     }
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
         const int c = tid + 512 * i;
-        xoff[i] = (uint32_t)((size_t)min(m0 + (c >> 3), m - 1) * kb + (c & 7));
+        xoff[i] = (uint32_t)((size_t)act_row(c >> 3) * kb + (c & 7));
     }
     auto load_act = [&](int s, ASet &A) {
         const int8_t *xqs = xq + (size_t)s * 256;
@@ -647,14 +678,14 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
-            const uint2 v = m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
+            const uint2 v = PAIRT || m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
             const uint2 h0 = i8x4_to_f16(v.x), h1 = i8x4_to_f16(v.y);
             *reinterpret_cast<uint4 *>(&As[buf][row * ST + 8 * c8]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
         }
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int c = tid + 512 * i, row = c >> 3, j = c & 7;
-            const bool ok = m0 + row < m;
+            const bool ok = PAIRT || m0 + row < m;
             sxs[buf][row * XST + j] = ok ? A.xs[i] : 0.f;
             sxsum[buf][row * XST + j] = ok ? A.xsum[i] : 0.f;
         }
@@ -815,8 +846,22 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[t][u][r] += red[((pair * 32) + 16 * t + 4 * u + r) * 64 + lane];
     }
-    // lane holds weight rows 4*lq + r of each 16x16 result, activation row li
     float *__restrict__ Y = a.Y;
+    if constexpr (PAIRT) {
+        // out[0] = gate, out[1] = up of h columns hb + 16g + 4lq + r
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int slot = s_slot[16 * u + li];
+            if (slot < 0) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = hb + 16 * g + 4 * lq + r;
+                if (col < n) Y[(size_t)slot * n + col] = silu(out[0][u][r]) * out[1][u][r];
+            }
+        }
+        return;
+    }
+    // lane holds weight rows 4*lq + r of each 16x16 result, activation row li
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int row = m0 + 64 * mg + 16 * u + li;
@@ -1809,8 +1854,15 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         hipLaunchKernelGGL((k_group_tiles<64>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
                            w.tile_slots);
         QMV_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true, true, true>), dim3((unsigned)div_up(inter, QMM_MOE64_BN / 2),
-                           (unsigned)mt), dim3(QMM_MOE64_NT), 0, s, gu);
+        // weight-side tile while its 32-bit lane offsets hold (an expert's
+        // rows and the activation rows below 2^32 bytes)
+        if (inter * (hidden / 256) * 144 < ((int64_t)1 << 32) && T * hidden < ((int64_t)1 << 32))
+            hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
+                               0, s, gu, 0);
+        else
+            hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true, true, true>),
+                               dim3((unsigned)div_up(inter, QMM_MOE64_BN / 2), (unsigned)mt), dim3(QMM_MOE64_NT), 0, s,
+                               gu);
         QMV_LAUNCH_CHECK();
         hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF64, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 128), (unsigned)mt),
                            dim3(512), 0, s, dn);
