@@ -553,14 +553,17 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
 // adds xs*T into acc, then out += d*acc and the min term of its blocks
 // (-dmin*m x xsum, one v_mfma_f32_16x16x4_f32 per four blocks).
 //
-// PAIRT: the MoE prefill gate/up GEMM on the tile table (k_group_tiles):
-// workgroup row block blockIdx.y is table tile blockIdx.y (its expert and 64
-// slots, -1 past the expert's count; spare tiles exit), activation row of
-// slot s is s / x_div, and the wave's two 16-row fragments are gate row i
-// (t = 0) and up row i (t = 1) of the same h column, so a lane holds both
-// dots of its outputs and writes h = silu(gate) * up.
-template <int NG, int MG, int KS, bool PAIRT = false>
+// MODE 1 (the MoE prefill gate/up GEMM on the tile table of
+// k_group_tiles): workgroup row block blockIdx.y is table tile blockIdx.y
+// (its expert and 64 slots, -1 past the expert's count; spare tiles exit),
+// activation row of slot s is s / x_div, and the wave's two 16-row fragments
+// are gate row i (t = 0) and up row i (t = 1) of the same h column, so a lane
+// holds both dots of its outputs and writes h = silu(gate) * up.
+// MODE 2 (moe_qmm_q4k): the same expert-indexed rows with the tile derived
+// in the kernel from ids (qmm_group), dense column layout, y[slot] rows.
+template <int NG, int MG, int KS, int MODE = 0>
 __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store) {
+    constexpr bool PAIRT = MODE == 1, GROUPED = MODE == 2, MOEM = MODE != 0;
     static_assert(NG * MG * KS == 8 && (KS == 1 || KS == 2), "eight waves");
     constexpr int BN = 32 * NG, BM = 64 * MG;
     constexpr int ST = 256 + 8;          // halves per LDS activation row (4-bank shift per row)
@@ -587,23 +590,30 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nsb = k / 256, kb = k / 32;
     const size_t row_bytes = (size_t)nsb * 144;
-    static_assert(!PAIRT || (MG == 1 && KS == 2), "paired tiles: one 64-slot group, split blocks");
+    static_assert(!MOEM || (MG == 1 && KS == 2), "expert-indexed tiles: one 64-slot group, split blocks");
 
     // weight banks of the two fragments (gate and up for PAIRT) and the
     // tile's slots
-    __shared__ int s_slot[PAIRT ? BM : 1];
+    __shared__ int s_slot[MOEM ? BM : 1];
     const uint8_t *wb[2] = {w, w};
     if constexpr (PAIRT) {
         const int esel = __builtin_amdgcn_readfirstlane(table_tile<BM, 512>(a.ntiles, a.tile_e, a.tile_slots, s_slot));
         if (esel < 0) return;  // uniform: past the last tile
         wb[0] = a.w + (size_t)esel * n * row_bytes;
         wb[1] = a.w2 + (size_t)esel * n * row_bytes;
+    } else if constexpr (GROUPED) {
+        // the activation buffers serve as the grouping's LDS scratch
+        static_assert(sizeof(As[0]) >= QMM_ID_CHUNK * 4 && sizeof(As[1]) >= QMM_MOE_MAX_E * 4, "grouping scratch");
+        const int esel = __builtin_amdgcn_readfirstlane(qmm_group<BM, BN, 512>(
+            a.ids, m, a.E, reinterpret_cast<int *>(&As[0][0]), reinterpret_cast<int *>(&As[1][0]), s_slot, a.Y, n, n0));
+        if (esel < 0) return;  // uniform: a spare workgroup (it wrote its zero rows)
+        wb[0] = wb[1] = a.w + (size_t)esel * n * row_bytes;
     }
     // PAIRT: h columns [hb, hb + BN/2) of the workgroup, 16 per wave group
     const int hb = blockIdx.x * (BN / 2);
     // activation row of staging row `row` (always a valid row to read)
     auto act_row = [&](int row) -> int {
-        if constexpr (PAIRT) {
+        if constexpr (MOEM) {
             const int sl = s_slot[row];
             return sl >= 0 ? sl / a.x_div : 0;
         } else {
@@ -678,14 +688,14 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
-            const uint2 v = PAIRT || m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
+            const uint2 v = MOEM || m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
             const uint2 h0 = i8x4_to_f16(v.x), h1 = i8x4_to_f16(v.y);
             *reinterpret_cast<uint4 *>(&As[buf][row * ST + 8 * c8]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
         }
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int c = tid + 512 * i, row = c >> 3, j = c & 7;
-            const bool ok = PAIRT || m0 + row < m;
+            const bool ok = MOEM || m0 + row < m;
             sxs[buf][row * XST + j] = ok ? A.xs[i] : 0.f;
             sxsum[buf][row * XST + j] = ok ? A.xsum[i] : 0.f;
         }
@@ -864,8 +874,10 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     // lane holds weight rows 4*lq + r of each 16x16 result, activation row li
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int row = m0 + 64 * mg + 16 * u + li;
-        if (row >= m) continue;
+        int row;
+        if constexpr (GROUPED) row = s_slot[16 * u + li];
+        else row = m0 + 64 * mg + 16 * u + li < m ? m0 + 64 * mg + 16 * u + li : -1;
+        if (row < 0) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int col = n0 + 32 * g + 16 * t + 4 * lq;
@@ -1294,7 +1306,14 @@ extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, 
     // tile count (every expert adds at most one partial tile) and the spare
     // workgroups exit after the grouping
     const dim3 grid((unsigned)div_up(n, QMM_MOE64_BN), (unsigned)(div_up(nslots, QMM_MOE64_BM) + std::min(E, nslots)));
-    hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
+    // the weight-side tile (128 weight rows x 64 slots, the same grid) while
+    // its 32-bit lane offsets hold: one expert's rows and the activation rows
+    // below 2^32 bytes
+    const int vec = aligned(y, 16) && n % 4 == 0;
+    if (n * (k / 256) * 144 < ((int64_t)1 << 32) && div_up(nslots, x_div) * k < ((int64_t)1 << 32))
+        hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 2>), grid, dim3(512), 0, s, a, vec);
+    else
+        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
@@ -1857,7 +1876,7 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         // weight-side tile while its 32-bit lane offsets hold (an expert's
         // rows and the activation rows below 2^32 bytes)
         if (inter * (hidden / 256) * 144 < ((int64_t)1 << 32) && T * hidden < ((int64_t)1 << 32))
-            hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
+            hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
                                0, s, gu, 0);
         else
             hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true, true, true>),
