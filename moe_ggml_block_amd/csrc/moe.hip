@@ -523,6 +523,23 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     // the token's experts (out of range -> -1) and weights
     __shared__ int s_e[64];
     __shared__ float s_w[64];
+    // f32 h rows of the first chunk: requested before the ids (they do not
+    // depend on them), so the two reads overlap instead of following each
+    // other; stored to LDS once the chunk's weight loads are in flight
+    constexpr int HPRE = 6;  // float4 per thread held: the layer's chunk, 8 slots x 768 values
+    const int k4 = a.k / 4;
+    const int nch0 = min(a.chunk, a.topk);
+    const bool hpre = !F::Q8 && nch0 * k4 <= HPRE * 256;
+    f32x4 hv0[HPRE];
+    if (!F::Q8 && hpre) {
+#pragma unroll
+        for (int r = 0; r < HPRE; ++r) {
+            const int i = tid + 256 * r;
+            const int ic = min(i, nch0 * k4 - 1);
+            const int j = ic / k4, c4 = ic - j * k4;
+            hv0[r] = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j) * a.k + 4 * c4);
+        }
+    }
     for (int i = tid; i < WAVES * a.rblk; i += 256) acc_lds[i] = 0.0f;
     if (tid < a.topk) {
         const int e = a.ids[(size_t)t * a.topk + tid];
@@ -572,8 +589,18 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
                 hlds[j * ust + F::ACT_STRIDE * u + 16 + g] = sc;
                 hlds[j * ust + F::ACT_STRIDE * (u + 1) + 16 + g] = sc;
             }
+        } else if (j0 == 0 && hpre) {
+#pragma unroll
+            for (int r = 0; r < HPRE; ++r) {
+                const int i = tid + 256 * r;
+                if (i < nch * k4) {
+                    const int j = i / k4, c4 = i - j * k4;
+                    int jj;
+                    const int u = F::xslot(4 * c4, &jj);
+                    *reinterpret_cast<f32x4 *>(hlds + j * ust + F::ACT_STRIDE * u + jj) = hv0[r];
+                }
+            }
         } else {
-            const int k4 = a.k / 4;
             for (int i = tid; i < nch * k4; i += 256) {
                 const int j = i / k4, c4 = i - j * k4;
                 const f32x4 hv = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j0 + j) * a.k + 4 * c4);
