@@ -39,6 +39,8 @@ Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
 # one qmv_q4k launch: every packed row (2,304 B) plus its f32 output, and x once
 Q4K_LAUNCH_BYTES = Q4K_BYTES + 4 * N2 + 4 * K2  # 33,103,872
 CALIB_BYTES = 64 << 20                         # the counter-calibration copy
+WARM_MS = 30.0            # untimed replays before each kernel timing
+HEADLINE_WARM_MS = 100.0  # untimed steps before the headline's timed region (beyond --warmup)
 TRAFFIC_JSON = os.path.join("profiles", "qmv_q4k_14336x4096_traffic.json")
 METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
 KERNEL_SOURCES = ["moe_ggml_block_amd/csrc/common.hpp",
@@ -90,12 +92,29 @@ def capture(fn, calls: int):
     return g
 
 
+def warm_replays(g, min_ms: float) -> int:
+    """Replays g, untimed, until at least min_ms of wall time has passed (at
+    least once): the GPU leaves its idle clocks during set-up phases that
+    run on the host (weight generation), and the timed region should see
+    the clocks a steady stream of launches runs at. Returns the replays run."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        g.replay()
+        n += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
+
+
 def time_graph(fn, calls: int, replays: int = 20) -> float:
-    """Average ms per fn call, over `replays` replays of a `calls`-call graph."""
+    """Average ms per fn call, over `replays` replays of a `calls`-call graph
+    (after at least WARM_MS of untimed replays)."""
     import torch
     g = capture(fn, calls)
-    g.replay()
-    torch.cuda.synchronize()
+    warm_replays(g, WARM_MS)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(replays):
@@ -180,6 +199,10 @@ def headline(steps: int, warmup: int, copies: int):
     for _ in range(max(1, warmup // copies)):
         full.replay()
     torch.cuda.synchronize()
+    # more untimed steps if the requested warm-up was shorter than the clock
+    # ramp (reported as warmup_steps_run)
+    extra = warm_replays(full, HEADLINE_WARM_MS)
+    warmup_run = max(1, warmup // copies) * copies + extra * copies
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps // copies):
@@ -205,6 +228,7 @@ def headline(steps: int, warmup: int, copies: int):
     torch.cuda.empty_cache()
     return {
         "ms_per_step": ms,
+        "warmup_steps_run": warmup_run,
         "q4k_launch_ms": q4k_ms,
         "kernels": {
             "qmv_q4k_cold_us": round(k_f32 * 1e3, 3),
@@ -602,7 +626,8 @@ def main():
     traffic = traffic_from_profile(khash)
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(h["ms_per_step"], 6),
+        "steps": a.steps, "warmup": a.warmup, "warmup_steps_run": h["warmup_steps_run"],
+        "ms_per_step": round(h["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "Q4_K matvec 14336x4096, batch 1: f32-activation matvec + q8 activation "
