@@ -29,7 +29,8 @@ def _run_dense(fmt, w, x, n, k):
 # (n, k): several tiles, ragged row tails, every unit tiling (G = 8..64,
 # UPL 1..4), the generic path (Q8_0 k % 64 == 32, very long rows).
 SMALL = {
-    "q8_0": [(1, 32), (37, 96), (5, 64), (130, 512), (67, 2048), (29, 4096), (33, 8192), (9, 16384)],
+    "q8_0": [(1, 32), (37, 96), (5, 64), (130, 512), (67, 2048), (29, 4096), (33, 8192), (9, 16384),
+             (4133, 2048)],  # past 16 rows per CU: the two-workgroup launch form
     "q4k": [(1, 256), (37, 256), (70, 768), (65, 2048), (33, 4096), (17, 8192), (5, 12288), (3, 20480)],
     "q6k": [(1, 256), (37, 256), (70, 768), (65, 2048), (33, 4096), (17, 8192), (5, 12288), (3, 20480)],
     "q4_0": [(1, 32), (37, 96), (5, 64), (130, 512), (67, 2048), (29, 4096), (33, 8192), (9, 16384)],
