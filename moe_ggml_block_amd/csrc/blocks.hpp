@@ -585,7 +585,9 @@ struct Q4KQ8Unit {
     static constexpr bool Q8 = true;  // activation: q8 rows (xq, xs, xsum)
     static constexpr int BW = 256, BB = 144;
     static constexpr int RING = QMV_RING_Q4KQ8;
-    static constexpr int MAX_WG_PER_CU = 3;
+    // 7.15 us at 14336 x 4096 with 4 workgroups per CU, 7.25 with 3, 7.31 with
+    // 5, 8.93 with 2; deeper rings were slower at every count
+    static constexpr int MAX_WG_PER_CU = 4;
     static constexpr int ACT_STRIDE = 20;
     using Act = ActQ8;
     using X = UnitQ8;
