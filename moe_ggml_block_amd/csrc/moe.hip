@@ -32,6 +32,7 @@
 #include <cmath>
 
 #include "blocks.hpp"
+#include "internal.hpp"
 
 namespace {
 
@@ -793,6 +794,33 @@ int check_moe_args(const void *bank, const float *x, int64_t x_div, const int32_
 }
 
 }  // namespace
+
+int qmv_internal::moe_layer_q8x_f32h(const void *gate, const void *up, const void *down, const int8_t *xq,
+                                     const float *xs, const float *xsum, const int32_t *ids, const float *wts,
+                                     float *y, float *h, int64_t T, int64_t topk, int64_t hidden, int64_t inter,
+                                     int64_t E, hipStream_t s) {
+    const int64_t ns = T * topk;
+    if (ns > MAX_SLOTS || E > MAX_E || hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(down, 16)) return QMV_EALIGN;
+    MoeArgs gu = gather_args(gate, up, nullptr, topk, ids, h, ns, 2 * inter, hidden, E);
+    gu.xq = xq;
+    gu.xs = xs;
+    gu.xsum = xsum;
+    int rc = launch_gate_up<Q4KQ8Unit>(gu, s);
+    if (rc) return rc;
+    DownArgs dn{};
+    dn.bank = static_cast<const uint8_t *>(down);
+    dn.h = h;
+    dn.ids = ids;
+    dn.wts = wts;
+    dn.y = y;
+    dn.n = (int)hidden;
+    dn.k = (int)inter;
+    dn.E = (int)E;
+    dn.topk = (int)topk;
+    dn.chunk = down_chunk<Q6KUnit>(inter, topk);
+    return launch_down<Q6KUnit>(dn, T, s);
+}
 
 extern "C" int moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t E,
                          int64_t topk, qmv_stream_t stream) {

@@ -151,11 +151,12 @@ def test_graph_replay_prefill_gemms():
     _check_replays(run, lambda r: x.copy_(xs_all[r]), [xq, xs, xsum, y64, y128, ysp], "prefill")
 
 
-@pytest.mark.parametrize("E_,T,hidden,inter", [(128, 64, 2048, 768), (16, 128, 1024, 512)])
+@pytest.mark.parametrize("E_,T,hidden,inter", [(128, 64, 2048, 768), (128, 100, 2048, 768), (16, 128, 1024, 512)])
 def test_graph_replay_moe_prefill_layer(E_, T, hidden, inter):
-    """The MoE prefill layer (32-slot tiles at 64 tokens over 128 experts,
-    64-slot tiles at 128 tokens over 16) and the expert-indexed Q4_K GEMM,
-    on new routes and activations per replay."""
+    """The MoE prefill layer (on the decode gathers at 64 tokens, 32-slot
+    tiles at 100 tokens over 128 experts, 64-slot tiles at 128 tokens over
+    16) and the expert-indexed Q4_K GEMM, on new routes and activations per
+    replay."""
     announce(f"graph moe prefill E={E_} T={T} hidden={hidden} inter={inter}")
     topk = 8
     gate = dev(synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E_, inter, hidden))

@@ -242,6 +242,15 @@ def test_moe_prefill_layer_small_full_output():
     _layer(T, topk, E, hidden, inter, 110)
 
 
+@pytest.mark.parametrize("T,topk,E", [(64, 8, 16), (65, 8, 16), (100, 8, 128)])
+def test_moe_prefill_layer_both_sides_of_the_gather_threshold(T, topk, E):
+    """Up to 512 slots the layer runs on the decode gathers, above on the
+    GEMM tiles (32-slot tiles below 32 slots per expert, 64-slot above)."""
+    hidden, inter = 512, 256
+    announce(f"moe prefill layer T={T} topk={topk} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 150 + T)
+
+
 def test_moe_prefill_layer_full_shape_sampled_tokens():
     """512 tokens routed top-8 over 128 experts, gate/up [768, 2048], down
     [2048, 768]: every output column of 12 sampled tokens."""
@@ -271,4 +280,7 @@ def test_moe_prefill_layer_workspace_reuse_smaller_second_call():
     b = host(qmv.moe_ffn_prefill_q4k_q6k(G, U, D, dev(x[:7]), dev(ids[:7]), dev(wts[:7]), 7, topk, hidden, inter,
                                          E, ws=ws))
     assert np.array_equal(a, first)   # same inputs, same bits (grouping order does not matter)
-    assert np.array_equal(b, first[:7])
+    # a token's rows agree across batch sizes to the f32 tolerance, not bit for
+    # bit: the launch shape (and, across 512 slots, the kernels) set the
+    # rounding order of the combine
+    assert scalerel(first[:7], b) <= TOL, scalerel(first[:7], b)
