@@ -349,6 +349,10 @@ int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32
  * grouped by expert on the device; nothing is synchronized with the host.
  * hidden, inter: multiples of 256 (<= 65536); 1 <= E <= 1024; T <= 65535;
  * T*topk <= 2^20. gate, up, x, y 16-byte aligned; down 2-byte; rest 4-byte.
+ * Up to 512 slots (with hidden, inter <= 4096 and down 16-byte aligned) the
+ * same arithmetic runs on the expert-grouped decode gathers, which stream
+ * the bank faster there; a token's output then agrees across batch sizes
+ * to f32 rounding rather than bit for bit.
  * ---------------------------------------------------------------------- */
 int64_t moe_ffn_prefill_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E);
 int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
