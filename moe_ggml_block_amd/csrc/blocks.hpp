@@ -67,7 +67,9 @@ QMV_DEV void load_x_runs(UnitX &X, const float *x, int r0, int r1, int r2, int r
 
 // Activation staging in LDS: unit u's 64 values (in X.v order) sit at float
 // offset XSTRIDE*u; the 4-float pad makes the 16-byte reads of 8 consecutive
-// lanes (consecutive units) fall in disjoint LDS banks.
+// lanes (consecutive units) fall in disjoint LDS banks, and the dense
+// matvecs keep the unit's four 16-value sums (X.s) in it, computed once per
+// workgroup while staging instead of by every lane that reads the unit.
 constexpr int XSTRIDE = 68;
 
 QMV_DEV void load_x_lds(UnitX &X, const float *xl, int u) {
@@ -142,6 +144,41 @@ QMV_DEV void store_x(float *xl, const StageRegs &S, int k) {
     }
 }
 
+// staging with the four 16-value run sums of each unit written into its pad
+// (a run is 4 consecutive granules, held by 4 consecutive lanes)
+template <class F, int NS>
+QMV_DEV void store_x_sums(float *xl, const StageRegs &S, int k) {
+    const int last = k / 4 - 1;
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int i4r = (int)threadIdx.x + 256 * m;
+        const int i4 = min(i4r, last);
+        int j;
+        const int u = F::xslot(4 * i4, &j);
+        *reinterpret_cast<f32x4 *>(xl + XSTRIDE * u + j) = S[m];
+        float v = (S[m].x + S[m].y) + (S[m].z + S[m].w);
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if ((threadIdx.x & 3) == 0 && i4r <= last) xl[XSTRIDE * u + 64 + (j >> 4)] = v;
+    }
+}
+QMV_DEV void load_x_lds_pre(UnitX &X, const float *xl, int u) {
+    const float4 *a = reinterpret_cast<const float4 *>(xl + XSTRIDE * u);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+        const float4 q = a[g];
+        X.v[4 * g + 0] = q.x;
+        X.v[4 * g + 1] = q.y;
+        X.v[4 * g + 2] = q.z;
+        X.v[4 * g + 3] = q.w;
+    }
+    const float4 sm = a[16];
+    X.s[0] = sm.x;
+    X.s[1] = sm.y;
+    X.s[2] = sm.z;
+    X.s[3] = sm.w;
+}
+
 // f32 activation pack and its per-unit staging (shared by the f32 units).
 struct ActF32 {
     const float *x;
@@ -159,6 +196,9 @@ struct F32Act {
     template <int NS>
     static __device__ __forceinline__ void store(float *xl, const Stage &S, int k) { store_x<F, NS>(xl, S, k); }
     static __device__ __forceinline__ void load_lds(UnitX &X, const float *xl, int u) { load_x_lds(X, xl, u); }
+    template <int NS>
+    static __device__ __forceinline__ void store_s(float *xl, const Stage &S, int k) { store_x_sums<F, NS>(xl, S, k); }
+    static __device__ __forceinline__ void load_lds_s(UnitX &X, const float *xl, int u) { load_x_lds_pre(X, xl, u); }
 };
 
 // ---------------------------------------------------------------- Q8_0 ---

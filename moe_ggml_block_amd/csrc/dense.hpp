@@ -11,7 +11,8 @@
 // row; lane i of the group decodes units i and i+G (UPL <= 2). The
 // activation values under a lane's units are the same for every row: the
 // block loads the activation once with coalesced 16-byte loads into a padded
-// LDS layout (conflict-free reads), and each lane then keeps its units'
+// LDS layout (conflict-free reads; for f32 activations each unit's four
+// 16-value sums go into its pad), and each lane then keeps its units'
 // values in registers while the wave streams rows, 64/G per pass.
 //
 // Pass q of a wave is global pass q*nwaves + wave, so at any moment the grid
@@ -29,6 +30,8 @@
 // at F::MAX_WG_PER_CU workgroups per CU) so that every wave is resident at
 // once (one round, no tail).
 #pragma once
+
+#include <type_traits>
 
 #include "blocks.hpp"
 
@@ -89,11 +92,18 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     }
     // activations: coalesced loads into the padded LDS layout, then each
     // lane reads its units' values (conflict-free) into registers
-    F::template store<stage_granules(G, UPL)>(xlds, S, k);
-    __syncthreads();
     typename F::X X[UPL];
+    if constexpr (!F::Q8 && std::is_same<typename F::X, UnitX>::value) {
+        F::template store_s<stage_granules(G, UPL)>(xlds, S, k);
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
+        for (int i = 0; i < UPL; ++i) F::load_lds_s(X[i], xlds, uu[i]);
+    } else {
+        F::template store<stage_granules(G, UPL)>(xlds, S, k);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
+    }
 
     int pass = p0;
     do {
