@@ -185,8 +185,12 @@ int moe_qmv_q8_0(const void *bank, const float *x, int64_t x_div, const int32_t 
  *   y_t = sum_j wts[t, j] * d_{topk*t + j}       (fixed j order)
  * x: f32[T, hidden]; ids: int32[T, topk]; wts: f32[T, topk]; y: f32[T, hidden].
  * ws: caller-owned device workspace of at least moe_ffn_workspace_bytes()
- * bytes (16-byte aligned); its contents on return are unspecified.
- * hidden % 256 == 0, inter % 256 == 0.
+ * bytes (16-byte aligned); on return it holds h f32[T*topk, inter] (row s:
+ * the activation slot s passed to the down projection; zero for a slot
+ * whose id is outside [0, E)).
+ * hidden % 256 == 0, inter % 256 == 0; hidden, inter <= 4096; T <= 65535;
+ * 1 <= topk <= 64 (a token's slots are held on chip by the down pass:
+ * QMV_EUNSUPPORTED above that, before any launch); T*topk <= 2048.
  * ---------------------------------------------------------------------- */
 int64_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter);
 int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
@@ -228,7 +232,8 @@ int moe_qmv_q6k_q8(const void *bank, const int8_t *xq, const float *xs, int64_t 
  * h = silu(gate) * up from int8 dots (f32), h quantized (quantize_act_q8
  * per 32 values of each slot row), down on int8 dots with the weighted
  * combine -- four launches. Same operands as moe_ffn_q4k_q6k; ws:
- * moe_ffn_q8_workspace_bytes() bytes (q8 x, h, q8 h), 256-byte aligned. */
+ * moe_ffn_q8_workspace_bytes() bytes (q8 x, h, q8 h), 256-byte aligned.
+ * Limits as moe_ffn_q4k_q6k (1 <= topk <= 64). */
 int64_t moe_ffn_q8_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter);
 int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
                        const float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,
@@ -349,7 +354,8 @@ int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32
  * grouped by expert on the device; nothing is synchronized with the host.
  * hidden, inter: multiples of 256 (<= 65536); 1 <= E <= 1024; T <= 65535;
  * T*topk <= 2^20. gate, up, x, y 16-byte aligned; down 2-byte; rest 4-byte.
- * Up to 512 slots (with hidden, inter <= 4096 and down 16-byte aligned) the
+ * Any topk >= 1 is accepted. Up to 512 slots (with topk <= 64, hidden,
+ * inter <= 4096 and down 16-byte aligned) the
  * same arithmetic runs on the expert-grouped decode gathers, which stream
  * the bank faster there; a token's output then agrees across batch sizes
  * to f32 rounding rather than bit for bit.

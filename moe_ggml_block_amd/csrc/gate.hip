@@ -25,6 +25,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace {
 
@@ -188,10 +189,8 @@ extern "C" int moe_block_q4k_q6k(const float *wr, const void *gate, const void *
     int rc = check_gate(wr, x, logits, ids, wts, T, E, hidden, topk);
     if (rc) return rc;
     // the layer's own checks before anything is launched
-    if (!gate || !up || !down || !y || !ws || hidden < 256 || inter < 256 || hidden % 256 || inter % 256)
-        return QMV_EINVAL;
-    if (ws_bytes < moe_ffn_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
-    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden, inter, E);
+    if (rc) return rc;
     rc = launch_logits(wr, x, logits, T, E, hidden, (hipStream_t)stream);
     if (rc) return rc;
     return moe_ffn_routed_q4k_q6k(gate, up, down, x, logits, ids, wts, y, ws, ws_bytes, T, topk, hidden, inter, E,

@@ -38,6 +38,9 @@ namespace {
 
 constexpr int MAX_E = 4096;
 constexpr int MAX_SLOTS = 2048;
+// a token's slots held by the down pass (its ids and weights live in LDS
+// arrays of this size)
+constexpr int MAX_LAYER_TOPK = 64;
 constexpr int WAVES = 4;
 constexpr int SMALL_E = 256;  // router: one workgroup per token up to this E
 constexpr int ROUTE_FUSED_E = 256;  // routing fused into the gather up to this E
@@ -522,8 +525,8 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     const int uu = uv ? gl : U - 1;
     const int bpasses = (len + RPP - 1) / RPP;
     // the token's experts (out of range -> -1) and weights
-    __shared__ int s_e[64];
-    __shared__ float s_w[64];
+    __shared__ int s_e[MAX_LAYER_TOPK];
+    __shared__ float s_w[MAX_LAYER_TOPK];
     // f32 h rows of the first chunk: requested before the ids (they do not
     // depend on them), so the two reads overlap instead of following each
     // other; stored to LDS once the chunk's weight loads are in flight
@@ -795,12 +798,34 @@ int check_moe_args(const void *bank, const float *x, int64_t x_div, const int32_
 
 }  // namespace
 
+// Every check of the f32 decode layer (moe_ffn_q4k_q6k and the routed
+// forms), so that an entry point that launches several kernels can run all
+// of them before the first launch.
+int qmv_internal::check_decode_layer(const void *gate, const void *up, const void *down, const float *x,
+                                     const int32_t *ids, const float *wts, const float *y, const void *ws,
+                                     int64_t ws_bytes, int64_t T, int64_t topk, int64_t hidden, int64_t inter,
+                                     int64_t E) {
+    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
+    if (T < 1 || topk < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
+    if (ws_bytes < moe_ffn_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
+    const int64_t ns = T * topk;
+    float *yw = const_cast<float *>(y);
+    int rc = check_moe_args(gate, x, topk, ids, yw, ns, 2 * inter, hidden, E);
+    if (rc) return rc;
+    rc = check_moe_args(down, x, 1, ids, yw, ns, hidden, inter, E);
+    if (rc) return rc;
+    if (topk > MAX_LAYER_TOPK || hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 16)) return QMV_EALIGN;
+    return QMV_OK;
+}
+
 int qmv_internal::moe_layer_q8x_f32h(const void *gate, const void *up, const void *down, const int8_t *xq,
                                      const float *xs, const float *xsum, const int32_t *ids, const float *wts,
                                      float *y, float *h, int64_t T, int64_t topk, int64_t hidden, int64_t inter,
                                      int64_t E, hipStream_t s) {
     const int64_t ns = T * topk;
-    if (ns > MAX_SLOTS || E > MAX_E || hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (topk > MAX_LAYER_TOPK || ns > MAX_SLOTS || E > MAX_E || hidden > 4096 || inter > 4096 || T > 65535)
+        return QMV_EUNSUPPORTED;
     if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(down, 16)) return QMV_EALIGN;
     MoeArgs gu = gather_args(gate, up, nullptr, topk, ids, h, ns, 2 * inter, hidden, E);
     gu.xq = xq;
@@ -879,17 +904,10 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
                                const int32_t *ids, const float *wts, float *y, void *ws, int64_t ws_bytes,
                                int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
                                qmv_stream_t stream) {
-    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
-    if (T < 1 || topk < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
-    const int64_t need = moe_ffn_workspace_bytes(T, topk, hidden, inter);
-    if (ws_bytes < need) return QMV_EINVAL;
+    int rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden,
+                                              inter, E);
+    if (rc) return rc;
     const int64_t ns = T * topk;
-    int rc = check_moe_args(gate, x, topk, ids, y, ns, 2 * inter, hidden, E);
-    if (rc) return rc;
-    rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
-    if (rc) return rc;
-    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
-    if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 16)) return QMV_EALIGN;
     float *h = static_cast<float *>(ws);
     hipStream_t s = (hipStream_t)stream;
     // h = silu(gate x) * (up x): one gather over interleaved gate/up rows
@@ -921,22 +939,15 @@ extern "C" int moe_ffn_routed_q4k_q6k(const void *gate, const void *up, const vo
                                       int64_t E, qmv_stream_t stream) {
     if (!logits || topk > E || topk > 64) return QMV_EINVAL;
     if (!aligned(logits, 4)) return QMV_EALIGN;
+    int rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden,
+                                              inter, E);
+    if (rc) return rc;
     if (E > ROUTE_FUSED_E || T > ROUTE_FUSED_T) {
-        if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
-        const int rc = moe_route(logits, ids, wts, T, E, topk, stream);
+        rc = moe_route(logits, ids, wts, T, E, topk, stream);
         if (rc) return rc;
         return moe_ffn_q4k_q6k(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden, inter, E, stream);
     }
-    if (!gate || !up || !down || !x || !ids || !wts || !y || !ws) return QMV_EINVAL;
-    if (T < 1 || topk < 1 || hidden < 256 || inter < 256 || hidden % 256 || inter % 256) return QMV_EINVAL;
-    if (ws_bytes < moe_ffn_workspace_bytes(T, topk, hidden, inter)) return QMV_EINVAL;
     const int64_t ns = T * topk;
-    int rc = check_moe_args(gate, x, topk, ids, y, ns, 2 * inter, hidden, E);
-    if (rc) return rc;
-    rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
-    if (rc) return rc;
-    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
-    if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 16)) return QMV_EALIGN;
     float *h = static_cast<float *>(ws);
     hipStream_t s = (hipStream_t)stream;
     MoeArgs gu = gather_args(gate, up, x, topk, nullptr, h, ns, 2 * inter, hidden, E);
@@ -1035,7 +1046,7 @@ extern "C" int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *
     if (rc) return rc;
     rc = check_moe_args(down, x, 1, ids, y, ns, hidden, inter, E);
     if (rc) return rc;
-    if (hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
+    if (topk > MAX_LAYER_TOPK || hidden > 4096 || inter > 4096 || T > 65535) return QMV_EUNSUPPORTED;
     if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 256)) return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
     const Q8LayerWs w = q8_layer_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter);

@@ -1861,7 +1861,8 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
     // faster than the GEMM tiles (128 experts of [768, 2048]: 145 against
     // 288 us at 256 slots, 267 against 308 us at 512; at 1024 the GEMMs win,
     // 313 against 513 us); same arithmetic, h in the same workspace.
-    if (S <= 512 && hidden <= 4096 && inter <= 4096 && aligned(down, 16))
+    // (the decode down pass holds at most 64 slots of a token)
+    if (S <= 512 && topk <= 64 && hidden <= 4096 && inter <= 4096 && aligned(down, 16))
         return qmv_internal::moe_layer_q8x_f32h(gate, up, down, w.xq, w.xs, w.xsum, ids, wts, y, w.h, T, topk,
                                                 hidden, inter, E, s);
     QmmArgs gu{static_cast<const uint8_t *>(gate), w.xq, w.xs, w.xsum, w.h, (int)S, (int)inter, (int)hidden, ids,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmv.h")
 LIB = os.path.join(ROOT, "moe_ggml_block_amd", "libqmv.so")
 
-QMV_EINVAL, QMV_EALIGN = -1, -2
+QMV_EINVAL, QMV_EALIGN, QMV_EUNSUPPORTED = -1, -2, -4
 
 
 def _declared():
@@ -89,3 +89,28 @@ def test_host_validation_returns_before_launch(lib):
                                None) == QMV_EINVAL  # workspace too small
     lib.qmv_strerror.restype = ctypes.c_char_p
     assert b"alignment" in lib.qmv_strerror(QMV_EALIGN)
+
+
+def test_layer_topk_above_64_is_rejected_on_the_host(lib):
+    """The decode layers keep a token's ids and weights in 64-entry on-chip
+    arrays: topk > 64 is refused before any launch (the prefill layer takes
+    its GEMM route there instead)."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    fake = ctypes.c_void_p(0x10000)
+    big = 1 << 40  # workspace size large enough to pass the size check
+    for name in ("moe_ffn_q4k_q6k", "moe_ffn_q4k_q6k_q8"):
+        f = getattr(lib, name)
+        f.argtypes = [vp] * 8 + [i64] * 6 + [vp]
+        f.restype = i32
+        assert f(fake, fake, fake, fake, fake, fake, fake, fake, big, 1, 65, 2048, 768, 128, None) == QMV_EUNSUPPORTED
+        assert f(fake, fake, fake, fake, fake, fake, fake, fake, big, 2, 72, 256, 256, 96, None) == QMV_EUNSUPPORTED
+    f = lib.moe_ffn_routed_q4k_q6k
+    f.argtypes = [vp] * 9 + [i64] * 6 + [vp]
+    f.restype = i32
+    assert f(fake, fake, fake, fake, fake, fake, fake, fake, fake, big, 1, 65, 2048, 768, 128, None) == QMV_EINVAL
+    f = lib.moe_block_q4k_q6k
+    f.argtypes = [vp] * 10 + [i64] * 6 + [vp]
+    f.restype = i32
+    assert f(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, big, 1, 65, 2048, 768, 128, None) == QMV_EINVAL
+    # T*topk above the layer's slot limit: refused before the gate GEMV is launched
+    assert f(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, big, 300, 8, 2048, 768, 128, None) == QMV_EUNSUPPORTED

@@ -284,3 +284,23 @@ def test_moe_prefill_layer_workspace_reuse_smaller_second_call():
     # bit: the launch shape (and, across 512 slots, the kernels) set the
     # rounding order of the combine
     assert scalerel(first[:7], b) <= TOL, scalerel(first[:7], b)
+
+
+@pytest.mark.parametrize("T", [32, 64])
+def test_moe_prefill_layer_bench_shape_on_the_gathers(T):
+    """The benched small-batch layer (top-8 over 128 experts, gate/up
+    [768, 2048], down [2048, 768]; 256 and 512 slots, which run on the
+    expert-grouped decode gathers): every output column of sampled tokens
+    against the oracle."""
+    topk, E, hidden, inter = 8, 128, 2048, 768
+    announce(f"moe prefill layer (gathers) T={T} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 160 + T, sample=np.array([0, 1, T // 2, T - 2, T - 1]))
+
+
+def test_moe_prefill_layer_topk_above_64_takes_the_gemm_route():
+    """72 slots per token (more than the decode down pass holds on chip):
+    216 slots would fit the gather route by count, but the layer must take
+    the GEMM tiles, whose combine takes any topk."""
+    T, topk, E, hidden, inter = 3, 72, 96, 256, 256
+    announce(f"moe prefill layer T={T} topk={topk} E={E}")
+    _layer(T, topk, E, hidden, inter, 170)

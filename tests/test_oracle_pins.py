@@ -271,6 +271,53 @@ def test_quantize_act_half_away_rounding_and_exact_scale():
     assert xsum[0, 0] == float(xq.astype(np.int64).sum())
 
 
+# Blocks whose codes depend on taking x*inv as ONE f32 product (the reading
+# of the quantizer: inv = 127/amax correctly rounded to f32, then the
+# product rounded to f32, then rounded half away from zero). In each case
+# below the exact product of the two f32 numbers lies just below k + 1/2
+# while its f32 rounding is exactly k + 1/2, so the f32 reading gives k + 1
+# and an exact (or f64) product gives k. The amax = 0.3 block also tells the
+# f32 product from the real quotient 127*x/amax, and the amax = 0.7 block from
+# dividing by the scale, x/xs, whose f32 result falls below the half.
+_O4_F32_PRODUCT_BLOCKS = [
+    # amax = 3.0: inv = f32(127/amax) = 0x42295555 (42.33333206176758), xs = 0x3cc18306
+    #   x = 0x3d71e3c8: exact x*inv = 21990232506669/8796093022208 = 2.4999999944462843, f32 product = 2.5 -> 3
+    #   x = 0x3dd9b367: exact x*inv = 158329671828531/35184372088832 = 4.499999926921731, f32 product = 4.5 -> 5
+    #   x = 0x3e1d3a75: exact x*inv = 114349206815193/17592186044416 = 6.499999859397178, f32 product = 6.5 -> 7
+    #   x = 0x3e356ad6: exact x*inv = 65970697520007/8796093022208 = 7.499999983338853, f32 product = 7.5 -> 8
+    #   x = 0xbd71e3c8, 0xbdd9b367, 0xbe1d3a75: the negatives of the first three -> -3, -5, -7
+    ([0x40400000, 0x3d71e3c8, 0x3dd9b367, 0x3e1d3a75, 0x3e356ad6, 0xbd71e3c8, 0xbdd9b367, 0xbe1d3a75],
+     [127, 3, 5, 7, 8, -3, -5, -7], 0x3cc18306),
+    # amax = 0.3 (0x3e99999a): inv = 0x43d3aaaa (423.33331298828125), xs = 0x3b1acf38
+    #   x = 0x3c2e291f: exact x*inv = 79164833100363/17592186044416 = 4.499999766969893, f32 product = 4.5 -> 5
+    #   x = 0x3ca47c2c: exact x*inv = 18691697571239/2199023255552 = 8.49999995409189, f32 product = 8.5 -> 9
+    #   x = 0x3cb7d613: exact x*inv = 83562882851663/8796093022208 = 9.499999902307422, f32 product = 9.5 -> 10
+    #   x = 0x3ccb2ffa: exact x*inv = 46179487709185/4398046511104 = 10.499999850522954, f32 product = 10.5 -> 11
+    #   x = 0xbc2e291f, 0xbca47c2c, 0xbcb7d613: the negatives of the first three -> -5, -9, -10
+    ([0x3e99999a, 0x3c2e291f, 0x3ca47c2c, 0x3cb7d613, 0x3ccb2ffa, 0xbc2e291f, 0xbca47c2c, 0xbcb7d613],
+     [127, 5, 9, 10, 11, -5, -9, -10], 0x3b1acf38),
+    # amax = 0.7 (0x3f333333): inv = 0x43356db7 (181.42857360839844), xs = 0x3bb49c6c
+    #   x = 0x3d3fe632: exact x*inv = 74766786849759/8796093022208 = 8.499999563555207, f32 product = 8.5 -> 9
+    #                   (x/xs in f32 = 8.499999046325684 -> 8)
+    #   x = 0x3d6d0d4d: exact x*inv = 184717946080011/17592186044416 = 10.499999580134215, f32 product = 10.5 -> 11
+    #   x = 0xbd3fe632: the negative of the first -> -9
+    ([0x3f333333, 0x3d3fe632, 0x3d6d0d4d, 0xbd3fe632], [127, 9, 11, -9], 0x3bb49c6c),
+]
+
+
+def test_quantize_act_single_f32_product_at_half_way_points():
+    x = np.zeros((1, 32 * len(_O4_F32_PRODUCT_BLOCKS)), dtype=np.float32)
+    want = np.zeros(x.shape, dtype=np.int8)
+    for b, (xbits, codes, _) in enumerate(_O4_F32_PRODUCT_BLOCKS):
+        x[0, 32 * b:32 * b + len(xbits)] = np.array(xbits, dtype=np.uint32).view(np.float32)
+        want[0, 32 * b:32 * b + len(codes)] = codes
+    xq, xs, xsum = oracle.quantize_act_q8(x, 1, x.shape[1])
+    np.testing.assert_array_equal(xq, want)
+    assert [int(v) for v in xs.reshape(-1).view(np.uint32)] == [c[2] for c in _O4_F32_PRODUCT_BLOCKS]
+    sums = want.reshape(-1, 32).astype(np.int64).sum(axis=1)
+    np.testing.assert_array_equal(xsum.reshape(-1), xs.reshape(-1) * sums.astype(np.float32))
+
+
 def test_quantize_act_zero_block_and_invariants():
     x = synth.normal(9, 4 * 256).reshape(4, 256)
     x[1, 32:64] = 0.0
