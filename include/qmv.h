@@ -198,6 +198,23 @@ int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const fl
                     int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
                     qmv_stream_t stream);
 
+/* The same layer without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): h lives in a library-owned device array
+ * of QMV_NOALLOC_SCRATCH_BYTES, one per GPU, held from the first call on
+ * that GPU until the process ends; the call allocates and frees nothing.
+ * Operands, limits and results as moe_ffn_q4k_q6k (the same kernels; y is
+ * bit-identical to it), run on the device current at the call, which must
+ * be the stream's. Needs moe_ffn_workspace_bytes(T, topk, hidden, inter) <=
+ * QMV_NOALLOC_SCRATCH_BYTES, else QMV_EUNSUPPORTED before any launch.
+ * Calls share their GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller.
+ * QMV_ELAUNCH also if the array's device address cannot be obtained. */
+#define QMV_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_ffn_q4k_q6k_noalloc(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
+                            const float *wts, float *y, int64_t T, int64_t topk, int64_t hidden, int64_t inter,
+                            int64_t E, qmv_stream_t stream);
+
 /* The same layer with the router fused into the gate/up gather (the
  * indexed-MoE design of hanzo-ml `src/vulkan_backend.rs`: `moe_route_vk`
  * softmax + top-k + renormalize feeding `moe_matvec_gpu` with ids kept on

@@ -41,6 +41,7 @@ _SIGS = {
     "moe_qmv_q6k": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmv_q8_0": [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
+    "moe_ffn_q4k_q6k_noalloc": [_vp] * 7 + [_i64] * 5 + [_vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
     "qmm_q4k_split": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
@@ -242,6 +243,26 @@ def moe_ffn_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=No
     _check(_lib.moe_ffn_q4k_q6k(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), _p(ws),
                                 ws.numel() * ws.element_size(), T, topk, hidden, inter, E, _stream(stream)),
            "moe_ffn_q4k_q6k")
+    return y
+
+
+# the layer's scratch limit (bytes of h) for moe_ffn_q4k_q6k_noalloc
+NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_ffn_q4k_q6k_noalloc(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=None, stream=None):
+    """The decode MoE layer with h in the library's own per-GPU scratch (no workspace)."""
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _need(gate, E * inter * row_bytes("q4k", hidden), "gate")
+    _need(up, E * inter * row_bytes("q4k", hidden), "up")
+    _need(down, E * hidden * row_bytes("q6k", inter), "down")
+    _need(x, 4 * T * hidden, "x")
+    _need(ids, 4 * T * topk, "ids")
+    _need(wts, 4 * T * topk, "wts")
+    _need(y, 4 * T * hidden, "y")
+    _check(_lib.moe_ffn_q4k_q6k_noalloc(_p(gate), _p(up), _p(down), _p(x), _p(ids), _p(wts), _p(y), T, topk,
+                                        hidden, inter, E, _stream(stream)), "moe_ffn_q4k_q6k_noalloc")
     return y
 
 

@@ -29,7 +29,9 @@
 // (row block, token) streams the rows of the block for each routed expert
 // and sums them with the routing weights itself, so no workgroup waits for
 // another and no separate combine kernel runs.
+#include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "blocks.hpp"
 #include "internal.hpp"
@@ -900,18 +902,29 @@ extern "C" int64_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t hidd
     return div_up(T * topk * inter * 4, 256) * 256;
 }
 
+static int launch_decode_layer(const void *gate, const void *up, const void *down, const float *x,
+                               const int32_t *ids, const float *wts, float *y, float *h, int64_t T, int64_t topk,
+                               int64_t hidden, int64_t inter, int64_t E, hipStream_t s);
+
 extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *down, const float *x,
                                const int32_t *ids, const float *wts, float *y, void *ws, int64_t ws_bytes,
                                int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E,
                                qmv_stream_t stream) {
-    int rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden,
-                                              inter, E);
+    const int rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, ws, ws_bytes, T, topk, hidden,
+                                                    inter, E);
     if (rc) return rc;
+    return launch_decode_layer(gate, up, down, x, ids, wts, y, static_cast<float *>(ws), T, topk, hidden, inter, E,
+                               (hipStream_t)stream);
+}
+
+// The decode layer's two launches (all checks done by the caller); h holds
+// T*topk*inter floats of scratch.
+static int launch_decode_layer(const void *gate, const void *up, const void *down, const float *x,
+                               const int32_t *ids, const float *wts, float *y, float *h, int64_t T, int64_t topk,
+                               int64_t hidden, int64_t inter, int64_t E, hipStream_t s) {
     const int64_t ns = T * topk;
-    float *h = static_cast<float *>(ws);
-    hipStream_t s = (hipStream_t)stream;
     // h = silu(gate x) * (up x): one gather over interleaved gate/up rows
-    rc = launch_gate_up<Q4KUnit>(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
+    int rc = launch_gate_up<Q4KUnit>(gather_args(gate, up, x, topk, ids, h, ns, 2 * inter, hidden, E), s);
     if (rc) return rc;
     DownArgs dn{};
     dn.bank = static_cast<const uint8_t *>(down);
@@ -925,6 +938,61 @@ extern "C" int moe_ffn_q4k_q6k(const void *gate, const void *up, const void *dow
     dn.topk = (int)topk;
     dn.chunk = down_chunk<Q6KUnit>(inter, topk);
     return launch_down<Q6KUnit>(dn, T, s);
+}
+
+// ------------------------------------------------ allocation-free layer ---
+// The decode layer for callers that cannot allocate device memory (graph
+// capture, tight serving loops): h lives in `scratch`, a library array of
+// QMV_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call on it
+// until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and only that address is used. Every call on a GPU shares
+// its array, so calls that overlap on one GPU race; nothing in it needs to
+// start at zero (the gate/up pass writes every h row the down pass reads).
+static __device__ __align__(256) float scratch[QMV_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the current device (looked up on first use).
+int scratch_address(float **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+        (void)hipGetLastError();
+        return QMV_ELAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return QMV_ELAUNCH;
+        }
+        g_scratch_addr[dev] = p;
+    }
+    *out = static_cast<float *>(g_scratch_addr[dev]);
+    return QMV_OK;
+}
+}  // namespace
+
+extern "C" int moe_ffn_q4k_q6k_noalloc(const void *gate, const void *up, const void *down, const float *x,
+                                       const int32_t *ids, const float *wts, float *y, int64_t T, int64_t topk,
+                                       int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream) {
+    // every check of moe_ffn_q4k_q6k except the workspace's (the placeholder
+    // is never dereferenced), then the scratch limit
+    const void *no_ws = reinterpret_cast<const void *>((uintptr_t)256);
+    int rc = qmv_internal::check_decode_layer(gate, up, down, x, ids, wts, y, no_ws, INT64_MAX, T, topk, hidden,
+                                              inter, E);
+    if (rc) return rc;
+    if (moe_ffn_workspace_bytes(T, topk, hidden, inter) > (int64_t)QMV_NOALLOC_SCRATCH_BYTES)
+        return QMV_EUNSUPPORTED;
+    float *h = nullptr;
+    rc = scratch_address(&h);
+    if (rc) return rc;
+    return launch_decode_layer(gate, up, down, x, ids, wts, y, h, T, topk, hidden, inter, E, (hipStream_t)stream);
 }
 
 // The layer with the router fused into the gate/up gather: every workgroup

@@ -114,3 +114,17 @@ def test_layer_topk_above_64_is_rejected_on_the_host(lib):
     assert f(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, big, 1, 65, 2048, 768, 128, None) == QMV_EINVAL
     # T*topk above the layer's slot limit: refused before the gate GEMV is launched
     assert f(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, big, 300, 8, 2048, 768, 128, None) == QMV_EUNSUPPORTED
+
+
+def test_noalloc_layer_checks_its_scratch_limit_on_the_host(lib):
+    """moe_ffn_q4k_q6k_noalloc keeps h in a 4 MiB library array: a call whose
+    h would not fit is refused before the device is touched."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.moe_ffn_q4k_q6k_noalloc
+    f.argtypes = [vp] * 7 + [i64] * 5 + [vp]
+    f.restype = i32
+    T = (4 << 20) // (4 * 8 * 768) + 1
+    assert f(fake, fake, fake, fake, fake, fake, fake, T, 8, 2048, 768, 128, None) == QMV_EUNSUPPORTED
+    assert f(fake, fake, fake, fake, fake, fake, fake, 1, 65, 2048, 768, 128, None) == QMV_EUNSUPPORTED
+    assert f(None, fake, fake, fake, fake, fake, fake, 1, 8, 2048, 768, 128, None) == QMV_EINVAL
