@@ -14,7 +14,17 @@ reported beside).
 The other workloads are measured after the headline and reported under
 "others": Q8_0 4096x4096, Q6_K 128256x4096, the MoE layer (router + fused
 gate/up/SiLU + down + combine, 128 experts, top-8, T = 1/4/16 tokens, in
-tokens/s) and the m=512 Q4_K prefill GEMM on int8 MFMA (TOPS).
+tokens/s) and the m=512 Q4_K prefill GEMM (TOPS; its exact integer block
+dots run on the f16 matrix instructions, and it is reported against both
+the f16 and the int8 dense MFMA peaks).
+
+Measured denominators beside the 8 TB/s datasheet peak: a 1 GiB
+device-to-device copy, and the fastest plain read (qmv_roofline_read, a
+sweep of grid sizes and loads in flight) of exactly the bytes one launch of
+each dense matvec moves, over cold rotating copies.
+
+cpu_baseline: the CPU oracle on the headline step, on one host thread and
+on all the host's cores (threads over row slices), with the CPU model.
 
 Prints ONE JSON line. `--gpus N` with N > 1 is refused: this path runs on a
 single GPU.
@@ -38,6 +48,8 @@ N2, K2 = 14336, 4096
 Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
 # one qmv_q4k launch: every packed row (2,304 B) plus its f32 output, and x once
 Q4K_LAUNCH_BYTES = Q4K_BYTES + 4 * N2 + 4 * K2  # 33,103,872
+Q8_LAUNCH_BYTES = 4096 * 128 * 34 + 4 * 4096 + 4 * 4096      # Q8_0 4096x4096: 17,858,560
+Q6K_LAUNCH_BYTES = 128256 * 16 * 210 + 4 * 128256 + 4 * 4096  # Q6_K 128256x4096: 431,469,568
 CALIB_BYTES = 64 << 20                         # the counter-calibration copy
 WARM_MS = 30.0            # untimed replays before each kernel timing
 HEADLINE_WARM_MS = 100.0  # untimed steps before the headline's timed region (beyond --warmup)
@@ -140,27 +152,127 @@ def traffic_from_profile(kernel_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model, logical CPU count and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+# threads the all-core oracle timing may use: the host's usable CPUs, at most
+# this many (a GPU box shares its host among its GPUs)
+CPU_THREADS_MAX = 16
+
+
 def cpu_baseline(seconds: float = 10.0):
     """The oracle, as it stands, on the headline step: f64 Q4_K matvec plus the
     f32 q8 quantizer and the f64 q8-activation matvec, full 14336x4096 shape,
-    repeated until `seconds` of CPU time have run. Single-threaded C."""
+    repeated until `seconds` of wall time have run, first on one host thread,
+    then with the rows split over all usable cores (one Python thread per core,
+    each calling the same single-threaded C oracle on a contiguous slice of
+    rows; ctypes releases the interpreter lock during the call)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     import synth
     w = synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2)
     x = synth.normal(synth.SEED_X, K2)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.matvec("q4k", w, x, N2, K2)
-        xq, xs, _ = oracle.quantize_act_q8(x, 1, K2)
-        oracle.matvec_q8act("q4k", w, xq, xs, N2, K2)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(2 * Q4K_BYTES * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full oracle steps (Q4_K 14336x4096 f64 matvec + q8 quantize + f64 q8-activation "
-                      f"matvec) in {el:.1f} s on one host thread"}
+    rb = (K2 // 256) * 144
+
+    def rows(r0, r1, xq, xs):
+        ws = w[r0 * rb:r1 * rb]
+        oracle.matvec("q4k", ws, x, r1 - r0, K2)
+        oracle.matvec_q8act("q4k", ws, xq, xs, r1 - r0, K2)
+
+    def run(nthreads, budget):
+        cuts = [N2 * i // nthreads for i in range(nthreads + 1)]
+        steps = 0
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            t0 = time.perf_counter()
+            while True:
+                xq, xs, _ = oracle.quantize_act_q8(x, 1, K2)
+                list(ex.map(lambda i: rows(cuts[i], cuts[i + 1], xq, xs), range(nthreads)))
+                steps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    return steps, el
+
+    host = host_cpu()
+    nthr = max(1, min(host["usable_cpus"], CPU_THREADS_MAX))
+    s1, e1 = run(1, seconds / 2)
+    sn, en = run(nthr, seconds / 2)
+    gbs = lambda st, el: round(2 * Q4K_BYTES * st / el / 1e9, 4)
+    return {"value": gbs(sn, en), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{sn} full oracle steps (Q4_K 14336x4096 f64 matvec + q8 quantize + f64 q8-activation "
+                      f"matvec) in {en:.1f} s, rows split over {nthr} threads",
+            "single_thread": {"value": gbs(s1, e1), "unit": "GB/s", "cores": 1,
+                              "sample": f"{s1} full oracle steps in {e1:.1f} s on one thread"},
+            "host": host}
+
+
+def measured_floors(copy_bytes: int = 1 << 30):
+    """Bandwidth denominators measured on this GPU: a one-shot device-to-device
+    copy of copy_bytes (reported as read + write bytes per second), and, for
+    each dense matvec of the bench, the fastest plain read of exactly the bytes
+    one of its launches moves (qmv_roofline_read over cold rotating copies:
+    1, 2, 4 or 8 workgroups of 256 per CU x 1, 2, 4 or 8 loads in flight per
+    thread, best of the 16)."""
+    import torch
+    import moe_ggml_block_amd as qmv
+    a = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    copy_ms = t0.elapsed_time(t1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    out = {"copy_1GiB_gbs": round(2 * copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+           "copy_note": "torch copy_ of 1 GiB device to device; read + write bytes / time"}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for name, nbytes in (("qmv_q4k_14336x4096", Q4K_LAUNCH_BYTES),
+                         ("qmv_q8_0_4096x4096", Q8_LAUNCH_BYTES),
+                         ("qmv_q6k_128256x4096", Q6K_LAUNCH_BYTES)):
+        nb = (nbytes + 15) // 16 * 16
+        copies = max(3, -(-(1 << 30) // nb))
+        big = torch.empty(nb * copies, dtype=torch.uint8, device="cuda")
+        big.fill_(3)
+        views = [big[i * nb:(i + 1) * nb] for i in range(copies)]
+        best = None
+        for wpc in (1, 2, 4, 8):
+            for unr in (1, 2, 4, 8):
+                ms = time_graph(lambda i: qmv.roofline_read(views[i % copies], nb, wpc * cus, unr, sink),
+                                max(2 * copies, 16), 5)
+                if best is None or ms < best[0]:
+                    best = (ms, wpc, unr)
+        ms, wpc, unr = best
+        out[f"stream_read_{name}"] = {"bytes": nb, "us": round(ms * 1e3, 3),
+                                      "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                                      "hbm_pct": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 1),
+                                      "workgroups_per_cu": wpc, "loads_in_flight": unr, "copies": copies}
+        del big, views
+        torch.cuda.empty_cache()
+    return out
 
 
 def headline(steps: int, warmup: int, copies: int):
@@ -347,7 +459,7 @@ def moe_other(bank_copies: int = 3, logit_sets: int = 64):
     return out
 
 
-def prefill_other(copies: int = 16):
+def prefill_other(copies: int = 64):
     import torch
     import moe_ggml_block_amd as qmv
     import synth
@@ -510,7 +622,28 @@ def profile_run(copies: int, other_shapes: bool = False):
                       "q4k_bytes": Q4K_BYTES, "copy_bytes": CALIB_BYTES}))
 
 
-def profile_prefill_run(copies: int = 16):
+def profile_q4k_run(copies: int, warm: bool):
+    """For rocprofv3 kernel-trace: exactly the headline kernel's roofline timing
+    (graphs of 4 x copies qmv_q4k launches over the rotating cold copies,
+    WARM_MS of untimed replays, then 10 replays), or with warm=True the same
+    on one resident copy, so that the profiler's average duration is of one
+    kind of launch only."""
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    big, W = rotated(synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2), copies)
+    x = torch.from_numpy(synth.normal(synth.SEED_X, K2)).cuda()
+    y = torch.empty(N2, device="cuda")
+    if warm:
+        ms = time_graph(lambda i: qmv.qmv_q4k(W[0], x, N2, K2, y=y), 128, 10)
+    else:
+        ms = time_graph(lambda i: qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y), 4 * copies, 10)
+    del big, W
+    print(json.dumps({"profile_run": f"qmv_q4k {N2}x{K2} {'warm (one copy)' if warm else f'cold ({copies} copies)'}",
+                      "event_us_per_launch": round(ms * 1e3, 3)}))
+
+
+def profile_prefill_run(copies: int = 64):
     """Short eager run for rocprofv3 counters of the Q4_K prefill GEMM:
     m=512 x W[4096, 4096], 20 launches each of qmm_q4k at bm = 64 and
     bm = 128 and of qmm_q4k_split over rotating weight copies, then the
@@ -587,6 +720,9 @@ def main():
     ap.add_argument("--profile", action="store_true", help="short eager run for rocprofv3")
     ap.add_argument("--profile-all", action="store_true", help="--profile plus the Q8_0 and Q6_K shapes")
     ap.add_argument("--profile-prefill", action="store_true", help="short eager prefill run for rocprofv3")
+    ap.add_argument("--profile-cold", action="store_true",
+                    help="only the headline kernel's cold roofline timing (graph replays), for rocprofv3")
+    ap.add_argument("--profile-warm", action="store_true", help="the same on one resident weight copy")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc runs of --profile into the traffic file, then exit")
     ap.add_argument("--gpus", type=int, default=1)
@@ -595,6 +731,7 @@ def main():
     ap.add_argument("--copies", type=int, default=32)
     ap.add_argument("--no-others", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-floors", action="store_true", help="skip the measured copy / read denominators")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     a = ap.parse_args()
     if a.write_traffic:
@@ -616,6 +753,9 @@ def main():
         return
     if a.profile_prefill:
         profile_prefill_run()
+        return
+    if a.profile_cold or a.profile_warm:
+        profile_q4k_run(a.copies, a.profile_warm)
         return
     khash = source_hash(KERNEL_SOURCES)
     h = headline(a.steps, a.warmup, a.copies)
@@ -640,12 +780,29 @@ def main():
                      "kernel_source_hash": khash},
         "kernels": h["kernels"],
     }
+    if not a.no_floors:
+        log("measured floors: 1 GiB copy, plain reads of each matvec's bytes")
+        fl = measured_floors()
+        res["measured_floors"] = fl
+        q4f = fl["stream_read_qmv_q4k_14336x4096"]["gbs"]
+        res["roofline"]["frac_of_measured_read"] = round(achieved / q4f, 4)
+        res["roofline"]["frac_of_copy_1GiB"] = round(achieved / fl["copy_1GiB_gbs"], 4)
+        res["kernels"]["qmv_q4k_cold_pct_of_measured_read"] = round(achieved / q4f * 100, 1)
+        q8a = Q4K_LAUNCH_BYTES - 4 * K2 + K2 + 8 * (K2 // 32)  # its launch: q8 x instead of f32 x
+        res["kernels"]["qmv_q4k_q8_cold_pct_of_measured_read"] = round(
+            q8a / (h["kernels"]["qmv_q4k_q8_cold_us"] * 1e-6) / 1e9 / q4f * 100, 1)
     if not a.no_others:
         others = {}
         log("others: q8_0")
         others["q8_0_4096x4096"] = dense_other("q8_0", 4096, 4096, 64)
         log("others: q6k")
         others["q6k_128256x4096"] = dense_other("q6k", 128256, 4096, 3)
+        if "measured_floors" in res:
+            fl = res["measured_floors"]
+            for key, fkey, lb in (("q8_0_4096x4096", "stream_read_qmv_q8_0_4096x4096", Q8_LAUNCH_BYTES),
+                                  ("q6k_128256x4096", "stream_read_qmv_q6k_128256x4096", Q6K_LAUNCH_BYTES)):
+                gbs = lb / (others[key]["cold_us"] * 1e-6) / 1e9
+                others[key]["cold_pct_of_measured_read"] = round(gbs / fl[fkey]["gbs"] * 100, 1)
         log("others: q4_0, q5k")
         others["q4_0_14336x4096"] = dense_other("q4_0", 14336, 4096, 32)
         others["q5k_14336x4096"] = dense_other("q5k", 14336, 4096, 32)

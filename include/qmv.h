@@ -382,6 +382,21 @@ int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const void *down, 
                             const float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,
                             int64_t hidden, int64_t inter, int64_t E, qmv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement probe (not a step of the path): one launch that reads `bytes`
+ * of device memory once with 16-byte loads and writes nothing (sink, one
+ * u32, is only written for a value ordinary data does not give). The pages
+ * price their kernels against a bandwidth measured on the device
+ * (hanzo-ml `src/vulkan_backend.rs`, the roofline profiling option and its
+ * start-up copy-bandwidth measurement); this probe gives the fastest plain
+ * read of a given size to compare a matvec of that size with.
+ * workgroups: grid size (256 threads each, 1 .. 2^20); unroll: loads in
+ * flight per thread, 1, 2, 4 or 8. bytes % 16 == 0, buf 16-byte aligned,
+ * sink 4-byte aligned; QMV_EINVAL / QMV_EALIGN otherwise.
+ * ---------------------------------------------------------------------- */
+int qmv_roofline_read(const void *buf, int64_t bytes, int64_t workgroups, int64_t unroll, uint32_t *sink,
+                      qmv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,7 @@ _SIGS = {
     "moe_ffn_q4k_q6k_q8": [_vp] * 8 + [_i64] * 6 + [_vp],
     "moe_ffn_routed_q4k_q6k": [_vp] * 9 + [_i64] * 6 + [_vp],
     "moe_block_q4k_q6k": [_vp] * 10 + [_i64] * 6 + [_vp],
+    "qmv_roofline_read": [_vp, _i64, _i64, _i64, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -244,6 +245,13 @@ def moe_ffn_q4k_q6k(gate, up, down, x, ids, wts, T, topk, hidden, inter, E, y=No
                                 ws.numel() * ws.element_size(), T, topk, hidden, inter, E, _stream(stream)),
            "moe_ffn_q4k_q6k")
     return y
+
+
+def roofline_read(buf, nbytes, workgroups, unroll, sink, stream=None):
+    """Measurement probe: one launch reading nbytes of buf (no result)."""
+    _need(buf, nbytes, "buf")
+    _check(_lib.qmv_roofline_read(_p(buf), nbytes, workgroups, unroll, _p(sink), _stream(stream)),
+           "qmv_roofline_read")
 
 
 # the layer's scratch limit (bytes of h) for moe_ffn_q4k_q6k_noalloc

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libqmv.so")
 BUILD = os.path.join(HERE, "_build")
 
-HIP_SOURCES = ["qmv_dense.hip", "qmv_q8act.hip", "moe.hip", "qmm.hip", "gate.hip"]
+HIP_SOURCES = ["qmv_dense.hip", "qmv_q8act.hip", "moe.hip", "qmm.hip", "gate.hip", "roofline.hip"]
 CPP_SOURCES = ["misc.cpp"]
 ARCH = "gfx950"
 
