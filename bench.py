@@ -469,6 +469,12 @@ def prefill_other(copies: int = 64):
     x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, m * k)).cuda()
     xq, xs, xsum = qmv.quantize_act_q8(x, m, k)
     res = {}
+    y8 = torch.empty((m, n), device="cuda")
+    ms_i8 = time_graph(lambda i: qmv.qmm_q4k_i8(W[i % copies], xq, xs, xsum, m, n, k, y=y8), 2 * copies, 5)
+    tops_i8 = 2.0 * m * n * k / (ms_i8 * 1e-3) / 1e12
+    res["int8_mfma_tile"] = {"us": round(ms_i8 * 1e3, 2), "tops": round(tops_i8, 2),
+                             "int8_peak_pct": round(tops_i8 / MFMA_I8_PEAK_TOPS * 100, 2),
+                             "note": "qmm_q4k_i8: the bm=64 tile with block dots on v_mfma_i32_16x16x32_i8"}
     for bm in (64, 128, 256):
         y = torch.empty((m, n), device="cuda")
         ms = time_graph(lambda i: qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y), 2 * copies, 5)
@@ -643,6 +649,48 @@ def profile_q4k_run(copies: int, warm: bool):
                       "event_us_per_launch": round(ms * 1e3, 3)}))
 
 
+def profile_moe_run(T: int, bank_copies: int = 3, calls: int = 48):
+    """Short eager run for rocprofv3 counters of the MoE decode layer at T
+    tokens (128 experts, top-8, gate/up Q4_K [768, 2048], down Q6_K
+    [2048, 768]): `calls` x (moe_route + moe_ffn_q4k_q6k) over rotating bank
+    copies and 64 logit sets, then the 64 MiB calibration copy (torch neg x8).
+    Prints the unique experts of each call's routing, so that the summary can
+    count the algorithmic bytes per dispatch."""
+    import numpy as np
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    E, topk, hidden, inter = 128, 8, 2048, 768
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, hidden, inter)
+    bg, G = rotated(gate, bank_copies)
+    bu, U = rotated(up, bank_copies)
+    bd, D = rotated(down, bank_copies)
+    lg = [torch.from_numpy(synth.moe_logits(T, E, r)).cuda() for r in range(64)]
+    x = torch.from_numpy(synth.normal(synth.SEED_X, T * hidden)).cuda()
+    ids = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, topk), device="cuda")
+    y = torch.empty((T, hidden), device="cuda")
+    ws = torch.empty(qmv.moe_ffn_workspace_bytes(T, topk, hidden, inter), dtype=torch.uint8, device="cuda")
+    uniq = []
+    for i in range(calls):
+        b = i % bank_copies
+        qmv.moe_route(lg[i % 64], T, E, topk, out=(ids, wts))
+        qmv.moe_ffn_q4k_q6k(G[b], U[b], D[b], x, ids, wts, T, topk, hidden, inter, E, y=y, ws=ws)
+        uniq.append(int(np.unique(ids.cpu().numpy()).size))
+    a = torch.ones(CALIB_BYTES // 4, device="cuda")
+    c = torch.empty_like(a)
+    for _ in range(8):
+        torch.neg(a, out=c)
+    torch.cuda.synchronize()
+    per_expert = (gate.nbytes + up.nbytes + down.nbytes) // E
+    print(json.dumps({"profile_run": f"moe layer T={T} x{calls} (route + gate/up + down), neg 64MiB x8",
+                      "unique_experts": uniq, "bytes_per_expert": per_expert,
+                      "gate_up_bytes_per_expert": 2 * gate.nbytes // E, "down_bytes_per_expert": down.nbytes // E,
+                      "copy_bytes": CALIB_BYTES}))
+
+
 def profile_prefill_run(copies: int = 64):
     """Short eager run for rocprofv3 counters of the Q4_K prefill GEMM:
     m=512 x W[4096, 4096], 20 launches each of qmm_q4k at bm = 64 and
@@ -659,6 +707,8 @@ def profile_prefill_run(copies: int = 64):
     for bm in (64, 128):
         for i in range(20):
             qmv.qmm_q4k(W[i % copies], xq, xs, xsum, m, n, k, bm=bm, y=y)
+    for i in range(20):
+        qmv.qmm_q4k_i8(W[i % copies], xq, xs, xsum, m, n, k, y=y)
     ws = torch.empty(qmv.qmm_q4k_split_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
     for i in range(20):
         qmv.qmm_q4k_split(W[i % copies], xq, xs, xsum, m, n, k, y=y, ws=ws)
@@ -667,7 +717,8 @@ def profile_prefill_run(copies: int = 64):
     for _ in range(8):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": "qmm_q4k 512x4096x4096 bm=64 x20, bm=128 x20, qmm_q4k_split x20, neg 64MiB x8",
+    print(json.dumps({"profile_run": "qmm_q4k 512x4096x4096 bm=64 x20, bm=128 x20, qmm_q4k_i8 x20, qmm_q4k_split x20, "
+                                     "neg 64MiB x8",
                       "copy_bytes": CALIB_BYTES}))
 
 
@@ -723,6 +774,7 @@ def main():
     ap.add_argument("--profile-cold", action="store_true",
                     help="only the headline kernel's cold roofline timing (graph replays), for rocprofv3")
     ap.add_argument("--profile-warm", action="store_true", help="the same on one resident weight copy")
+    ap.add_argument("--profile-moe", type=int, metavar="T", help="short eager MoE decode layer run at T tokens")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc runs of --profile into the traffic file, then exit")
     ap.add_argument("--gpus", type=int, default=1)
@@ -753,6 +805,9 @@ def main():
         return
     if a.profile_prefill:
         profile_prefill_run()
+        return
+    if a.profile_moe:
+        profile_moe_run(a.profile_moe)
         return
     if a.profile_cold or a.profile_warm:
         profile_q4k_run(a.copies, a.profile_warm)

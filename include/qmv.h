@@ -272,6 +272,18 @@ int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const
 int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
             int64_t m, int64_t n, int64_t k, int bm, qmv_stream_t stream);
 
+/* The same product with each block's integer dot on the int8 matrix
+ * instructions (the int8 MMQ tiles of `mul_mm_q4k_tiled_dp4a`, as
+ * `mmq_q4k_rt_gpu` benches them): the bm = 64 tile of qmm_q4k with the
+ * codes q and xq as int8 operands (T = sum q*xq exact in int32) and the
+ * scales sc*xs applied per output and block on the vector ALU. A comparison
+ * form: qmm_q4k(bm = 64) is the faster one on gfx950, because the 6-bit
+ * sub-block scale rides in its f16 operand and not in an int8 one.
+ * Operands and results as qmm_q4k; n*(k/256)*144 and m*k below 2^32 (else
+ * QMV_EUNSUPPORTED). */
+int qmm_q4k_i8(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y, int64_t m, int64_t n,
+               int64_t k, qmv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * The same Q4_K prefill product (`mmq_q4k_rt_gpu` on its q8 activation),
  *   Y[i, r] = sum_c W_deq[r, c] * xs[i, c/32] * xq[i, c],

@@ -43,6 +43,7 @@ _SIGS = {
     "moe_ffn_q4k_q6k": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "moe_ffn_q4k_q6k_noalloc": [_vp] * 7 + [_i64] * 5 + [_vp],
     "qmm_q4k": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp],
+    "qmm_q4k_i8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "qmm_q4k_split": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "moe_qmm_q4k": [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "qmm_q6k": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
@@ -280,6 +281,16 @@ def qmm_q4k(w, xq, xs, xsum, m, n, k, bm=128, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     _check(_lib.qmm_q4k(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), m, n, k, bm, _stream(stream)), "qmm_q4k")
+    return y
+
+
+def qmm_q4k_i8(w, xq, xs, xsum, m, n, k, y=None, stream=None):
+    """qmm_q4k with the block dots on the int8 matrix instructions (comparison form)."""
+    _need(w, n * row_bytes("q4k", k), "w")
+    _need(xq, m * k, "xq")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(_lib.qmm_q4k_i8(_p(w), _p(xq), _p(xs), _p(xsum), _p(y), m, n, k, _stream(stream)), "qmm_q4k_i8")
     return y
 
 

@@ -894,6 +894,261 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     }
 }
 
+// ------------------------------------- Q4_K prefill on the int8 matrix cores
+// The bm = 64 weight-side tile of k_qmm2_q4k<4, 1, 2> (128 weight rows x 64
+// activation rows, eight waves, each superblock's eight blocks split 4 + 4
+// over two waves) with the integer dot of each block on
+// v_mfma_i32_16x16x32_i8 instead of the f16 instruction: the weight codes q
+// (0..15, the nibbles masked in place) and the activation codes xq enter as
+// int8, K = 32 is one q8 block, and T = sum q*xq is exact in int32. The
+// activations are staged as raw int8 (no conversion). What the int8 operands
+// cannot carry is the weight's 6-bit sub-block scale (sc*q reaches 945), so
+// the epilogue takes, per output and block, the conversion of T and a fused
+// multiply-add with sc*xs, plus one product sc*xs per output and block:
+// three vector instructions where the f16 form (sc folded into its
+// operand) needs one. Kept as the int8 form of the tile, to compare with.
+template <int NG>
+__global__ __launch_bounds__(512) void k_qmm_i8_q4k(const QmmArgs a, int vec_store) {
+    constexpr int KS = 2;
+    static_assert(NG * KS == 8, "eight waves");
+    constexpr int BN = 32 * NG, BM = 64;
+    constexpr int ST = 256 + 16;         // bytes per LDS activation row: 8-byte reads of 32 lanes conflict-free
+    constexpr int NBW = 8 / KS;          // blocks of a superblock per wave
+    constexpr int NPW = NBW / 2;         // code-byte pairs per wave
+    constexpr int AC = BM * 32 / 512;    // 8-byte activation chunks per thread and superblock
+    constexpr int XV = BM * 8 / 512;     // xs (and xsum) values per thread and superblock
+    static_assert(AC >= 1 && XV >= 1, "staging");
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * ST];
+    constexpr int XST = 12;
+    __shared__ __attribute__((aligned(16))) float sxs[2][BM * XST];
+    __shared__ __attribute__((aligned(16))) float sxsum[2][BM * XST];
+
+    const uint8_t *__restrict__ w = a.w;
+    const int8_t *__restrict__ xq = a.xq;
+    const float *__restrict__ xs = a.xs;
+    const float *__restrict__ xsum = a.xsum;
+    const int m = a.m, n = a.n, k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = wave % KS, g = wave / KS;
+    const int li = lane & 15, lq = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int nsb = k / 256, kb = k / 32;
+    const size_t row_bytes = (size_t)nsb * 144;
+
+    // uniform base plus a per-lane 32-bit offset (the host routes shapes
+    // whose offsets could pass 2^32 elsewhere); rows past n are clamped for
+    // the loads and masked at the store
+    uint32_t woff[2], qoff[2][NPW];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int wr = n0 + 32 * g + 16 * t + li;
+        woff[t] = (uint32_t)((size_t)min(wr, n - 1) * row_bytes);
+#pragma unroll
+        for (int pp = 0; pp < NPW; ++pp) qoff[t][pp] = woff[t] + 16 + 32 * (NPW * h + pp) + 8 * lq;
+    }
+    struct WSet {
+        uint4 hdr[2];
+        uint2 qc[2][NPW];
+    };
+    auto load_w = [&](int s, WSet &W) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint8_t *wsb = w + (size_t)s * 144;
+            W.hdr[t] = ld16(wsb + woff[t]);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) W.qc[t][pp] = *reinterpret_cast<const uint2 *>(wsb + qoff[t][pp]);
+        }
+    };
+    struct ASet {
+        uint2 q[AC];
+        float xs[XV], xsum[XV];
+    };
+    uint32_t aoff[AC], xoff[XV];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 512 * i;
+        aoff[i] = (uint32_t)((size_t)min(m0 + (c >> 5), m - 1) * k + 8 * (c & 31));
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        const int c = tid + 512 * i;
+        xoff[i] = (uint32_t)((size_t)min(m0 + (c >> 3), m - 1) * kb + (c & 7));
+    }
+    auto load_act = [&](int s, ASet &A) {
+        const int8_t *xqs = xq + (size_t)s * 256;
+        const float *xss = xs + (size_t)s * 8, *xms = xsum + (size_t)s * 8;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) A.q[i] = *reinterpret_cast<const uint2 *>(xqs + aoff[i]);
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            A.xs[i] = xss[xoff[i]];
+            A.xsum[i] = xms[xoff[i]];
+        }
+    };
+    auto store_act = [&](int buf, const ASet &A) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int c = tid + 512 * i, row = c >> 5, c8 = c & 31;
+            const uint2 v = m0 + row < m ? A.q[i] : make_uint2(0u, 0u);
+            *reinterpret_cast<uint2 *>(&As[buf][row * ST + 8 * c8]) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int c = tid + 512 * i, row = c >> 3, j = c & 7;
+            const bool ok = m0 + row < m;
+            sxs[buf][row * XST + j] = ok ? A.xs[i] : 0.f;
+            sxsum[buf][row * XST + j] = ok ? A.xsum[i] : 0.f;
+        }
+    };
+
+    v4f acc[2][4], out[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+    WSet wset[2];
+    ASet aset[2];
+    load_w(0, wset[0]);
+    load_act(0, aset[0]);
+    load_w(min(1, nsb - 1), wset[1]);
+    load_act(min(1, nsb - 1), aset[1]);
+    store_act(0, aset[0]);
+    __syncthreads();
+
+    auto superblock = [&](int s, auto Pc) {
+        constexpr int P = decltype(Pc)::value;
+        // per weight row of the lane's fragment (row li): the four blocks'
+        // sc as bytes; the lane's outputs are rows 4*lq + r, whose sc and d
+        // come from the lanes holding those rows
+        float amn[2], dout[2][4];
+        uint32_t scr[2][4];
+        uint2 q[2][NPW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint4 hd = wset[P].hdr[t];
+            const float dmin = h2f(hd.x >> 16);
+            uint32_t sc2[NPW], mn2[NPW];
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q4k_scales(hd.y, hd.z, hd.w, NPW * h + pp, &sc2[pp], &mn2[pp]);
+            const uint32_t sc4 = sc2[0] | (sc2[1] << 16);  // blocks 0..3 of the wave
+#pragma unroll
+            for (int r = 0; r < 4; ++r) scr[t][r] = __shfl(sc4, 4 * lq + r);
+            {
+                const uint32_t lo = mn2[0], hi = mn2[1];
+                const uint32_t pr = lo ^ ((lo ^ hi) & (0u - (uint32_t)(lq >> 1)));
+                amn[t] = -dmin * (float)((pr >> (8 * (lq & 1))) & 0xFFu);
+            }
+            const float down = h2f(hd.x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[P].qc[t][pp];
+        }
+        load_w(min(s + 2, nsb - 1), wset[P]);
+        load_act(min(s + 2, nsb - 1), aset[P]);
+        float xv[4][NBW];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *p = &sxs[P][(16 * u + li) * XST + NBW * h];
+            const v4f v = *reinterpret_cast<const v4f *>(p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[u][e] = v[e];
+        }
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+            const int jb = NBW * h + bl;
+            long bf[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                bf[u] = *reinterpret_cast<const long *>(&As[P][(16 * u + li) * ST + 32 * jb + 8 * lq]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint2 cw = q[t][bl / 2];
+                const uint32_t c0 = (bl & 1) ? (cw.x >> 4) & 0x0F0F0F0Fu : cw.x & 0x0F0F0F0Fu;
+                const uint32_t c1 = (bl & 1) ? (cw.y >> 4) & 0x0F0F0F0Fu : cw.y & 0x0F0F0F0Fu;
+                const long af = (long)(((uint64_t)c1 << 32) | c0);
+                float scf[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) scf[r] = (float)((scr[t][r] >> (8 * bl)) & 0xFFu);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const v4i T = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, bf[u], (v4i){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float f = scf[r] * xv[u][bl];
+                        acc[t][u][r] = bl == 0 ? f * (float)T[r] : fmaf(f, (float)T[r], acc[t][u][r]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[t][u][r] = dout[t][r] * acc[t][u][r] + out[t][u][r];
+        {
+            float xb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xb[u] = sxsum[P][(16 * u + li) * XST + NBW * h + lq];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(amn[t], xb[u], out[t][u], 0, 0, 0);
+        }
+        store_act(P ^ 1, aset[P ^ 1]);
+        __syncthreads();
+    };
+    for (int s = 0; s < nsb; s += 2) {
+        superblock(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nsb) superblock(s + 1, std::integral_constant<int, 1>{});
+    }
+    // the second half of each superblock's blocks adds in through LDS (the
+    // staging buffers are free after the loop's last barrier)
+    float *red = reinterpret_cast<float *>(&As[0][0]);
+    static_assert(sizeof(As) >= 4 * 32 * 64 * 4, "reduction scratch");
+    if (h == 1) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[((g * 32) + 16 * t + 4 * u + r) * 64 + lane] = out[t][u][r];
+    }
+    __syncthreads();
+    if (h == 1) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[t][u][r] += red[((g * 32) + 16 * t + 4 * u + r) * 64 + lane];
+    float *__restrict__ Y = a.Y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = m0 + 16 * u + li;
+        if (row >= m) continue;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = n0 + 32 * g + 16 * t + 4 * lq;
+            float *dst = Y + (size_t)row * n + col;
+            if (vec_store && col + 3 < n) {
+                *reinterpret_cast<v4f *>(dst) = out[t][u];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < n) dst[r] = out[t][u][r];
+            }
+        }
+    }
+}
+
 // ------------------------------------ Q4_K prefill on a split f16 activation
 // Y = W_deq x_deq with x_deq = xs * xq (the q8 activation, dequantized):
 // a pre-pass writes each row of x_deq, scaled by a power of two rs that puts
@@ -1241,6 +1496,24 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
         const dim3 grid((unsigned)div_up(n, QMM_CFG256_BN), (unsigned)div_up(m, QMM_CFG256_BM));
         hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG256>), grid, dim3(QMM_CFG256_NT), 0, s, a);
     }
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
+// The same product on the int8 matrix instructions (k_qmm_i8_q4k): a
+// comparison form of the bm = 64 tile.
+extern "C" int qmm_q4k_i8(const void *w, const int8_t *xq, const float *xs, const float *xsum, float *y,
+                          int64_t m, int64_t n, int64_t k, qmv_stream_t stream) {
+    if (!w || !xq || !xs || !xsum || !y || m < 1 || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (m > (1 << 24) || n > (1 << 24) || k > (1 << 20) || n * (k / 256) * 144 >= ((int64_t)1 << 32) ||
+        m * k >= ((int64_t)1 << 32))
+        return QMV_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(y, 4))
+        return QMV_EALIGN;
+    QmmArgs a{static_cast<const uint8_t *>(w), xq, xs, xsum, y, (int)m, (int)n, (int)k, nullptr, 1, 1};
+    const int vec = aligned(y, 16) && n % 4 == 0;
+    const dim3 grid((unsigned)div_up(n, 128), (unsigned)div_up(m, 64));
+    hipLaunchKernelGGL((k_qmm_i8_q4k<4>), grid, dim3(512), 0, (hipStream_t)stream, a, vec);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

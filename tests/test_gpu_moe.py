@@ -266,6 +266,52 @@ def test_qmm_full_config_sampled_rows(bm):
 
 @pytest.mark.parametrize("m,n,k", [(1, 32, 256), (40, 70, 512), (65, 130, 768), (200, 257, 1024),
                                    (64, 128, 2048), (129, 131, 512), (257, 33, 2048)])
+def test_qmm_i8_small_shapes(m, n, k):
+    """qmm_q4k_i8 (block dots on the int8 matrix instructions) against the
+    oracle, with ragged row and column tiles."""
+    announce(f"qmm_i8 m={m} n={n} k={k}")
+    w = synth.weights(synth.FMT_Q4K, 66, n, k)
+    x = synth.normal(67, m * k).reshape(m, k)
+    xq, xs, xsum = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q4k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q4k_i8(dev(w), dev(xq), dev(xs), dev(xsum), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_i8_random_blocks_every_code_and_scale():
+    """Random raw Q4_K blocks (every nibble, every 6-bit scale and min, the
+    high-bit packing of sub-blocks 4..7) through the int8 tile."""
+    m, n, k = 70, 130, 1024
+    announce("qmm_i8 random blocks")
+    w = synth.random_blocks(synth.FMT_Q4K, 68, n * k // 256, subnormal_every=0)
+    x = synth.normal(69, m * k).reshape(m, k)
+    xq, xs, xsum = oracle.quantize_act_q8(x, m, k)
+    ref = oracle.qmm("q4k", w, xq, xs, m, n, k)
+    got = host(qmv.qmm_q4k_i8(dev(w), dev(xq), dev(xs), dev(xsum), m, n, k))
+    assert scalerel(ref, got) <= TOL, scalerel(ref, got)
+
+
+def test_qmm_i8_full_config_sampled_rows():
+    """m=512 tokens x W[4096, 4096] on the int8 tile: 24 sampled rows against
+    the oracle, all rows against qmm_q4k(bm = 64) within 1e-4."""
+    m, n, k = 512, 4096, 4096
+    announce("qmm_i8 full")
+    w = synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k)
+    x = synth.normal(synth.SEED_PREFILL_X, m * k).reshape(m, k)
+    xq, xs, xsum = qmv.quantize_act_q8(dev(x), m, k)
+    rq, rs, _ = oracle.quantize_act_q8(x, m, k)
+    wd = dev(w)
+    Y = host(qmv.qmm_q4k_i8(wd, xq, xs, xsum, m, n, k))
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 128, 129, 200, 255, 256, 300, 383, 384, 400, 450,
+                     479, 480, 495, 500, 509, 510, 511])
+    ref = oracle.qmm("q4k", w, rq, rs, m, n, k, mrows=rows)
+    assert scalerel(ref, Y[rows]) <= TOL, scalerel(ref, Y[rows])
+    Y64 = host(qmv.qmm_q4k(wd, xq, xs, xsum, m, n, k, bm=64))
+    assert scalerel(Y64, Y) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 32, 256), (40, 70, 512), (65, 130, 768), (200, 257, 1024),
+                                   (64, 128, 2048), (129, 131, 512), (257, 33, 2048)])
 def test_qmm_split_small_shapes(m, n, k):
     """qmm_q4k_split (dequantized activation as two f16 halves) against the
     same oracle as qmm_q4k, with ragged row and column tiles."""
