@@ -233,19 +233,38 @@ struct MoeArgs {
 // Dynamic LDS of k_moe: activation staging, ids (int16, -1 = out of
 // range), slot list, present experts (uint16), per-expert slot counts and
 // item offsets (int32).
-size_t moe_lds_bytes(int k, int act_stride, int nslots, int E) {
+size_t moe_lds_bytes(int k, int act_stride, int nslots, int E, int nsp) {
     const int64_t p = E < nslots ? E : nslots;  // present experts at most
-    return (size_t)(k / 64) * act_stride * 4 + (size_t)div_up(nslots, 2) * 4 * 2 + (size_t)div_up(p, 2) * 4 +
-           (size_t)(2 * p + 1) * 4;
+    return (size_t)nsp * (k / 64) * act_stride * 4 + (size_t)div_up(nslots, 2) * 4 * 2 +
+           (size_t)div_up(p, 2) * 4 + (size_t)(2 * p + 1) * 4;
+}
+
+// Slots of one item staged at once by k_moe (each in its own LDS region,
+// one region of (k/64)*ACT_STRIDE floats per slot). q8 activations: as many
+// of 4, 2, 1 as fit 36 KB at the largest k of the lane mapping (G lanes of
+// UPL units). f32 activations: one -- their gathers are bound by the vector
+// ALU at many slots per expert (one FMA per weight and slot), and splitting
+// the waves among slots halved the rows each workgroup kept in flight
+// (128 experts, top-8, 16 tokens: 89.5 -> 94.8 us, while the q8 layer went
+// 85.7 -> 82.9 us).
+template <class F, int G, int UPL>
+constexpr int moe_nsp() {
+    constexpr int region = G * UPL * F::ACT_STRIDE * 4;
+    return !F::Q8 ? 1 : (4 * region <= 36864 ? 4 : (2 * region <= 36864 ? 2 : 1));
 }
 
 // Persistent over work items: an item is a block of rows of one present
 // expert, for every slot routed to that expert (in slot order):
 // y[s, r] = W[e, r, :] . x[s / x_div]. An expert chosen by c slots gets
 // row blocks about 1/c as tall as a single-slot expert's, so every item
-// costs about the same; the rows of a block are read from HBM once and from
-// L2 for the further slots. The items (known only on the device) are dealt
-// to the workgroups in turn.
+// costs about the same. The slots of an item are taken NSP at a time (up to
+// 4, see moe_nsp): each has its activation row staged in its own LDS region
+// and its own share of the workgroup's four waves (4, 2 or 1 waves per
+// slot), and all of them walk the block's rows in the same order at the
+// same time, so a row read from HBM for one slot is still in the CU's
+// caches when the others read it (one slot after another, a block's rows
+// have left the L2 before the next slot comes back to them). The items
+// (known only on the device) are dealt to the workgroups in turn.
 // PAIR: virtual row 2i is gate row i and 2i+1 is up row i; a pass holds
 // whole pairs (64/G even), and the lane group of the up row writes
 // y[s, i] = silu(gate . x) * (up . x).
@@ -262,11 +281,14 @@ QMV_DEV typename F::Act moe_act(const MoeArgs &a, int row) {
 
 template <class F, int G, int UPL, bool PAIR>
 __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
+    constexpr int NSP = moe_nsp<F, G, UPL>();
+    static_assert(WAVES == 4, "slot groups split four waves");
     extern __shared__ float4 dyn4[];
     float *xlds = reinterpret_cast<float *>(dyn4);
+    const int xreg = (a.k / 64) * F::ACT_STRIDE;  // floats per staged slot
     const int ns2 = (a.nslots + 1) / 2 * 2;
     const int pmax = a.E < a.nslots ? a.E : a.nslots;
-    int16_t *s_ids = reinterpret_cast<int16_t *>(xlds + (a.k / 64) * F::ACT_STRIDE);
+    int16_t *s_ids = reinterpret_cast<int16_t *>(xlds + NSP * xreg);
     uint16_t *slot_list = reinterpret_cast<uint16_t *>(s_ids + ns2);
     uint16_t *experts = slot_list + ns2;
     int *cnt = reinterpret_cast<int *>(experts + (pmax + 1) / 2 * 2);
@@ -429,35 +451,63 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
         const int count = sh[2];
         const uint8_t *wb = a.bank + (size_t)expert * nrows_bank * row_bytes;
         const uint8_t *wb2 = PAIR ? a.bank2 + (size_t)expert * nrows_bank * row_bytes : wb;
-        // passes of RPP rows inside the block; pass q of this wave is block
-        // pass q*WAVES + wave. Spare waves run one clamped pass, store nothing.
+        // passes of RPP rows inside the block
         const int bpasses = (len + RPP - 1) / RPP;
-        const int pr = (bpasses - wave + WAVES - 1) / WAVES;
-        const int p1 = pr > 1 ? pr : 1;
-        auto load_pass = [&](Raw (&B)[UPL], int pass) {
-            const int v = r0 + min((pass * WAVES + wave) * RPP + grow, len - 1);
-            const uint8_t *row = PAIR ? ((v & 1) ? wb2 : wb) + (size_t)(v >> 1) * row_bytes
-                                      : wb + (size_t)v * row_bytes;
-#pragma unroll
-            for (int i = 0; i < UPL; ++i) F::load(B[i], row, uu[i]);
-        };
 
-        for (int c = 0; c < count; ++c) {
-            const int slot = slot_list[c];
-            typename F::Stage S;
-            F::template fetch<stage_granules(G, UPL)>(S, moe_act<F>(a, slot / a.x_div), a.k);
-            Raw R[NB][UPL];
+        for (int c0 = 0; c0 < count; c0 += NSP) {
+            // this group of up to NSP slots: wps waves per slot; this wave
+            // takes slot c0 + si, block passes q*wps + wo. Spare waves (a
+            // group of 3 leaves one) run one clamped pass and store nothing.
+            const int ns = min(NSP, count - c0);
+            const int wsh = ns == 1 ? 2 : (ns == 2 ? 1 : 0);  // log2 of waves per slot
+            const int wps = 1 << wsh;
+            const int si = wave >> wsh, wo = wave & (wps - 1);
+            const bool active = si < ns;
+            const int slot = slot_list[c0 + (active ? si : 0)];
+            const int pr = active ? (bpasses - wo + wps - 1) / wps : 0;
+            const int p1 = pr > 1 ? pr : 1;
+            auto load_pass = [&](Raw (&B)[UPL], int pass) {
+                const int v = r0 + min((pass * wps + wo) * RPP + grow, len - 1);
+                const uint8_t *row = PAIR ? ((v & 1) ? wb2 : wb) + (size_t)(v >> 1) * row_bytes
+                                          : wb + (size_t)v * row_bytes;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                load_pass(R[j], min(j, p1 - 1));
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < UPL; ++i) F::load(B[i], row, uu[i]);
+            };
+            // the group's activation rows, slot c0 + j into region j, loaded
+            // before the weight ring and stored after it (one slot alone:
+            // one row; a group: every region filled, with clamped slots, so
+            // that the loads issue unconditionally)
+            Raw R[NB][UPL];
+            auto ring = [&]() {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    load_pass(R[j], min(j, p1 - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (NSP == 1 || ns == 1) {
+                typename F::Stage S;
+                F::template fetch<stage_granules(G, UPL)>(S, moe_act<F>(a, slot / a.x_div), a.k);
+                ring();
+                __syncthreads();  // the previous group's LDS reads are done
+                F::template store<stage_granules(G, UPL)>(xlds, S, a.k);
+            } else {
+                typename F::Stage S[NSP];
+#pragma unroll
+                for (int j = 0; j < NSP; ++j) {
+                    const int sj = slot_list[c0 + min(j, ns - 1)];
+                    F::template fetch<stage_granules(G, UPL)>(S[j], moe_act<F>(a, sj / a.x_div), a.k);
+                }
+                ring();
+                __syncthreads();  // the previous group's LDS reads are done
+#pragma unroll
+                for (int j = 0; j < NSP; ++j)
+                    F::template store<stage_granules(G, UPL)>(xlds + j * xreg, S[j], a.k);
             }
-            __syncthreads();  // the previous slot's LDS reads are done
-            F::template store<stage_granules(G, UPL)>(xlds, S, a.k);
             __syncthreads();
             typename F::X X[UPL];
 #pragma unroll
-            for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
+            for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds + (active ? si : 0) * xreg, uu[i]);
             float *yrow = a.y + (size_t)slot * ny;
             int pass = 0;
             do {
@@ -474,7 +524,7 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
                     load_pass(R[j], min(ps + NB, p1 - 1));
                     __builtin_amdgcn_sched_barrier(0);
                     acc = group_sum_last<G>(acc);
-                    const int rr = (ps * WAVES + wave) * RPP + grow;
+                    const int rr = (ps * wps + wo) * RPP + grow;
                     if (PAIR) {
                         const float gate = __shfl(acc, lane - G);  // the pair's gate row
                         if ((grow & 1) && gl == G - 1 && ps < pr && rr < len)
@@ -557,12 +607,15 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     for (int j0 = 0; j0 < a.topk; j0 += a.chunk) {
         const int nch = min(a.chunk, a.topk - j0);
         const int nitems = nch * bpasses;
-        // this wave's items q = wave, wave + 4, ...: slot j0 + q / bpasses,
-        // pass q % bpasses
-        const int pr = (nitems - wave + WAVES - 1) / WAVES;
+        // this wave's items: a contiguous run q = qbeg, qbeg + 1, ... (slot
+        // j0 + q / bpasses, pass q % bpasses), so that consecutive items
+        // mostly share a slot and its activation registers are filled once
+        // per slot instead of once per item
+        const int ipw = (nitems + WAVES - 1) / WAVES, qbeg = wave * ipw;
+        const int pr = max(0, min(nitems - qbeg, ipw));
         const int p1 = pr > 1 ? pr : 1;
         auto load_item = [&](Raw &B, int qi) {
-            const int q = min(qi * WAVES + wave, nitems - 1);
+            const int q = min(qbeg + qi, nitems - 1);
             const int j = q / bpasses;
             const int rr = (q - j * bpasses) * RPP + grow;
             const int e = max(s_e[j0 + j], 0);
@@ -623,7 +676,7 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int qs = qi + b;
-                const int q = min(qs * WAVES + wave, nitems - 1);
+                const int q = min(qbeg + qs, nitems - 1);
                 const int j = q / bpasses;
                 const int rr = (q - j * bpasses) * RPP + grow;
                 if (j != cur) {  // wave-uniform
@@ -672,7 +725,7 @@ double expected_present(int64_t nslots, int64_t E) {
 
 template <class F, int G, int UPL, bool PAIR>
 int launch_moe_t(MoeArgs a, hipStream_t s) {
-    const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E);
+    const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E, moe_nsp<F, G, UPL>());
     static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
     if (cache[0] != (int64_t)lds) {
         cache[1] = resident_wgs(k_moe<F, G, UPL, PAIR>, lds);
@@ -725,6 +778,12 @@ int launch_gate_up(MoeArgs a, hipStream_t s) {
     }
 }
 
+// Row passes per slot of a down-pass workgroup at least (its rows are
+// rblk = passes * RPP).
+#ifndef QMV_DOWN_MIN_PASSES
+#define QMV_DOWN_MIN_PASSES 1
+#endif
+
 // Slots staged at once by the down pass: as many as fit 48 KB of LDS, <= 8.
 template <class F>
 int down_chunk(int64_t k, int64_t topk) {
@@ -749,7 +808,8 @@ int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
     // (at most 1024 rows: the row accumulators take WAVES*rblk floats of LDS)
     int rblk = RPP;
     while (rblk < a.n && rblk < 1024 &&
-           (div_up(a.n, rblk) * T > cache[1] || (int64_t)a.topk * (rblk / RPP) < WAVES))
+           (div_up(a.n, rblk) * T > cache[1] || (int64_t)a.topk * (rblk / RPP) < WAVES ||
+            rblk / RPP < QMV_DOWN_MIN_PASSES))
         rblk *= 2;
     a.rblk = rblk;
     const size_t lds = lds0 + (size_t)WAVES * a.rblk * 4;
