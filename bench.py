@@ -691,6 +691,44 @@ def profile_moe_run(T: int, bank_copies: int = 3, calls: int = 48):
                       "copy_bytes": CALIB_BYTES}))
 
 
+def profile_moe_prefill_run(bank_copies: int = 3, calls: int = 12):
+    """Short eager run for rocprofv3 counters of the MoE prefill layer at 512
+    tokens (128 experts, top-8, gate/up Q4_K [768, 2048], down Q6_K
+    [2048, 768]) and of the standalone f32-activation down GEMM
+    (moe_qmm_q6k_f32, 4096 slots): `calls` of each over rotating bank copies,
+    then the 64 MiB calibration copy (torch neg x8)."""
+    import torch
+    import moe_ggml_block_amd as qmv
+    import synth
+    T, topk, E, hidden, inter = 512, 8, 128, 2048, 768
+    ns = T * topk
+    gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, inter, hidden)
+    up = synth.moe_bank(synth.FMT_Q4K, synth.SEED_UP, E, inter, hidden)
+    down = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, hidden, inter)
+    bg, G = rotated(gate, bank_copies)
+    bu, U = rotated(up, bank_copies)
+    bd, D = rotated(down, bank_copies)
+    del gate, up, down
+    lg = torch.from_numpy(synth.moe_logits(T, E)).cuda()
+    ids, w = qmv.moe_route(lg, T, E, topk)
+    x = torch.from_numpy(synth.normal(synth.SEED_PREFILL_X, T * hidden)).cuda()
+    y = torch.empty((T, hidden), device="cuda")
+    ws = torch.empty(qmv.moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E), dtype=torch.uint8, device="cuda")
+    h = torch.from_numpy(synth.normal(synth.SEED_X, ns * inter)).cuda()
+    yd = torch.empty((ns, hidden), device="cuda")
+    for i in range(calls):
+        b = i % bank_copies
+        qmv.moe_ffn_prefill_q4k_q6k(G[b], U[b], D[b], x, ids, w, T, topk, hidden, inter, E, y=y, ws=ws)
+        qmv.moe_qmm_q6k_f32(D[b], h, 1, ids, ns, hidden, inter, E, y=yd)
+    a = torch.ones(CALIB_BYTES // 4, device="cuda")
+    c = torch.empty_like(a)
+    for _ in range(8):
+        torch.neg(a, out=c)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": f"moe prefill layer T={T} x{calls}, moe_qmm_q6k_f32 {ns} slots x{calls}, "
+                                     "neg 64MiB x8", "copy_bytes": CALIB_BYTES}))
+
+
 def profile_prefill_run(copies: int = 64):
     """Short eager run for rocprofv3 counters of the Q4_K prefill GEMM:
     m=512 x W[4096, 4096], 20 launches each of qmm_q4k at bm = 64 and
@@ -775,6 +813,7 @@ def main():
                     help="only the headline kernel's cold roofline timing (graph replays), for rocprofv3")
     ap.add_argument("--profile-warm", action="store_true", help="the same on one resident weight copy")
     ap.add_argument("--profile-moe", type=int, metavar="T", help="short eager MoE decode layer run at T tokens")
+    ap.add_argument("--profile-moe-prefill", action="store_true", help="short eager MoE prefill layer run")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc runs of --profile into the traffic file, then exit")
     ap.add_argument("--gpus", type=int, default=1)
@@ -808,6 +847,9 @@ def main():
         return
     if a.profile_moe:
         profile_moe_run(a.profile_moe)
+        return
+    if a.profile_moe_prefill:
+        profile_moe_prefill_run()
         return
     if a.profile_cold or a.profile_warm:
         profile_q4k_run(a.copies, a.profile_warm)

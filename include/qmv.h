@@ -245,12 +245,15 @@ int moe_qmv_q4k_q8(const void *bank, const int8_t *xq, const float *xs, const fl
 int moe_qmv_q6k_q8(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids,
                    float *y, int64_t nslots, int64_t n, int64_t k, int64_t E, qmv_stream_t stream);
 
-/* The MoE layer with q8 activations on both projections: x quantized once,
- * h = silu(gate) * up from int8 dots (f32), h quantized (quantize_act_q8
- * per 32 values of each slot row), down on int8 dots with the weighted
- * combine -- four launches. Same operands as moe_ffn_q4k_q6k; ws:
- * moe_ffn_q8_workspace_bytes() bytes (q8 x, h, q8 h), 256-byte aligned.
- * Limits as moe_ffn_q4k_q6k (1 <= topk <= 64). */
+/* The MoE layer with q8 activations on both projections: x quantized
+ * (quantize_act_q8 per 32 values of each token row), h = silu(gate) * up
+ * from int8 dots (f32), h quantized (per 32 values of each slot row), down
+ * on int8 dots with the weighted combine. Up to 8 tokens two launches
+ * (each workgroup quantizes the rows it stages), above that four (x and h
+ * quantized by launches of their own); both use the steps of
+ * quantize_act_q8, so the codes and scales are the same bits either way.
+ * Same operands as moe_ffn_q4k_q6k; ws: moe_ffn_q8_workspace_bytes() bytes,
+ * 256-byte aligned. Limits as moe_ffn_q4k_q6k (1 <= topk <= 64). */
 int64_t moe_ffn_q8_workspace_bytes(int64_t T, int64_t topk, int64_t hidden, int64_t inter);
 int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *down, const float *x, const int32_t *ids,
                        const float *wts, float *y, void *ws, int64_t ws_bytes, int64_t T, int64_t topk,

@@ -789,6 +789,46 @@ struct Q6KQ8Unit {
     }
 };
 
+// The Q6_K int8-dot unit on an f32 activation that is quantized while it is
+// staged (the steps of quantize_act_q8 per 32 values, so the codes and scales
+// are the same bits): the MoE down pass stages its h rows this way instead of
+// reading a separately quantized copy (see k_moe_down).
+struct Q6KQ8XUnit {
+    static constexpr bool Q8 = false;  // takes f32 rows
+    static constexpr bool QX = true;   // quantized in the staging
+    static constexpr int BW = 256, BB = 210;
+    static constexpr int RING = QMV_RING_Q6K;
+    static constexpr int MAX_WG_PER_CU = 2;
+    static constexpr int ACT_STRIDE = Q6KQ8Unit::ACT_STRIDE;
+    using Act = ActF32;
+    using X = UnitQ8x4;
+    using Raw = Q6KUnit::Raw;
+    static __device__ __forceinline__ int units_per_row(int k) { return (k / 256) * 4; }
+    static __device__ __forceinline__ void load(Raw &R, const uint8_t *row, int u) { Q6KUnit::load(R, row, u); }
+    static __device__ __forceinline__ int granule_unit(int i, int *g) { return Q6KQ8Unit::granule_unit(i, g); }
+    static __device__ __forceinline__ int block_unit(int b, int *g) { return Q6KQ8Unit::block_unit(b, g); }
+    // f32 values 4c4..4c4+3 of a row, quantized with the 8 lanes that hold
+    // the rest of their 32-value block (call with all 8 lanes active), into
+    // the Q6KQ8Unit layout of the row staged at xl
+    static __device__ __forceinline__ void store_quantized(float *xl, f32x4 v, int c4, bool valid) {
+        float sc, xsum;
+        const uint32_t packed = quantize_q8_lanes(make_float4(v.x, v.y, v.z, v.w), &sc, &xsum);
+        if (valid) {
+            int g;
+            const int u = granule_unit(c4 >> 2, &g);
+            reinterpret_cast<uint32_t *>(xl)[ACT_STRIDE * u + 4 * g + (c4 & 3)] = packed;
+            if ((c4 & 7) == 0) {
+                int gb;
+                const int ub = block_unit(c4 >> 3, &gb);
+                xl[ACT_STRIDE * ub + 16 + gb] = sc;
+                xl[ACT_STRIDE * (ub + 1) + 16 + gb] = sc;
+            }
+        }
+    }
+    static __device__ __forceinline__ void load_lds(UnitQ8x4 &X, const float *xl, int u) { Q6KQ8Unit::load_lds(X, xl, u); }
+    static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8x4 &X, int u) { return Q6KQ8Unit::dot(R, X, u); }
+};
+
 // ---------------------------------------- Q4_K x q8, quantizing in-kernel ---
 // The Q4KQ8Unit decode with the activation given in f32: every workgroup
 // quantizes x itself while staging it (the same IEEE steps as

@@ -32,6 +32,7 @@
 #include <climits>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "blocks.hpp"
 #include "internal.hpp"
@@ -49,6 +50,10 @@ constexpr int ROUTE_FUSED_E = 256;  // routing fused into the gather up to this 
 // and up to this many tokens: every workgroup routes every token, which
 // beat a separate router launch at 1 and 4 tokens and lost at 16 (measured)
 constexpr int ROUTE_FUSED_T = 8;
+// q8 decode layer: up to this many tokens the gathers quantize the rows they
+// stage instead of separate quantizer launches (measured: one token 23.2 ->
+// 21.3 us, four the same, sixteen 82.4 -> 83.3)
+constexpr int Q8_STAGED_T = 8;
 // Row passes in flight per wave in the gathers: their row blocks are short
 // (a few passes per wave), so every pass of a block is requested up front.
 constexpr int MOE_RING = 2;
@@ -240,9 +245,10 @@ size_t moe_lds_bytes(int k, int act_stride, int nslots, int E, int nsp) {
 }
 
 // Slots of one item staged at once by k_moe (each in its own LDS region,
-// one region of (k/64)*ACT_STRIDE floats per slot). q8 activations: as many
-// of 4, 2, 1 as fit 36 KB at the largest k of the lane mapping (G lanes of
-// UPL units). f32 activations: one -- their gathers are bound by the vector
+// one region of (k/64)*ACT_STRIDE floats per slot). int8 dots (q8
+// activations, given or quantized in the staging): as many of 4, 2, 1 as
+// fit 36 KB at the largest k of the lane mapping (G lanes of UPL units).
+// f32 dots: one -- their gathers are bound by the vector
 // ALU at many slots per expert (one FMA per weight and slot), and splitting
 // the waves among slots halved the rows each workgroup kept in flight
 // (128 experts, top-8, 16 tokens: 89.5 -> 94.8 us, while the q8 layer went
@@ -250,8 +256,15 @@ size_t moe_lds_bytes(int k, int act_stride, int nslots, int E, int nsp) {
 template <class F, int G, int UPL>
 constexpr int moe_nsp() {
     constexpr int region = G * UPL * F::ACT_STRIDE * 4;
-    return !F::Q8 ? 1 : (4 * region <= 36864 ? 4 : (2 * region <= 36864 ? 2 : 1));
+    constexpr bool f32_dots = std::is_same<typename F::X, UnitX>::value;
+    return f32_dots ? 1 : (4 * region <= 36864 ? 4 : (2 * region <= 36864 ? 2 : 1));
 }
+
+// Units whose f32 activation rows are quantized while staged (F::QX).
+template <class F, class = void>
+struct moe_stage_qx : std::false_type {};
+template <class F>
+struct moe_stage_qx<F, std::void_t<decltype(F::QX)>> : std::bool_constant<F::QX> {};
 
 // Persistent over work items: an item is a block of rows of one present
 // expert, for every slot routed to that expert (in slot order):
@@ -647,6 +660,29 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
                 const int u = F::block_unit(b, &g);
                 hlds[j * ust + F::ACT_STRIDE * u + 16 + g] = sc;
                 hlds[j * ust + F::ACT_STRIDE * (u + 1) + 16 + g] = sc;
+            }
+        } else if constexpr (moe_stage_qx<F>::value) {
+            // f32 h rows quantized while staged (8 consecutive lanes hold one
+            // 32-value block; nch * k4 is a multiple of 8, so every group of
+            // 8 is wholly inside or wholly past the end, and the lanes past
+            // it quantize clamped values and store nothing)
+            const int n4 = nch * k4;
+            if (j0 == 0 && hpre) {
+#pragma unroll
+                for (int r = 0; r < HPRE; ++r) {
+                    if (256 * r < n4) {
+                        const int i = tid + 256 * r, ic = min(i, n4 - 1);
+                        const int j = ic / k4, c4 = ic - j * k4;
+                        F::store_quantized(hlds + j * ust, hv0[r], c4, i < n4);
+                    }
+                }
+            } else {
+                for (int i0 = 0; i0 < n4; i0 += 256) {
+                    const int i = i0 + tid, ic = min(i, n4 - 1);
+                    const int j = ic / k4, c4 = ic - j * k4;
+                    const f32x4 hv = *reinterpret_cast<const f32x4 *>(a.h + ((size_t)t * a.topk + j0 + j) * a.k + 4 * c4);
+                    F::store_quantized(hlds + j * ust, hv, c4, i < n4);
+                }
             }
         } else if (j0 == 0 && hpre) {
 #pragma unroll
@@ -1178,7 +1214,29 @@ extern "C" int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *
     if (!aligned(up, 16) || !aligned(wts, 4) || !aligned(ws, 256)) return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
     const Q8LayerWs w = q8_layer_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter);
-    // x -> q8 once; h = silu(gate x) * (up x) on int8 dots; h -> q8; down on int8 dots + combine
+    DownArgs dn{};
+    dn.bank = static_cast<const uint8_t *>(down);
+    dn.ids = ids;
+    dn.wts = wts;
+    dn.y = y;
+    dn.n = (int)hidden;
+    dn.k = (int)inter;
+    dn.E = (int)E;
+    dn.topk = (int)topk;
+    if (T <= Q8_STAGED_T) {
+        // h = silu(gate x) * (up x) on int8 dots, x quantized as each
+        // workgroup stages it; down on int8 dots + combine, h quantized as it
+        // is staged (the steps of quantize_act_q8: the same codes as the two
+        // quantizer launches below, which at a few tokens cost more than the
+        // repeated quantization: 23.2 -> 21.3 us at one token)
+        rc = launch_gate_up<Q4KQ8XUnit>(gather_args(gate, up, x, topk, ids, w.h, ns, 2 * inter, hidden, E), s);
+        if (rc) return rc;
+        dn.h = w.h;
+        dn.chunk = down_chunk<Q6KQ8XUnit>(inter, topk);
+        return launch_down<Q6KQ8XUnit>(dn, T, s);
+    }
+    // x -> q8 once; h = silu(gate x) * (up x) on int8 dots; h -> q8; down on
+    // int8 dots + combine
     rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
     if (rc) return rc;
     MoeArgs gu = gather_args(gate, up, nullptr, topk, ids, w.h, ns, 2 * inter, hidden, E);
@@ -1189,17 +1247,9 @@ extern "C" int moe_ffn_q4k_q6k_q8(const void *gate, const void *up, const void *
     if (rc) return rc;
     rc = quantize_act_q8(w.h, w.hq, w.hs, w.hsum, ns, inter, stream);
     if (rc) return rc;
-    DownArgs dn{};
-    dn.bank = static_cast<const uint8_t *>(down);
     dn.hq = w.hq;
     dn.hs = w.hs;
-    dn.ids = ids;
-    dn.wts = wts;
-    dn.y = y;
-    dn.n = (int)hidden;
-    dn.k = (int)inter;
-    dn.E = (int)E;
-    dn.topk = (int)topk;
     dn.chunk = down_chunk<Q6KQ8Unit>(inter, topk);
     return launch_down<Q6KQ8Unit>(dn, T, s);
 }
+
