@@ -360,9 +360,11 @@ int qmm_q8_0(const void *w, const int8_t *xq, const float *xs, float *y, int64_t
  * grouped by expert on the device as in moe_qmm_q4k):
  *   moe_qmm_q6k:     y[s, r] = sum_c W_deq[ids[s], r, c] * xs[a, c/32] * xq[a, c]
  *   moe_qmm_q6k_f32: y[s, r] = sum_c W_deq[ids[s], r, c] * x[a, c]
- * with a = s / x_div. The f32 form splits each activation (scaled by a power
- * of two per 32 values) into two f16 halves on the matrix cores, which keeps
- * f32 accuracy. bank: E*n*(k/256)*210 bytes; y: f32[nslots, n], every row
+ * with a = s / x_div. The f32 form splits each activation into two f16
+ * halves on the matrix cores, under a power of two per activation row for
+ * k <= 1024 (the rows of a workgroup's 32 slots then stay in LDS) and per 32
+ * values above, which keeps f32 accuracy. bank: E*n*(k/256)*210 bytes; y:
+ * f32[nslots, n], every row
  * written (zero for an expert outside [0, E)). k % 256 == 0; 1 <= E <= 1024;
  * nslots <= 2^20; xq and x 16-byte aligned, bank 2-byte, the rest 4-byte. */
 int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, int64_t x_div, const int32_t *ids, float *y,
@@ -381,7 +383,8 @@ int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32
  *   e = ids[t, j] in [0, E): h = silu(Wg[e] x_deq[t]) * (Wu[e] x_deq[t]),
  *   d = Wd[e] h (h kept in f32); y[t] = sum_j wts[t, j] * d_s.
  * Same operands as moe_ffn_q4k_q6k; ws: moe_ffn_prefill_workspace_bytes()
- * bytes of device scratch (q8 activation, tile table, h, d), 256-byte
+ * bytes of device scratch (q8 activation, tile table and its 32-slot
+ * segments, h, d), 256-byte
  * aligned, caller-owned, contents undefined after the call. Slots are
  * grouped by expert on the device; nothing is synchronized with the host.
  * hidden, inter: multiples of 256 (<= 65536); 1 <= E <= 1024; T <= 65535;

@@ -96,14 +96,14 @@ constexpr int QMM_MOE_MAX_E = 1024;
 // its expert's slots into s_slot (-1 past the expert's count). Returns esel,
 // or -1 for a workgroup past the last tile: the grid has more row blocks
 // than tiles (each present expert adds less than one tile to nslots / BM),
-// and those spare workgroups write the zero rows (columns [n0, n0 + BN)) of
+// and those spare workgroups write the zero rows (columns [n0, n0 + ncols)) of
 // slots whose expert is outside [0, E), spare j taking slots
 // [j*chunk, (j+1)*chunk). s_ids (QMM_ID_CHUNK ints) and s_cnt (E ints) are
 // LDS scratch that the caller reuses afterwards; the function ends with a
 // barrier. Call from every thread of the workgroup.
 template <int BM, int BN, int NTHREADS>
 QMV_DEV int qmm_group(const int32_t *__restrict__ ids, int m, int E, int *s_ids, int *s_cnt, int *s_slot,
-                      float *__restrict__ Y, int n, int n0) {
+                      float *__restrict__ Y, int n, int n0, int ncols = BN) {
     constexpr int IPT = QMM_ID_CHUNK / NTHREADS;  // ids per thread per chunk
     constexpr int NW = NTHREADS / 64;
     __shared__ int s_wsum[NW];
@@ -176,7 +176,7 @@ QMV_DEV int qmm_group(const int32_t *__restrict__ ids, int m, int E, int *s_ids,
         for (int sl = s0 + tid; sl < s1; sl += NTHREADS) {
             const int e = ids[sl];
             if (e < 0 || e >= E)
-                for (int c = n0; c < min(n0 + BN, n); ++c) Y[(size_t)sl * n + c] = 0.0f;
+                for (int c = n0; c < min(n0 + ncols, n); ++c) Y[(size_t)sl * n + c] = 0.0f;
         }
         return -1;
     }
@@ -1921,6 +1921,429 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
 #define QMM6_PF64 64, 128, 2, 2, 512   // the prefill layer's down projection, 64-slot tiles
 #define QMM6_PF32 32, 256, 2, 2, 512   // and 32-slot tiles
 
+// ------------------------- Q6_K expert GEMM on a resident f32 activation
+// The MoE down projection at prefill has tens of slots per expert and a
+// short k (the expert's inner size): the tile GEMM above then spends most of
+// its time waiting on loads between its per-phase barriers. This form keeps
+// a workgroup's activation rows in LDS for the whole product and lets every
+// wave stream its own weight rows:
+//  - a workgroup takes up to 32 slots of one expert and rw weight rows. It
+//    stages the slots' rows once as two f16 halves per value under a per-row
+//    power of two: v = 2^e x with the row's largest magnitude in
+//    [2^14, 2^15), hi = f16(v), lo = f16(v - hi) (22 bits of each value; a
+//    value far below the row's largest keeps an absolute error under 2^-25
+//    of the scaled units, 2^-39 of that largest). Four values take 16 bytes,
+//    [hi x4 | lo x4]; rows are 4k + 16 bytes apart, so that the 16-byte
+//    fragment reads of sixteen consecutive rows hit distinct banks.
+//  - each wave owns groups of 32 weight rows (two 16-row fragments) and
+//    walks each group superblock by superblock, with a ring of register sets
+//    holding the raw codes of the next steps in flight. There is no barrier
+//    after the staging.
+//  - per 16-value sub-block a lane decodes the four codes at its fragment
+//    position (q - 32, exact in f16) and the matrix cores form
+//    T = A_hi B + A_lo B on two v_mfma_f32_16x16x16_f16. The activation rows
+//    are the A operand and the weight rows the B operand, so a lane's four
+//    results share its weight row, and the VALU adds d*sc*T of that row.
+// Loads read clamped rows unconditionally and stores are masked, so that the
+// compiler waits for exactly the oldest step of the ring.
+#ifndef QMV_Q6R
+#define QMV_Q6R 1               // 0: the tile GEMM for every k
+#endif
+constexpr int Q6R_SLOTS = 32;   // activation rows per workgroup
+constexpr int Q6R_MAX_NSB = 4;  // k <= 1024: 32 staged rows of 4k + 16 bytes
+
+// Codes of four consecutive positions l..l+3 in the four 32-value runs of a
+// 128-value half: ql0 = ql bytes l..l+3 (runs 0 and 2), ql1 = ql bytes
+// 32+l.. (runs 1 and 3), qh = qh bytes l..l+3 (two bits per run). Each
+// result holds four 6-bit codes, one per byte.
+QMV_DEV void q6_run_codes(uint32_t ql0, uint32_t ql1, uint32_t qh, uint32_t (&c)[4]) {
+    c[0] = (ql0 & 0x0F0F0F0Fu) | ((qh << 4) & 0x30303030u);
+    c[1] = (ql1 & 0x0F0F0F0Fu) | ((qh << 2) & 0x30303030u);
+    c[2] = ((ql0 >> 4) & 0x0F0F0F0Fu) | (qh & 0x30303030u);
+    c[3] = ((ql1 >> 4) & 0x0F0F0F0Fu) | ((qh >> 2) & 0x30303030u);
+}
+
+// 4x4 transpose of dwords across the four 16-lane rows of a wave: row p's
+// dword c becomes row c's dword p (v_permlane32_swap exchanges the upper
+// rows of its first operand with the lower rows of its second,
+// v_permlane16_swap the odd rows of its first with the even rows of its
+// second).
+QMV_DEV uint4 rows_transpose(uint4 v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return make_uint4(c[0], c[1], d[0], d[1]);
+}
+
+// Raw codes of one step (a superblock of the wave's FPW 16-row fragments).
+// Lane row lq loads the 16 bytes of its home (hh, lh) = (lq >> 1, lq & 1):
+// ql bytes 64hh + 16lh.. (runs 0 and 2), ql bytes 64hh + 32 + 16lh.. (runs 1
+// and 3) and qh bytes 32hh + 16lh..; after rows_transpose, dword 2hh + lh of
+// each holds positions 16lh + 4lq.. of half hh, the lane's fragment
+// positions. sc and d are the row's scales.
+template <int FPW>
+struct Q6rRaw {
+    uint4 ql0[FPW], ql1[FPW], qh[FPW], sc[FPW];
+    uint32_t d[FPW];
+};
+
+#ifndef Q6R_RING
+#define Q6R_RING 2
+#endif
+#ifndef Q6R_FPW
+#define Q6R_FPW 1               // 16-row weight fragments per wave (1: 16 waves, 2: 8 waves)
+#endif
+
+// Work: the product splits into units of one 32-slot segment (the slots of
+// one expert, packed) by 256 weight rows. One workgroup per CU (the staged
+// rows fill most of its LDS), each taking an equal run of consecutive units,
+// so a workgroup stages once per segment its run touches (one or two) and
+// every CU gets the same amount of work. GROUPED: the segments are the
+// expert's slots in ascending slot order, 32 at a time, derived in every
+// workgroup from ids (per-expert counts, then a ballot compaction of the
+// segment's slots); the workgroups also share the zeroing of the rows of
+// slots whose expert is outside [0, E). Otherwise the segments come from the
+// layer's tile table (nseg, seg_off).
+// FPW weight fragments per wave, 16 / FPW waves: 256 weight rows per unit.
+template <int NSB, bool GROUPED, int FPW>
+__global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const int *__restrict__ nseg_p,
+                                                       const int *__restrict__ seg_off, int bmt) {
+    static_assert(NSB >= 1 && NSB <= Q6R_MAX_NSB, "k <= 1024");
+    static_assert(FPW == 1 || FPW == 2, "fragments per wave");
+    constexpr int NW = 16 / FPW, NT = 64 * NW;           // waves, threads
+    constexpr int PITCH = 1024 * NSB + 16;                // bytes per staged row
+    constexpr int D = Q6R_RING;                           // steps in flight per wave
+    constexpr int LPR = NT / Q6R_SLOTS;                   // staging lanes per row
+    constexpr int CPL = 64 * NSB / LPR;                   // staged float4 per lane
+    __shared__ __attribute__((aligned(16))) uint8_t act[Q6R_SLOTS * PITCH];
+    __shared__ int s_slot[Q6R_SLOTS];
+    __shared__ float s_inv[Q6R_SLOTS];
+    __shared__ int s_misc[4], s_wsum[NW];
+    __shared__ int s_cnt[GROUPED ? QMM_MOE_MAX_E : 1], s_sb[GROUPED ? QMM_MOE_MAX_E : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lq = lane >> 4;
+    const int n = a.n, m = a.m, E = a.E;
+    const int nrc = (n + 255) / 256;  // 256-row chunks
+    const int32_t *__restrict__ ids = a.ids;
+    float *__restrict__ Y = a.Y;
+    int nseg;
+    if constexpr (GROUPED) {
+        for (int e = tid; e < E; e += NT) s_cnt[e] = 0;
+        __syncthreads();
+        for (int sl = tid; sl < m; sl += NT) {
+            const int e = ids[sl];
+            if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // exclusive prefix of the per-expert segment counts, lane l
+            // holding experts [l*EPL, l*EPL + EPL)
+            constexpr int EPL = QMM_MOE_MAX_E / 64;
+            int tl = 0;
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                if (e < E) tl += (s_cnt[e] + 31) / 32;
+            }
+            int inc = tl;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(inc, d);
+                if (lane >= d) inc += v;
+            }
+            int run = inc - tl;
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                if (e < E) {
+                    s_sb[e] = run;
+                    run += (s_cnt[e] + 31) / 32;
+                }
+            }
+            if (lane == 63) s_misc[0] = inc;
+        }
+        __syncthreads();
+        nseg = s_misc[0];
+        // rows of slots whose expert is outside [0, E) are zero: this
+        // workgroup's share of the slots, a wave per slot
+        const int z0 = (int)((int64_t)m * blockIdx.x / gridDim.x), z1 = (int)((int64_t)m * (blockIdx.x + 1) / gridDim.x);
+        for (int sl = z0 + wave; sl < z1; sl += NW) {
+            const int e = ids[sl];
+            if (e < 0 || e >= E)
+                for (int c = lane; c < n; c += 64) Y[(size_t)sl * n + c] = 0.0f;
+        }
+    } else {
+        nseg = *nseg_p;
+    }
+
+    const size_t row_bytes = (size_t)NSB * 210;
+    const int oq = 64 * (lq >> 1) + 16 * (lq & 1), oh = 128 + 32 * (lq >> 1) + 16 * (lq & 1);
+    const int64_t total = (int64_t)nseg * nrc;
+    const int64_t u1 = total * (blockIdx.x + 1) / gridDim.x;
+    int64_t u = total * blockIdx.x / gridDim.x;
+    while (u < u1) {
+        const int seg = (int)(u / nrc), c0 = (int)(u - (int64_t)seg * nrc);
+        const int nrg = (int)min((int64_t)(nrc - c0), u1 - u);  // 256-row chunks of this segment
+        u += nrg;
+        __syncthreads();  // the last segment's readers of act, s_slot, s_inv are done
+        int esel;
+        if constexpr (GROUPED) {
+            for (int e = tid; e < E; e += NT) {
+                const int b = s_sb[e], ns = (s_cnt[e] + 31) / 32;
+                if (seg >= b && seg < b + ns) {
+                    s_misc[1] = e;
+                    s_misc[2] = 32 * (seg - b);
+                }
+            }
+            if (tid < Q6R_SLOTS) s_slot[tid] = -1;
+            __syncthreads();
+            esel = s_misc[1];
+            const int rank0 = s_misc[2];
+            // ascending compaction: per chunk, wave w takes ids [w*CW, (w+1)*CW)
+            // in order; a rank is the running count plus the earlier waves'
+            // counts plus the ballot prefix
+            constexpr int CW = QMM_ID_CHUNK / NW;
+            int run = 0;
+            for (int q0 = 0; q0 < m && run < rank0 + Q6R_SLOTS; q0 += QMM_ID_CHUNK) {
+                int cw = 0;
+                for (int b = 0; b < CW; b += 64) {
+                    const int sl = q0 + wave * CW + b + lane;
+                    cw += __popcll(__ballot(sl < m && ids[sl] == esel));
+                }
+                if (lane == 0) s_wsum[wave] = cw;
+                __syncthreads();
+                int base = run;
+                for (int v = 0; v < NW; ++v) {
+                    if (v < wave) base += s_wsum[v];
+                    run += s_wsum[v];
+                }
+                for (int b = 0; b < CW; b += 64) {
+                    const int sl = q0 + wave * CW + b + lane;
+                    const bool hit = sl < m && ids[sl] == esel;
+                    const uint64_t bal = __ballot(hit);
+                    const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+                    if (hit && rank >= rank0 && rank < rank0 + Q6R_SLOTS) s_slot[rank - rank0] = sl;
+                    base += __popcll(bal);
+                }
+                __syncthreads();  // s_wsum is rewritten by the next chunk
+            }
+        } else {
+            const int off = seg_off[seg];
+            if (tid < Q6R_SLOTS) s_slot[tid] = a.tile_slots[off + tid];
+            esel = a.tile_e[off / bmt];
+            __syncthreads();
+        }
+        esel = __builtin_amdgcn_readfirstlane(esel);
+
+        // staging: lanes of row tid / LPR, float4 chunks l + LPR*i; the row's
+        // largest magnitude over those lanes, the power of two, then
+        // [hi x4 | lo x4] per chunk (rows of slots past the segment are 0)
+        {
+            const int srow = tid / LPR, l = tid % LPR;
+            const int sslot = s_slot[srow];
+            const float *xr = a.x + (size_t)(sslot >= 0 ? sslot / a.x_div : 0) * (256 * NSB);
+            float4 xv[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) xv[i] = *reinterpret_cast<const float4 *>(xr + 4 * (l + LPR * i));
+            float am = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                am = fmaxf(am, fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w))));
+#pragma unroll
+            for (int d = 1; d < LPR; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
+            const int e = am > 0.f ? ((int)((__float_as_uint(am) >> 23) & 0xFF) - 127) : 0;
+            const int ee = max(min(14 - e, 126), -126);  // 2^ee and 2^-ee are normal
+            const float sc = sslot >= 0 ? __uint_as_float((uint32_t)(ee + 127) << 23) : 0.f;
+            const float inv = __uint_as_float((uint32_t)(127 - ee) << 23);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const float y0 = xv[i].x * sc, y1 = xv[i].y * sc, y2 = xv[i].z * sc, y3 = xv[i].w * sc;
+                const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1, h2v = (_Float16)y2, h3 = (_Float16)y3;
+                const h4 hi = {h0, h1, h2v, h3};
+                const h4 lo = {(_Float16)(y0 - (float)h0), (_Float16)(y1 - (float)h1), (_Float16)(y2 - (float)h2v),
+                               (_Float16)(y3 - (float)h3)};
+                const uint2 hb = __builtin_bit_cast(uint2, hi), lb = __builtin_bit_cast(uint2, lo);
+                *reinterpret_cast<uint4 *>(act + srow * PITCH + 16 * (l + LPR * i)) = make_uint4(hb.x, hb.y, lb.x, lb.y);
+            }
+            if (l == 0) s_inv[srow] = inv;
+        }
+        __syncthreads();
+
+        // the weight ring: step j of this wave is superblock j % NSB of its
+        // rows in chunk c0 + j / NSB
+        const uint8_t *__restrict__ wb = a.w + (size_t)esel * n * row_bytes;
+        const int r0 = 256 * c0;
+        auto load_step = [&](Q6rRaw<FPW> &R, int j) {
+            const int i = j / NSB, s = j - i * NSB;
+#pragma unroll
+            for (int f = 0; f < FPW; ++f) {
+                const int row = min(r0 + 256 * i + 16 * FPW * wave + 16 * f + li, n - 1);
+                const uint8_t *p = wb + (size_t)row * row_bytes + 210 * s;
+                R.ql0[f] = ld16(p + oq);
+                R.ql1[f] = ld16(p + oq + 32);
+                R.qh[f] = ld16(p + oh);
+                R.sc[f] = ld16(p + 192);
+                R.d[f] = ld2(p + 208);
+            }
+        };
+        const int J = nrg * NSB;  // steps of this wave
+        Q6rRaw<FPW> R[D];
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            load_step(R[q], min(q, J - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // the wave's steps with NF 16-slot fragments (uniform per segment)
+        auto run = [&](auto NFc) {
+            constexpr int NF = decltype(NFc)::value;
+            v4f out[FPW][NF];
+            auto compute = [&](const Q6rRaw<FPW> &Rs, int s) {
+                const uint8_t *abase = act + li * PITCH + 16 * lq + 1024 * s;
+                float dd[FPW];
+                uint32_t q0[FPW][4], q1[FPW][4], qh[FPW][4];
+#pragma unroll
+                for (int f = 0; f < FPW; ++f) {
+                    dd[f] = h2f(Rs.d[f]);
+                    const uint4 a0 = rows_transpose(Rs.ql0[f]), a1 = rows_transpose(Rs.ql1[f]),
+                                ah = rows_transpose(Rs.qh[f]);
+                    q0[f][0] = a0.x; q0[f][1] = a0.y; q0[f][2] = a0.z; q0[f][3] = a0.w;
+                    q1[f][0] = a1.x; q1[f][1] = a1.y; q1[f][2] = a1.z; q1[f][3] = a1.w;
+                    qh[f][0] = ah.x; qh[f][1] = ah.y; qh[f][2] = ah.z; qh[f][3] = ah.w;
+                }
+                // Sub-blocks in the order m = 4 (2 hh + lh) + g (one decode per
+                // (hh, lh) group). The fragments of sub-block m + 1 are read
+                // from LDS while m is on the matrix cores, and the products of
+                // m are added while those of m + 1 are (Tp, cp: the pending ones).
+                auto sub_of = [](int mm) { return 8 * ((mm >> 3) & 1) + 2 * (mm & 3) + ((mm >> 2) & 1); };
+                auto read_a = [&](uint4(&A)[NF], int mm) {
+#pragma unroll
+                    for (int t = 0; t < NF; ++t)
+                        A[t] = *reinterpret_cast<const uint4 *>(abase + 16 * t * PITCH + 64 * sub_of(mm));
+                };
+                v4f Tp[FPW][NF];
+                float cp[FPW];
+                uint4 An[NF];
+                read_a(An, 0);
+                uint2 B[FPW][4];
+#pragma unroll
+                for (int mm = 0; mm < 16; ++mm) {
+                    const int hh = mm >> 3, lh = (mm >> 2) & 1, g = mm & 3, sub = sub_of(mm);
+                    if (g == 0) {
+#pragma unroll
+                        for (int f = 0; f < FPW; ++f) {
+                            uint32_t c[4];
+                            q6_run_codes(q0[f][2 * hh + lh], q1[f][2 * hh + lh], qh[f][2 * hh + lh], c);
+#pragma unroll
+                            for (int gg = 0; gg < 4; ++gg) B[f][gg] = q6x4_to_f16(c[gg]);
+                        }
+                    }
+                    uint4 A[NF];
+#pragma unroll
+                    for (int t = 0; t < NF; ++t) A[t] = An[t];
+                    if (mm + 1 < 16) read_a(An, mm + 1);
+                    v4f Tn[FPW][NF];
+                    float cn[FPW];
+#pragma unroll
+                    for (int f = 0; f < FPW; ++f) {
+                        const uint4 s4 = Rs.sc[f];
+                        const uint32_t sw =
+                            (sub >> 2) == 0 ? s4.x : (sub >> 2) == 1 ? s4.y : (sub >> 2) == 2 ? s4.z : s4.w;
+                        cn[f] = dd[f] * (float)(int8_t)((sw >> (8 * (sub & 3))) & 0xFFu);
+                        const h4 bw = __builtin_bit_cast(h4, B[f][g]);
+#pragma unroll
+                        for (int t = 0; t < NF; ++t) {
+                            v4f T = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                                __builtin_bit_cast(h4, make_uint2(A[t].x, A[t].y)), bw, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            Tn[f][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                                __builtin_bit_cast(h4, make_uint2(A[t].z, A[t].w)), bw, T, 0, 0, 0);
+                        }
+                    }
+                    if (mm > 0) {
+#pragma unroll
+                        for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                            for (int t = 0; t < NF; ++t) out[f][t] = cp[f] * Tp[f][t] + out[f][t];
+                    }
+                    // the additions stay here: left to itself the compiler
+                    // issues every product of the step first and keeps them in
+                    // scratch memory
+#pragma unroll
+                    for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                        for (int t = 0; t < NF; ++t) asm volatile("" : "+v"(out[f][t]));
+#pragma unroll
+                    for (int f = 0; f < FPW; ++f) {
+                        cp[f] = cn[f];
+#pragma unroll
+                        for (int t = 0; t < NF; ++t) Tp[f][t] = Tn[f][t];
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                    for (int t = 0; t < NF; ++t) out[f][t] = cp[f] * Tp[f][t] + out[f][t];
+            };
+            for (int j0 = 0; j0 < J; j0 += D) {
+#pragma unroll
+                for (int q = 0; q < D; ++q) {
+                    const int j = j0 + q, i = j / NSB, s = j - i * NSB;
+                    if (s == 0) {
+#pragma unroll
+                        for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                            for (int t = 0; t < NF; ++t) out[f][t] = (v4f){0.f, 0.f, 0.f, 0.f};
+                    }
+                    compute(R[q], s);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_step(R[q], min(j + D, J - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s == NSB - 1 && i < nrg) {
+                        // lane: slots 16t + 4lq + r of weight row `row`
+#pragma unroll
+                        for (int f = 0; f < FPW; ++f) {
+                            const int row = r0 + 256 * i + 16 * FPW * wave + 16 * f + li;
+                            if (row >= n) continue;
+#pragma unroll
+                            for (int t = 0; t < NF; ++t)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int ts = 16 * t + 4 * lq + r, slot = s_slot[ts];
+                                    if (slot >= 0) Y[(size_t)slot * n + row] = out[f][t][r] * s_inv[ts];
+                                }
+                        }
+                    }
+                }
+            }
+        };
+        if (s_slot[16] >= 0) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
+    }
+}
+
+// k_qmm6r, one workgroup per CU (k <= 1024): GROUPED derives its 32-slot
+// segments from ids, otherwise they come from the tile table (nseg, seg_off).
+template <bool GROUPED>
+void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt, hipStream_t s) {
+    static thread_local int c_dev = -1, c_cus = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != c_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        c_dev = dev;
+        c_cus = cus;
+    }
+    const dim3 grid((unsigned)c_cus), block(1024 / Q6R_FPW);
+    switch (a.k / 256) {
+        case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 3: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        default: hipLaunchKernelGGL((k_qmm6r<4, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+    }
+}
+
 int check_q6k_shape(int64_t n, int64_t k) {
     if (n < 1 || k < 256 || k % 256) return QMV_EINVAL;
     if (n > (1 << 24) || k > (1 << 20)) return QMV_EUNSUPPORTED;
@@ -1978,9 +2401,15 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
     if (!aligned(x, 16)) return QMV_EALIGN;
     Qmm6Args a{static_cast<const uint8_t *>(bank), nullptr, nullptr, x, y, (int)nslots, (int)n, (int)k, ids, (int)E,
                (int)x_div};
-    const dim3 grid((unsigned)div_up(n, QMM6_MOEF_BN), (unsigned)(div_up(nslots, QMM6_MOEF_BM) + std::min(E, nslots)));
-    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOEF, ACT_F32, true, false, QMM6_MOEF_KP>), grid, dim3(QMM6_MOEF_NT), 0,
-                       (hipStream_t)stream, a);
+    if (QMV_Q6R && k <= 256 * Q6R_MAX_NSB) {
+        // 32-slot tiles grouped in the kernel, the activation resident in LDS
+        launch_q6r<true>(a, nullptr, nullptr, Q6R_SLOTS, (hipStream_t)stream);
+    } else {
+        const dim3 grid((unsigned)div_up(n, QMM6_MOEF_BN),
+                        (unsigned)(div_up(nslots, QMM6_MOEF_BM) + std::min(E, nslots)));
+        hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOEF, ACT_F32, true, false, QMM6_MOEF_KP>), grid, dim3(QMM6_MOEF_NT), 0,
+                           (hipStream_t)stream, a);
+    }
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }
@@ -2005,12 +2434,16 @@ namespace {
 // expert map with the pad of each expert's last tile set to -1, then every
 // valid slot is placed in its expert's tiles. The order of an expert's slots
 // within its tiles follows the atomics and may differ between runs; every
-// output row depends only on its own slot, so the results do not.
+// output row depends only on its own slot, so the results do not. It also
+// lists the 32-slot segments of the table (nseg, and for each the offset in
+// tile_slots of its first slot: an expert's slots are packed from the start
+// of its first tile, so its segment j starts 32 j past it).
 template <int BM>
 __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict__ ids, int S, int E,
                                                       int *__restrict__ ntiles, int *__restrict__ tile_e,
-                                                      int *__restrict__ tile_slots) {
-    __shared__ int s_cnt[QMM_MOE_MAX_E], s_off[QMM_MOE_MAX_E], s_wtot[16];
+                                                      int *__restrict__ tile_slots, int *__restrict__ nseg,
+                                                      int *__restrict__ seg_off) {
+    __shared__ int s_cnt[QMM_MOE_MAX_E], s_off[QMM_MOE_MAX_E], s_wtot[16], s_wseg[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
     __syncthreads();
@@ -2020,25 +2453,38 @@ __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict_
     }
     __syncthreads();
     const int cnt = tid < E ? s_cnt[tid] : 0;
-    const int nt = (cnt + BM - 1) / BM;
-    int inc = nt;
+    const int nt = (cnt + BM - 1) / BM, ns = (cnt + 31) / 32;
+    int inc = nt, incs = ns;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(inc, d);
-        if (lane >= d) inc += v;
+        const int v = __shfl_up(inc, d), vs = __shfl_up(incs, d);
+        if (lane >= d) {
+            inc += v;
+            incs += vs;
+        }
     }
-    if (lane == 63) s_wtot[wave] = inc;
+    if (lane == 63) {
+        s_wtot[wave] = inc;
+        s_wseg[wave] = incs;
+    }
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wtot[w];
-    const int off = base + inc - nt;
+    int base = 0, bases = 0;
+    for (int w = 0; w < wave; ++w) {
+        base += s_wtot[w];
+        bases += s_wseg[w];
+    }
+    const int off = base + inc - nt, offs = bases + incs - ns;
     if (tid < E) {
         s_off[tid] = off;
         for (int i = 0; i < nt; ++i) tile_e[off + i] = tid;
         for (int j = cnt; j < nt * BM; ++j) tile_slots[(size_t)off * BM + j] = -1;
+        for (int j = 0; j < ns; ++j) seg_off[offs + j] = off * BM + 32 * j;
         s_cnt[tid] = 0;  // now the running position of the expert's slots
     }
-    if (tid == 1023) ntiles[0] = base + inc;
+    if (tid == 1023) {
+        ntiles[0] = base + inc;
+        nseg[0] = bases + incs;
+    }
     __syncthreads();
     for (int sl = tid; sl < S; sl += 1024) {
         const int e = ids[sl];
@@ -2074,7 +2520,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ d
 struct PrefillWs {
     int8_t *xq;
     float *xs, *xsum, *h, *d;
-    int *ntiles, *tile_e, *tile_slots;
+    int *ntiles, *tile_e, *tile_slots, *nseg, *seg_off;
     int64_t bytes;
 };
 
@@ -2096,6 +2542,8 @@ PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int
     w.ntiles = reinterpret_cast<int *>(take(4));
     w.tile_e = reinterpret_cast<int *>(take(4 * mt));
     w.tile_slots = reinterpret_cast<int *>(take(4 * mt * bm));
+    w.nseg = reinterpret_cast<int *>(take(4));
+    w.seg_off = reinterpret_cast<int *>(take(4 * pf_max_tiles(S, E, 32)));
     w.h = reinterpret_cast<float *>(take(4 * S * inter));
     w.d = reinterpret_cast<float *>(take(4 * S * hidden));
     w.bytes = o;
@@ -2144,16 +2592,19 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
                 (int)E, 1, w.ntiles, w.tile_e, w.tile_slots};
     if (bm == 32) {
         hipLaunchKernelGGL((k_group_tiles<32>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                           w.tile_slots);
+                           w.tile_slots, w.nseg, w.seg_off);
         QMV_LAUNCH_CHECK();
         hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt),
                            dim3(256), 0, s, gu);
         QMV_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF32, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 256), (unsigned)mt),
-                           dim3(512), 0, s, dn);
+        if (QMV_Q6R && inter <= 256 * Q6R_MAX_NSB)
+            launch_q6r<false>(dn, w.nseg, w.seg_off, 32, s);
+        else
+            hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF32, ACT_F32, true, true>),
+                               dim3((unsigned)div_up(hidden, 256), (unsigned)mt), dim3(512), 0, s, dn);
     } else {
         hipLaunchKernelGGL((k_group_tiles<64>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                           w.tile_slots);
+                           w.tile_slots, w.nseg, w.seg_off);
         QMV_LAUNCH_CHECK();
         // weight-side tile while its 32-bit lane offsets hold (an expert's
         // rows and the activation rows below 2^32 bytes)
@@ -2165,8 +2616,11 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
                                dim3((unsigned)div_up(inter, QMM_MOE64_BN / 2), (unsigned)mt), dim3(QMM_MOE64_NT), 0, s,
                                gu);
         QMV_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF64, ACT_F32, true, true>), dim3((unsigned)div_up(hidden, 128), (unsigned)mt),
-                           dim3(512), 0, s, dn);
+        if (QMV_Q6R && inter <= 256 * Q6R_MAX_NSB)
+            launch_q6r<false>(dn, w.nseg, w.seg_off, 64, s);
+        else
+            hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF64, ACT_F32, true, true>),
+                               dim3((unsigned)div_up(hidden, 128), (unsigned)mt), dim3(512), 0, s, dn);
     }
     QMV_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)div_up(hidden, 1024), (unsigned)T), dim3(256), 0, s, w.d, ids,

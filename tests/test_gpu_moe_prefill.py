@@ -181,9 +181,19 @@ def _check6(ids, n, k, E, x_div, seed, f32, sample=None):
 
 
 @pytest.mark.parametrize("f32", [False, True])
-@pytest.mark.parametrize("case", ["pages", "ragged", "id_chunks"])
+@pytest.mark.parametrize("case", ["pages", "ragged", "id_chunks", "k1024", "k1280"])
 def test_moe_qmm_q6k(case, f32):
-    if case == "pages":
+    if case == "k1024":
+        # the longest rows the f32 form keeps resident in LDS, a ragged last tile
+        ids = ((np.arange(300) * 7) % 5).astype(np.int32)
+        args = (ids, 272, 1024, 5, 2, 97)
+        sample = np.array([0, 1, 2, 150, 298, 299])
+    elif case == "k1280":
+        # past that limit (the staged tile GEMM)
+        ids = ((np.arange(90) * 3) % 4).astype(np.int32)
+        args = (ids, 80, 1280, 4, 1, 95)
+        sample = None
+    elif case == "pages":
         # down shape [2048, 768], 32 tokens x top-8 over 16 experts, a row per slot
         args = (_stride_ids(32, 8, 16), 2048, 768, 16, 1, 94)
         sample = np.arange(0, 256, 5)
@@ -200,9 +210,9 @@ def test_moe_qmm_q6k(case, f32):
 
 
 def test_moe_qmm_q6k_f32_wide_dynamic_range():
-    """Activation blocks spanning many binades (1e-6 .. 1e4) and an all-zero
-    block: the per-block power-of-two scale and the two-half split keep f32
-    accuracy without f16 overflow."""
+    """Activation values spanning many binades (1e-6 .. 1e4) and an all-zero
+    block: the power-of-two scaling and the two-half split keep f32 accuracy
+    without f16 overflow."""
     E, n, k, ns = 3, 64, 512, 12
     bank = synth.moe_bank(synth.FMT_Q6K, 99, E, n, k)
     x = synth.normal(100, ns * k).reshape(ns, k)
