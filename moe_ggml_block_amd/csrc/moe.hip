@@ -552,6 +552,120 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     }
 }
 
+// Small batches (at most QMV_DIRECT_SLOTS slots): an item is one slot and a
+// block of rblk rows, with no grouping by expert. A workgroup reads its
+// slot's expert (or routes the slot's token itself, each wave on its own:
+// ids == nullptr) and issues its weight loads at once; the item of a slot's
+// first block publishes the routed id and weight. An expert chosen by c
+// slots is read c times (from the caches where the reads meet). At a few
+// slots that costs less than the grouping's serial steps: ids, present
+// experts, counts, item offsets and the slot list, each behind a barrier,
+// all before the first weight load (about half of a workgroup's time at
+// one token, 128 experts, top-8).
+template <class F, int G, int UPL, bool PAIR>
+__global__ __launch_bounds__(256) void k_moe_direct(MoeArgs a, int rblk) {
+    extern __shared__ float4 dyn4[];
+    float *xlds = reinterpret_cast<float *>(dyn4);
+    constexpr int NB = MOE_RING;
+    constexpr int RPP = 64 / G;
+    static_assert(!PAIR || RPP % 2 == 0, "pairs need an even number of rows per pass");
+    using Raw = typename F::Raw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int U = F::units_per_row(a.k);
+    const size_t row_bytes = (size_t)(a.k / F::BW) * F::BB;
+    const int nrows_bank = PAIR ? a.n / 2 : a.n;  // rows per expert in a bank
+    const int ny = PAIR ? a.n / 2 : a.n;          // output row length
+    const int gl = lane & (G - 1), grow = lane / G;
+    bool uv[UPL];
+    int uu[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+        uv[i] = gl + G * i < U;
+        uu[i] = uv[i] ? gl + G * i : U - 1;
+    }
+    const int nblk = (a.n + rblk - 1) / rblk;
+    for (int it = blockIdx.x; it < a.nslots * nblk; it += gridDim.x) {
+        const int slot = it / nblk, rb = it - slot * nblk;
+        const int r0 = rb * rblk, len = min(a.n, r0 + rblk) - r0;
+        int expert;
+        if (a.logits) {
+            const int t = slot / a.topk, j = slot - t * a.topk;
+            int e;
+            float w;
+            route_token_wave<ROUTE_FUSED_E / 64>(a.logits + (size_t)t * a.E, a.E, a.topk, lane, &e, &w);
+            expert = __builtin_amdgcn_readlane(e, j);
+            if (rb == 0 && wave == 0 && lane == j) {
+                a.ids_out[slot] = e;
+                a.wts_out[slot] = w;
+            }
+        } else {
+            expert = __builtin_amdgcn_readfirstlane(a.ids[slot]);
+        }
+        if (expert < 0 || expert >= a.E) {
+            // an out-of-range id: zero rows (the pair form leaves h unwritten,
+            // the down pass skips the slot)
+            if (!PAIR)
+                for (int r = tid; r < len; r += 256) a.y[(size_t)slot * ny + r0 + r] = 0.0f;
+            continue;
+        }
+        const uint8_t *wb = a.bank + (size_t)expert * nrows_bank * row_bytes;
+        const uint8_t *wb2 = PAIR ? a.bank2 + (size_t)expert * nrows_bank * row_bytes : wb;
+        // this wave takes block passes q*WAVES + wave (spare waves run one
+        // clamped pass and store nothing)
+        const int bpasses = (len + RPP - 1) / RPP;
+        const int pr = (bpasses - wave + WAVES - 1) / WAVES;
+        const int p1 = pr > 1 ? pr : 1;
+        auto load_pass = [&](Raw (&B)[UPL], int pass) {
+            const int v = r0 + min((pass * WAVES + wave) * RPP + grow, len - 1);
+            const uint8_t *row = PAIR ? ((v & 1) ? wb2 : wb) + (size_t)(v >> 1) * row_bytes
+                                      : wb + (size_t)v * row_bytes;
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) F::load(B[i], row, uu[i]);
+        };
+        // the activation row first (its wait must not drain the weight ring)
+        typename F::Stage S;
+        F::template fetch<stage_granules(G, UPL)>(S, moe_act<F>(a, slot / a.x_div), a.k);
+        Raw R[NB][UPL];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            load_pass(R[j], min(j, p1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();  // the previous item's LDS reads are done
+        F::template store<stage_granules(G, UPL)>(xlds, S, a.k);
+        __syncthreads();
+        typename F::X X[UPL];
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) F::load_lds(X[i], xlds, uu[i]);
+        float *yrow = a.y + (size_t)slot * ny;
+        int pass = 0;
+        do {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int ps = pass + j;
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < UPL; ++i) {
+                    const float d = F::dot(R[j][i], X[i], uu[i]);
+                    acc += uv[i] ? d : 0.0f;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_pass(R[j], min(ps + NB, p1 - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                acc = group_sum_last<G>(acc);
+                const int rr = (ps * WAVES + wave) * RPP + grow;
+                if (PAIR) {
+                    const float gate = __shfl(acc, lane - G);  // the pair's gate row
+                    if ((grow & 1) && gl == G - 1 && ps < pr && rr < len) yrow[(r0 + rr) >> 1] = silu(gate) * acc;
+                } else if (gl == G - 1 && ps < pr && rr < len) {
+                    yrow[r0 + rr] = acc;
+                }
+            }
+            pass += NB;
+        } while (pass < p1);
+    }
+}
+
 // ------------------------------------------- down pass + weighted combine ---
 // Workgroup (row block rb, token t):
 //   y[t, r] = sum_j wts[t, j] * W_down[ids[t, j], r, :] . h[topk*t + j, :]
@@ -592,15 +706,20 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     // the token's experts (out of range -> -1) and weights
     __shared__ int s_e[MAX_LAYER_TOPK];
     __shared__ float s_w[MAX_LAYER_TOPK];
-    // f32 h rows of the first chunk: requested before the ids (they do not
-    // depend on them), so the two reads overlap instead of following each
-    // other; stored to LDS once the chunk's weight loads are in flight
+    // the ids and weights are requested first, then the f32 h rows of the
+    // first chunk (they do not depend on the ids), so the two reads overlap
+    // and the ids' wait does not include the h rows' (loads complete in
+    // order); h is stored to LDS once the chunk's weight loads are in flight
+    // (every load unconditional, at clamped in-range indices: a branch
+    // around either would make the compiler wait for all of them at once)
+    const int e_in = a.ids[(size_t)t * a.topk + min(tid, a.topk - 1)];
+    const float w_in = a.wts[(size_t)t * a.topk + min(tid, a.topk - 1)];
     constexpr int HPRE = 6;  // float4 per thread held: the layer's chunk, 8 slots x 768 values
     const int k4 = a.k / 4;
     const int nch0 = min(a.chunk, a.topk);
     const bool hpre = !F::Q8 && nch0 * k4 <= HPRE * 256;
     f32x4 hv0[HPRE];
-    if (!F::Q8 && hpre) {
+    if constexpr (!F::Q8) {
 #pragma unroll
         for (int r = 0; r < HPRE; ++r) {
             const int i = tid + 256 * r;
@@ -611,13 +730,14 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     }
     for (int i = tid; i < WAVES * a.rblk; i += 256) acc_lds[i] = 0.0f;
     if (tid < a.topk) {
-        const int e = a.ids[(size_t)t * a.topk + tid];
-        s_e[tid] = (e >= 0 && e < a.E) ? e : -1;
-        s_w[tid] = a.wts[(size_t)t * a.topk + tid];
+        s_e[tid] = (e_in >= 0 && e_in < a.E) ? e_in : -1;
+        s_w[tid] = w_in;
     }
     __syncthreads();
 
-    for (int j0 = 0; j0 < a.topk; j0 += a.chunk) {
+    // one chunk of the token's slots; the first is peeled off the loop, so
+    // that its weight loads do not wait on registers the loop reloads
+    auto chunk_pass = [&](int j0) {
         const int nch = min(a.chunk, a.topk - j0);
         const int nitems = nch * bpasses;
         // this wave's items: a contiguous run q = qbeg, qbeg + 1, ... (slot
@@ -730,7 +850,9 @@ __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
             }
             qi += NB;
         } while (qi < p1);
-    }
+    };
+    chunk_pass(0);
+    for (int j0 = a.chunk; j0 < a.topk; j0 += a.chunk) chunk_pass(j0);
     __syncthreads();
     for (int r = tid; r < len; r += 256) {
         float v = 0.0f;
@@ -759,8 +881,34 @@ double expected_present(int64_t nslots, int64_t E) {
     return p < 1.0 ? 1.0 : p;
 }
 
+// Slots up to which the gathers take the direct form (k_moe_direct).
+#ifndef QMV_DIRECT_SLOTS
+#define QMV_DIRECT_SLOTS 32
+#endif
+
+template <class F, int G, int UPL, bool PAIR>
+int launch_direct_t(MoeArgs a, hipStream_t s) {
+    const size_t lds = (size_t)(a.k / 64) * F::ACT_STRIDE * 4;
+    static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
+    if (cache[0] != (int64_t)lds) {
+        cache[1] = resident_wgs(k_moe_direct<F, G, UPL, PAIR>, lds);
+        cache[0] = (int64_t)lds;
+    }
+    // blocks of whole passes (one per wave and more), about one item per
+    // resident workgroup
+    const int64_t step = WAVES * (64 / G);
+    int64_t rblk = div_up(div_up((int64_t)a.n * a.nslots, cache[1]), step) * step;
+    if (rblk > a.n) rblk = div_up(a.n, step) * step;
+    const int64_t items = a.nslots * div_up(a.n, rblk);
+    const int64_t grid = items < cache[1] ? items : cache[1];
+    hipLaunchKernelGGL((k_moe_direct<F, G, UPL, PAIR>), dim3((unsigned)grid), dim3(256), lds, s, a, (int)rblk);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}
+
 template <class F, int G, int UPL, bool PAIR>
 int launch_moe_t(MoeArgs a, hipStream_t s) {
+    if (a.nslots <= QMV_DIRECT_SLOTS) return launch_direct_t<F, G, UPL, PAIR>(a, s);
     const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E, moe_nsp<F, G, UPL>());
     static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
     if (cache[0] != (int64_t)lds) {
