@@ -562,17 +562,17 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
 // holds both dots of its outputs and writes h = silu(gate) * up.
 // MODE 2 (moe_qmm_q4k): the same expert-indexed rows with the tile derived
 // in the kernel from ids (qmm_group), dense column layout, y[slot] rows.
-template <int NG, int MG, int KS, int MODE = 0>
+template <int NG, int MG, int KS, int MODE = 0, int NU = 4>
 __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store) {
     constexpr bool PAIRT = MODE == 1, GROUPED = MODE == 2, MOEM = MODE != 0;
     static_assert(NG * MG * KS == 8 && (KS == 1 || KS == 2), "eight waves");
-    constexpr int BN = 32 * NG, BM = 64 * MG;
+    constexpr int BN = 32 * NG, BM = 16 * NU * MG;  // NU 16-row activation fragments per group
     constexpr int ST = 256 + 8;          // halves per LDS activation row (4-bank shift per row)
     constexpr int NBW = 8 / KS;          // blocks of a superblock per wave
     constexpr int NPW = NBW / 2;         // code-byte pairs per wave
     constexpr int AC = BM * 32 / 512;    // 8-byte activation chunks per thread and superblock
-    constexpr int XV = BM * 8 / 512;     // xs (and xsum) values per thread and superblock
-    static_assert(AC >= 1 && XV >= 1, "staging");
+    constexpr int XV = (BM * 8 + 511) / 512;  // xs (and xsum) values per thread and superblock
+    static_assert(AC >= 1 && AC * 512 == BM * 32 && (NU == 3 || NU == 4), "staging");
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * ST];
     constexpr int XST = 12;              // floats per xs row: 16-byte reads of 16 rows conflict-free
     __shared__ __attribute__((aligned(16))) float sxs[2][BM * XST];
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nsb = k / 256, kb = k / 32;
     const size_t row_bytes = (size_t)nsb * 144;
-    static_assert(!MOEM || (MG == 1 && KS == 2), "expert-indexed tiles: one 64-slot group, split blocks");
+    static_assert(!MOEM || (MG == 1 && KS == 2), "expert-indexed tiles: one group of slots, split blocks");
 
     // weight banks of the two fragments (gate and up for PAIRT) and the
     // tile's slots
@@ -671,7 +671,7 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     }
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-        const int c = tid + 512 * i;
+        const int c = min(tid + 512 * i, BM * 8 - 1);  // threads past the tile's xs read its last one
         xoff[i] = (uint32_t)((size_t)act_row(c >> 3) * kb + (c & 7));
     }
     auto load_act = [&](int s, ASet &A) {
@@ -696,17 +696,18 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int c = tid + 512 * i, row = c >> 3, j = c & 7;
+            if (BM * 8 % 512 != 0 && c >= BM * 8) continue;
             const bool ok = MOEM || m0 + row < m;
             sxs[buf][row * XST + j] = ok ? A.xs[i] : 0.f;
             sxsum[buf][row * XST + j] = ok ? A.xsum[i] : 0.f;
         }
     };
 
-    v4f acc[2][4], out[2][4];
+    v4f acc[2][NU], out[2][NU];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NU; ++u) {
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
             out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
@@ -760,10 +761,10 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         load_w(min(s + 2, nsb - 1), wset[P]);
         load_act(min(s + 2, nsb - 1), aset[P]);
         // xs of the lane's activation rows for the wave's blocks
-        float xv[4][NBW];
+        float xv[NU][NBW];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float *p = &sxs[P][(64 * mg + 16 * u + li) * XST + NBW * h];
+        for (int u = 0; u < NU; ++u) {
+            const float *p = &sxs[P][(16 * NU * mg + 16 * u + li) * XST + NBW * h];
 #pragma unroll
             for (int c = 0; c < NBW / 4; ++c) {
                 const v4f v = *reinterpret_cast<const v4f *>(p + 4 * c);
@@ -771,12 +772,12 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
                 for (int e = 0; e < 4; ++e) xv[u][4 * c + e] = v[e];
             }
         }
-        auto mma = [&](int bl, v4f (&R)[2][4]) {
+        auto mma = [&](int bl, v4f (&R)[2][NU]) {
             const int jb = NBW * h + bl;  // block within the superblock
-            h8 bf[4];
+            h8 bf[NU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                bf[u] = *reinterpret_cast<const h8 *>(&As[P][(64 * mg + 16 * u + li) * ST + 32 * jb + 8 * lq]);
+            for (int u = 0; u < NU; ++u)
+                bf[u] = *reinterpret_cast<const h8 *>(&As[P][(16 * NU * mg + 16 * u + li) * ST + 32 * jb + 8 * lq]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 // the block's sc as an f16 pair (exact: the half 1024 + sc,
@@ -792,37 +793,37 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
                 const uint2 v1 = q4x4_to_f16(cw.y & msk, mul, add);
                 const h8 af = __builtin_bit_cast(h8, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < NU; ++u)
                     R[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[u], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             }
         };
 #pragma unroll
         for (int bl = 0; bl < NBW; ++bl) {
-            v4f T[2][4];
+            v4f T[2][NU];
             mma(bl, T);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[t][u] = bl == 0 ? xv[u][bl] * T[t][u] : xv[u][bl] * T[t][u] + acc[t][u];
+                for (int u = 0; u < NU; ++u) acc[t][u] = bl == 0 ? xv[u][bl] * T[t][u] : xv[u][bl] * T[t][u] + acc[t][u];
         }
 
         // superblock done: out += d*acc, then the min term of the wave's blocks
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NU; ++u) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[t][u][r] = dout[t][r] * acc[t][u][r] + out[t][u][r];
             }
 #pragma unroll
         for (int i = 0; i < (KS == 1 ? 2 : 1); ++i) {
-            float xb[4];
+            float xb[NU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) xb[u] = sxsum[P][(64 * mg + 16 * u + li) * XST + NBW * h + 4 * i + lq];
+            for (int u = 0; u < NU; ++u) xb[u] = sxsum[P][(16 * NU * mg + 16 * u + li) * XST + NBW * h + 4 * i + lq];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < NU; ++u)
                     out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(amn[t][i], xb[u], out[t][u], 0, 0, 0);
         }
         // superblock s + 1's activations (loaded a superblock ago) into the
@@ -844,24 +845,24 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < NU; ++u)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) red[((pair * 32) + 16 * t + 4 * u + r) * 64 + lane] = out[t][u][r];
+                    for (int r = 0; r < 4; ++r) red[((pair * 2 + t) * 4 * NU + 4 * u + r) * 64 + lane] = out[t][u][r];
         }
         __syncthreads();
         if (h == 1) return;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) out[t][u][r] += red[((pair * 32) + 16 * t + 4 * u + r) * 64 + lane];
+                for (int r = 0; r < 4; ++r) out[t][u][r] += red[((pair * 2 + t) * 4 * NU + 4 * u + r) * 64 + lane];
     }
     float *__restrict__ Y = a.Y;
     if constexpr (PAIRT) {
         // out[0] = gate, out[1] = up of h columns hb + 16g + 4lq + r
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NU; ++u) {
             const int slot = s_slot[16 * u + li];
             if (slot < 0) continue;
 #pragma unroll
@@ -874,10 +875,10 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     }
     // lane holds weight rows 4*lq + r of each 16x16 result, activation row li
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
         int row;
         if constexpr (GROUPED) row = s_slot[16 * u + li];
-        else row = m0 + 64 * mg + 16 * u + li < m ? m0 + 64 * mg + 16 * u + li : -1;
+        else row = m0 + 16 * NU * mg + 16 * u + li < m ? m0 + 16 * NU * mg + 16 * u + li : -1;
         if (row < 0) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -1950,6 +1951,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q6k(const Qmm6Args a) {
 #define QMV_Q6R 1               // 0: the tile GEMM for every k
 #endif
 constexpr int Q6R_SLOTS = 32;   // activation rows per workgroup
+constexpr int Q6R_SEG_SHIFT = 25;  // a table segment: slot count (<= 32) << 25 | offset in tile_slots
 constexpr int Q6R_MAX_NSB = 4;  // k <= 1024: 32 staged rows of 4k + 16 bytes
 
 // Codes of four consecutive positions l..l+3 in the four 32-value runs of a
@@ -2129,8 +2131,9 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
                 __syncthreads();  // s_wsum is rewritten by the next chunk
             }
         } else {
-            const int off = seg_off[seg];
-            if (tid < Q6R_SLOTS) s_slot[tid] = a.tile_slots[off + tid];
+            // only the segment's own entries (c << 25 | offset, k_group_tiles)
+            const int so = seg_off[seg], off = so & ((1 << Q6R_SEG_SHIFT) - 1), scnt = so >> Q6R_SEG_SHIFT;
+            if (tid < Q6R_SLOTS) s_slot[tid] = tid < scnt ? a.tile_slots[off + tid] : -1;
             esel = a.tile_e[off / bmt];
             __syncthreads();
         }
@@ -2424,10 +2427,15 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
 // slots in slot order.
 namespace {
 
-// Slots per tile in the layer (both projections share the tile table): 32
-// below a mean of 32 slots per expert, else 64 (measured: the 64-slot
-// eight-wave tiles were faster from 32 slots per expert up, the 32-slot ones
-// at 8).
+// Slots per tile in the layer (both projections share the tile table): 48
+// from QMV_PF48_LO to QMV_PF48_HI slots per expert on average, else 32 below
+// a mean of 32 and 64 above (measured: the 64-slot eight-wave tiles were
+// faster than 32-slot ones from 32 slots per expert up, the 32-slot ones at
+// 8).
+#ifndef QMV_PF48_LO
+#define QMV_PF48_LO 24
+#define QMV_PF48_HI 40
+#endif
 
 // One workgroup builds the tile table: per-expert slot counts (LDS
 // atomics), an exclusive prefix of the per-expert tile counts, the tile ->
@@ -2435,9 +2443,12 @@ namespace {
 // valid slot is placed in its expert's tiles. The order of an expert's slots
 // within its tiles follows the atomics and may differ between runs; every
 // output row depends only on its own slot, so the results do not. It also
-// lists the 32-slot segments of the table (nseg, and for each the offset in
-// tile_slots of its first slot: an expert's slots are packed from the start
-// of its first tile, so its segment j starts 32 j past it).
+// lists the 32-slot segments of the table: nseg, and for each its slot count
+// c (1..32) and the offset o in tile_slots of its first slot, as
+// c << 25 | o (an expert's slots are packed from the start of its first
+// tile, so its segment j starts 32 j past it; with 48-slot tiles a
+// segment's 32 entries can pass the end of its expert's tiles, so only its
+// first c entries are its slots).
 template <int BM>
 __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict__ ids, int S, int E,
                                                       int *__restrict__ ntiles, int *__restrict__ tile_e,
@@ -2478,7 +2489,7 @@ __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict_
         s_off[tid] = off;
         for (int i = 0; i < nt; ++i) tile_e[off + i] = tid;
         for (int j = cnt; j < nt * BM; ++j) tile_slots[(size_t)off * BM + j] = -1;
-        for (int j = 0; j < ns; ++j) seg_off[offs + j] = off * BM + 32 * j;
+        for (int j = 0; j < ns; ++j) seg_off[offs + j] = (min(32, cnt - 32 * j) << Q6R_SEG_SHIFT) | (off * BM + 32 * j);
         s_cnt[tid] = 0;  // now the running position of the expert's slots
     }
     if (tid == 1023) {
@@ -2524,11 +2535,18 @@ struct PrefillWs {
     int64_t bytes;
 };
 
-int pf_bm(int64_t S, int64_t E) { return S < 32 * E ? 32 : 64; }
+int pf_bm(int64_t S, int64_t E, int64_t T, int64_t hidden, int64_t inter) {
+    // 48-slot tiles need the weight-side gate/up tile (its 32-bit lane
+    // offsets) and the resident-activation down GEMM
+    const bool w48 = inter * (hidden / 256) * 144 < ((int64_t)1 << 32) && T * hidden < ((int64_t)1 << 32) &&
+                     QMV_Q6R && inter <= 256 * Q6R_MAX_NSB;
+    if (w48 && S >= QMV_PF48_LO * E && S < QMV_PF48_HI * E) return 48;
+    return S < 32 * E ? 32 : 64;
+}
 int64_t pf_max_tiles(int64_t S, int64_t E, int bm) { return div_up(S, bm) + std::min(E, S); }
 
 PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int64_t inter, int64_t E) {
-    const int64_t S = T * topk, bm = pf_bm(S, E), mt = pf_max_tiles(S, E, (int)bm);
+    const int64_t S = T * topk, bm = pf_bm(S, E, T, hidden, inter), mt = pf_max_tiles(S, E, (int)bm);
     PrefillWs w{};
     int64_t o = 0;
     auto take = [&](int64_t nbytes) {
@@ -2574,7 +2592,7 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         return QMV_EALIGN;
     hipStream_t s = (hipStream_t)stream;
     const PrefillWs w = prefill_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter, E);
-    const int bm = pf_bm(S, E);
+    const int bm = pf_bm(S, E, T, hidden, inter);
     const int64_t mt = pf_max_tiles(S, E, bm);
     int rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
     if (rc != QMV_OK) return rc;
@@ -2602,6 +2620,16 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         else
             hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF32, ACT_F32, true, true>),
                                dim3((unsigned)div_up(hidden, 256), (unsigned)mt), dim3(512), 0, s, dn);
+    } else if (bm == 48) {
+        // every expert's slots fit one tile up to 48 slots per expert: a
+        // quarter less padding than 64-slot tiles where experts hold 20-47
+        hipLaunchKernelGGL((k_group_tiles<48>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
+                           w.tile_slots, w.nseg, w.seg_off);
+        QMV_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1, 3>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
+                           0, s, gu, 0);
+        QMV_LAUNCH_CHECK();
+        launch_q6r<false>(dn, w.nseg, w.seg_off, 48, s);
     } else {
         hipLaunchKernelGGL((k_group_tiles<64>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
                            w.tile_slots, w.nseg, w.seg_off);
