@@ -316,7 +316,8 @@ int qmm_q4k_split(const void *w, const int8_t *xq, const float *xs, const float 
  * xs, xsum: f32[ceil(nslots/x_div), k/32] (quantize_act_q8); ids:
  * int32[nslots]; y: f32[nslots, n], every row written (a slot whose expert
  * is outside [0, E) gets a zero row). Slots are grouped by expert on the
- * device (each expert's rows are read once per tile of its slots); no
+ * device (each expert's rows are read once per tile of its slots: 32 slots
+ * whose activation rows stay in LDS for k <= 2048, 64 above); no
  * workspace, no host synchronization.
  * k % 256 == 0; 1 <= E <= 1024; 1 <= nslots <= 2^20; bank and xq 16-byte
  * aligned, the rest 4-byte.

@@ -1561,6 +1561,16 @@ extern "C" int qmm_q4k_split(const void *w, const int8_t *xq, const float *xs, c
     return QMV_OK;
 }
 
+namespace {
+// The resident-activation Q4_K GEMM of the MoE prefill (k_qmm4r, below).
+#ifndef QMV_Q4R
+#define QMV_Q4R 1               // 0: the tile GEMMs
+#endif
+constexpr int Q4R_MAX_NSB = 8;  // k <= 2048
+template <bool PAIR, bool GROUPED>
+void launch_q4r(const QmmArgs &a, const int *nseg, const int *seg_off, int bmt, hipStream_t s);
+}  // namespace
+
 extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, const float *xsum, int64_t x_div,
                            const int32_t *ids, float *y, int64_t nslots, int64_t n, int64_t k, int64_t E,
                            qmv_stream_t stream) {
@@ -1585,7 +1595,10 @@ extern "C" int moe_qmm_q4k(const void *bank, const int8_t *xq, const float *xs, 
     // its 32-bit lane offsets hold: one expert's rows and the activation rows
     // below 2^32 bytes
     const int vec = aligned(y, 16) && n % 4 == 0;
-    if (n * (k / 256) * 144 < ((int64_t)1 << 32) && div_up(nslots, x_div) * k < ((int64_t)1 << 32))
+    if (QMV_Q4R && k <= 256 * Q4R_MAX_NSB)
+        // 32-slot segments grouped in the kernel, the activation resident in LDS
+        launch_q4r<false, true>(a, nullptr, nullptr, 32, s);
+    else if (n * (k / 256) * 144 < ((int64_t)1 << 32) && div_up(nslots, x_div) * k < ((int64_t)1 << 32))
         hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 2>), grid, dim3(512), 0, s, a, vec);
     else
         hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE64, true>), grid, dim3(QMM_MOE64_NT), 0, s, a);
@@ -2347,6 +2360,419 @@ void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt,
     }
 }
 
+// ============================================ Q4_K GEMM, resident activations
+// The expert-grouped Q4_K x q8 products of the MoE prefill (the layer's
+// paired gate/up projection, and moe_qmm_q4k) with the work split of
+// k_qmm6r: a workgroup of 16 waves stages the q8 rows of up to 32 slots of
+// one expert once (codes as exact f16, rows 2k + 16 bytes apart so that the
+// 16-byte fragment reads of sixteen consecutive rows hit distinct banks; xs
+// and xsum per block, rows 4 floats longer than a row's blocks), and each
+// wave then streams its own 16 weight rows superblock by superblock, with a
+// ring of raw-code register sets in flight and no barrier. The matrix roles
+// are those of k_qmm2_q4k: the weight rows are the A operand (per 32-value
+// block a lane decodes the 8 codes at its fragment position as f16 sc*q,
+// exact), the slots the B operand. One v_mfma_f32_16x16x32_f16 per 16-slot
+// fragment and block gives the block's integer dot T, the VALU adds xs*T
+// into a per-superblock accumulator, and d times that accumulator plus the
+// min term (v_mfma_f32_16x16x4_f32 over four blocks) go into the output tile
+// once per superblock.
+// PAIR (the layer's gate/up): rows 0-7 of a wave's fragment are gate rows
+// c..c+7 and rows 8-15 the up rows of the same h columns, so lane l < 32 and
+// lane l + 32 hold the gate and up dots of the same outputs. They exchange
+// them with v_permlane32_swap, and each lane stores h = silu(gate) * up for
+// one of the two slot fragments.
+#ifndef Q4R_RING
+#define Q4R_RING 1
+#endif
+constexpr int Q4R_SLOTS = 32;   // slots staged per workgroup (one table segment)
+
+// Raw codes of one step (a superblock of the wave's 16 rows): the lane's
+// row header (d, dmin, 12 scale bytes) and code bytes 8lq.. of each of the
+// four 32-byte pairs (values 8lq.. of the pair's two sub-blocks).
+struct Q4rRaw {
+    uint4 hdr;
+    uint2 qc[4];
+};
+
+// Work: units of one segment (up to 32 slots of one expert) by NW fragments
+// of CW output columns; each workgroup takes an equal run of consecutive
+// units and stages once per segment of its run (one or two). GROUPED: the
+// segments come from ids (per-expert counts, a ballot compaction; the
+// workgroups also zero the rows of slots whose expert is outside [0, E)),
+// otherwise from the layer's tile table (nseg, seg_off).
+template <int NSB, bool PAIR, bool GROUPED>
+__global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__restrict__ nseg_p,
+                                                const int *__restrict__ seg_off, int bmt) {
+    static_assert(NSB >= 1 && NSB <= Q4R_MAX_NSB, "k <= 2048");
+    constexpr int NW = 16, NT = 64 * NW;
+    constexpr int KV = 256 * NSB, KB = 8 * NSB;  // values and q8 blocks per row
+    constexpr int PITCH = 2 * KV + 16;            // bytes per staged row
+    constexpr int XP = KB + 4;                    // floats per staged xs / xsum row
+    constexpr int D = Q4R_RING;                   // steps in flight per wave
+    constexpr int CW = PAIR ? 8 : 16;             // output columns of a wave's fragment
+    constexpr int LPR = NT / Q4R_SLOTS;           // staging lanes per row
+    __shared__ __attribute__((aligned(16))) uint8_t act[Q4R_SLOTS * PITCH];
+    __shared__ __attribute__((aligned(16))) float sxs[Q4R_SLOTS * XP];
+    __shared__ __attribute__((aligned(16))) float sxm[Q4R_SLOTS * XP];
+    __shared__ int s_slot[Q4R_SLOTS];
+    __shared__ int s_misc[4], s_wsum[NW];
+    __shared__ int s_cnt[GROUPED ? QMM_MOE_MAX_E : 1], s_sb[GROUPED ? QMM_MOE_MAX_E : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lq = lane >> 4;
+    const int n = a.n, m = a.m, E = a.E;
+    const int ncg = (n + CW - 1) / CW;  // column groups (one wave fragment each) of a segment
+    const int32_t *__restrict__ ids = a.ids;
+    float *__restrict__ Y = a.Y;
+    int nseg;
+    if constexpr (GROUPED) {
+        for (int e = tid; e < E; e += NT) s_cnt[e] = 0;
+        __syncthreads();
+        for (int sl = tid; sl < m; sl += NT) {
+            const int e = ids[sl];
+            if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // exclusive prefix of the per-expert segment counts, lane l
+            // holding experts [l*EPL, l*EPL + EPL)
+            constexpr int EPL = QMM_MOE_MAX_E / 64;
+            int tl = 0;
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                if (e < E) tl += (s_cnt[e] + Q4R_SLOTS - 1) / Q4R_SLOTS;
+            }
+            int inc = tl;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(inc, d);
+                if (lane >= d) inc += v;
+            }
+            int run = inc - tl;
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                if (e < E) {
+                    s_sb[e] = run;
+                    run += (s_cnt[e] + Q4R_SLOTS - 1) / Q4R_SLOTS;
+                }
+            }
+            if (lane == 63) s_misc[0] = inc;
+        }
+        __syncthreads();
+        nseg = s_misc[0];
+        // rows of slots whose expert is outside [0, E) are zero: this
+        // workgroup's share of the slots, a wave per slot
+        const int z0 = (int)((int64_t)m * blockIdx.x / gridDim.x), z1 = (int)((int64_t)m * (blockIdx.x + 1) / gridDim.x);
+        for (int sl = z0 + wave; sl < z1; sl += NW) {
+            const int e = ids[sl];
+            if (e < 0 || e >= E)
+                for (int c = lane; c < n; c += 64) Y[(size_t)sl * n + c] = 0.0f;
+        }
+    } else {
+        nseg = *nseg_p;
+    }
+
+    const size_t row_bytes = (size_t)NSB * 144;
+    // A unit is ug column groups of a segment: NW (one group per wave) when
+    // there are six such units per workgroup or more (the waves of a
+    // workgroup then take equal shares of each segment), else single groups
+    // (the workgroups' shares stay within a group of each other).
+    const int ug = (int64_t)nseg * ((ncg + NW - 1) / NW) >= 6 * (int64_t)gridDim.x ? NW : 1;
+    const int nu = (ncg + ug - 1) / ug;  // units per segment
+    const int64_t total = (int64_t)nseg * nu;
+    const int64_t u1 = total * (blockIdx.x + 1) / gridDim.x;
+    int64_t u = total * blockIdx.x / gridDim.x;
+    while (u < u1) {
+        // column groups g0 .. g1 - 1 of segment seg; wave w takes g0 + w,
+        // g0 + w + NW, ...
+        const int seg = (int)(u / nu), c0 = (int)(u - (int64_t)seg * nu);
+        const int c1 = (int)min((int64_t)nu, c0 + (u1 - u));
+        u += c1 - c0;
+        const int g0 = c0 * ug, g1 = min(ncg, c1 * ug);
+        const int nrg = g1 - g0 > wave ? (g1 - g0 - wave + NW - 1) / NW : 0;  // this wave's groups
+        __syncthreads();  // the last segment's readers of act, sxs, sxm, s_slot are done
+        int esel;
+        if constexpr (GROUPED) {
+            for (int e = tid; e < E; e += NT) {
+                const int b = s_sb[e], ns = (s_cnt[e] + Q4R_SLOTS - 1) / Q4R_SLOTS;
+                if (seg >= b && seg < b + ns) {
+                    s_misc[1] = e;
+                    s_misc[2] = Q4R_SLOTS * (seg - b);
+                }
+            }
+            if (tid < Q4R_SLOTS) s_slot[tid] = -1;
+            __syncthreads();
+            esel = s_misc[1];
+            const int rank0 = s_misc[2];
+            // ascending compaction: per chunk, wave w takes ids [w*CWI, (w+1)*CWI)
+            // in order; a rank is the running count plus the earlier waves'
+            // counts plus the ballot prefix
+            constexpr int CWI = QMM_ID_CHUNK / NW;
+            int run = 0;
+            for (int q0 = 0; q0 < m && run < rank0 + Q4R_SLOTS; q0 += QMM_ID_CHUNK) {
+                int cw = 0;
+                for (int b = 0; b < CWI; b += 64) {
+                    const int sl = q0 + wave * CWI + b + lane;
+                    cw += __popcll(__ballot(sl < m && ids[sl] == esel));
+                }
+                if (lane == 0) s_wsum[wave] = cw;
+                __syncthreads();
+                int base = run;
+                for (int v = 0; v < NW; ++v) {
+                    if (v < wave) base += s_wsum[v];
+                    run += s_wsum[v];
+                }
+                for (int b = 0; b < CWI; b += 64) {
+                    const int sl = q0 + wave * CWI + b + lane;
+                    const bool hit = sl < m && ids[sl] == esel;
+                    const uint64_t bal = __ballot(hit);
+                    const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+                    if (hit && rank >= rank0 && rank < rank0 + Q4R_SLOTS) s_slot[rank - rank0] = sl;
+                    base += __popcll(bal);
+                }
+                __syncthreads();  // s_wsum is rewritten by the next chunk
+            }
+        } else {
+            // only the segment's own entries (count << 25 | offset, k_group_tiles)
+            const int so = seg_off[seg], off = so & ((1 << Q6R_SEG_SHIFT) - 1), scnt = so >> Q6R_SEG_SHIFT;
+            if (tid < Q4R_SLOTS) s_slot[tid] = tid < scnt ? a.tile_slots[off + tid] : -1;
+            esel = a.tile_e[off / bmt];
+            __syncthreads();
+        }
+        esel = __builtin_amdgcn_readfirstlane(esel);
+
+        // staging: lanes of row tid / LPR take its 8-code chunks l + LPR*i
+        // (16 f16 bytes each) and its blocks l, l + LPR, ... (rows of slots
+        // past the segment are zero)
+        {
+            const int srow = tid / LPR, l = tid % LPR;
+            const int sslot = s_slot[srow];
+            const size_t xrow = (size_t)(sslot >= 0 ? sslot / a.x_div : 0);
+            const int8_t *xr = a.xq + xrow * KV;
+            uint2 v[NSB];
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) v[i] = *reinterpret_cast<const uint2 *>(xr + 8 * (l + LPR * i));
+            for (int b = l; b < KB; b += LPR) {
+                const float s0 = a.xs[xrow * KB + b], s1 = a.xsum[xrow * KB + b];
+                sxs[srow * XP + b] = sslot >= 0 ? s0 : 0.f;
+                sxm[srow * XP + b] = sslot >= 0 ? s1 : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) {
+                const uint2 w = sslot >= 0 ? v[i] : make_uint2(0u, 0u);
+                const uint2 h0 = i8x4_to_f16(w.x), h1 = i8x4_to_f16(w.y);
+                *reinterpret_cast<uint4 *>(act + srow * PITCH + 16 * (l + LPR * i)) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            }
+        }
+        __syncthreads();
+
+        if (nrg == 0) continue;  // wave-uniform; no barrier follows before the next segment's
+        // the weight ring: step j of this wave is superblock j % NSB of its
+        // fragment in group g0 + wave + NW * (j / NSB) (rows past n read row
+        // n - 1, their outputs are not stored)
+        const uint8_t *__restrict__ wl =
+            (PAIR && li >= 8 ? a.w2 : a.w) + (size_t)esel * n * row_bytes;  // this lane's bank
+        const int rl = PAIR ? (li & 7) : li;                                 // its row in the fragment
+        auto load_step = [&](Q4rRaw &R, int j) {
+            const int i = j / NSB, s = j - i * NSB;
+            const int row = min(CW * (g0 + wave + NW * i) + rl, n - 1);
+            const uint8_t *p = wl + (size_t)row * row_bytes + 144 * s;
+            R.hdr = ld16(p);
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) R.qc[pp] = *reinterpret_cast<const uint2 *>(p + 16 + 32 * pp + 8 * lq);
+        };
+        const int J = nrg * NSB;  // steps of this wave
+        Q4rRaw R[D];
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            load_step(R[q], min(q, J - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // the wave's steps with NF 16-slot fragments (uniform per segment)
+        auto run = [&](auto NFc) {
+            constexpr int NF = decltype(NFc)::value;
+            v4f out[NF];
+            auto compute = [&](const Q4rRaw &Rs, int s) {
+                const float dl = h2f(Rs.hdr.x), dml = h2f(Rs.hdr.x >> 16);
+                uint32_t sc2[4], mn2[4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) q4k_scales(Rs.hdr.y, Rs.hdr.z, Rs.hdr.w, pp, &sc2[pp], &mn2[pp]);
+                // d of the lane's output rows 4lq + r; the min-term operand of
+                // row li, blocks 4i + lq (bit selects rather than an indexed
+                // array, which the compiler would place in scratch)
+                float dout[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dout[r] = __shfl(dl, 4 * lq + r);
+                float amn[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t lo = mn2[2 * i], hi = mn2[2 * i + 1];
+                    const uint32_t pr = lo ^ ((lo ^ hi) & (0u - (uint32_t)(lq >> 1)));
+                    amn[i] = -dml * (float)((pr >> (8 * (lq & 1))) & 0xFFu);
+                }
+                // xs of the lane's slots (column li of each fragment), four
+                // blocks at a time. Software-pipelined over the blocks: the
+                // fragments of block jb + 1 are read from LDS while jb is
+                // decoded, and the products of jb - 1 are added after the
+                // matrix instructions of jb are issued (Tp: the pending ones).
+                const float *xsp = &sxs[li * XP + 8 * s];
+                const uint8_t *abase = act + li * PITCH + 512 * s + 16 * lq;
+                v4f acc[NF], xv[NF], Tp[NF];
+                h8 bn[NF];
+#pragma unroll
+                for (int t = 0; t < NF; ++t) bn[t] = *reinterpret_cast<const h8 *>(abase + 16 * t * PITCH);
+#pragma unroll
+                for (int jb = 0; jb < 8; ++jb) {
+                    h8 bf[NF];
+#pragma unroll
+                    for (int t = 0; t < NF; ++t) bf[t] = bn[t];
+                    if (jb + 1 < 8) {
+#pragma unroll
+                        for (int t = 0; t < NF; ++t)
+                            bn[t] = *reinterpret_cast<const h8 *>(abase + 16 * t * PITCH + 64 * (jb + 1));
+                    }
+                    // the block's sc as an f16 pair (exact: the half 1024 + sc,
+                    // minus 1024); the high nibbles stay in place (16q), which
+                    // the scale pair absorbs: (1024 + 16q)*(sc/16) - 64*sc = q*sc
+                    const uint32_t sb = __builtin_amdgcn_perm(0x64646464u, sc2[jb / 2], (jb & 1) ? 0x04010401u : 0x04000400u);
+                    const h2 sch = as_h2(sb) + splat(-1024.0f);
+                    const h2 mul = (jb & 1) ? sch * splat(0.0625f) : sch;
+                    const h2 add = sch * splat((jb & 1) ? -64.0f : -1024.0f);
+                    const uint2 cw = Rs.qc[jb / 2];
+                    const uint32_t msk = (jb & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+                    const uint2 v0 = q4x4_to_f16(cw.x & msk, mul, add);
+                    const uint2 v1 = q4x4_to_f16(cw.y & msk, mul, add);
+                    const h8 af = __builtin_bit_cast(h8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    v4f Tn[NF];
+#pragma unroll
+                    for (int t = 0; t < NF; ++t)
+                        Tn[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if (jb > 0) {
+#pragma unroll
+                        for (int t = 0; t < NF; ++t)
+                            acc[t] = jb == 1 ? xv[t][0] * Tp[t] : xv[t][(jb - 1) & 3] * Tp[t] + acc[t];
+                    }
+                    if ((jb & 3) == 0) {
+#pragma unroll
+                        for (int t = 0; t < NF; ++t) xv[t] = *reinterpret_cast<const v4f *>(xsp + 16 * t * XP + jb);
+                    }
+                    // the additions stay here: left to itself the compiler
+                    // issues every product of the step first and spills them
+#pragma unroll
+                    for (int t = 0; t < NF; ++t) {
+                        if (jb > 0) asm volatile("" : "+v"(acc[t]));
+                        Tp[t] = Tn[t];
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NF; ++t) acc[t] = xv[t][3] * Tp[t] + acc[t];
+#pragma unroll
+                for (int t = 0; t < NF; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) out[t][r] = dout[r] * acc[t][r] + out[t][r];
+                // the min term: xsum of the lane's slot column, blocks 4i + lq
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int t = 0; t < NF; ++t)
+                        out[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            amn[i], sxm[(16 * t + li) * XP + 8 * s + 4 * i + lq], out[t], 0, 0, 0);
+            };
+            const bool vec = !PAIR && (((uintptr_t)Y & 15) == 0) && (n & 3) == 0;
+            for (int j0 = 0; j0 < J; j0 += D) {
+#pragma unroll
+                for (int q = 0; q < D; ++q) {
+                    const int j = j0 + q, i = j / NSB, s = j - i * NSB;
+                    if (s == 0) {
+#pragma unroll
+                        for (int t = 0; t < NF; ++t) out[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+                    }
+                    compute(R[q], s);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_step(R[q], min(j + D, J - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s == NSB - 1 && i < nrg) {
+                        const int cg = g0 + wave + NW * i;  // the wave's column group
+                        if constexpr (PAIR) {
+                            // lanes l and l + 32: gate and up of h columns
+                            // CW*cg + 4(lq & 1) + r, slot column li; lanes
+                            // below 32 store fragment 0, the others fragment 1
+                            float hv[NF][4];
+#pragma unroll
+                            for (int t = 0; t < NF; ++t)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float x = out[t][r];
+                                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                                    const float p = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
+                                    const float g = lane < 32 ? x : p, up = lane < 32 ? p : x;
+                                    hv[t][r] = silu(g) * up;
+                                }
+                            const int uo = lane >> 5;
+                            const int col = CW * cg + 4 * (lq & 1);
+                            if (uo < NF) {
+                                const int slot = s_slot[16 * uo + li];
+                                float4 o;
+                                o.x = uo ? hv[NF - 1][0] : hv[0][0];
+                                o.y = uo ? hv[NF - 1][1] : hv[0][1];
+                                o.z = uo ? hv[NF - 1][2] : hv[0][2];
+                                o.w = uo ? hv[NF - 1][3] : hv[0][3];
+                                if (slot >= 0 && col < n) *reinterpret_cast<float4 *>(Y + (size_t)slot * n + col) = o;
+                            }
+                        } else {
+                            const int col = CW * cg + 4 * lq;
+#pragma unroll
+                            for (int t = 0; t < NF; ++t) {
+                                const int slot = s_slot[16 * t + li];
+                                if (slot < 0) continue;
+                                float *dst = Y + (size_t)slot * n + col;
+                                if (vec && col + 3 < n) {
+                                    *reinterpret_cast<v4f *>(dst) = out[t];
+                                } else {
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r)
+                                        if (col + r < n) dst[r] = out[t][r];
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        if (s_slot[16] >= 0) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
+    }
+}
+
+// k_qmm4r, one workgroup per CU (k <= 2048): GROUPED derives its 32-slot
+// segments from ids, otherwise they come from the tile table (nseg,
+// seg_off, tiles of bmt slots).
+template <bool PAIR, bool GROUPED>
+void launch_q4r(const QmmArgs &a, const int *nseg, const int *seg_off, int bmt, hipStream_t s) {
+    static thread_local int c_dev = -1, c_cus = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != c_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        c_dev = dev;
+        c_cus = cus;
+    }
+    const dim3 grid((unsigned)c_cus), block(1024);
+    switch (a.k / 256) {
+        case 1: hipLaunchKernelGGL((k_qmm4r<1, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 2: hipLaunchKernelGGL((k_qmm4r<2, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 3: hipLaunchKernelGGL((k_qmm4r<3, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 4: hipLaunchKernelGGL((k_qmm4r<4, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 5: hipLaunchKernelGGL((k_qmm4r<5, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 6: hipLaunchKernelGGL((k_qmm4r<6, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 7: hipLaunchKernelGGL((k_qmm4r<7, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        default: hipLaunchKernelGGL((k_qmm4r<8, PAIR, GROUPED>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+    }
+}
+
 int check_q6k_shape(int64_t n, int64_t k) {
     if (n < 1 || k < 256 || k % 256) return QMV_EINVAL;
     if (n > (1 << 24) || k > (1 << 20)) return QMV_EUNSUPPORTED;
@@ -2594,6 +3020,8 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
     const PrefillWs w = prefill_ws(static_cast<uint8_t *>(ws), T, topk, hidden, inter, E);
     const int bm = pf_bm(S, E, T, hidden, inter);
     const int64_t mt = pf_max_tiles(S, E, bm);
+    // gate/up on the resident-activation GEMM over the table's 32-slot segments
+    const bool q4r = QMV_Q4R && hidden <= 256 * Q4R_MAX_NSB;
     int rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
     if (rc != QMV_OK) return rc;
     // Up to 512 slots the expert-grouped decode gathers stream the bank
@@ -2612,8 +3040,11 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         hipLaunchKernelGGL((k_group_tiles<32>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
                            w.tile_slots, w.nseg, w.seg_off);
         QMV_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt),
-                           dim3(256), 0, s, gu);
+        if (q4r)
+            launch_q4r<true, false>(gu, w.nseg, w.seg_off, 32, s);
+        else
+            hipLaunchKernelGGL((k_qmm_q4k<QMM_MOE32, true, true, true>), dim3((unsigned)div_up(inter, 64), (unsigned)mt),
+                               dim3(256), 0, s, gu);
         QMV_LAUNCH_CHECK();
         if (QMV_Q6R && inter <= 256 * Q6R_MAX_NSB)
             launch_q6r<false>(dn, w.nseg, w.seg_off, 32, s);
@@ -2626,8 +3057,11 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         hipLaunchKernelGGL((k_group_tiles<48>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
                            w.tile_slots, w.nseg, w.seg_off);
         QMV_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1, 3>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
-                           0, s, gu, 0);
+        if (q4r)
+            launch_q4r<true, false>(gu, w.nseg, w.seg_off, 48, s);
+        else
+            hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1, 3>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
+                               0, s, gu, 0);
         QMV_LAUNCH_CHECK();
         launch_q6r<false>(dn, w.nseg, w.seg_off, 48, s);
     } else {
@@ -2636,7 +3070,9 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         QMV_LAUNCH_CHECK();
         // weight-side tile while its 32-bit lane offsets hold (an expert's
         // rows and the activation rows below 2^32 bytes)
-        if (inter * (hidden / 256) * 144 < ((int64_t)1 << 32) && T * hidden < ((int64_t)1 << 32))
+        if (q4r)
+            launch_q4r<true, false>(gu, w.nseg, w.seg_off, 64, s);
+        else if (inter * (hidden / 256) * 144 < ((int64_t)1 << 32) && T * hidden < ((int64_t)1 << 32))
             hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
                                0, s, gu, 0);
         else

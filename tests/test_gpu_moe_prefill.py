@@ -84,6 +84,20 @@ def test_moe_qmm_edges(case):
     _check(*args, sample=sample)
 
 
+@pytest.mark.parametrize("k", [256, 768, 1792, 2048, 2304])
+def test_moe_qmm_resident_segments(k):
+    """k up to 2048 runs the resident-activation GEMM (one staged row width
+    per k), k = 2304 the tile GEMM. Per-expert slot counts straddle the
+    16-slot fragments and the 32-slot segments (15, 16, 17, 31, 32, 33, 48,
+    64, 65 slots, one expert absent), ids interleaved, x_div = 3, ragged n,
+    out-of-range ids."""
+    counts = [15, 16, 17, 31, 32, 33, 0, 48, 64, 65]
+    ids = np.concatenate([np.full(c, e, dtype=np.int32) for e, c in enumerate(counts)] + [np.array([-1, 10, 99], dtype=np.int32)])
+    ids = ids[np.random.default_rng(k).permutation(ids.size)]
+    announce(f"moe_qmm resident segments k={k} slots={ids.size}")
+    _check(ids, 100, k, len(counts), 3, 84 + k // 256)
+
+
 def test_moe_qmm_rejects_too_many_experts():
     import torch
     t = torch.zeros(1025 * 144, dtype=torch.uint8, device="cuda")
@@ -259,6 +273,17 @@ def test_moe_prefill_layer_both_sides_of_the_gather_threshold(T, topk, E):
     hidden, inter = 512, 256
     announce(f"moe prefill layer T={T} topk={topk} E={E} hidden={hidden} inter={inter}")
     _layer(T, topk, E, hidden, inter, 150 + T)
+
+
+@pytest.mark.parametrize("T,E,hidden,inter", [(80, 16, 1024, 512), (300, 8, 768, 256), (66, 64, 2048, 256)])
+def test_moe_prefill_layer_resident_gate_up_shapes(T, E, hidden, inter):
+    """The gate/up GEMM on resident activations at other staged widths
+    (hidden 768, 1024, 2048) and h widths (256, 512 columns: 32 or 64 wave
+    groups), with 40 to 300 slots per expert (one to ten segments; single
+    column groups or whole chunks as the units)."""
+    topk = 8
+    announce(f"moe prefill layer T={T} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 180 + T, sample=np.array([0, 1, T // 2, T - 1]))
 
 
 def test_moe_prefill_layer_full_shape_sampled_tokens():
