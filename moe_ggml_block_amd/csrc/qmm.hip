@@ -2619,6 +2619,18 @@ __global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__re
                 // matrix instructions of jb are issued (Tp: the pending ones).
                 const float *xsp = &sxs[li * XP + 8 * s];
                 const uint8_t *abase = act + li * PITCH + 512 * s + 16 * lq;
+                // per pair of blocks, the two sub-block scales as an f16 pair
+                // (exact: the halves 1024 + sc, minus 1024), and from them
+                // the multipliers and offsets of the code conversion. The
+                // high nibbles stay in place (16q), which the odd block's
+                // pair absorbs: (1024 + 16q)*(sc/16) - 64*sc = q*sc.
+                h2 mulp[4], addp[4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const h2 scp = as_h2(__builtin_amdgcn_perm(0x64646464u, sc2[pp], 0x04010400u)) + splat(-1024.0f);
+                    mulp[pp] = scp * h2{(_Float16)1.0f, (_Float16)0.0625f};
+                    addp[pp] = scp * h2{(_Float16)-1024.0f, (_Float16)-64.0f};
+                }
                 v4f acc[NF], xv[NF], Tp[NF];
                 h8 bn[NF];
 #pragma unroll
@@ -2633,13 +2645,9 @@ __global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__re
                         for (int t = 0; t < NF; ++t)
                             bn[t] = *reinterpret_cast<const h8 *>(abase + 16 * t * PITCH + 64 * (jb + 1));
                     }
-                    // the block's sc as an f16 pair (exact: the half 1024 + sc,
-                    // minus 1024); the high nibbles stay in place (16q), which
-                    // the scale pair absorbs: (1024 + 16q)*(sc/16) - 64*sc = q*sc
-                    const uint32_t sb = __builtin_amdgcn_perm(0x64646464u, sc2[jb / 2], (jb & 1) ? 0x04010401u : 0x04000400u);
-                    const h2 sch = as_h2(sb) + splat(-1024.0f);
-                    const h2 mul = (jb & 1) ? sch * splat(0.0625f) : sch;
-                    const h2 add = sch * splat((jb & 1) ? -64.0f : -1024.0f);
+                    // the block's multiplier and offset, one half of its pair's
+                    const h2 mul = (jb & 1) ? h2{mulp[jb / 2].y, mulp[jb / 2].y} : h2{mulp[jb / 2].x, mulp[jb / 2].x};
+                    const h2 add = (jb & 1) ? h2{addp[jb / 2].y, addp[jb / 2].y} : h2{addp[jb / 2].x, addp[jb / 2].x};
                     const uint2 cw = Rs.qc[jb / 2];
                     const uint32_t msk = (jb & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
                     const uint2 v0 = q4x4_to_f16(cw.x & msk, mul, add);
@@ -2708,7 +2716,9 @@ __global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__re
                                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
                                     const float p = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
                                     const float g = lane < 32 ? x : p, up = lane < 32 ? p : x;
-                                    hv[t][r] = silu(g) * up;
+                                    // silu with a hardware reciprocal (1 ulp) in place of the
+                                    // division: the h of a step is stored once per eight
+                                    hv[t][r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up;
                                 }
                             const int uo = lane >> 5;
                             const int col = CW * cg + 4 * (lq & 1);
