@@ -390,7 +390,7 @@ int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, const int32
  * grouped by expert on the device; nothing is synchronized with the host.
  * hidden, inter: multiples of 256 (<= 65536); 1 <= E <= 1024; T <= 65535;
  * T*topk <= 2^20. gate, up, x, y 16-byte aligned; down 2-byte; rest 4-byte.
- * Any topk >= 1 is accepted. Up to 512 slots (with topk <= 64, hidden,
+ * Any topk >= 1 is accepted. Up to 256 slots (with topk <= 64, hidden,
  * inter <= 4096 and down 16-byte aligned) the
  * same arithmetic runs on the expert-grouped decode gathers, which stream
  * the bank faster there; a token's output then agrees across batch sizes

@@ -2971,6 +2971,9 @@ struct PrefillWs {
     int64_t bytes;
 };
 
+#ifndef QMV_PF_GATHER_SLOTS
+#define QMV_PF_GATHER_SLOTS 256  // the layer runs on the decode gathers up to this many slots
+#endif
 int pf_bm(int64_t S, int64_t E, int64_t T, int64_t hidden, int64_t inter) {
     // 48-slot tiles need the weight-side gate/up tile (its 32-bit lane
     // offsets) and the resident-activation down GEMM
@@ -3034,12 +3037,12 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
     const bool q4r = QMV_Q4R && hidden <= 256 * Q4R_MAX_NSB;
     int rc = quantize_act_q8(x, w.xq, w.xs, w.xsum, T, hidden, stream);
     if (rc != QMV_OK) return rc;
-    // Up to 512 slots the expert-grouped decode gathers stream the bank
-    // faster than the GEMM tiles (128 experts of [768, 2048]: 145 against
-    // 288 us at 256 slots, 267 against 308 us at 512; at 1024 the GEMMs win,
-    // 313 against 513 us); same arithmetic, h in the same workspace.
+    // Up to 256 slots the expert-grouped decode gathers stream the bank
+    // faster than the GEMMs (128 experts of [768, 2048]: 135.6 against
+    // 158 us at 256 slots; at 288 the GEMMs win, 162 against 200 us, and at
+    // 512 by 170 against 251); same arithmetic, h in the same workspace.
     // (the decode down pass holds at most 64 slots of a token)
-    if (S <= 512 && topk <= 64 && hidden <= 4096 && inter <= 4096 && aligned(down, 16))
+    if (S <= QMV_PF_GATHER_SLOTS && topk <= 64 && hidden <= 4096 && inter <= 4096 && aligned(down, 16))
         return qmv_internal::moe_layer_q8x_f32h(gate, up, down, w.xq, w.xs, w.xsum, ids, wts, y, w.h, T, topk,
                                                 hidden, inter, E, s);
     QmmArgs gu{static_cast<const uint8_t *>(gate), w.xq, w.xs, w.xsum, w.h, (int)S, (int)inter, (int)hidden, ids,

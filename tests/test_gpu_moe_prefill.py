@@ -266,10 +266,10 @@ def test_moe_prefill_layer_small_full_output():
     _layer(T, topk, E, hidden, inter, 110)
 
 
-@pytest.mark.parametrize("T,topk,E", [(64, 8, 16), (65, 8, 16), (100, 8, 128)])
+@pytest.mark.parametrize("T,topk,E", [(32, 8, 16), (33, 8, 16), (64, 8, 16), (65, 8, 16), (100, 8, 128)])
 def test_moe_prefill_layer_both_sides_of_the_gather_threshold(T, topk, E):
-    """Up to 512 slots the layer runs on the decode gathers, above on the
-    GEMM tiles (32-slot tiles below 32 slots per expert, 64-slot above)."""
+    """Up to 256 slots the layer runs on the decode gathers, above on the
+    GEMMs (table tiles of 32, 48 or 64 slots by the mean slots per expert)."""
     hidden, inter = 512, 256
     announce(f"moe prefill layer T={T} topk={topk} E={E} hidden={hidden} inter={inter}")
     _layer(T, topk, E, hidden, inter, 150 + T)
@@ -324,8 +324,8 @@ def test_moe_prefill_layer_workspace_reuse_smaller_second_call():
 @pytest.mark.parametrize("T", [32, 64])
 def test_moe_prefill_layer_bench_shape_on_the_gathers(T):
     """The benched small-batch layer (top-8 over 128 experts, gate/up
-    [768, 2048], down [2048, 768]; 256 and 512 slots, which run on the
-    expert-grouped decode gathers): every output column of sampled tokens
+    [768, 2048], down [2048, 768]; 256 slots, on the expert-grouped decode
+    gathers, and 512, on the GEMMs): every output column of sampled tokens
     against the oracle."""
     topk, E, hidden, inter = 8, 128, 2048, 768
     announce(f"moe prefill layer (gathers) T={T} E={E} hidden={hidden} inter={inter}")
