@@ -2041,7 +2041,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
     const int n = a.n, m = a.m, E = a.E;
-    const int nrc = (n + 255) / 256;  // 256-row chunks
+    const int ngr = (n + 16 * FPW - 1) / (16 * FPW);  // row groups (one wave's fragments) of a segment
     const int32_t *__restrict__ ids = a.ids;
     float *__restrict__ Y = a.Y;
     int nseg;
@@ -2094,13 +2094,22 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
 
     const size_t row_bytes = (size_t)NSB * 210;
     const int oq = 64 * (lq >> 1) + 16 * (lq & 1), oh = 128 + 32 * (lq >> 1) + 16 * (lq & 1);
-    const int64_t total = (int64_t)nseg * nrc;
+    // A unit is ug row groups of a segment: NW (one group per wave, 256
+    // rows) when there are six such units per workgroup or more, else single
+    // groups (as in k_qmm4r).
+    const int ug = (int64_t)nseg * ((ngr + NW - 1) / NW) >= 6 * (int64_t)gridDim.x ? NW : 1;
+    const int nu = (ngr + ug - 1) / ug;  // units per segment
+    const int64_t total = (int64_t)nseg * nu;
     const int64_t u1 = total * (blockIdx.x + 1) / gridDim.x;
     int64_t u = total * blockIdx.x / gridDim.x;
     while (u < u1) {
-        const int seg = (int)(u / nrc), c0 = (int)(u - (int64_t)seg * nrc);
-        const int nrg = (int)min((int64_t)(nrc - c0), u1 - u);  // 256-row chunks of this segment
-        u += nrg;
+        // row groups g0 .. g1 - 1 of segment seg; wave w takes g0 + w,
+        // g0 + w + NW, ...
+        const int seg = (int)(u / nu), c0 = (int)(u - (int64_t)seg * nu);
+        const int c1 = (int)min((int64_t)nu, c0 + (u1 - u));
+        u += c1 - c0;
+        const int g0 = c0 * ug, g1 = min(ngr, c1 * ug);
+        const int nrg = g1 - g0 > wave ? (g1 - g0 - wave + NW - 1) / NW : 0;  // this wave's groups
         __syncthreads();  // the last segment's readers of act, s_slot, s_inv are done
         int esel;
         if constexpr (GROUPED) {
@@ -2186,15 +2195,15 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
         }
         __syncthreads();
 
+        if (nrg == 0) continue;  // wave-uniform; no barrier follows before the next segment's
         // the weight ring: step j of this wave is superblock j % NSB of its
-        // rows in chunk c0 + j / NSB
+        // rows in group g0 + wave + NW * (j / NSB)
         const uint8_t *__restrict__ wb = a.w + (size_t)esel * n * row_bytes;
-        const int r0 = 256 * c0;
         auto load_step = [&](Q6rRaw<FPW> &R, int j) {
             const int i = j / NSB, s = j - i * NSB;
 #pragma unroll
             for (int f = 0; f < FPW; ++f) {
-                const int row = min(r0 + 256 * i + 16 * FPW * wave + 16 * f + li, n - 1);
+                const int row = min(16 * FPW * (g0 + wave + NW * i) + 16 * f + li, n - 1);
                 const uint8_t *p = wb + (size_t)row * row_bytes + 210 * s;
                 R.ql0[f] = ld16(p + oq);
                 R.ql1[f] = ld16(p + oq + 32);
@@ -2319,7 +2328,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
                         // lane: slots 16t + 4lq + r of weight row `row`
 #pragma unroll
                         for (int f = 0; f < FPW; ++f) {
-                            const int row = r0 + 256 * i + 16 * FPW * wave + 16 * f + li;
+                            const int row = 16 * FPW * (g0 + wave + NW * i) + 16 * f + li;
                             if (row >= n) continue;
 #pragma unroll
                             for (int t = 0; t < NF; ++t)
