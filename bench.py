@@ -694,9 +694,10 @@ def profile_moe_run(T: int, bank_copies: int = 3, calls: int = 48):
 def profile_moe_prefill_run(bank_copies: int = 3, calls: int = 12):
     """Short eager run for rocprofv3 counters of the MoE prefill layer at 512
     tokens (128 experts, top-8, gate/up Q4_K [768, 2048], down Q6_K
-    [2048, 768]) and of the standalone f32-activation down GEMM
-    (moe_qmm_q6k_f32, 4096 slots): `calls` of each over rotating bank copies,
-    then the 64 MiB calibration copy (torch neg x8)."""
+    [2048, 768]) and of the standalone expert GEMMs at 4096 slots (the gate
+    projection moe_qmm_q4k on the q8 x, the f32-activation down
+    moe_qmm_q6k_f32): `calls` of each over rotating bank copies, then the
+    64 MiB calibration copy (torch neg x8)."""
     import torch
     import moe_ggml_block_amd as qmv
     import synth
@@ -716,17 +717,20 @@ def profile_moe_prefill_run(bank_copies: int = 3, calls: int = 12):
     ws = torch.empty(qmv.moe_ffn_prefill_workspace_bytes(T, topk, hidden, inter, E), dtype=torch.uint8, device="cuda")
     h = torch.from_numpy(synth.normal(synth.SEED_X, ns * inter)).cuda()
     yd = torch.empty((ns, hidden), device="cuda")
+    xq, xs, xsum = qmv.quantize_act_q8(x, T, hidden)
+    yg = torch.empty((ns, inter), device="cuda")
     for i in range(calls):
         b = i % bank_copies
         qmv.moe_ffn_prefill_q4k_q6k(G[b], U[b], D[b], x, ids, w, T, topk, hidden, inter, E, y=y, ws=ws)
+        qmv.moe_qmm_q4k(G[b], xq, xs, xsum, topk, ids, ns, inter, hidden, E, y=yg)
         qmv.moe_qmm_q6k_f32(D[b], h, 1, ids, ns, hidden, inter, E, y=yd)
     a = torch.ones(CALIB_BYTES // 4, device="cuda")
     c = torch.empty_like(a)
     for _ in range(8):
         torch.neg(a, out=c)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": f"moe prefill layer T={T} x{calls}, moe_qmm_q6k_f32 {ns} slots x{calls}, "
-                                     "neg 64MiB x8", "copy_bytes": CALIB_BYTES}))
+    print(json.dumps({"profile_run": f"moe prefill layer T={T} x{calls}, moe_qmm_q4k and moe_qmm_q6k_f32 {ns} "
+                                     f"slots x{calls}, neg 64MiB x8", "copy_bytes": CALIB_BYTES}))
 
 
 def profile_prefill_run(copies: int = 64):
