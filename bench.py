@@ -2,11 +2,13 @@
 
 Headline workload: Q4_K matvec, W[14336, 4096] (uniform[-1,1) quantized to
 Q4_K, 33,030,144 packed bytes), x[4096] ~ N(0,1). One step runs every row
-of the path that this workload has, on HBM-resident inputs:
-  qmv_q4k          f32 activation
-  quantize_act_q8  the activation to (xq, xs, xsum)
+of the path that this workload has, on HBM-resident inputs, in two launches:
+  qmv_q4k_qx       the f32-activation matvec, whose first workgroup also
+                   writes quantize_act_q8(x) = (xq, xs, xsum)
   qmv_q4k_q8       int8 dot4 against the same weights
-value = packed weight bytes read by the two matvecs / step time (GB/s).
+value = packed weight bytes read by the two matvecs / step time (GB/s). The
+same step as three launches (qmv_q4k, quantize_act_q8, qmv_q4k_q8) is timed
+and reported beside it.
 Weights rotate over 32 device copies (1.06 GB) so every launch reads them
 from HBM, not from the 256 MB last-level cache (warm numbers, one copy, are
 reported beside).
@@ -48,6 +50,8 @@ N2, K2 = 14336, 4096
 Q4K_BYTES = N2 * (K2 // 256) * 144           # 33,030,144
 # one qmv_q4k launch: every packed row (2,304 B) plus its f32 output, and x once
 Q4K_LAUNCH_BYTES = Q4K_BYTES + 4 * N2 + 4 * K2  # 33,103,872
+# one qmv_q4k_qx launch: the same plus the q8 row it writes (xq, xs, xsum)
+QX_LAUNCH_BYTES = Q4K_LAUNCH_BYTES + K2 + 8 * (K2 // 32)  # 33,108,992
 Q8_LAUNCH_BYTES = 4096 * 128 * 34 + 4 * 4096 + 4 * 4096      # Q8_0 4096x4096: 17,858,560
 Q6K_LAUNCH_BYTES = 128256 * 16 * 210 + 4 * 128256 + 4 * 4096  # Q6_K 128256x4096: 431,469,568
 CALIB_BYTES = 64 << 20                         # the counter-calibration copy
@@ -138,7 +142,7 @@ def time_graph(fn, calls: int, replays: int = 20) -> float:
 
 
 def traffic_from_profile(kernel_hash: str):
-    """HBM bytes per launch of qmv_q4k from the committed PMC summary, if it was
+    """HBM bytes per launch of qmv_q4k_qx from the committed PMC summary, if it was
     taken on the current kernel source (else None)."""
     p = os.path.join(ROOT, TRAFFIC_JSON)
     if not os.path.exists(p):
@@ -291,10 +295,15 @@ def headline(steps: int, warmup: int, copies: int):
     xsum = torch.empty(K2 // 32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # a step: the f32-activation matvec, the q8 activation quantizer and the
-    # int8-dot matvec; the same work with the quantizer inside the int8
-    # matvec's kernel (qmv_q4k_q8x, one launch) is timed below as well
+    # a step: the f32-activation matvec that also writes the q8 activation,
+    # then the int8-dot matvec; the same work as three launches (separate
+    # quantizer) and with the quantizer inside the int8 matvec's kernel
+    # (qmv_q4k_q8x) is timed below as well
     def step(i):
+        qmv.qmv_q4k_qx(W[i % copies], x, N2, K2, y=y, out=(xq, xs, xsum))
+        qmv.qmv_q4k_q8(W[(i + copies // 2) % copies], xq, xs, xsum, N2, K2, y=y8)
+
+    def step_three(i):
         qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
         qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum))
         qmv.qmv_q4k_q8(W[(i + copies // 2) % copies], xq, xs, xsum, N2, K2, y=y8)
@@ -328,12 +337,14 @@ def headline(steps: int, warmup: int, copies: int):
 
     # the dominant kernel alone: 4 passes over the copies per graph, on the
     # same stream, timed with events around the replays
-    q4k_ms = time_graph(lambda i: qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y), 4 * copies, 10)
-    k_f32 = q4k_ms
+    qx_ms = time_graph(lambda i: qmv.qmv_q4k_qx(W[i % copies], x, N2, K2, y=y, out=(xq, xs, xsum)),
+                       4 * copies, 10)
+    k_f32 = time_graph(lambda i: qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y), 4 * copies, 10)
     k_qa = time_graph(lambda i: qmv.quantize_act_q8(x, 1, K2, out=(xq, xs, xsum)), 128, 10)
     k_q8 = time_graph(lambda i: qmv.qmv_q4k_q8(W[i % copies], xq, xs, xsum, N2, K2, y=y8), 4 * copies, 10)
     k_q8x = time_graph(lambda i: qmv.qmv_q4k_q8x(W[i % copies], x, N2, K2, y=y8), 4 * copies, 10)
     ms_fused = time_graph(step_fused, copies, 10)
+    ms_three = time_graph(step_three, copies, 10)
     k_f32_warm = time_graph(lambda i: qmv.qmv_q4k(W[0], x, N2, K2, y=y), 128, 10)
     k_q8_warm = time_graph(lambda i: qmv.qmv_q4k_q8(W[0], xq, xs, xsum, N2, K2, y=y8), 128, 10)
     del big, W
@@ -341,8 +352,10 @@ def headline(steps: int, warmup: int, copies: int):
     return {
         "ms_per_step": ms,
         "warmup_steps_run": warmup_run,
-        "q4k_launch_ms": q4k_ms,
+        "qx_launch_ms": qx_ms,
         "kernels": {
+            "qmv_q4k_qx_cold_us": round(qx_ms * 1e3, 3),
+            "qmv_q4k_qx_cold_gbs": round(Q4K_BYTES / qx_ms / 1e6, 1),
             "qmv_q4k_cold_us": round(k_f32 * 1e3, 3),
             "qmv_q4k_cold_gbs": round(Q4K_BYTES / k_f32 / 1e6, 1),
             "qmv_q4k_warm_gbs": round(Q4K_BYTES / k_f32_warm / 1e6, 1),
@@ -352,7 +365,8 @@ def headline(steps: int, warmup: int, copies: int):
             "qmv_q4k_q8_warm_gbs": round(Q4K_BYTES / k_q8_warm / 1e6, 1),
             "qmv_q4k_q8x_cold_us": round(k_q8x * 1e3, 3),
             "qmv_q4k_q8x_cold_gbs": round(Q4K_BYTES / k_q8x / 1e6, 1),
-            "step_with_quantizer_in_kernel_us": round(ms_fused * 1e3, 3),
+            "step_three_launches_us": round(ms_three * 1e3, 3),
+            "step_with_quantizer_in_int8_kernel_us": round(ms_fused * 1e3, 3),
         },
     }
 
@@ -590,8 +604,8 @@ def moe_prefill_other(bank_copies: int = 3):
 
 
 def profile_run(copies: int, other_shapes: bool = False):
-    """Short eager run for rocprofv3: 64 launches each of qmv_q4k and
-    qmv_q4k_q8 over the rotating weight copies, 64 quantize_act_q8 calls, and
+    """Short eager run for rocprofv3: 64 launches each of qmv_q4k_qx, qmv_q4k
+    and qmv_q4k_q8 over the rotating weight copies, 64 quantize_act_q8 calls, and
     8 launches of torch's elementwise neg over 16 Mi floats (a copy kernel
     that reads and writes exactly 64 MiB: it calibrates the FETCH_SIZE and
     WRITE_SIZE counters)."""
@@ -603,6 +617,8 @@ def profile_run(copies: int, other_shapes: bool = False):
     x = torch.from_numpy(synth.normal(synth.SEED_X, K2)).cuda()
     y = torch.empty(N2, device="cuda")
     xq, xs, xsum = qmv.quantize_act_q8(x, 1, K2)
+    for i in range(64):
+        qmv.qmv_q4k_qx(W[i % copies], x, N2, K2, y=y, out=(xq, xs, xsum))
     for i in range(64):
         qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y)
     for i in range(64):
@@ -623,14 +639,14 @@ def profile_run(copies: int, other_shapes: bool = False):
                 fn(Wo[i % 3], x, n, k, y=yo)
             del bigo, Wo
     torch.cuda.synchronize()
-    print(json.dumps({"profile_run": "qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, neg 64MiB x8"
+    print(json.dumps({"profile_run": "qmv_q4k_qx x64, qmv_q4k x64, quantize_act_q8 x64, qmv_q4k_q8 x64, neg 64MiB x8"
                       + (", qmv_q8_0 4096x4096 x32, qmv_q6k 128256x4096 x8" if other_shapes else ""),
                       "q4k_bytes": Q4K_BYTES, "copy_bytes": CALIB_BYTES}))
 
 
 def profile_q4k_run(copies: int, warm: bool):
     """For rocprofv3 kernel-trace: exactly the headline kernel's roofline timing
-    (graphs of 4 x copies qmv_q4k launches over the rotating cold copies,
+    (graphs of 4 x copies qmv_q4k_qx launches over the rotating cold copies,
     WARM_MS of untimed replays, then 10 replays), or with warm=True the same
     on one resident copy, so that the profiler's average duration is of one
     kind of launch only."""
@@ -640,12 +656,13 @@ def profile_q4k_run(copies: int, warm: bool):
     big, W = rotated(synth.weights(synth.FMT_Q4K, synth.SEED_W, N2, K2), copies)
     x = torch.from_numpy(synth.normal(synth.SEED_X, K2)).cuda()
     y = torch.empty(N2, device="cuda")
+    q8 = qmv.quantize_act_q8(x, 1, K2)
     if warm:
-        ms = time_graph(lambda i: qmv.qmv_q4k(W[0], x, N2, K2, y=y), 128, 10)
+        ms = time_graph(lambda i: qmv.qmv_q4k_qx(W[0], x, N2, K2, y=y, out=q8), 128, 10)
     else:
-        ms = time_graph(lambda i: qmv.qmv_q4k(W[i % copies], x, N2, K2, y=y), 4 * copies, 10)
+        ms = time_graph(lambda i: qmv.qmv_q4k_qx(W[i % copies], x, N2, K2, y=y, out=q8), 4 * copies, 10)
     del big, W
-    print(json.dumps({"profile_run": f"qmv_q4k {N2}x{K2} {'warm (one copy)' if warm else f'cold ({copies} copies)'}",
+    print(json.dumps({"profile_run": f"qmv_q4k_qx {N2}x{K2} {'warm (one copy)' if warm else f'cold ({copies} copies)'}",
                       "event_us_per_launch": round(ms * 1e3, 3)}))
 
 
@@ -777,7 +794,7 @@ def counter_rows(csv_path: str, counter: str):
 
 
 def write_traffic(fetch_csv: str, write_csv: str) -> dict:
-    """HBM-side bytes per qmv_q4k launch from two rocprofv3 --pmc runs of
+    """HBM-side bytes per qmv_q4k_qx launch from two rocprofv3 --pmc runs of
     `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
     scaled by what the counter reads for the 64 MiB neg copy. Writes the
     summary next to the other profiles and returns it."""
@@ -790,18 +807,18 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
         return statistics.median(vals), len(vals)
 
     fetch, write = counter_rows(fetch_csv, "FETCH_SIZE"), counter_rows(write_csv, "WRITE_SIZE")
-    f_q, nf = pick(fetch, "k_dense<Q4KUnit, 64, 1>")
-    w_q, nw = pick(write, "k_dense<Q4KUnit, 64, 1>")
+    f_q, nf = pick(fetch, "k_dense<Q4KQOutUnit, 64, 1>")
+    w_q, nw = pick(write, "k_dense<Q4KQOutUnit, 64, 1>")
     f_c, _ = pick(fetch, "neg_kernel")
     w_c, _ = pick(write, "neg_kernel")
     fs, ws = CALIB_BYTES / (f_c * 1024), CALIB_BYTES / (w_c * 1024)
     hbm = f_q * 1024 * fs + w_q * 1024 * ws
-    d = {"kernel": "qmv_q4k (k_dense<Q4KUnit, 64, 1>)", "workload": "Q4_K 14336x4096, 32 rotating weight copies",
+    d = {"kernel": "qmv_q4k_qx (k_dense<Q4KQOutUnit, 64, 1>)", "workload": "Q4_K 14336x4096, 32 rotating weight copies",
          "kernel_source_hash": source_hash(KERNEL_SOURCES),
          "fetch_kib_median": f_q, "write_kib_median": w_q, "dispatches": [nf, nw],
          "calib_fetch_kib": f_c, "calib_write_kib": w_c, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
-         "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": Q4K_LAUNCH_BYTES,
-         "ratio_to_algorithmic": round(hbm / Q4K_LAUNCH_BYTES, 4)}
+         "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": QX_LAUNCH_BYTES,
+         "ratio_to_algorithmic": round(hbm / QX_LAUNCH_BYTES, 4)}
     with open(os.path.join(ROOT, TRAFFIC_JSON), "w") as f:
         json.dump(d, f, indent=1)
         f.write("\n")
@@ -862,8 +879,8 @@ def main():
     h = headline(a.steps, a.warmup, a.copies)
     log(f"headline done: {h['ms_per_step'] * 1e3:.2f} us/step")
     value = 2 * Q4K_BYTES / (h["ms_per_step"] * 1e-3) / 1e9
-    q4k_us = h["q4k_launch_ms"] * 1e3
-    achieved = Q4K_LAUNCH_BYTES / (h["q4k_launch_ms"] * 1e-3) / 1e9
+    qx_us = h["qx_launch_ms"] * 1e3
+    achieved = QX_LAUNCH_BYTES / (h["qx_launch_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile(khash)
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -871,13 +888,13 @@ def main():
         "ms_per_step": round(h["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Q4_K matvec 14336x4096, batch 1: f32-activation matvec + q8 activation "
-                               "quantize + int8-dot4 matvec per step",
+        "config": {"workload": "Q4_K matvec 14336x4096, batch 1: f32-activation matvec (writing the q8 "
+                               "activation) + int8-dot4 matvec per step",
                    "n": N2, "k": K2, "weight_copies": a.copies, "cache": "cold (rotating copies)"},
         "hbm_pct": round(value / HBM_PEAK_GBS * 100, 2),
-        "roofline": {"kernel": "qmv_q4k", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "qmv_q4k_qx", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": Q4K_LAUNCH_BYTES, "avg_launch_us": round(q4k_us, 3),
+                     "algorithmic_bytes_per_launch": QX_LAUNCH_BYTES, "avg_launch_us": round(qx_us, 3),
                      "kernel_source_hash": khash},
         "kernels": h["kernels"],
     }
@@ -888,7 +905,9 @@ def main():
         q4f = fl["stream_read_qmv_q4k_14336x4096"]["gbs"]
         res["roofline"]["frac_of_measured_read"] = round(achieved / q4f, 4)
         res["roofline"]["frac_of_copy_1GiB"] = round(achieved / fl["copy_1GiB_gbs"], 4)
-        res["kernels"]["qmv_q4k_cold_pct_of_measured_read"] = round(achieved / q4f * 100, 1)
+        res["kernels"]["qmv_q4k_qx_cold_pct_of_measured_read"] = round(achieved / q4f * 100, 1)
+        res["kernels"]["qmv_q4k_cold_pct_of_measured_read"] = round(
+            Q4K_LAUNCH_BYTES / (h["kernels"]["qmv_q4k_cold_us"] * 1e-6) / 1e9 / q4f * 100, 1)
         q8a = Q4K_LAUNCH_BYTES - 4 * K2 + K2 + 8 * (K2 // 32)  # its launch: q8 x instead of f32 x
         res["kernels"]["qmv_q4k_q8_cold_pct_of_measured_read"] = round(
             q8a / (h["kernels"]["qmv_q4k_q8_cold_us"] * 1e-6) / 1e9 / q4f * 100, 1)

@@ -94,6 +94,20 @@ int quantize_act_q8(const float *x, int8_t *xq, float *xs, float *xsum, int64_t 
                     qmv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * qmv_q4k and quantize_act_q8 of the same activation in one call: y is
+ * bit-identical to qmv_q4k(w, x, y, n, k) and (xq, xs, xsum) to
+ * quantize_act_q8(x, xq, xs, xsum, 1, k) (both defined above; the q8 row is
+ * what the int8-dot decode path of `matvec_q4k_gpu_off` consumes next, so a
+ * decode step that runs both formats needs no quantizer launch). For
+ * k <= 8192 the first workgroup of the matvec writes the q8 row from the
+ * activation values it loads anyway; beyond that the two run as separate
+ * launches on the stream. Buffers as in the two calls; xq, xs, xsum must not
+ * overlap x, w or y. k % 256 == 0; n >= 1.
+ * ---------------------------------------------------------------------- */
+int qmv_q4k_qx(const void *w, const float *x, float *y, int8_t *xq, float *xs, float *xsum, int64_t n,
+               int64_t k, qmv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Q4_K matvec against a q8 activation (the int8-dot decode path of
  * `matvec_q4k_gpu_off` / `matvec_q4k_dp4a_blk`):
  *   y[r] = sum_b ( d*sc_j*xs[b]*S[r,b] - dmin*m_j*xsum[b] ),

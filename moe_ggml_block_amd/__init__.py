@@ -34,6 +34,7 @@ _SIGS = {
     "quantize_act_q8": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q4k_q8": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "qmv_q4k_q8x": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "qmv_q4k_qx": [_vp] * 6 + [_i64, _i64, _vp],
     "qmv_debug_blocksums_q4k_q8": [_vp, _vp, _vp, _i64, _i64, _vp],
     "moe_route": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "moe_gate_route": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
@@ -171,6 +172,25 @@ def qmv_q4k_q8(w, xq, xs, xsum, n, k, y=None, stream=None):
 def qmv_q4k_q8x(w, x, n, k, y=None, stream=None):
     """int8-dot Q4_K matvec from an f32 activation, quantized inside the kernel."""
     return _dense("qmv_q4k_q8x", "q4k", w, x, n, k, y, stream)
+
+
+def qmv_q4k_qx(w, x, n, k, y=None, out=None, stream=None):
+    """f32 Q4_K matvec that also returns quantize_act_q8(x) for one row: (y, (xq, xs, xsum))."""
+    _need(w, n * row_bytes("q4k", k), "w")
+    _need(x, 4 * k, "x")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _need(y, 4 * n, "y")
+    if out is None:
+        out = (torch.empty((1, k), dtype=torch.int8, device=x.device),
+               torch.empty((1, k // 32), dtype=torch.float32, device=x.device),
+               torch.empty((1, k // 32), dtype=torch.float32, device=x.device))
+    xq, xs, xsum = out
+    _need(xq, k, "xq")
+    _need(xs, 4 * (k // 32), "xs")
+    _need(xsum, 4 * (k // 32), "xsum")
+    _check(_lib.qmv_q4k_qx(_p(w), _p(x), _p(y), _p(xq), _p(xs), _p(xsum), n, k, _stream(stream)), "qmv_q4k_qx")
+    return y, (xq, xs, xsum)
 
 
 def qmv_debug_blocksums_q4k_q8(w, xq, n, k, stream=None):

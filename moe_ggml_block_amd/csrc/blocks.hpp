@@ -874,3 +874,41 @@ struct Q4KQ8XUnit {
     static __device__ __forceinline__ void load_lds(UnitQ8 &X, const float *xl, int u) { Q4KQ8Unit::load_lds(X, xl, u); }
     static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8 &X, int u) { return Q4KQ8Unit::dot(R, X, u); }
 };
+
+// ------------------------------- Q4_K matvec with the q8 activation beside ---
+// The f32 Q4_K matvec (Q4KUnit, same arithmetic and output bits) whose first
+// workgroup also writes quantize_act_q8(x) (one row: codes xq, scale xs and
+// dequantized sum xsum per 32-value block, the same IEEE steps and bits) from
+// the activation registers it stages anyway, so that an int8-dot matvec of
+// the same x needs no quantizer launch of its own.
+struct ActF32Q {
+    const float *x;
+    int8_t *xq;
+    float *xs, *xsum;
+};
+struct Q4KQOutUnit : Q4KUnit {
+    using Act = ActF32Q;
+    template <int NS>
+    static __device__ __forceinline__ void fetch(Stage &S, ActF32Q a, int k) { fetch_x<NS>(S, a.x, k); }
+    // every lane quantizes its staged float4s (8 lanes per 32-value block,
+    // lanes past the end in whole groups of 8 with clamped values) and
+    // writes what lies inside x
+    template <int NS>
+    static __device__ __forceinline__ void side(const Stage &S, ActF32Q a, int k) {
+        const int n4 = k / 4;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int i = (int)threadIdx.x + 256 * m;
+            float sc, xsum;
+            const f32x4 v = S[m];
+            const uint32_t packed = quantize_q8_lanes(make_float4(v.x, v.y, v.z, v.w), &sc, &xsum);
+            if (i < n4) {
+                reinterpret_cast<uint32_t *>(a.xq)[i] = packed;
+                if ((i & 7) == 0) {
+                    a.xs[i >> 3] = sc;
+                    a.xsum[i >> 3] = xsum;
+                }
+            }
+        }
+    }
+};

@@ -39,6 +39,13 @@ namespace qmv_dense {
 
 constexpr int WAVES_PER_BLOCK = 4;
 
+// Units whose first workgroup also writes a side output from the staged
+// activation registers (F::side).
+template <class F, class = void>
+struct has_side : std::false_type {};
+template <class F>
+struct has_side<F, std::void_t<decltype(&F::template side<1>)>> : std::true_type {};
+
 template <class F, int G, int UPL>
 __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
                                                typename F::Act act,
@@ -93,6 +100,9 @@ __global__ __launch_bounds__(256) void k_dense(const uint8_t *__restrict__ w,
     // activations: coalesced loads into the padded LDS layout, then each
     // lane reads its units' values (conflict-free) into registers
     typename F::X X[UPL];
+    if constexpr (has_side<F>::value) {
+        if (blockIdx.x == 0) F::template side<stage_granules(G, UPL)>(S, act, k);  // uniform
+    }
     if constexpr (!F::Q8 && std::is_same<typename F::X, UnitX>::value) {
         F::template store_s<stage_granules(G, UPL)>(xlds, S, k);
         __syncthreads();

@@ -172,3 +172,23 @@ extern "C" int qmv_q4_0(const void *w, const float *x, float *y, int64_t n, int6
 extern "C" int qmv_q5k(const void *w, const float *x, float *y, int64_t n, int64_t k, qmv_stream_t s) {
     return dense_entry<Q5KUnit>(w, x, y, n, k, s);
 }
+
+// Q4_K matvec of an f32 activation that also writes that activation's q8
+// form (one row of quantize_act_q8) from the first workgroup's staged
+// registers; past the tiled range the two run as separate launches.
+extern "C" int qmv_q4k_qx(const void *w, const float *x, float *y, int8_t *xq, float *xs, float *xsum,
+                          int64_t n, int64_t k, qmv_stream_t stream) {
+    if (!w || !x || !y || !xq || !xs || !xsum || n < 1 || k < 256 || k % 256) return QMV_EINVAL;
+    if (n > (int64_t)1 << 30 || k > (int64_t)1 << 24) return QMV_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(xq, 4) || !aligned(xs, 4) ||
+        !aligned(xsum, 4))
+        return QMV_EALIGN;
+    const hipStream_t s = (hipStream_t)stream;
+    if (k > 8192) {
+        const int rc = launch_dense<Q4KUnit>(static_cast<const uint8_t *>(w), x, y, n, k, s);
+        return rc != QMV_OK ? rc : quantize_act_q8(x, xq, xs, xsum, 1, k, stream);
+    }
+    qmv_dense::launch_tiled<Q4KQOutUnit>(static_cast<const uint8_t *>(w), ActF32Q{x, xq, xs, xsum}, y, n, k, s);
+    QMV_LAUNCH_CHECK();
+    return QMV_OK;
+}

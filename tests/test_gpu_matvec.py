@@ -191,3 +191,42 @@ def test_q4k_q8x_fused_quantize_matches_two_step(n, k):
     oq, os_, _ = oracle.quantize_act_q8(x, 1, k)
     ref = oracle.matvec_q8act("q4k", w, oq[0], os_[0], n, k)
     assert scalerel(ref, fused) <= TOL
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (37, 256), (70, 768), (33, 2048), (70, 4096), (9, 8192),
+                                 (14336, 4096), (3, 12288)])
+def test_q4k_qx_matvec_and_q8_row_bit_exact(n, k):
+    """qmv_q4k_qx: y bit-identical to qmv_q4k, the q8 row bit-identical to the
+    oracle's quantize_act_q8 (k = 12288 takes the two-launch form)."""
+    announce(f"q4k qx n={n} k={k}")
+    w = synth.weights(synth.FMT_Q4K, 13, n, k)
+    x = synth.normal(14, k)
+    x[::41] *= 300.0
+    x[:32] = 0.0  # a zero block: scale 1, codes 0
+    if k >= 64:
+        x[32:64] = np.arange(32, dtype=np.float32) - 15.5  # half-way codes
+    W, X = dev(w), dev(x)
+    y, (xq, xs, xsum) = qmv.qmv_q4k_qx(W, X, n, k)
+    y_plain = host(qmv.qmv_q4k(W, X, n, k))
+    assert np.array_equal(host(y).view(np.uint32), y_plain.view(np.uint32))
+    rq, rs, rsum = oracle.quantize_act_q8(x, 1, k)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(xsum).view(np.uint32), rsum.view(np.uint32))
+    ref = oracle.matvec("q4k", w, x, n, k)
+    assert scalerel(ref, host(y)) <= TOL
+
+
+def test_q4k_qx_feeds_q8_matvec():
+    """The decode step form: the q8 row written by qmv_q4k_qx drives
+    qmv_q4k_q8 to the same bits as the separate quantizer launch."""
+    n, k = 14336, 4096
+    announce("q4k qx -> q4k_q8")
+    w = synth.weights(synth.FMT_Q4K, synth.SEED_W, n, k)
+    x = synth.normal(synth.SEED_X, k)
+    W, X = dev(w), dev(x)
+    _, (xq, xs, xsum) = qmv.qmv_q4k_qx(W, X, n, k)
+    y = host(qmv.qmv_q4k_q8(W, xq, xs, xsum, n, k))
+    q2, s2, m2 = qmv.quantize_act_q8(X, 1, k)
+    y2 = host(qmv.qmv_q4k_q8(W, q2, s2, m2, n, k))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
