@@ -57,7 +57,7 @@ Q6K_LAUNCH_BYTES = 128256 * 16 * 210 + 4 * 128256 + 4 * 4096  # Q6_K 128256x4096
 CALIB_BYTES = 64 << 20                         # the counter-calibration copy
 WARM_MS = 30.0            # untimed replays before each kernel timing
 HEADLINE_WARM_MS = 100.0  # untimed steps before the headline's timed region (beyond --warmup)
-TRAFFIC_JSON = os.path.join("profiles", "qmv_q4k_14336x4096_traffic.json")
+TRAFFIC_JSON = os.path.join("profiles", "qmv_q4k_qx_14336x4096_traffic.json")
 METRIC = "packed-weight GB/s (+% HBM peak) for Q4_K matvec 14336x4096; MoE tokens/s"
 KERNEL_SOURCES = ["moe_ggml_block_amd/csrc/common.hpp",
                   "moe_ggml_block_amd/csrc/blocks.hpp", "moe_ggml_block_amd/csrc/dense.hpp",
