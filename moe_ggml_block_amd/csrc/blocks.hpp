@@ -690,14 +690,15 @@ struct Q4KQ8Unit {
 // A Q6_K unit (64 weights of one superblock, Q6KUnit) against a q8
 // activation. Its values are four runs of 16: run g covers values
 // 128h + 32g + 16lh + [0, 16) of the superblock, half of q8 block
-// 8s + 4h + g. q - 32 (in [-32, 31]) becomes a signed byte: r = q ^ 0x20 is
-// q - 32 modulo 64, and setting the top two bits where bit 5 of r is set
-// sign-extends it. Each run's integer dot S_g = sum (q - 32) * xq is one
-// v_dot4 chain (exact), and the unit adds d * sc_g * xs_g * S_g for its four
-// runs (sc_g: the run's int8 sub-scale).
+// 8s + 4h + g. Each run's integer dot S_g = sum (q - 32) * xq is one v_dot4
+// chain (exact): the 6-bit codes q (0..63) are non-negative signed bytes as
+// they stand, and the chain starts from -32 * sum(xq) of the run, taken once
+// when the activation registers are filled. The unit adds
+// d * sc_g * xs_g * S_g for its four runs (sc_g: the run's int8 sub-scale).
 struct UnitQ8x4 {
     int32_t q[16];  // dwords 4g..4g+3: xq of run g
     float xs[4];    // xs of run g's q8 block
+    int32_t m32[4]; // -32 * (sum of the 16 xq of run g)
 };
 
 struct Q6KQ8Unit {
@@ -755,27 +756,29 @@ struct Q6KQ8Unit {
         }
         const float4 f = reinterpret_cast<const float4 *>(xl + ACT_STRIDE * u)[4];
         X.xs[0] = f.x; X.xs[1] = f.y; X.xs[2] = f.z; X.xs[3] = f.w;
-    }
-    // four 6-bit codes (one per byte) -> four signed bytes q - 32
-    static __device__ __forceinline__ int centred(uint32_t q) {
-        const uint32_t r = q ^ 0x20202020u;
-        return (int)(r | (((r >> 5) & 0x01010101u) * 0xC0u));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            int sum = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sum = __builtin_amdgcn_sdot4(X.q[4 * g + t], 0x01010101, sum, false);
+            X.m32[g] = -32 * sum;
+        }
     }
     static __device__ __forceinline__ float dot(const Raw &R, const UnitQ8x4 &X, int u) {
         const uint32_t A[4] = {R.a.x, R.a.y, R.a.z, R.a.w};
         const uint32_t B[4] = {R.b.x, R.b.y, R.b.z, R.b.w};
         const uint32_t H[4] = {R.h.x, R.h.y, R.h.z, R.h.w};
-        int S[4] = {0, 0, 0, 0};
+        int S[4] = {X.m32[0], X.m32[1], X.m32[2], X.m32[3]};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t q0 = (A[t] & 0x0F0F0F0Fu) | ((H[t] << 4) & 0x30303030u);
             const uint32_t q1 = (B[t] & 0x0F0F0F0Fu) | ((H[t] << 2) & 0x30303030u);
             const uint32_t q2 = ((A[t] >> 4) & 0x0F0F0F0Fu) | (H[t] & 0x30303030u);
             const uint32_t q3 = ((B[t] >> 4) & 0x0F0F0F0Fu) | ((H[t] >> 2) & 0x30303030u);
-            S[0] = __builtin_amdgcn_sdot4(centred(q0), X.q[t], S[0], false);
-            S[1] = __builtin_amdgcn_sdot4(centred(q1), X.q[4 + t], S[1], false);
-            S[2] = __builtin_amdgcn_sdot4(centred(q2), X.q[8 + t], S[2], false);
-            S[3] = __builtin_amdgcn_sdot4(centred(q3), X.q[12 + t], S[3], false);
+            S[0] = __builtin_amdgcn_sdot4((int)q0, X.q[t], S[0], false);
+            S[1] = __builtin_amdgcn_sdot4((int)q1, X.q[4 + t], S[1], false);
+            S[2] = __builtin_amdgcn_sdot4((int)q2, X.q[8 + t], S[2], false);
+            S[3] = __builtin_amdgcn_sdot4((int)q3, X.q[12 + t], S[3], false);
         }
         // sub-scale of run g: byte 2g + lh of the 8 scale bytes of half h
         const int lh = u & 1;
