@@ -78,7 +78,10 @@ QMV_DEV float group_sum_last(float v) {
     return v;
 }
 
-QMV_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), the division by the hardware reciprocal (1 ulp)
+// instead of the correctly rounded division sequence; z below about -88
+// gives e^-z = inf and -0, as the division would.
+QMV_DEV float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Non-temporal-free plain 16-byte load.
 QMV_DEV uint4 ld16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }

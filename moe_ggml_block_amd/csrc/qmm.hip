@@ -2725,9 +2725,7 @@ __global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__re
                                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
                                     const float p = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
                                     const float g = lane < 32 ? x : p, up = lane < 32 ? p : x;
-                                    // silu with a hardware reciprocal (1 ulp) in place of the
-                                    // division: the h of a step is stored once per eight
-                                    hv[t][r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up;
+                                    hv[t][r] = silu(g) * up;
                                 }
                             const int uo = lane >> 5;
                             const int col = CW * cg + 4 * (lq & 1);
