@@ -2021,6 +2021,33 @@ struct Q6rRaw {
 // slots whose expert is outside [0, E). Otherwise the segments come from the
 // layer's tile table (nseg, seg_off).
 // FPW weight fragments per wave, 16 / FPW waves: 256 weight rows per unit.
+// Units [u, u1) of this workgroup in the resident-activation GEMMs (nseg
+// segments of nu units each). A workgroup whose run crosses a segment
+// boundary stages twice and ramps its weight loads up twice, so when the
+// segments are at most the workgroups (grid / nseg >= 2, or 1 with the
+// segments filling three quarters of the grid or more) every segment is
+// cut into grid / nseg equal runs and each workgroup takes at most one
+// (128 experts, gate projection, 127 segments of 48 units: 52.3 us with
+// contiguous shares, 41.1 us at 128 segments, where the shares align);
+// otherwise every workgroup takes an equal contiguous share of all units.
+__device__ __forceinline__ void resident_unit_range(int nseg, int nu, int64_t *u, int64_t *u1) {
+    const int grid = (int)gridDim.x, b = (int)blockIdx.x;
+    const int kper = nseg > 0 ? grid / nseg : 0;
+    if (kper >= 2 || (kper == 1 && 4 * nseg >= 3 * grid)) {
+        if (b < nseg * kper) {
+            const int seg = b / kper, part = b - seg * kper;
+            *u = (int64_t)seg * nu + (int64_t)nu * part / kper;
+            *u1 = (int64_t)seg * nu + (int64_t)nu * (part + 1) / kper;
+        } else {
+            *u = *u1 = 0;  // no run left for this workgroup
+        }
+        return;
+    }
+    const int64_t total = (int64_t)nseg * nu;
+    *u = total * b / grid;
+    *u1 = total * (b + 1) / grid;
+}
+
 template <int NSB, bool GROUPED, int FPW>
 __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const int *__restrict__ nseg_p,
                                                        const int *__restrict__ seg_off, int bmt) {
@@ -2099,9 +2126,8 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
     // groups (as in k_qmm4r).
     const int ug = (int64_t)nseg * ((ngr + NW - 1) / NW) >= 6 * (int64_t)gridDim.x ? NW : 1;
     const int nu = (ngr + ug - 1) / ug;  // units per segment
-    const int64_t total = (int64_t)nseg * nu;
-    const int64_t u1 = total * (blockIdx.x + 1) / gridDim.x;
-    int64_t u = total * blockIdx.x / gridDim.x;
+    int64_t u, u1;
+    resident_unit_range(nseg, nu, &u, &u1);
     while (u < u1) {
         // row groups g0 .. g1 - 1 of segment seg; wave w takes g0 + w,
         // g0 + w + NW, ...
@@ -2489,9 +2515,8 @@ __global__ __launch_bounds__(1024) void k_qmm4r(const QmmArgs a, const int *__re
     // (the workgroups' shares stay within a group of each other).
     const int ug = (int64_t)nseg * ((ncg + NW - 1) / NW) >= 6 * (int64_t)gridDim.x ? NW : 1;
     const int nu = (ncg + ug - 1) / ug;  // units per segment
-    const int64_t total = (int64_t)nseg * nu;
-    const int64_t u1 = total * (blockIdx.x + 1) / gridDim.x;
-    int64_t u = total * blockIdx.x / gridDim.x;
+    int64_t u, u1;
+    resident_unit_range(nseg, nu, &u, &u1);
     while (u < u1) {
         // column groups g0 .. g1 - 1 of segment seg; wave w takes g0 + w,
         // g0 + w + NW, ...
