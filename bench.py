@@ -583,7 +583,7 @@ def moe_prefill_other(bank_copies: int = 3):
     bu, U = rotated(up, bank_copies)
     per_layer = (gate.nbytes + up.nbytes) // E + per_down
     del gate, up
-    for TT in (32, 128, 512, 2048):
+    for TT in (32, 64, 128, 512, 2048):
         lgT = torch.from_numpy(synth.moe_logits(TT, E)).cuda()
         idsT, wT = qmv.moe_route(lgT, TT, E, topk)
         uT = len(np.unique(idsT.cpu().numpy()))
