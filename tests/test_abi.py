@@ -58,6 +58,13 @@ def test_host_validation_returns_before_launch(lib):
     assert lib.qmv_q4k(fake, fake, fake, 4, 300, None) == QMV_EINVAL
     assert lib.qmv_q4k(fake, fake, fake, 0, 256, None) == QMV_EINVAL
     assert lib.qmv_q4k(odd, fake, fake, 4, 256, None) == QMV_EALIGN
+    lib.qmv_q4k_qx.argtypes = [vp] * 6 + [i64, i64, vp]
+    lib.qmv_q4k_qx.restype = i32
+    assert lib.qmv_q4k_qx(fake, fake, fake, None, fake, fake, 4, 256, None) == QMV_EINVAL   # no xq
+    assert lib.qmv_q4k_qx(fake, fake, fake, fake, fake, fake, 4, 288, None) == QMV_EINVAL   # k % 256
+    assert lib.qmv_q4k_qx(fake, fake, fake, fake, fake, fake, 0, 256, None) == QMV_EINVAL   # n < 1
+    assert lib.qmv_q4k_qx(fake, odd, fake, fake, fake, fake, 4, 256, None) == QMV_EALIGN    # x
+    assert lib.qmv_q4k_qx(fake, fake, fake, odd, fake, fake, 4, 256, None) == QMV_EALIGN    # xq
     lib.qmv_q8_0.argtypes = lib.qmv_q4k.argtypes
     lib.qmv_q8_0.restype = i32
     assert lib.qmv_q8_0(fake, fake, fake, 4, 48, None) == QMV_EINVAL
