@@ -967,10 +967,15 @@ int launch_gate_up(MoeArgs a, hipStream_t s) {
 }
 
 // Row passes per slot of a down-pass workgroup at least (its rows are
-// rblk = passes * RPP).
-#ifndef QMV_DOWN_MIN_PASSES
-#define QMV_DOWN_MIN_PASSES 1
-#endif
+// rblk = passes * RPP). A workgroup that quantizes its h rows while staging
+// them (moe_stage_qx) repeats that work for every row block of its token, so
+// it takes more rows: q8 layer at one token 18.28 -> 17.40 us with two
+// passes (19.19 with four), at four tokens 33.04 -> 30.59 us with four.
+template <class F>
+int down_min_passes(int64_t T) {
+    if constexpr (moe_stage_qx<F>::value) return T >= 4 ? 4 : 2;
+    return 1;
+}
 
 // Slots staged at once by the down pass: as many as fit 48 KB of LDS, <= 8.
 template <class F>
@@ -997,7 +1002,7 @@ int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
     int rblk = RPP;
     while (rblk < a.n && rblk < 1024 &&
            (div_up(a.n, rblk) * T > cache[1] || (int64_t)a.topk * (rblk / RPP) < WAVES ||
-            rblk / RPP < QMV_DOWN_MIN_PASSES))
+            rblk / RPP < down_min_passes<F>(T)))
         rblk *= 2;
     a.rblk = rblk;
     const size_t lds = lds0 + (size_t)WAVES * a.rblk * 4;
