@@ -562,11 +562,10 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
 // experts, counts, item offsets and the slot list, each behind a barrier,
 // all before the first weight load (about half of a workgroup's time at
 // one token, 128 experts, top-8).
-template <class F, int G, int UPL, bool PAIR>
+template <class F, int G, int UPL, bool PAIR, int NB>
 __global__ __launch_bounds__(256) void k_moe_direct(MoeArgs a, int rblk) {
     extern __shared__ float4 dyn4[];
     float *xlds = reinterpret_cast<float *>(dyn4);
-    constexpr int NB = MOE_RING;
     constexpr int RPP = 64 / G;
     static_assert(!PAIR || RPP % 2 == 0, "pairs need an even number of rows per pass");
     using Raw = typename F::Raw;
@@ -890,12 +889,25 @@ double expected_present(int64_t nslots, int64_t E) {
 #define QMV_DIRECT_SLOTS 256
 #endif
 
-template <class F, int G, int UPL, bool PAIR>
-int launch_direct_t(MoeArgs a, hipStream_t s) {
+// Row passes in flight per wave of the direct gathers (measured, 128
+// experts, top-8, gate/up [768, 2048]): the f32 dots want a deeper ring at
+// many slots (layer at 16 tokens 83.3 us with two passes, 79.4 with three;
+// at 8 tokens 48.4 against 48.7, at one 17.3 against 18.0 with two), the
+// int8 dots a shallower one (q8 layer at 4 / 8 / 16 tokens 30.6 / 47.2 /
+// 76.8 us with two, 29.0 / 46.2 / 75.3 with one; 17.3 against 17.6 us at
+// one token with two).
+template <class F>
+int direct_ring(int64_t nslots) {
+    if constexpr (!std::is_same<typename F::X, UnitX>::value) return nslots >= 32 ? 1 : 2;  // int8 dots
+    return nslots >= 96 ? 3 : 2;
+}
+
+template <class F, int G, int UPL, bool PAIR, int NB>
+int launch_direct_nb(MoeArgs a, hipStream_t s) {
     const size_t lds = (size_t)(a.k / 64) * F::ACT_STRIDE * 4;
     static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
     if (cache[0] != (int64_t)lds) {
-        cache[1] = resident_wgs(k_moe_direct<F, G, UPL, PAIR>, lds);
+        cache[1] = resident_wgs(k_moe_direct<F, G, UPL, PAIR, NB>, lds);
         cache[0] = (int64_t)lds;
     }
     // blocks of whole passes (one per wave and more), about one item per
@@ -905,9 +917,18 @@ int launch_direct_t(MoeArgs a, hipStream_t s) {
     if (rblk > a.n) rblk = div_up(a.n, step) * step;
     const int64_t items = a.nslots * div_up(a.n, rblk);
     const int64_t grid = items < cache[1] ? items : cache[1];
-    hipLaunchKernelGGL((k_moe_direct<F, G, UPL, PAIR>), dim3((unsigned)grid), dim3(256), lds, s, a, (int)rblk);
+    hipLaunchKernelGGL((k_moe_direct<F, G, UPL, PAIR, NB>), dim3((unsigned)grid), dim3(256), lds, s, a, (int)rblk);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
+}
+
+template <class F, int G, int UPL, bool PAIR>
+int launch_direct_t(MoeArgs a, hipStream_t s) {
+    switch (direct_ring<F>(a.nslots)) {
+        case 1: return launch_direct_nb<F, G, UPL, PAIR, 1>(a, s);
+        case 3: return launch_direct_nb<F, G, UPL, PAIR, 3>(a, s);
+        default: return launch_direct_nb<F, G, UPL, PAIR, 2>(a, s);
+    }
 }
 
 template <class F, int G, int UPL, bool PAIR>
