@@ -684,12 +684,11 @@ struct DownArgs {
     int n, k, E, topk, rblk, chunk;
 };
 
-template <class F, int G>
+template <class F, int G, int NB>
 __global__ __launch_bounds__(256) void k_moe_down(DownArgs a) {
     extern __shared__ float4 dyn4[];
     float *hlds = reinterpret_cast<float *>(dyn4);  // chunk x (k/64) units
     float *acc_lds = hlds + (size_t)a.chunk * (a.k / 64) * F::ACT_STRIDE;  // [WAVES][rblk]
-    constexpr int NB = F::RING;
     constexpr int RPP = 64 / G;
     using Raw = typename F::Raw;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1008,13 +1007,13 @@ int down_chunk(int64_t k, int64_t topk) {
     return (int)(c < topk ? c : topk);
 }
 
-template <class F, int G>
-int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
+template <class F, int G, int NB>
+int launch_down_nb(DownArgs a, int64_t T, hipStream_t s) {
     constexpr int RPP = 64 / G;
     const size_t lds0 = (size_t)a.chunk * (a.k / 64) * F::ACT_STRIDE * 4;
     static thread_local int64_t cache[2] = {-1, -1};
     if (cache[0] != (int64_t)lds0) {
-        cache[1] = resident_wgs(k_moe_down<F, G>, lds0 + WAVES * 64 * 4);
+        cache[1] = resident_wgs(k_moe_down<F, G, NB>, lds0 + WAVES * 64 * 4);
         cache[0] = (int64_t)lds0;
     }
     // rows per workgroup: within one round of resident workgroups, and
@@ -1028,9 +1027,21 @@ int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
     a.rblk = rblk;
     const size_t lds = lds0 + (size_t)WAVES * a.rblk * 4;
     const dim3 grid((unsigned)div_up(a.n, a.rblk), (unsigned)T);
-    hipLaunchKernelGGL((k_moe_down<F, G>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_moe_down<F, G, NB>), grid, dim3(256), lds, s, a);
     QMV_LAUNCH_CHECK();
     return QMV_OK;
+}
+
+// Row passes in flight per wave of the down pass: the unit's own depth, but
+// one for the f32 dots at a single token (layer 17.34 -> 17.07 us; with one
+// pass at 4 and 16 tokens 30.9 -> 32.2 and 79.2 -> 83.7 us, and the int8
+// down at one token 17.4 -> 18.1 us).
+template <class F, int G>
+int launch_down_g(DownArgs a, int64_t T, hipStream_t s) {
+    if constexpr (std::is_same<typename F::X, UnitX>::value && F::RING == 2) {
+        if (T == 1) return launch_down_nb<F, G, 1>(a, T, s);
+    }
+    return launch_down_nb<F, G, F::RING>(a, T, s);
 }
 
 template <class F>
