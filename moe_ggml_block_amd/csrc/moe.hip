@@ -53,7 +53,10 @@ constexpr int ROUTE_FUSED_T = 8;
 // q8 decode layer: up to this many tokens the gathers quantize the rows they
 // stage instead of separate quantizer launches (measured: one token 23.2 ->
 // 21.3 us, four the same, sixteen 82.4 -> 83.3)
-constexpr int Q8_STAGED_T = 8;
+#ifndef QMV_Q8_STAGED_T
+#define QMV_Q8_STAGED_T 32
+#endif
+constexpr int Q8_STAGED_T = QMV_Q8_STAGED_T;
 // Row passes in flight per wave in the gathers: their row blocks are short
 // (a few passes per wave), so every pass of a block is requested up front.
 constexpr int MOE_RING = 2;
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     }
 }
 
-// Small batches (at most QMV_DIRECT_SLOTS slots): an item is one slot and a
+// Small batches (up to direct_slots<F>() slots): an item is one slot and a
 // block of rblk rows, with no grouping by expert. A workgroup reads its
 // slot's expert (or routes the slot's token itself, each wave on its own:
 // ids == nullptr) and issues its weight loads at once; the item of a slot's
@@ -879,14 +882,23 @@ double expected_present(int64_t nslots, int64_t E) {
     return p < 1.0 ? 1.0 : p;
 }
 
-// Slots up to which the gathers take the direct form (k_moe_direct):
-// 128 experts, top-8, gate/up [768, 2048], down [2048, 768], layer at 8 /
-// 16 / 24 / 32 tokens 52.4 / 88.0 / 119.9 / 156.9 us with the grouping from
-// 64 slots up, 48.5 / 82.8 / 114.7 / 149.6 us direct; at 64 tokens (512
-// slots) the grouping is faster (q8 layer 222.9 against 245.8 us).
-#ifndef QMV_DIRECT_SLOTS
-#define QMV_DIRECT_SLOTS 256
+// Slots up to which the gathers take the direct form (k_moe_direct), by
+// the dots' kind (128 experts, top-8, gate/up [768, 2048], down
+// [2048, 768]): the f32 layer at 8 / 16 / 32 / 33 / 48 / 64 tokens takes
+// 52.4 / 88.0 / 156.9 / 202.3 / 215.7 / 328.4 us with the grouping and
+// 48.5 / 82.8 / 149.6 / 178.3 / 193.2 / 300.9 direct; the q8 layer at 33 /
+// 48 tokens 164.5 / 212.7 grouped, 146.0 / 168.2 direct, but at 64 tokens
+// (512 slots) 222.4 grouped against 230.1 direct.
+#ifndef QMV_DIRECT_SLOTS_F32
+#define QMV_DIRECT_SLOTS_F32 512
 #endif
+#ifndef QMV_DIRECT_SLOTS_Q8
+#define QMV_DIRECT_SLOTS_Q8 384
+#endif
+template <class F>
+constexpr int64_t direct_slots() {
+    return std::is_same<typename F::X, UnitX>::value ? QMV_DIRECT_SLOTS_F32 : QMV_DIRECT_SLOTS_Q8;
+}
 
 // Row passes in flight per wave of the direct gathers (measured, 128
 // experts, top-8, gate/up [768, 2048]): the f32 dots want a deeper ring at
@@ -932,7 +944,7 @@ int launch_direct_t(MoeArgs a, hipStream_t s) {
 
 template <class F, int G, int UPL, bool PAIR>
 int launch_moe_t(MoeArgs a, hipStream_t s) {
-    if (a.nslots <= QMV_DIRECT_SLOTS) return launch_direct_t<F, G, UPL, PAIR>(a, s);
+    if (a.nslots <= direct_slots<F>()) return launch_direct_t<F, G, UPL, PAIR>(a, s);
     const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E, moe_nsp<F, G, UPL>());
     static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
     if (cache[0] != (int64_t)lds) {

@@ -138,9 +138,9 @@ def _banks():
     return _BANKS
 
 
-# 32 and 33 tokens straddle the gathers' switch from one item per slot
-# (up to 256 slots) to items grouped by expert
-@pytest.mark.parametrize("T", [1, 4, 16, 32, 33])
+# 64 and 65 tokens straddle the f32 gathers' switch from one item per slot
+# (up to 512 slots) to items grouped by expert
+@pytest.mark.parametrize("T", [1, 4, 16, 64, 65])
 def test_moe_layer_full_config(T):
     """Router + fused FFN at the full MoE shape (128 experts, top-8, gate/up
     Q4_K [768, 2048], down Q6_K [2048, 768])."""

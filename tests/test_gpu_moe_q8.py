@@ -32,7 +32,10 @@ def _ids(T, topk, E_, seed=0):
     return np.array([(i * 7 + 3 + seed) % E_ for i in range(T * topk)], dtype=np.int32)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 32, 33])
+# 32 / 33 tokens straddle the layer's switch from quantizing in the staging
+# to the quantizer launches, 48 / 49 the int8 gathers' switch from one item
+# per slot (up to 384 slots) to items grouped by expert
+@pytest.mark.parametrize("T", [1, 4, 16, 32, 33, 49])
 def test_moe_qmv_q4k_q8_gate_shape(T):
     announce(f"moe_qmv_q4k_q8 T={T}")
     bank = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, INTER, HIDDEN)
@@ -44,7 +47,7 @@ def test_moe_qmv_q4k_q8_gate_shape(T):
     assert scalerel(ref, got) <= TOL, scalerel(ref, got)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 32, 33])
+@pytest.mark.parametrize("T", [1, 4, 16, 32, 33, 49])
 def test_moe_qmv_q6k_q8_down_shape(T):
     announce(f"moe_qmv_q6k_q8 T={T}")
     bank = synth.moe_bank(synth.FMT_Q6K, synth.SEED_DOWN, E, HIDDEN, INTER)
@@ -82,7 +85,7 @@ def _expert_slice(bank, fmt, e, rows, k):
     return oracle.dequant(fmt, bank.reshape(-1, rb)[e * rows:(e + 1) * rows]).reshape(rows, k)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 32, 33])
+@pytest.mark.parametrize("T", [1, 4, 16, 32, 33, 49])
 def test_moe_layer_q8_matches_oracle_up_to_h_code_ties(T):
     announce(f"moe layer q8 T={T}")
     gate = synth.moe_bank(synth.FMT_Q4K, synth.SEED_GATE, E, INTER, HIDDEN)
