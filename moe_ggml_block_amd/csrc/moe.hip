@@ -49,16 +49,22 @@ constexpr int SMALL_E = 256;  // router: one workgroup per token up to this E
 constexpr int ROUTE_FUSED_E = 256;  // routing fused into the gather up to this E
 // and up to this many tokens: every workgroup routes every token, which
 // beat a separate router launch at 1 and 4 tokens and lost at 16 (measured)
-constexpr int ROUTE_FUSED_T = 8;
+#ifndef QMV_ROUTE_FUSED_T
+#define QMV_ROUTE_FUSED_T 8
+#endif
+constexpr int ROUTE_FUSED_T = QMV_ROUTE_FUSED_T;
 // q8 decode layer: up to this many tokens the gathers quantize the rows they
-// stage instead of separate quantizer launches (measured: one token 23.2 ->
-// 21.3 us, four the same, sixteen 82.4 -> 83.3)
+// stage instead of separate quantizer launches (measured with the direct
+// gathers: sixteen / twenty-four / thirty-two tokens 74.7 / 98.4 / 125.9 ->
+// 72.3 / 95.2 / 123.4 us; at thirty-three the launches win, 164.2 against
+// 173.0)
 #ifndef QMV_Q8_STAGED_T
 #define QMV_Q8_STAGED_T 32
 #endif
 constexpr int Q8_STAGED_T = QMV_Q8_STAGED_T;
-// Row passes in flight per wave in the gathers: their row blocks are short
-// (a few passes per wave), so every pass of a block is requested up front.
+// Row passes in flight per wave in the grouped gathers (k_moe): their row
+// blocks are short (a few passes per wave), so every pass of a block is
+// requested up front. The direct gathers choose theirs per launch.
 constexpr int MOE_RING = 2;
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
