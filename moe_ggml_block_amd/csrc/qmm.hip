@@ -2003,8 +2003,11 @@ struct Q6rRaw {
     uint32_t d[FPW];
 };
 
+// Steps in flight per wave: one (with the segment-aligned unit runs, MoE
+// prefill layer at 64 / 128 / 512 tokens 146.8 / 149.2 / 236.6 us with two,
+// 143.7 / 146.5 / 223.5 with one).
 #ifndef Q6R_RING
-#define Q6R_RING 2
+#define Q6R_RING 1
 #endif
 #ifndef Q6R_FPW
 #define Q6R_FPW 1               // 16-row weight fragments per wave (1: 16 waves, 2: 8 waves)
