@@ -2051,7 +2051,7 @@ __device__ __forceinline__ void resident_unit_range(int nseg, int nu, int64_t *u
     *u1 = total * (b + 1) / grid;
 }
 
-template <int NSB, bool GROUPED, int FPW>
+template <int NSB, bool GROUPED, int FPW, int SL>
 __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const int *__restrict__ nseg_p,
                                                        const int *__restrict__ seg_off, int bmt) {
     static_assert(NSB >= 1 && NSB <= Q6R_MAX_NSB, "k <= 1024");
@@ -2059,11 +2059,12 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
     constexpr int NW = 16 / FPW, NT = 64 * NW;           // waves, threads
     constexpr int PITCH = 1024 * NSB + 16;                // bytes per staged row
     constexpr int D = Q6R_RING;                           // steps in flight per wave
-    constexpr int LPR = NT / Q6R_SLOTS;                   // staging lanes per row
+    static_assert(SL == 32 || SL == 48, "slots per segment");
+    constexpr int LPR = SL == 32 ? NT / 32 : NT / 64;     // staging lanes per row (a power of two)
     constexpr int CPL = 64 * NSB / LPR;                   // staged float4 per lane
-    __shared__ __attribute__((aligned(16))) uint8_t act[Q6R_SLOTS * PITCH];
-    __shared__ int s_slot[Q6R_SLOTS];
-    __shared__ float s_inv[Q6R_SLOTS];
+    __shared__ __attribute__((aligned(16))) uint8_t act[SL * PITCH];
+    __shared__ int s_slot[SL];
+    __shared__ float s_inv[SL];
     __shared__ int s_misc[4], s_wsum[NW];
     __shared__ int s_cnt[GROUPED ? QMM_MOE_MAX_E : 1], s_sb[GROUPED ? QMM_MOE_MAX_E : 1];
 
@@ -2090,7 +2091,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
             int tl = 0;
             for (int i = 0; i < EPL; ++i) {
                 const int e = lane * EPL + i;
-                if (e < E) tl += (s_cnt[e] + 31) / 32;
+                if (e < E) tl += (s_cnt[e] + SL - 1) / SL;
             }
             int inc = tl;
 #pragma unroll
@@ -2103,7 +2104,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
                 const int e = lane * EPL + i;
                 if (e < E) {
                     s_sb[e] = run;
-                    run += (s_cnt[e] + 31) / 32;
+                    run += (s_cnt[e] + SL - 1) / SL;
                 }
             }
             if (lane == 63) s_misc[0] = inc;
@@ -2143,13 +2144,13 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
         int esel;
         if constexpr (GROUPED) {
             for (int e = tid; e < E; e += NT) {
-                const int b = s_sb[e], ns = (s_cnt[e] + 31) / 32;
+                const int b = s_sb[e], ns = (s_cnt[e] + SL - 1) / SL;
                 if (seg >= b && seg < b + ns) {
                     s_misc[1] = e;
-                    s_misc[2] = 32 * (seg - b);
+                    s_misc[2] = SL * (seg - b);
                 }
             }
-            if (tid < Q6R_SLOTS) s_slot[tid] = -1;
+            if (tid < SL) s_slot[tid] = -1;
             __syncthreads();
             esel = s_misc[1];
             const int rank0 = s_misc[2];
@@ -2158,7 +2159,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
             // counts plus the ballot prefix
             constexpr int CW = QMM_ID_CHUNK / NW;
             int run = 0;
-            for (int q0 = 0; q0 < m && run < rank0 + Q6R_SLOTS; q0 += QMM_ID_CHUNK) {
+            for (int q0 = 0; q0 < m && run < rank0 + SL; q0 += QMM_ID_CHUNK) {
                 int cw = 0;
                 for (int b = 0; b < CW; b += 64) {
                     const int sl = q0 + wave * CW + b + lane;
@@ -2176,7 +2177,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
                     const bool hit = sl < m && ids[sl] == esel;
                     const uint64_t bal = __ballot(hit);
                     const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
-                    if (hit && rank >= rank0 && rank < rank0 + Q6R_SLOTS) s_slot[rank - rank0] = sl;
+                    if (hit && rank >= rank0 && rank < rank0 + SL) s_slot[rank - rank0] = sl;
                     base += __popcll(bal);
                 }
                 __syncthreads();  // s_wsum is rewritten by the next chunk
@@ -2184,7 +2185,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
         } else {
             // only the segment's own entries (c << 25 | offset, k_group_tiles)
             const int so = seg_off[seg], off = so & ((1 << Q6R_SEG_SHIFT) - 1), scnt = so >> Q6R_SEG_SHIFT;
-            if (tid < Q6R_SLOTS) s_slot[tid] = tid < scnt ? a.tile_slots[off + tid] : -1;
+            if (tid < SL) s_slot[tid] = tid < scnt ? a.tile_slots[off + tid] : -1;
             esel = a.tile_e[off / bmt];
             __syncthreads();
         }
@@ -2193,7 +2194,7 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
         // staging: lanes of row tid / LPR, float4 chunks l + LPR*i; the row's
         // largest magnitude over those lanes, the power of two, then
         // [hi x4 | lo x4] per chunk (rows of slots past the segment are 0)
-        {
+        if (tid < SL * LPR) {  // whole waves (SL * LPR is a multiple of 64)
             const int srow = tid / LPR, l = tid % LPR;
             const int sslot = s_slot[srow];
             const float *xr = a.x + (size_t)(sslot >= 0 ? sslot / a.x_div : 0) * (256 * NSB);
@@ -2371,15 +2372,27 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
                 }
             }
         };
-        if (s_slot[16] >= 0) run(std::integral_constant<int, 2>{});
-        else run(std::integral_constant<int, 1>{});
+        if constexpr (SL == 48) {
+            if (s_slot[32] >= 0) run(std::integral_constant<int, 3>{});
+            else if (s_slot[16] >= 0) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 1>{});
+        } else {
+            if (s_slot[16] >= 0) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 1>{});
+        }
     }
 }
 
-// k_qmm6r, one workgroup per CU (k <= 1024): GROUPED derives its 32-slot
-// segments from ids, otherwise they come from the tile table (nseg, seg_off).
+// Slots per k_qmm6r segment: 48 (three 16-slot fragments on one weight
+// decode) where the experts average more than 16 slots and 48 staged rows fit
+// LDS (k <= 768), else 32.
+int q6r_segment_slots(int64_t nslots, int64_t E, int64_t k) { return k <= 768 && nslots > 16 * E ? 48 : 32; }
+
+// k_qmm6r, one workgroup per CU (k <= 1024): GROUPED derives its segments of
+// sl slots from ids, otherwise they come from the tile table (nseg, seg_off,
+// listed for sl-slot segments).
 template <bool GROUPED>
-void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt, hipStream_t s) {
+void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt, int sl, hipStream_t s) {
     static thread_local int c_dev = -1, c_cus = 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
@@ -2390,11 +2403,19 @@ void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt,
         c_cus = cus;
     }
     const dim3 grid((unsigned)c_cus), block(1024 / Q6R_FPW);
+    if (sl == 48 && a.k <= 768) {
+        switch (a.k / 256) {
+            case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+            case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+            default: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        }
+        return;
+    }
     switch (a.k / 256) {
-        case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        case 3: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        default: hipLaunchKernelGGL((k_qmm6r<4, GROUPED, Q6R_FPW>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 3: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        default: hipLaunchKernelGGL((k_qmm6r<4, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
     }
 }
 
@@ -2876,8 +2897,8 @@ extern "C" int moe_qmm_q6k_f32(const void *bank, const float *x, int64_t x_div, 
     Qmm6Args a{static_cast<const uint8_t *>(bank), nullptr, nullptr, x, y, (int)nslots, (int)n, (int)k, ids, (int)E,
                (int)x_div};
     if (QMV_Q6R && k <= 256 * Q6R_MAX_NSB) {
-        // 32-slot tiles grouped in the kernel, the activation resident in LDS
-        launch_q6r<true>(a, nullptr, nullptr, Q6R_SLOTS, (hipStream_t)stream);
+        // segments grouped in the kernel, the activation resident in LDS
+        launch_q6r<true>(a, nullptr, nullptr, Q6R_SLOTS, q6r_segment_slots(nslots, E, k), (hipStream_t)stream);
     } else {
         const dim3 grid((unsigned)div_up(n, QMM6_MOEF_BN),
                         (unsigned)(div_up(nslots, QMM6_MOEF_BM) + std::min(E, nslots)));
@@ -2914,7 +2935,8 @@ namespace {
 // valid slot is placed in its expert's tiles. The order of an expert's slots
 // within its tiles follows the atomics and may differ between runs; every
 // output row depends only on its own slot, so the results do not. It also
-// lists the 32-slot segments of the table: nseg, and for each its slot count
+// lists the 32-slot segments of the table (and, given nseg48, the 48-slot
+// ones the same way): nseg, and for each its slot count
 // c (1..32) and the offset o in tile_slots of its first slot, as
 // c << 25 | o (an expert's slots are packed from the start of its first
 // tile, so its segment j starts 32 j past it; with 48-slot tiles a
@@ -2924,8 +2946,9 @@ template <int BM>
 __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict__ ids, int S, int E,
                                                       int *__restrict__ ntiles, int *__restrict__ tile_e,
                                                       int *__restrict__ tile_slots, int *__restrict__ nseg,
-                                                      int *__restrict__ seg_off) {
-    __shared__ int s_cnt[QMM_MOE_MAX_E], s_off[QMM_MOE_MAX_E], s_wtot[16], s_wseg[16];
+                                                      int *__restrict__ seg_off, int *__restrict__ nseg48,
+                                                      int *__restrict__ seg_off48) {
+    __shared__ int s_cnt[QMM_MOE_MAX_E], s_off[QMM_MOE_MAX_E], s_wtot[16], s_wseg[16], s_wseg48[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
     __syncthreads();
@@ -2935,37 +2958,44 @@ __global__ __launch_bounds__(1024) void k_group_tiles(const int32_t *__restrict_
     }
     __syncthreads();
     const int cnt = tid < E ? s_cnt[tid] : 0;
-    const int nt = (cnt + BM - 1) / BM, ns = (cnt + 31) / 32;
-    int inc = nt, incs = ns;
+    const int nt = (cnt + BM - 1) / BM, ns = (cnt + 31) / 32, ns48 = (cnt + 47) / 48;
+    int inc = nt, incs = ns, incs48 = ns48;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(inc, d), vs = __shfl_up(incs, d);
+        const int v = __shfl_up(inc, d), vs = __shfl_up(incs, d), vs48 = __shfl_up(incs48, d);
         if (lane >= d) {
             inc += v;
             incs += vs;
+            incs48 += vs48;
         }
     }
     if (lane == 63) {
         s_wtot[wave] = inc;
         s_wseg[wave] = incs;
+        s_wseg48[wave] = incs48;
     }
     __syncthreads();
-    int base = 0, bases = 0;
+    int base = 0, bases = 0, bases48 = 0;
     for (int w = 0; w < wave; ++w) {
         base += s_wtot[w];
         bases += s_wseg[w];
+        bases48 += s_wseg48[w];
     }
-    const int off = base + inc - nt, offs = bases + incs - ns;
+    const int off = base + inc - nt, offs = bases + incs - ns, offs48 = bases48 + incs48 - ns48;
     if (tid < E) {
         s_off[tid] = off;
         for (int i = 0; i < nt; ++i) tile_e[off + i] = tid;
         for (int j = cnt; j < nt * BM; ++j) tile_slots[(size_t)off * BM + j] = -1;
         for (int j = 0; j < ns; ++j) seg_off[offs + j] = (min(32, cnt - 32 * j) << Q6R_SEG_SHIFT) | (off * BM + 32 * j);
+        if (seg_off48)
+            for (int j = 0; j < ns48; ++j)
+                seg_off48[offs48 + j] = (min(48, cnt - 48 * j) << Q6R_SEG_SHIFT) | (off * BM + 48 * j);
         s_cnt[tid] = 0;  // now the running position of the expert's slots
     }
     if (tid == 1023) {
         ntiles[0] = base + inc;
         nseg[0] = bases + incs;
+        if (nseg48) nseg48[0] = bases48 + incs48;
     }
     __syncthreads();
     for (int sl = tid; sl < S; sl += 1024) {
@@ -3002,7 +3032,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ d
 struct PrefillWs {
     int8_t *xq;
     float *xs, *xsum, *h, *d;
-    int *ntiles, *tile_e, *tile_slots, *nseg, *seg_off;
+    int *ntiles, *tile_e, *tile_slots, *nseg, *seg_off, *nseg48, *seg_off48;
     int64_t bytes;
 };
 
@@ -3036,6 +3066,8 @@ PrefillWs prefill_ws(uint8_t *base, int64_t T, int64_t topk, int64_t hidden, int
     w.tile_slots = reinterpret_cast<int *>(take(4 * mt * bm));
     w.nseg = reinterpret_cast<int *>(take(4));
     w.seg_off = reinterpret_cast<int *>(take(4 * pf_max_tiles(S, E, 32)));
+    w.nseg48 = reinterpret_cast<int *>(take(4));
+    w.seg_off48 = reinterpret_cast<int *>(take(4 * pf_max_tiles(S, E, 48)));
     w.h = reinterpret_cast<float *>(take(4 * S * inter));
     w.d = reinterpret_cast<float *>(take(4 * S * hidden));
     w.bytes = o;
@@ -3084,9 +3116,14 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
                (int)E, (int)topk, w.ntiles, w.tile_e, w.tile_slots, static_cast<const uint8_t *>(up)};
     Qmm6Args dn{static_cast<const uint8_t *>(down), nullptr, nullptr, w.h, w.d, (int)S, (int)hidden, (int)inter, ids,
                 (int)E, 1, w.ntiles, w.tile_e, w.tile_slots};
+    // the down GEMM's segments: 48 slots where the experts average more
+    // than 16 (k_group_tiles lists them beside the 32-slot ones)
+    const int sl6 = q6r_segment_slots(S, E, inter);
+    int *const n48 = sl6 == 48 ? w.nseg48 : nullptr, *const s48 = sl6 == 48 ? w.seg_off48 : nullptr;
+    const int *const nseg6 = sl6 == 48 ? w.nseg48 : w.nseg, *const segoff6 = sl6 == 48 ? w.seg_off48 : w.seg_off;
     if (bm == 32) {
         hipLaunchKernelGGL((k_group_tiles<32>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                           w.tile_slots, w.nseg, w.seg_off);
+                           w.tile_slots, w.nseg, w.seg_off, n48, s48);
         QMV_LAUNCH_CHECK();
         if (q4r)
             launch_q4r<true, false>(gu, w.nseg, w.seg_off, 32, s);
@@ -3095,7 +3132,7 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
                                dim3(256), 0, s, gu);
         QMV_LAUNCH_CHECK();
         if (QMV_Q6R && inter <= 256 * Q6R_MAX_NSB)
-            launch_q6r<false>(dn, w.nseg, w.seg_off, 32, s);
+            launch_q6r<false>(dn, nseg6, segoff6, 32, sl6, s);
         else
             hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF32, ACT_F32, true, true>),
                                dim3((unsigned)div_up(hidden, 256), (unsigned)mt), dim3(512), 0, s, dn);
@@ -3103,7 +3140,7 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
         // every expert's slots fit one tile up to 48 slots per expert: a
         // quarter less padding than 64-slot tiles where experts hold 20-47
         hipLaunchKernelGGL((k_group_tiles<48>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                           w.tile_slots, w.nseg, w.seg_off);
+                           w.tile_slots, w.nseg, w.seg_off, n48, s48);
         QMV_LAUNCH_CHECK();
         if (q4r)
             launch_q4r<true, false>(gu, w.nseg, w.seg_off, 48, s);
@@ -3111,10 +3148,10 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
             hipLaunchKernelGGL((k_qmm2_q4k<4, 1, 2, 1, 3>), dim3((unsigned)div_up(inter, 64), (unsigned)mt), dim3(512),
                                0, s, gu, 0);
         QMV_LAUNCH_CHECK();
-        launch_q6r<false>(dn, w.nseg, w.seg_off, 48, s);
+        launch_q6r<false>(dn, nseg6, segoff6, 48, sl6, s);
     } else {
         hipLaunchKernelGGL((k_group_tiles<64>), dim3(1), dim3(1024), 0, s, ids, (int)S, (int)E, w.ntiles, w.tile_e,
-                           w.tile_slots, w.nseg, w.seg_off);
+                           w.tile_slots, w.nseg, w.seg_off, n48, s48);
         QMV_LAUNCH_CHECK();
         // weight-side tile while its 32-bit lane offsets hold (an expert's
         // rows and the activation rows below 2^32 bytes)
@@ -3129,7 +3166,7 @@ extern "C" int moe_ffn_prefill_q4k_q6k(const void *gate, const void *up, const v
                                gu);
         QMV_LAUNCH_CHECK();
         if (QMV_Q6R && inter <= 256 * Q6R_MAX_NSB)
-            launch_q6r<false>(dn, w.nseg, w.seg_off, 64, s);
+            launch_q6r<false>(dn, nseg6, segoff6, 64, sl6, s);
         else
             hipLaunchKernelGGL((k_qmm_q6k<QMM6_PF64, ACT_F32, true, true>),
                                dim3((unsigned)div_up(hidden, 128), (unsigned)mt), dim3(512), 0, s, dn);
