@@ -236,8 +236,9 @@ struct MoeArgs {
     const int32_t *ids;
     float *y;  // [nslots, n]; PAIR: [nslots, n/2]
     int nslots, n, k, E;
-    // fused routing (ids == nullptr): logits [nslots / topk, E] are routed
-    // here (E <= ROUTE_FUSED_E); workgroup 0 writes ids_out / wts_out
+    // fused routing (ids == nullptr; the direct gathers only): logits
+    // [nslots / topk, E] are routed here (E <= ROUTE_FUSED_E); the item of a
+    // slot's first row block writes its ids_out / wts_out
     const float *logits;
     int topk;
     int32_t *ids_out;
@@ -331,32 +332,12 @@ __global__ __launch_bounds__(256) void k_moe(MoeArgs a) {
     for (int i = tid; i < pmax; i += 256) cnt[i] = 0;
     if (tid == 0) sh[1] = 0;
     __syncthreads();
-    if (a.logits) {
-        // fused routing: wave w routes tokens w, w + WAVES, ... (every
-        // workgroup routes all tokens; workgroup 0 publishes the result)
-        const int T = a.nslots / a.topk;
-        for (int t = wave; t < T; t += WAVES) {
-            int e;
-            float w;
-            route_token_wave<ROUTE_FUSED_E / 64>(a.logits + (size_t)t * a.E, a.E, a.topk, lane, &e, &w);
-            if (lane < a.topk) {
-                const int s = t * a.topk + lane;
-                s_ids[s] = (int16_t)e;
-                atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-                if (blockIdx.x == 0) {
-                    a.ids_out[s] = e;
-                    a.wts_out[s] = w;
-                }
-            }
-        }
-    } else {
-        for (int s = tid; s < a.nslots; s += 256) {
-            const int e = a.ids[s];
-            const bool ok = e >= 0 && e < a.E;
-            s_ids[s] = (int16_t)(ok ? e : -1);
-            if (ok) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-            else atomicAdd(&sh[1], 1);
-        }
+    for (int s = tid; s < a.nslots; s += 256) {
+        const int e = a.ids[s];
+        const bool ok = e >= 0 && e < a.E;
+        s_ids[s] = (int16_t)(ok ? e : -1);
+        if (ok) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+        else atomicAdd(&sh[1], 1);
     }
     __syncthreads();
     if (wave == 0) {
@@ -950,7 +931,8 @@ int launch_direct_t(MoeArgs a, hipStream_t s) {
 
 template <class F, int G, int UPL, bool PAIR>
 int launch_moe_t(MoeArgs a, hipStream_t s) {
-    if (a.nslots <= direct_slots<F>()) return launch_direct_t<F, G, UPL, PAIR>(a, s);
+    // the fused routing (logits instead of ids) runs in the direct form only
+    if (a.nslots <= direct_slots<F>() || a.logits) return launch_direct_t<F, G, UPL, PAIR>(a, s);
     const size_t lds = moe_lds_bytes(a.k, F::ACT_STRIDE, a.nslots, a.E, moe_nsp<F, G, UPL>());
     static thread_local int64_t cache[2] = {-1, -1};  // lds, resident workgroups
     if (cache[0] != (int64_t)lds) {
