@@ -562,7 +562,7 @@ __global__ __launch_bounds__(NTHREADS) void k_qmm_q4k(const QmmArgs a) {
 // holds both dots of its outputs and writes h = silu(gate) * up.
 // MODE 2 (moe_qmm_q4k): the same expert-indexed rows with the tile derived
 // in the kernel from ids (qmm_group), dense column layout, y[slot] rows.
-template <int NG, int MG, int KS, int MODE = 0, int NU = 4, bool R1 = false>
+template <int NG, int MG, int KS, int MODE = 0, int NU = 4>
 __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store) {
     constexpr bool PAIRT = MODE == 1, GROUPED = MODE == 2, MOEM = MODE != 0;
     static_assert(NG * MG * KS == 8 && (KS == 1 || KS == 2), "eight waves");
@@ -637,9 +637,9 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
     }
 
     // Raw superblock codes of this lane (header and NPW 8-byte pieces per
-    // row) and the staged activation chunks come in two register sets: the
-    // loads of superblock s + 2 are issued at the top of superblock s into
-    // the set that s used, so every load has two superblocks of work to land.
+    // row) and the activation chunks it stages, in registers between the
+    // load and their use (one superblock of work to land for the weights,
+    // two for the activations).
     struct WSet {
         uint4 hdr[2];
         uint2 qc[2][NPW];
@@ -712,28 +712,25 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
             out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
 
-    // R1: one register set each (the next superblock's loads go out as the
-    // current one is copied out of them), else two (two superblocks ahead)
-    WSet wset[R1 ? 1 : 2];
-    ASet aset[R1 ? 1 : 2];
+    // One register set each: the next superblock's weights are requested as
+    // soon as the current ones are copied out of the set, and the activations
+    // of superblock s + 2 as soon as those of s + 1 are stored to LDS (two
+    // sets, two superblocks ahead, took more registers and measured slower).
+    WSet wset;
+    ASet aset;
     // Every load and store below is unconditional: superblock indices past
     // the end are clamped to the last one (its data is loaded again and
     // never used). A branch around them would make the compiler's wait
     // counts assume the shorter path and wait for every load in flight.
-    load_w(0, wset[0]);
-    load_act(0, aset[0]);
-    if constexpr (!R1) {
-        load_w(min(1, nsb - 1), wset[1]);
-        load_act(min(1, nsb - 1), aset[1]);
-    }
-    store_act(0, aset[0]);
-    if constexpr (R1) load_act(min(1, nsb - 1), aset[0]);
+    load_w(0, wset);
+    load_act(0, aset);
+    store_act(0, aset);
+    load_act(min(1, nsb - 1), aset);
     __syncthreads();
 
     // one superblock: P = s % 2 names its register set and LDS buffer
     auto superblock = [&](int s, auto Pc) {
         constexpr int P = decltype(Pc)::value;
-        constexpr int PW = R1 ? 0 : P;  // the register set
         // this superblock's scales: sc of the wave's blocks as f16 splats,
         // -dmin*m of the min-term operand, d of the lane's output rows
         uint32_t scpk[2][NPW];
@@ -741,7 +738,7 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         uint2 q[2][NPW];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint4 hd = wset[PW].hdr[t];
+            const uint4 hd = wset.hdr[t];
             const float dmin = h2f(hd.x >> 16);
             uint32_t sc2[NPW], mn2[NPW];
 #pragma unroll
@@ -761,16 +758,10 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
 #pragma unroll
             for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
 #pragma unroll
-            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[PW].qc[t][pp];
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset.qc[t][pp];
         }
-        // the next weights go into the registers just read: superblock s + 1
-        // (R1) or s + 2
-        if constexpr (R1) {
-            load_w(min(s + 1, nsb - 1), wset[0]);
-        } else {
-            load_w(min(s + 2, nsb - 1), wset[P]);
-            load_act(min(s + 2, nsb - 1), aset[P]);
-        }
+        // the next superblock's weights go into the registers just read
+        load_w(min(s + 1, nsb - 1), wset);
         // xs of the lane's activation rows for the wave's blocks
         float xv[NU][NBW];
 #pragma unroll
@@ -839,13 +830,10 @@ __global__ __launch_bounds__(512) void k_qmm2_q4k(const QmmArgs a, int vec_store
         }
         // superblock s + 1's activations (loaded a superblock ago) into the
         // other buffer, which every wave finished reading before the last
-        // barrier (after the last superblock this stores unused data)
-        if constexpr (R1) {
-            store_act(P ^ 1, aset[0]);
-            load_act(min(s + 2, nsb - 1), aset[0]);
-        } else {
-            store_act(P ^ 1, aset[P ^ 1]);
-        }
+        // barrier (after the last superblock this stores unused data), then
+        // superblock s + 2's into the registers just stored
+        store_act(P ^ 1, aset);
+        load_act(min(s + 2, nsb - 1), aset);
         __syncthreads();
     };
     for (int s = 0; s < nsb; s += 2) {
@@ -1507,13 +1495,12 @@ extern "C" int qmm_q4k(const void *w, const int8_t *xq, const float *xs, const f
     if (bm == 64 && !off32) bm = 128;
     if (bm == 64) {
         const dim3 grid((unsigned)div_up(n, 32 * QMM2_BM64_NG), (unsigned)div_up(m, 64 * QMM2_BM64_MG));
-        hipLaunchKernelGGL((k_qmm2_q4k<QMM2_BM64_NG, QMM2_BM64_MG, QMM2_BM64_KS, 0, 4, true>), grid, dim3(512), 0, s, a,
-                           vec);
+        hipLaunchKernelGGL((k_qmm2_q4k<QMM2_BM64_NG, QMM2_BM64_MG, QMM2_BM64_KS>), grid, dim3(512), 0, s, a, vec);
     } else if (bm == 128 && off32) {
         // the weight-side tile with 128 activation rows (two groups of 64),
         // one register set of loads in flight: 256 VGPRs, no spills
         const dim3 grid((unsigned)div_up(n, 64), (unsigned)div_up(m, 128));
-        hipLaunchKernelGGL((k_qmm2_q4k<2, 2, 2, 0, 4, true>), grid, dim3(512), 0, s, a, vec);
+        hipLaunchKernelGGL((k_qmm2_q4k<2, 2, 2>), grid, dim3(512), 0, s, a, vec);
     } else if (bm == 128) {
         const dim3 grid((unsigned)div_up(n, QMM_CFG128_BN), (unsigned)div_up(m, QMM_CFG128_BM));
         hipLaunchKernelGGL((k_qmm_q4k<QMM_CFG128>), grid, dim3(QMM_CFG128_NT), 0, s, a);

@@ -286,6 +286,17 @@ def test_moe_prefill_layer_resident_gate_up_shapes(T, E, hidden, inter):
     _layer(T, topk, E, hidden, inter, 180 + T, sample=np.array([0, 1, T // 2, T - 1]))
 
 
+@pytest.mark.parametrize("E", [48, 24, 8])
+def test_moe_prefill_layer_wide_hidden_tile_gate_up(E):
+    """hidden 2304 (past the widest resident activation row): the gate/up
+    GEMM runs on the tile GEMMs -- 16 slots per expert (E = 48, 32-slot
+    table tiles), 32 (E = 24, 48-slot tiles on the weight-side tile) or 96
+    (E = 8, 64-slot tiles on the weight-side tile)."""
+    T, topk, hidden, inter = 96, 8, 2304, 256
+    announce(f"moe prefill layer T={T} E={E} hidden={hidden} inter={inter}")
+    _layer(T, topk, E, hidden, inter, 190 + E, sample=np.array([0, 1, 47, 48, T - 1]))
+
+
 def test_moe_prefill_layer_full_shape_sampled_tokens():
     """512 tokens routed top-8 over 128 experts, gate/up [768, 2048], down
     [2048, 768]: every output column of 12 sampled tokens."""
