@@ -2035,6 +2035,8 @@ struct Q6rRaw {
 // slots whose expert is outside [0, E). Otherwise the segments come from the
 // layer's tile table (nseg, seg_off).
 // FPW weight fragments per wave, 16 / FPW waves: 256 weight rows per unit.
+// Q8A: the activation rows are q8 (xq, xs per 32 values); staging forms
+// each value as xq * xs in f32 and then splits it like an f32 row.
 // Units [u, u1) of this workgroup in the resident-activation GEMMs (nseg
 // segments of nu units each). A workgroup whose run crosses a segment
 // boundary stages twice and ramps its weight loads up twice, so when the
@@ -2062,7 +2064,7 @@ __device__ __forceinline__ void resident_unit_range(int nseg, int nu, int64_t *u
     *u1 = total * (b + 1) / grid;
 }
 
-template <int NSB, bool GROUPED, int FPW, int SL>
+template <int NSB, bool GROUPED, int FPW, int SL, bool Q8A = false>
 __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const int *__restrict__ nseg_p,
                                                        const int *__restrict__ seg_off, int bmt) {
     static_assert(NSB >= 1 && NSB <= Q6R_MAX_NSB, "k <= 1024");
@@ -2208,14 +2210,47 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
         if (tid < SL * LPR) {  // whole waves (SL * LPR is a multiple of 64)
             const int srow = tid / LPR, l = tid % LPR;
             const int sslot = s_slot[srow];
-            const float *xr = a.x + (size_t)(sslot >= 0 ? sslot / a.x_div : 0) * (256 * NSB);
-            float4 xv[CPL];
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) xv[i] = *reinterpret_cast<const float4 *>(xr + 4 * (l + LPR * i));
+            const size_t xrow = (size_t)(sslot >= 0 ? sslot / a.x_div : 0);
+            // f32 rows: float4 chunks; q8 rows (Q8A): the chunk's four codes
+            // and their block's scale, the values xq * xs formed when written
+            float4 xv[Q8A ? 1 : CPL];
+            uint32_t q4v[Q8A ? CPL : 1];
+            float bsv[Q8A ? CPL : 1];
             float am = 0.f;
+            if constexpr (Q8A) {
+                const int8_t *qr = a.xq + xrow * (256 * NSB);
+                const float *sr = a.xs + xrow * (8 * NSB);
 #pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                am = fmaxf(am, fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w))));
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = 4 * (l + LPR * i);
+                    q4v[i] = *reinterpret_cast<const uint32_t *>(qr + c);
+                    bsv[i] = sr[c >> 5];
+                }
+                // |xq * xs| is largest where |xq| is (the rounding is monotonic)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int q0 = abs((int)(int8_t)(q4v[i] & 0xFFu)), q1 = abs((int)(int8_t)((q4v[i] >> 8) & 0xFFu));
+                    const int q2 = abs((int)(int8_t)((q4v[i] >> 16) & 0xFFu)), q3 = abs((int)(int8_t)(q4v[i] >> 24));
+                    am = fmaxf(am, (float)max(max(q0, q1), max(q2, q3)) * fabsf(bsv[i]));
+                }
+            } else {
+                const float *xr = a.x + xrow * (256 * NSB);
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) xv[i] = *reinterpret_cast<const float4 *>(xr + 4 * (l + LPR * i));
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    am = fmaxf(am, fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w))));
+            }
+            auto chunk = [&](int i) -> float4 {
+                if constexpr (Q8A) {
+                    const uint32_t q = q4v[i];
+                    const float bs = bsv[i];
+                    return make_float4((float)(int8_t)(q & 0xFFu) * bs, (float)(int8_t)((q >> 8) & 0xFFu) * bs,
+                                       (float)(int8_t)((q >> 16) & 0xFFu) * bs, (float)(int8_t)(q >> 24) * bs);
+                } else {
+                    return xv[i];
+                }
+            };
 #pragma unroll
             for (int d = 1; d < LPR; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
             const int e = am > 0.f ? ((int)((__float_as_uint(am) >> 23) & 0xFF) - 127) : 0;
@@ -2224,7 +2259,8 @@ __global__ __launch_bounds__(1024 / FPW) void k_qmm6r(const Qmm6Args a, const in
             const float inv = __uint_as_float((uint32_t)(127 - ee) << 23);
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                const float y0 = xv[i].x * sc, y1 = xv[i].y * sc, y2 = xv[i].z * sc, y3 = xv[i].w * sc;
+                const float4 v = chunk(i);
+                const float y0 = v.x * sc, y1 = v.y * sc, y2 = v.z * sc, y3 = v.w * sc;
                 const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1, h2v = (_Float16)y2, h3 = (_Float16)y3;
                 const h4 hi = {h0, h1, h2v, h3};
                 const h4 lo = {(_Float16)(y0 - (float)h0), (_Float16)(y1 - (float)h1), (_Float16)(y2 - (float)h2v),
@@ -2402,7 +2438,7 @@ int q6r_segment_slots(int64_t nslots, int64_t E, int64_t k) { return k <= 768 &&
 // k_qmm6r, one workgroup per CU (k <= 1024): GROUPED derives its segments of
 // sl slots from ids, otherwise they come from the tile table (nseg, seg_off,
 // listed for sl-slot segments).
-template <bool GROUPED>
+template <bool GROUPED, bool Q8A = false>
 void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt, int sl, hipStream_t s) {
     static thread_local int c_dev = -1, c_cus = 0;
     int dev = 0;
@@ -2416,17 +2452,17 @@ void launch_q6r(const Qmm6Args &a, const int *nseg, const int *seg_off, int bmt,
     const dim3 grid((unsigned)c_cus), block(1024 / Q6R_FPW);
     if (sl == 48 && a.k <= 768) {
         switch (a.k / 256) {
-            case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-            case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-            default: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 48>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+            case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 48, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+            case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 48, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+            default: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 48, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
         }
         return;
     }
     switch (a.k / 256) {
-        case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        case 3: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
-        default: hipLaunchKernelGGL((k_qmm6r<4, GROUPED, Q6R_FPW, 32>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 1: hipLaunchKernelGGL((k_qmm6r<1, GROUPED, Q6R_FPW, 32, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 2: hipLaunchKernelGGL((k_qmm6r<2, GROUPED, Q6R_FPW, 32, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        case 3: hipLaunchKernelGGL((k_qmm6r<3, GROUPED, Q6R_FPW, 32, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
+        default: hipLaunchKernelGGL((k_qmm6r<4, GROUPED, Q6R_FPW, 32, Q8A>), grid, block, 0, s, a, nseg, seg_off, bmt); break;
     }
 }
 
@@ -2893,8 +2929,16 @@ extern "C" int moe_qmm_q6k(const void *bank, const int8_t *xq, const float *xs, 
     if (!aligned(xq, 16) || !aligned(xs, 4)) return QMV_EALIGN;
     Qmm6Args a{static_cast<const uint8_t *>(bank), xq, xs, nullptr, y, (int)nslots, (int)n, (int)k, ids, (int)E,
                (int)x_div};
-    const dim3 grid((unsigned)div_up(n, QMM6_MOE_BN), (unsigned)(div_up(nslots, QMM6_MOE_BM) + std::min(E, nslots)));
-    hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_Q8, true>), grid, dim3(QMM6_MOE_NT), 0, (hipStream_t)stream, a);
+    if (QMV_Q6R && k <= 256 * Q6R_MAX_NSB) {
+        // the f32 form's resident GEMM, staging each value as xq * xs
+        // (48-slot segments where they apply, as for f32: at 4,096 slots over
+        // 128 experts, k = 768, 85 us against 108 us with 32-slot ones)
+        launch_q6r<true, true>(a, nullptr, nullptr, Q6R_SLOTS, q6r_segment_slots(nslots, E, k), (hipStream_t)stream);
+    } else {
+        const dim3 grid((unsigned)div_up(n, QMM6_MOE_BN),
+                        (unsigned)(div_up(nslots, QMM6_MOE_BM) + std::min(E, nslots)));
+        hipLaunchKernelGGL((k_qmm_q6k<QMM6_MOE, ACT_Q8, true>), grid, dim3(QMM6_MOE_NT), 0, (hipStream_t)stream, a);
+    }
     QMV_LAUNCH_CHECK();
     return QMV_OK;
 }

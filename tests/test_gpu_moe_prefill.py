@@ -182,7 +182,10 @@ def _check6(ids, n, k, E, x_div, seed, f32, sample=None):
     if f32:
         got = host(qmv.moe_qmm_q6k_f32(dev(bank), dev(x), x_div, dev(ids), ns, n, k, E))
         sl = np.arange(ns) if sample is None else np.asarray(sample)
-        ref = oracle.moe_qmv("q6k", bank, x, x_div, ids, ns, n, k, E)[sl]
+        # a slot's output depends only on its id and its activation row: the
+        # sampled slots alone, one activation row each
+        xs_ = np.ascontiguousarray(x[sl // x_div])
+        ref = oracle.moe_qmv("q6k", bank, xs_, 1, np.ascontiguousarray(ids[sl]), sl.size, n, k, E)
     else:
         xq, xs, _ = oracle.quantize_act_q8(x, rows_x, k)
         got = host(qmv.moe_qmm_q6k(dev(bank), dev(xq), dev(xs), x_div, dev(ids), ns, n, k, E))
@@ -195,9 +198,17 @@ def _check6(ids, n, k, E, x_div, seed, f32, sample=None):
 
 
 @pytest.mark.parametrize("f32", [False, True])
-@pytest.mark.parametrize("case", ["pages", "ragged", "id_chunks", "k1024", "k1280"])
+@pytest.mark.parametrize("case", ["pages", "ragged", "id_chunks", "k1024", "k1280", "layer_down"])
 def test_moe_qmm_q6k(case, f32):
-    if case == "k1024":
+    if case == "layer_down":
+        # the prefill layer's down shape: 512 tokens routed top-8 over 128
+        # experts, [2048, 768] experts, 32 slots per expert on average
+        # (48-slot segments of three 256-value superblocks)
+        lg = synth.moe_logits(512, 128)
+        ids, _ = oracle.moe_route(lg, 512, 128, 8)
+        args = (ids.reshape(-1), 2048, 768, 128, 1, 93)
+        sample = np.sort(np.random.default_rng(5).choice(4096, 24, replace=False))
+    elif case == "k1024":
         # the longest rows the f32 form keeps resident in LDS, a ragged last tile
         ids = ((np.arange(300) * 7) % 5).astype(np.int32)
         args = (ids, 272, 1024, 5, 2, 97)
