@@ -1016,13 +1016,15 @@ __global__ __launch_bounds__(512) void k_qmm_i8_q4k(const QmmArgs a, int vec_sto
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
             out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
-    WSet wset[2];
-    ASet aset[2];
-    load_w(0, wset[0]);
-    load_act(0, aset[0]);
-    load_w(min(1, nsb - 1), wset[1]);
-    load_act(min(1, nsb - 1), aset[1]);
-    store_act(0, aset[0]);
+    // one register set each, as in k_qmm2_q4k: the next superblock's
+    // weights, and the activations of superblock s + 2 once those of s + 1
+    // are in LDS
+    WSet wset;
+    ASet aset;
+    load_w(0, wset);
+    load_act(0, aset);
+    store_act(0, aset);
+    load_act(min(1, nsb - 1), aset);
     __syncthreads();
 
     auto superblock = [&](int s, auto Pc) {
@@ -1035,7 +1037,7 @@ __global__ __launch_bounds__(512) void k_qmm_i8_q4k(const QmmArgs a, int vec_sto
         uint2 q[2][NPW];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint4 hd = wset[P].hdr[t];
+            const uint4 hd = wset.hdr[t];
             const float dmin = h2f(hd.x >> 16);
             uint32_t sc2[NPW], mn2[NPW];
 #pragma unroll
@@ -1052,10 +1054,9 @@ __global__ __launch_bounds__(512) void k_qmm_i8_q4k(const QmmArgs a, int vec_sto
 #pragma unroll
             for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
 #pragma unroll
-            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[P].qc[t][pp];
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset.qc[t][pp];
         }
-        load_w(min(s + 2, nsb - 1), wset[P]);
-        load_act(min(s + 2, nsb - 1), aset[P]);
+        load_w(min(s + 1, nsb - 1), wset);
         float xv[4][NBW];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1107,7 +1108,8 @@ __global__ __launch_bounds__(512) void k_qmm_i8_q4k(const QmmArgs a, int vec_sto
                 for (int u = 0; u < 4; ++u)
                     out[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(amn[t], xb[u], out[t][u], 0, 0, 0);
         }
-        store_act(P ^ 1, aset[P ^ 1]);
+        store_act(P ^ 1, aset);
+        load_act(min(s + 2, nsb - 1), aset);
         __syncthreads();
     };
     for (int s = 0; s < nsb; s += 2) {
