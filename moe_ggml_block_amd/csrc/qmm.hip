@@ -1309,12 +1309,13 @@ __global__ __launch_bounds__(512) void k_qmm4_q4k(const QmmArgs a, const _Float1
         for (int u = 0; u < 4; ++u) out[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     // unconditional loads, indices past the end clamped (exact wait counts)
-    WSet wset[2];
+    // (one register set of weights: the next superblock's are requested
+    // as soon as the current ones are copied out of it)
+    WSet wset;
     {
         ASet a0;
-        load_w(0, wset[0]);
+        load_w(0, wset);
         load_act(0, a0);
-        load_w(min(1, nsb - 1), wset[1]);
         store_act(0, a0);
     }
     __syncthreads();
@@ -1326,7 +1327,7 @@ __global__ __launch_bounds__(512) void k_qmm4_q4k(const QmmArgs a, const _Float1
         uint2 q[2][NPW];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint4 hd = wset[P].hdr[t];
+            const uint4 hd = wset.hdr[t];
             const float dmin = h2f(hd.x >> 16);
             uint32_t mn2[NPW];
 #pragma unroll
@@ -1337,14 +1338,14 @@ __global__ __launch_bounds__(512) void k_qmm4_q4k(const QmmArgs a, const _Float1
 #pragma unroll
             for (int r = 0; r < 4; ++r) dout[t][r] = __shfl(down, 4 * lq + r);
 #pragma unroll
-            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset[P].qc[t][pp];
+            for (int pp = 0; pp < NPW; ++pp) q[t][pp] = wset.qc[t][pp];
         }
         // the activations (stored at the end of this superblock) are
-        // requested before the weights (used two superblocks on), so that
-        // their wait leaves the weight loads in flight
+        // requested before the weights (used by the next superblock), so
+        // that their wait leaves the weight loads in flight
         ASet aset;  // lives within this superblock only (kept in registers)
         load_act(min(s + 1, nsb - 1), aset);
-        load_w(min(s + 2, nsb - 1), wset[P]);
+        load_w(min(s + 1, nsb - 1), wset);
         v4f acc[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
